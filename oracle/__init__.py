@@ -1,0 +1,186 @@
+"""CPU float64 oracle for the CSR sparse-dense operations (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The GPU library never imports, links or calls this
+package; only the tests, the smoke check and the benchmark's CPU-baseline leg
+do.  Definitions and their sources are documented in oracle.c (spops README,
+sections "Usage", "Sparse Addition", "Sparse Matrix Multiplication (SpMM)",
+"Sampled Dense-Dense Matrix Multiplication (SDDMM)", "CSR Transpose").
+
+Host arrays use the storage conventions of the input generators: 'f32' ->
+float32, 'f16' -> float16, 'bf16' -> uint16 bit patterns; int16/int32 indices.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_DT = {"f32": 0, "f16": 1, "bf16": 2}
+_NP = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 with OpenMP and no fast-math; atomic replace of `out`."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-Wall", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = load(_LIB)
+    return _lib
+
+
+def load(path: str):
+    """Load a compiled oracle library and declare its signatures."""
+    L = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.oracle_spmm.argtypes = [i64, i64, i64, vp, vp, i32, vp, i32, vp, i32, i64, vp]
+    L.oracle_sddmm.argtypes = [i64, i64, i64, vp, vp, i32, vp, i64, vp, i64, i32, vp]
+    L.oracle_csr_add.argtypes = [i64, i64, vp, vp, i32, vp, i32, vp, i32, i64]
+    L.oracle_csr_transpose.argtypes = [i64, i64, vp, vp, i32, vp, i64, vp, vp, vp, i32]
+    L.oracle_row_idx.argtypes = [i64, vp, vp, i32]
+    L.oracle_check_csr.argtypes = [i64, i64, vp, vp, i32]
+    L.oracle_decode_array.argtypes = [vp, i32, i64, vp]
+    L.oracle_encode_array.argtypes = [vp, i32, i64, vp]
+    L.oracle_num_threads.restype = i32
+    for f in ("oracle_spmm", "oracle_sddmm", "oracle_csr_add", "oracle_csr_transpose",
+              "oracle_row_idx", "oracle_check_csr"):
+        getattr(L, f).restype = i32
+    return L
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _itype(a: np.ndarray) -> int:
+    if a.dtype == np.int16:
+        return 0
+    if a.dtype == np.int32:
+        return 1
+    raise TypeError(f"index arrays must be int16 or int32, got {a.dtype}")
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype=dtype))
+    return a
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def check_csr(m, n, row_offsets, col_idx) -> int:
+    ro, ci = _c(row_offsets, np.int32), _c(col_idx)
+    return int(lib().oracle_check_csr(m, n, _p(ro), _p(ci), _itype(ci)))
+
+
+def spmm(m: int, row_offsets, col_idx, values, val_dt: str, B, b_dt: str) -> np.ndarray:
+    """C = A @ B in float64, A given by (row_offsets, col_idx, values)."""
+    ro, ci, v = _c(row_offsets, np.int32), _c(col_idx), _c(values, _NP[val_dt])
+    B = _c(B, _NP[b_dt])
+    k, N = B.shape
+    C = np.empty((m, N), dtype=np.float64)
+    rc = lib().oracle_spmm(m, k, N, _p(ro), _p(ci), _itype(ci), _p(v), _DT[val_dt],
+                           _p(B), _DT[b_dt], N, _p(C))
+    assert rc == 0
+    return C
+
+
+def sddmm(row_offsets, col_idx, A, BT, in_dt: str) -> np.ndarray:
+    """out[p] = <A[r(p), :], BT[col(p), :]> in float64 at every mask position."""
+    ro, ci = _c(row_offsets, np.int32), _c(col_idx)
+    A, BT = _c(A, _NP[in_dt]), _c(BT, _NP[in_dt])
+    m, K = A.shape
+    n = BT.shape[0]
+    assert BT.shape[1] == K and len(ro) == m + 1
+    out = np.empty(int(ro[-1]), dtype=np.float64)
+    rc = lib().oracle_sddmm(m, n, K, _p(ro), _p(ci), _itype(ci), _p(A), K, _p(BT), K,
+                            _DT[in_dt], _p(out))
+    assert rc == 0
+    return out
+
+
+def csr_add(row_offsets, col_idx, values, val_dt: str, W, w_dt: str) -> np.ndarray:
+    """Returns a copy of W with the sparse matrix added at its positions."""
+    ro, ci, v = _c(row_offsets, np.int32), _c(col_idx), _c(values, _NP[val_dt])
+    Wc = np.array(W, dtype=_NP[w_dt], copy=True, order="C")
+    m, n = Wc.shape
+    assert len(ro) == m + 1
+    rc = lib().oracle_csr_add(m, n, _p(ro), _p(ci), _itype(ci), _p(v), _DT[val_dt],
+                              _p(Wc), _DT[w_dt], n)
+    assert rc == 0
+    return Wc
+
+
+def csr_transpose(m: int, n: int, row_offsets, col_idx, values=None, out_index_dtype=None):
+    """A^T as (values_T, row_offsets_T[n+1], col_idx_T); values moved bitwise."""
+    ro, ci = _c(row_offsets, np.int32), _c(col_idx)
+    nnz = int(ro[-1])
+    odt = out_index_dtype or (np.int16 if m <= 32767 else np.int32)
+    out_ro = np.empty(n + 1, dtype=np.int32)
+    out_ci = np.empty(nnz, dtype=odt)
+    if values is not None:
+        v = _c(values)
+        out_v = np.empty_like(v)
+        vb = v.dtype.itemsize
+    else:
+        v = out_v = np.empty(0, dtype=np.uint8)
+        vb = 0
+    rc = lib().oracle_csr_transpose(m, n, _p(ro), _p(ci), _itype(ci), _p(v), vb, _p(out_v),
+                                    _p(out_ro), _p(out_ci), _itype(out_ci))
+    assert rc == 0
+    return (out_v if values is not None else None), out_ro, out_ci
+
+
+def row_idx(row_offsets, index_dtype=None) -> np.ndarray:
+    """Rows ordered by stored-entry count, most first, ties by ascending row."""
+    ro = _c(row_offsets, np.int32)
+    m = len(ro) - 1
+    out = np.empty(m, dtype=index_dtype or (np.int16 if m <= 32767 else np.int32))
+    rc = lib().oracle_row_idx(m, _p(ro), _p(out), _itype(out))
+    assert rc == 0
+    return out
+
+
+def decode(bits: np.ndarray, dt: str) -> np.ndarray:
+    b = _c(bits).view(np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib().oracle_decode_array(_p(b), _DT[dt], b.size, _p(out))
+    return out
+
+
+def encode(x: np.ndarray, dt: str) -> np.ndarray:
+    xd = _c(x, np.float64)
+    out = np.empty(xd.shape, dtype=np.uint16)
+    lib().oracle_encode_array(_p(xd), _DT[dt], xd.size, _p(out))
+    return out
+
+
+def to_f64(x: np.ndarray, dt: str) -> np.ndarray:
+    """Exact float64 view of stored values (own decoders for 16-bit formats)."""
+    if dt == "f32":
+        return np.asarray(x, dtype=np.float64)
+    return decode(x, dt)

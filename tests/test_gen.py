@@ -1,0 +1,117 @@
+"""Seeded input generators: reproducibility, CSR invariants, workload statistics."""
+import numpy as np
+import pytest
+
+from unstructured_sparse_linear_amd import gen
+
+
+def check_csr(A: gen.CSR, sorted_rows=True):
+    ro = A.row_offsets
+    assert ro.dtype == np.int32 and len(ro) == A.m + 1 and ro[0] == 0
+    assert np.all(np.diff(ro.astype(np.int64)) >= 0)
+    assert ro[-1] == len(A.col_idx)
+    assert A.col_idx.dtype == (np.int16 if A.n <= 32767 else np.int32)
+    c = A.col_idx.astype(np.int64)
+    assert np.all((c >= 0) & (c < A.n))
+    for r in range(0, A.m, max(1, A.m // 200)):
+        row = c[ro[r]:ro[r + 1]]
+        assert len(np.unique(row)) == len(row), "duplicate column in a row"
+        if sorted_rows:
+            assert np.all(np.diff(row) > 0)
+    if A.values is not None:
+        assert A.values.shape == (A.nnz,)
+
+
+def test_reproducible_and_seed_dependent():
+    a = gen.make_config(1, seed=0).get("A")
+    b = gen.make_config(1, seed=0).get("A")
+    c = gen.make_config(1, seed=1).get("A")
+    assert np.array_equal(a.row_offsets, b.row_offsets) and np.array_equal(a.col_idx, b.col_idx)
+    assert np.array_equal(a.values, b.values)
+    assert not np.array_equal(a.col_idx[:100], c.col_idx[:100])
+
+
+def test_arrays_independent_of_request_order():
+    w1, w2 = gen.make_config(1), gen.make_config(1)
+    b1 = w1.get("B")
+    _ = w2.get("A")
+    assert np.array_equal(b1, w2.get("B"))
+
+
+def test_config1_stats():
+    w = gen.make_config(1)
+    A = w.get("A")
+    check_csr(A)
+    assert (A.m, A.n) == (512, 512) and A.values.dtype == np.float32
+    assert abs(A.nnz / (512 * 512) - 0.02) < 0.002
+    assert w.get("B").shape == (512, 64) and w.get("BT").shape == (512, 64)
+
+
+def test_config2_stats():
+    w = gen.make_config(2)
+    A = w.get("A")
+    check_csr(A)
+    assert A.values.dtype == np.float16
+    assert abs(A.nnz / 4096 ** 2 - 0.01) < 0.0005
+    v = A.values.astype(np.float64)
+    assert abs(v.std() - 0.02) < 0.001
+    assert w.get("B").dtype == np.float16 and w.get("B").shape == (4096, 2048)
+
+
+def test_config3_cross_structure():
+    w = gen.make_config(3, dt="bf16")
+    M = w.get("mask")
+    check_csr(M)
+    assert M.nnz == 450_888 and M.col_idx.dtype == np.int16
+    hot_r, hot_c = M.hot_rows, M.hot_cols
+    assert len(hot_r) == 205 and len(hot_c) == 550
+    rows = np.repeat(np.arange(M.m), M.row_counts())
+    cols = M.col_idx.astype(np.int64)
+    in_cross = np.isin(rows, hot_r) | np.isin(cols, hot_c)
+    assert in_cross.sum() == round(0.9 * 450_888)
+    assert w.get("A").values.dtype == np.uint16
+
+
+def test_config4_symmetric_spd_pattern():
+    w = gen.make_config(4)
+    A = w.get("A")
+    check_csr(A)
+    assert A.m == A.n == 123_440 and A.col_idx.dtype == np.int32
+    assert abs(A.nnz / A.m - 25) < 1.0
+    rows = np.repeat(np.arange(A.m, dtype=np.int64), A.row_counts())
+    cols = A.col_idx.astype(np.int64)
+    key = rows * A.n + cols
+    tkey = cols * A.n + rows
+    order, torder = np.argsort(key), np.argsort(tkey)
+    assert np.array_equal(key[order], tkey[torder])                       # symmetric pattern
+    assert np.array_equal(A.values[order], A.values[torder])              # symmetric values
+    band = np.abs(rows - cols) <= 8
+    assert np.bincount(rows[band], minlength=A.m).min() >= 9              # full band
+    diag = rows == cols
+    off = np.abs(A.values.astype(np.float64))
+    off[diag] = 0
+    assert np.all(A.values[diag] > np.bincount(rows, weights=off, minlength=A.m))
+
+
+def test_config5_zipf_rows():
+    A = gen.make_config(5).get("mask")
+    check_csr(A)
+    cnt = A.row_counts()
+    assert cnt.min() >= 1 and cnt.max() <= 4096
+    assert abs(cnt.sum() - 64 * 16384) < 64
+    assert 0.5 < (cnt == 1).mean() < 0.7
+    assert cnt[cnt >= 1024].sum() / cnt.sum() > 0.6
+
+
+def test_random_csr_options():
+    A = gen.random_csr(3, 40, 50, 0.3, "bf16", empty_row_frac=0.5, shuffle_within_rows=True)
+    check_csr(A, sorted_rows=False)
+    assert (A.row_counts() == 0).sum() > 5
+    B = gen.random_csr(3, 40, 50, 0.3, "f16", integer_values=True)
+    assert set(np.unique(B.values.astype(np.float64))) <= set(range(-3, 4))
+
+
+@pytest.mark.parametrize("kind", ["identity", "reversed", "random"])
+def test_permutations(kind):
+    p = gen.permutation(0, 1000, kind)
+    assert np.array_equal(np.sort(p), np.arange(1000)) and p.dtype == np.int16
