@@ -1,0 +1,206 @@
+/*
+ * spops.h -- C ABI of libspops, unstructured CSR sparse-dense products on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (all defined on the spops README, IST-DASLab):
+ *   spops_spmm            section "Sparse Matrix Multiplication (SpMM)"
+ *   spops_sddmm           section "Sampled Dense-Dense Matrix Multiplication (SDDMM)"
+ *   spops_csr_add         section "Sparse Addition"
+ *   spops_csr_transpose   section "CSR Transpose"
+ *   spops_sort_rows_by_nnz  the row_idx list of section "Usage"
+ *
+ * Sparse layout (section "Usage"): an m x n matrix with nnz stored entries is
+ *   values[nnz]        the stored values (f32, f16 or bf16);
+ *   row_offsets[m+1]   int32; row r owns positions [row_offsets[r], row_offsets[r+1]);
+ *   col_idx[nnz]       column of each stored value; int16 when n <= 32767, else int32;
+ *   row_idx[m]         a permutation of 0..m-1 ordering the rows by entry count.
+ * Section "Important Notes" of the same page asks for contiguous inputs,
+ * int32 row offsets and int16 for the other index lists; int32 is accepted
+ * wherever 16 bits cannot address the extent (n or m above 32767).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller (e.g. a
+ *     torch tensor's storage).  Dense matrices are row-major with an explicit
+ *     leading dimension (elements between consecutive rows) and unit stride
+ *     inside a row.  Element pointers must be aligned to their element size.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  Execute calls never allocate device memory and
+ *     never synchronize; plan-creation calls do both and say so.
+ *   - Validation reads host-side metadata only (sizes, types, pointers).  On
+ *     any error status nothing is launched and no output is written.
+ *     Device-resident index data is not validated: indices outside their
+ *     range never cause out-of-bounds accesses (kernels skip or clamp them)
+ *     but the results for such entries are unspecified.
+ *   - Duplicate (row, column) entries inside a row are a precondition
+ *     violation for spmm/sddmm/csr_add (results unspecified).
+ *   - Floating-point accumulation is in fp32.  Results are deterministic: the
+ *     same call on the same inputs gives bitwise-identical outputs.
+ *   - Asynchronous device errors surface at the caller's next synchronization.
+ *   - Every function is reentrant.  Two calls whose outputs overlap race.
+ */
+#ifndef SPOPS_H
+#define SPOPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPOPS_ABI_VERSION 1
+
+typedef enum spops_status {
+  SPOPS_OK = 0,
+  SPOPS_ERR_NULL = 1,          /* a required pointer is NULL */
+  SPOPS_ERR_SHAPE = 2,         /* negative, inconsistent or too large sizes / leading dims */
+  SPOPS_ERR_DTYPE = 3,         /* unknown dtype or unsupported combination */
+  SPOPS_ERR_INDEX_WIDTH = 4,   /* int16 index list whose extent exceeds 32767 */
+  SPOPS_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than the size query returned */
+  SPOPS_ERR_UNSUPPORTED = 6,   /* valid request this build does not implement */
+  SPOPS_ERR_PLAN = 7,          /* plan built for a different mask */
+  SPOPS_ERR_HIP = 8            /* a HIP runtime call or kernel launch failed */
+} spops_status;
+
+typedef enum spops_dtype { SPOPS_F32 = 0, SPOPS_F16 = 1, SPOPS_BF16 = 2 } spops_dtype;
+typedef enum spops_itype { SPOPS_I16 = 0, SPOPS_I32 = 1 } spops_itype;
+
+/* The two SDDMM kernels of section "Sampled Dense-Dense Matrix Multiplication
+ * (SDDMM)": the general one (named after sputnik on the page) and the
+ * structure-aware one, which is the default there. */
+typedef enum spops_sddmm_backend {
+  SPOPS_SDDMM_STRUCTURE_AWARE = 0,
+  SPOPS_SDDMM_GENERAL = 1
+} spops_sddmm_backend;
+
+/* A CSR matrix (layout above).  `values` may be NULL where only the pattern
+ * is used (an SDDMM output mask, a pattern-only transpose).  `row_idx` may be
+ * NULL where an entry point says so; when given it must be a permutation of
+ * 0..rows-1 (any order is correct; most-entries-first balances the work). */
+typedef struct spops_csr {
+  int64_t rows, cols, nnz;
+  spops_dtype val_type;          /* ignored when values == NULL */
+  spops_itype col_type;          /* SPOPS_I16 requires cols <= 32767 */
+  spops_itype row_idx_type;      /* SPOPS_I16 requires rows <= 32767 */
+  const void* values;            /* [nnz] */
+  const int32_t* row_offsets;    /* [rows+1]: [0] = 0, nondecreasing, [rows] = nnz */
+  const void* row_idx;           /* [rows] */
+  const void* col_idx;           /* [nnz]; need not be sorted within a row */
+} spops_csr;
+
+/* ABI version (SPOPS_ABI_VERSION) and a static description of a status. */
+int spops_abi_version(void);
+const char* spops_status_string(spops_status status);
+
+/* ------------------------------------------------------------------ SpMM --
+ * Section "Sparse Matrix Multiplication (SpMM)": C = A * B.
+ *   A:  rows x cols CSR with values; row_idx required.
+ *   B:  cols x N dense, element type b_type == A->val_type, leading dim ldb >= N.
+ *   C:  rows x N dense, written (not accumulated), leading dim ldc >= N;
+ *       c_type is SPOPS_F32 or b_type (then the fp32 sum is rounded to
+ *       nearest-even once).  Rows of A without entries give zero rows.
+ *   C[r][j] = sum over the entries (r, c, v) of A of v * B[c][j].
+ *   plan (nullable): a schedule from spops_spmm_plan_create for A.  Without
+ *   one no row is split, which is correct but slow for rows with thousands
+ *   of entries.  With one, `workspace` must hold
+ *   spops_spmm_workspace_size(plan, N) bytes (may be 0, then NULL is fine). */
+typedef struct spops_spmm_plan spops_spmm_plan;
+
+spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, int64_t N,
+                        int64_t ldb, void* C, spops_dtype c_type, int64_t ldc,
+                        const spops_spmm_plan* plan, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+
+/* Builds the row-splitting schedule for A's pattern (row_offsets, row_idx):
+ * rows longer than one chunk are split into fixed chunks whose fp32 partial
+ * rows are summed in chunk order, so results stay deterministic.  Allocates
+ * device memory and synchronizes `hip_stream`.  The plan stays valid while
+ * A's row_offsets and row_idx contents are unchanged; it serves any B, N and
+ * dtype. */
+spops_status spops_spmm_plan_create(const spops_csr* A, void* hip_stream,
+                                    spops_spmm_plan** plan);
+spops_status spops_spmm_plan_destroy(spops_spmm_plan* plan);
+/* Bytes of workspace spops_spmm needs with this plan for N columns. */
+spops_status spops_spmm_workspace_size(const spops_spmm_plan* plan, int64_t N, size_t* bytes);
+/* Plan summary: rows split, chunks they were split into, longest row. */
+spops_status spops_spmm_plan_info(const spops_spmm_plan* plan, int64_t* split_rows,
+                                  int64_t* chunks, int64_t* max_row_nnz);
+
+/* ----------------------------------------------------------------- SDDMM --
+ * Section "Sampled Dense-Dense Matrix Multiplication (SDDMM)":
+ *   out[p] = sum_k A[r][k] * BT[c][k]  for every stored position p = (r, c)
+ *   of `mask` (values ignored; row_idx required), in the mask's CSR order.
+ *   A:  mask->rows x K dense, leading dim lda >= K.
+ *   BT: mask->cols x K dense (B transposed), leading dim ldbt >= K.
+ *   A and BT share in_type; out_type is SPOPS_F32 or in_type.
+ *   backend SPOPS_SDDMM_GENERAL: one kernel for any pattern; `plan` ignored.
+ *   backend SPOPS_SDDMM_STRUCTURE_AWARE: runs the rows and columns where the
+ *   mask's entries cluster as dense tiles on the matrix cores and the rest
+ *   with the general kernel; needs a plan for this mask.  With plan == NULL
+ *   a temporary plan is built and freed inside the call (that call then
+ *   allocates and synchronizes).  Both backends compute the same values up
+ *   to fp32 summation order. */
+typedef struct spops_sddmm_plan spops_sddmm_plan;
+
+spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_t lda,
+                         const void* BT, int64_t ldbt, spops_dtype in_type, void* out_values,
+                         spops_dtype out_type, spops_sddmm_backend backend,
+                         const spops_sddmm_plan* plan, void* hip_stream);
+
+/* Finds the clustered rows/columns of the mask and partitions its entries.
+ * A row is dense when its entry count is at least tau * cols; a column is
+ * dense when, over the remaining rows, its count is at least tau * rows.
+ * tau <= 0 selects the default.  tau > 1 disables the dense tiles (all
+ * entries go to the general kernel).  Allocates, synchronizes.  Valid while
+ * the mask's row_offsets / col_idx / row_idx contents are unchanged. */
+spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hip_stream,
+                                     spops_sddmm_plan** plan);
+spops_status spops_sddmm_plan_destroy(spops_sddmm_plan* plan);
+/* Plan summary: dense rows, dense columns, entries covered by dense tiles,
+ * entries left to the general kernel, number of dense tiles. */
+spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_rows,
+                                   int64_t* dense_cols, int64_t* tiled_nnz,
+                                   int64_t* rest_nnz, int64_t* tiles);
+
+/* --------------------------------------------------------------- csr_add --
+ * Section "Sparse Addition", in place on the dense operand:
+ *   W[r][c] = round(W[r][c] + v)  for every entry (r, c, v) of A;
+ * every other element of W keeps its bits.  w_type == A->val_type; the sum
+ * is formed in fp32 and rounded once to w_type (nearest-even), which equals
+ * the correctly rounded sum for f32, f16 and bf16.  W is A->rows x A->cols
+ * with leading dim ldw >= A->cols.  row_idx required. */
+spops_status spops_csr_add(const spops_csr* A, void* W, spops_dtype w_type, int64_t ldw,
+                           void* hip_stream);
+
+/* --------------------------------------------------------- csr_transpose --
+ * Section "CSR Transpose": A^T (cols x rows) as a CSR, i.e. the CSC of A.
+ *   out_row_offsets[cols+1], out_col_idx[nnz] (type out_col_type; SPOPS_I16
+ *   requires rows <= 32767), out_values[nnz] (same dtype as A; ignored when
+ *   A->values is NULL).  Entries of each output row appear in ascending
+ *   source-row order (a stable sort by column), so the result is unique and
+ *   independent of the order of columns inside A's rows.  Index outputs are
+ *   exact; values are moved bit for bit.  row_idx is not used.
+ *   The workspace (size from spops_csr_transpose_workspace_size) is scratch
+ *   for the radix passes; its contents on entry do not matter. */
+spops_status spops_csr_transpose_workspace_size(int64_t rows, int64_t cols, int64_t nnz,
+                                                size_t* bytes);
+spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* out_row_offsets,
+                                 void* out_col_idx, spops_itype out_col_type, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------ row order --
+ * The row_idx list of section "Usage": rows sorted by entry count, most
+ * entries first, equal counts in ascending row order (the page leaves
+ * direction and ties open; this is the reading taken).  `cols` bounds every
+ * row's count (counts are clamped to it).  row_idx_type SPOPS_I16 requires
+ * rows <= 32767. */
+spops_status spops_sort_rows_by_nnz_workspace_size(int64_t rows, int64_t cols, size_t* bytes);
+spops_status spops_sort_rows_by_nnz(const int32_t* row_offsets, int64_t rows, int64_t cols,
+                                    void* row_idx, spops_itype row_idx_type, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPOPS_H */

@@ -93,11 +93,24 @@ uint16_t oracle_encode_bf16(double x) { return encode_small_float(x, 7, -126, 8)
 
 /* ----------------------------------------------------------------- access */
 
+/* Every 16-bit pattern decoded once by the decoders above (speed only). */
+static double f16_table[65536], bf16_table[65536];
+static int tables_ready = 0;
+
+static void init_tables(void) {
+  if (tables_ready) return;
+  for (int i = 0; i < 65536; ++i) {
+    f16_table[i] = oracle_decode_f16((uint16_t)i);
+    bf16_table[i] = oracle_decode_bf16((uint16_t)i);
+  }
+  tables_ready = 1;
+}
+
 static double load_val(const void* p, int dt, int64_t i) {
   switch (dt) {
     case OR_F32: return (double)((const float*)p)[i];
-    case OR_F16: return oracle_decode_f16(((const uint16_t*)p)[i]);
-    default:     return oracle_decode_bf16(((const uint16_t*)p)[i]);
+    case OR_F16: return f16_table[((const uint16_t*)p)[i]];
+    default:     return bf16_table[((const uint16_t*)p)[i]];
   }
 }
 
@@ -143,6 +156,7 @@ int oracle_check_csr(int64_t m, int64_t n, const int32_t* ro, const void* col, i
  * contiguous, float64. */
 int oracle_spmm(int64_t m, int64_t k, int64_t N, const int32_t* ro, const void* col, int ct,
                 const void* val, int vt, const void* B, int bt, int64_t ldb, double* C) {
+  init_tables();
   (void)k;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < m; ++r) {
@@ -170,6 +184,7 @@ int oracle_spmm(int64_t m, int64_t k, int64_t N, const int32_t* ro, const void* 
 int oracle_sddmm(int64_t m, int64_t n, int64_t K, const int32_t* ro, const void* col, int ct,
                  const void* A, int64_t lda, const void* BT, int64_t ldbt, int it,
                  double* out) {
+  init_tables();
   (void)n;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < m; ++r) {
@@ -198,6 +213,7 @@ int oracle_sddmm(int64_t m, int64_t n, int64_t K, const int32_t* ro, const void*
  * other. */
 int oracle_csr_add(int64_t m, int64_t n, const int32_t* ro, const void* col, int ct,
                    const void* val, int vt, void* W, int wt, int64_t ldw) {
+  init_tables();
   (void)n;
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t r = 0; r < m; ++r) {

@@ -1,0 +1,145 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device.
+
+Pointers below are never dereferenced: every call here fails host-side
+validation, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from unstructured_sparse_linear_amd import spops as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spops.h")
+FAKE = 0x10000  # placeholder address; validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(S.LIB_PATH):
+        from unstructured_sparse_linear_amd import build
+        build.build()
+    return S.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spops_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for f in ("spops_spmm", "spops_sddmm", "spops_csr_add", "spops_csr_transpose",
+              "spops_sort_rows_by_nnz"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in spops.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (spops_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(L):
+    assert L.spops_abi_version() == 1
+    for code in range(9):
+        assert L.spops_status_string(code)
+    assert L.spops_status_string(0) == b"ok"
+
+
+def desc(rows=4, cols=4, nnz=4, val_type=0, col_type=0, ri_type=0, values=FAKE, ro=FAKE,
+         ri=FAKE, col=FAKE):
+    d = S.CSRDesc()
+    d.rows, d.cols, d.nnz = rows, cols, nnz
+    d.val_type, d.col_type, d.row_idx_type = val_type, col_type, ri_type
+    d.values, d.row_offsets, d.row_idx, d.col_idx = values, ro, ri, col
+    return d
+
+
+def spmm(L, d, b_type=0, N=8, ldb=8, C=FAKE, c_type=0, ldc=8, plan=None, ws=None, wsb=0):
+    return L.spops_spmm(ctypes.byref(d), FAKE, b_type, N, ldb, C, c_type, ldc, plan, ws, wsb,
+                        None)
+
+
+def test_spmm_rejects_bad_arguments(L):
+    assert L.spops_spmm(None, FAKE, 0, 8, 8, FAKE, 0, 8, None, None, 0, None) == 1
+    assert spmm(L, desc(cols=40000, col_type=0)) == 4        # int16 cannot address 40000
+    assert spmm(L, desc(rows=40000, ri_type=0)) == 4
+    assert spmm(L, desc(), b_type=1) == 3                     # B dtype != values dtype
+    assert spmm(L, desc(val_type=1), b_type=1, c_type=2) == 3  # C must be f32 or B's dtype
+    assert spmm(L, desc(val_type=7), b_type=7) == 3
+    assert spmm(L, desc(), ldb=4) == 2                        # ldb < N
+    assert spmm(L, desc(), ldc=4) == 2
+    assert spmm(L, desc(rows=-1)) == 2
+    assert spmm(L, desc(rows=0, nnz=3)) == 2                  # entries without rows
+    assert spmm(L, desc(ro=None)) == 1
+    assert spmm(L, desc(ri=None)) == 1
+    assert spmm(L, desc(values=None)) == 1
+    assert spmm(L, desc(), C=None) == 1
+    assert spmm(L, desc(), N=0) == 0                          # nothing to do
+
+
+def test_sddmm_rejects_bad_arguments(L):
+    d = desc(values=None)
+    f = L.spops_sddmm
+    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, FAKE, 2, 0, None, None) == 3  # out bf16, in f16
+    assert f(ctypes.byref(d), FAKE, 8, 4, FAKE, 8, 1, FAKE, 0, 0, None, None) == 2  # lda < K
+    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 9, None, None) == 6  # backend
+    assert f(ctypes.byref(d), None, 8, 8, FAKE, 8, 1, FAKE, 0, 1, None, None) == 1
+    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1, None, None) == 1
+    assert f(ctypes.byref(desc(cols=70000, col_type=0)), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 1,
+             None, None) == 4
+    e = desc(nnz=0, col=None)
+    assert f(ctypes.byref(e), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1, None, None) == 0
+
+
+def test_csr_add_rejects_bad_arguments(L):
+    f = L.spops_csr_add
+    assert f(ctypes.byref(desc()), FAKE, 1, 4, None) == 3     # W dtype != values dtype
+    assert f(ctypes.byref(desc()), FAKE, 0, 3, None) == 2     # ldw < cols
+    assert f(ctypes.byref(desc()), None, 0, 4, None) == 1
+
+
+def test_transpose_and_sort_reject_bad_arguments(L):
+    b = ctypes.c_size_t()
+    assert L.spops_csr_transpose_workspace_size(4, 4, 4, ctypes.byref(b)) == 0 and b.value > 0
+    f = L.spops_csr_transpose
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE, 0, FAKE, b.value - 1, None) == 5
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE, 0, None, b.value, None) == 5
+    assert f(ctypes.byref(desc(rows=40000, ri_type=1)), FAKE, FAKE, FAKE, 0, FAKE, 1 << 30,
+             None) == 4                                       # transposed indices need int32
+    assert f(ctypes.byref(desc()), FAKE, None, FAKE, 0, FAKE, b.value, None) == 1
+    assert L.spops_sort_rows_by_nnz_workspace_size(100, 50, ctypes.byref(b)) == 0
+    g = L.spops_sort_rows_by_nnz
+    assert g(FAKE, 100, 50, FAKE, 0, FAKE, b.value - 1, None) == 5
+    assert g(FAKE, 40000, 50, FAKE, 0, FAKE, 1 << 30, None) == 4
+    assert g(None, 100, 50, FAKE, 0, FAKE, b.value, None) == 1
+    assert g(FAKE, 0, 50, None, 0, None, 0, None) == 0
+
+
+def test_python_binding_validates_before_the_library():
+    import torch
+    cpu = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        S.sort_rows_by_nnz(cpu, 4)                            # not a GPU tensor
+    with pytest.raises(ValueError):
+        S.csr_desc(None, torch.zeros(8, dtype=torch.int32)[::2], None,
+                   torch.zeros(3, dtype=torch.int16), 3, 3)   # non-contiguous
+
+
+def test_product_path_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "unstructured_sparse_linear_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text and "oracle.c" not in text, f

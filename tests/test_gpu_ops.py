@@ -1,0 +1,327 @@
+"""GPU parity of every operation against the float64 oracle, on small seeded
+inputs that span several tiles and ragged tails, plus the edge cases.
+
+Index outputs (row order, transpose) must be bit-exact; csr_add must be
+bit-exact (one correctly rounded addition); SpMM / SDDMM values must be within
+1e-5 (f32 inputs) or 2e-3 (f16/bf16 inputs) of the oracle in the RMS-guarded
+relative measure of helpers.rel_err, and bit-exact on integer-valued inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unstructured_sparse_linear_amd as S
+from unstructured_sparse_linear_amd import gen
+from helpers import TORCH_DT, assert_close, csr_dev, dev, host, host_f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    S.lib()
+    yield
+    S.clear_plan_caches()
+    torch.cuda.synchronize()
+
+
+def row_order(A, kind, seed=0):
+    """row_idx on the device: the GPU sort (checked bit-exact elsewhere) or a
+    fixed permutation."""
+    ro = dev(A.row_offsets)
+    if kind == "sorted":
+        return S.sort_rows_by_nnz(ro, A.n)
+    return dev(gen.permutation(seed, A.m, kind))
+
+
+def heavy_csr(seed, m, n, lengths, dt):
+    """CSR whose first rows (in a shuffled order) have the given lengths."""
+    rng = np.random.default_rng(seed)
+    counts = np.concatenate([lengths, rng.integers(0, 6, m - len(lengths))])
+    rng.shuffle(counts)
+    rows = [np.sort(rng.choice(n, int(c), replace=False)) for c in counts]
+    A = gen.csr_from_row_lists(m, n, rows)
+    return A.with_values(gen.normal(rng, A.nnz, dt), dt)
+
+
+# ------------------------------------------------------------ row order --
+
+@pytest.mark.parametrize("m,n,density,kw", [
+    (1, 5, 0.5, {}), (37, 53, 0.2, {"empty_row_frac": 0.3}), (3000, 700, 0.01, {}),
+    (5000, 64, 0.5, {}), (40000, 100, 0.02, {})])
+def test_sort_rows_bitexact(m, n, density, kw):
+    A = gen.random_csr(1, m, n, density, None, **kw)
+    ri = S.sort_rows_by_nnz(dev(A.row_offsets), n)
+    assert ri.dtype == (torch.int16 if m <= 32767 else torch.int32)
+    assert np.array_equal(host(ri), oracle.row_idx(A.row_offsets))
+
+
+def test_sort_rows_heavy_and_int32_output():
+    A = heavy_csr(2, 2000, 5000, [4096 - 1, 3000, 3000, 700, 129], "f32")
+    ri = S.sort_rows_by_nnz(dev(A.row_offsets), A.n, index_dtype=torch.int32)
+    assert np.array_equal(host(ri), oracle.row_idx(A.row_offsets, np.int32))
+
+
+# ------------------------------------------------------------ transpose --
+
+TRANSPOSE_CASES = [
+    (1, 37, 53, 0.2, "f32", {}),
+    (2, 64, 17, 0.5, "f16", {"empty_row_frac": 0.3}),
+    (3, 19, 200, 0.1, "bf16", {"shuffle_within_rows": True}),
+    (4, 300, 5000, 0.02, "f32", {"col_index_dtype": np.int32}),
+    (5, 2500, 300, 0.05, "bf16", {}),
+    (6, 40000, 7, 0.2, "f16", {}),       # rows > 32767: int32 transposed indices
+    (7, 50, 50, 0.0, "f32", {}),         # no entries
+    (8, 1, 1, 1.0, "f32", {}),
+]
+
+
+@pytest.mark.parametrize("seed,m,n,density,dt,kw", TRANSPOSE_CASES)
+def test_transpose_bitexact(seed, m, n, density, dt, kw):
+    A = gen.random_csr(seed, m, n, density, dt, **kw)
+    v, ro, ci = csr_dev(A)
+    vT, roT, ciT = S.csr_transpose(v, ro, ci, m, n)
+    ev, ero, eci = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx, A.values)
+    assert np.array_equal(host(roT), ero)
+    assert np.array_equal(host(ciT), eci)
+    assert np.array_equal(host(vT).view(np.uint8), ev.view(np.uint8))
+
+
+def test_transpose_pattern_only_and_twice():
+    A = gen.random_csr(9, 700, 900, 0.03, "f32")
+    v, ro, ci = csr_dev(A)
+    _, roT, ciT = S.csr_transpose(None, ro, ci, A.m, A.n)
+    _, ero, eci = oracle.csr_transpose(A.m, A.n, A.row_offsets, A.col_idx)
+    assert np.array_equal(host(roT), ero) and np.array_equal(host(ciT), eci)
+    vT, roT, ciT = S.csr_transpose(v, ro, ci, A.m, A.n)
+    v2, ro2, ci2 = S.csr_transpose(vT, roT, ciT, A.n, A.m)
+    assert torch.equal(ro2, ro) and torch.equal(ci2, ci) and torch.equal(v2, v)
+
+
+# ------------------------------------------------------------------ SpMM --
+
+SPMM_CASES = [
+    # seed, m, n, density, dt, N, kw
+    (1, 37, 53, 0.2, "f32", 64, {}),
+    (2, 64, 70, 0.3, "f16", 24, {"empty_row_frac": 0.3}),
+    (3, 200, 190, 0.05, "bf16", 256, {"shuffle_within_rows": True}),
+    (4, 130, 400, 0.1, "f32", 100, {"col_index_dtype": np.int32}),
+    (5, 90, 33, 0.3, "f16", 2050, {}),        # 2050 % 8 != 0: scalar path
+    (6, 300, 500, 0.02, "f32", 1, {}),         # SpMV
+    (7, 300, 500, 0.2, "bf16", 1, {}),
+    (8, 50, 60, 0.2, "f32", 3, {}),            # ragged N
+    (9, 33, 33, 0.0, "f16", 16, {}),           # no entries: all-zero output
+    (10, 1000, 2000, 0.01, "bf16", 512, {}),
+]
+
+
+def run_spmm(A, B, dt, kind="sorted", out_dtype=torch.float32, use_plan=True, seed=0):
+    v, ro, ci = csr_dev(A)
+    ri = row_order(A, kind, seed)
+    return S.spmm(v, ro, ri, ci, dev(B, dt), A.m, out_dtype=out_dtype, use_plan=use_plan)
+
+
+@pytest.mark.parametrize("seed,m,n,density,dt,N,kw", SPMM_CASES)
+@pytest.mark.parametrize("kind", ["sorted", "random"])
+def test_spmm_parity(seed, m, n, density, dt, N, kw, kind):
+    A = gen.random_csr(seed, m, n, density, dt, **kw)
+    B = gen.dense(seed, 100, gen.S_B, (n, N), dt)
+    C = run_spmm(A, B, dt, kind)
+    ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert_close(host_f64(C), ref, dt, "spmm")
+
+
+@pytest.mark.parametrize("kind", ["identity", "reversed"])
+def test_spmm_any_row_order_same_bits(kind):
+    A = gen.random_csr(11, 400, 300, 0.05, "f16")
+    B = gen.dense(11, 100, gen.S_B, (300, 64), "f16")
+    ref = run_spmm(A, B, "f16", "sorted")
+    assert torch.equal(run_spmm(A, B, "f16", kind), ref)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_spmm_low_precision_output(dt):
+    A = gen.random_csr(12, 150, 170, 0.1, dt)
+    B = gen.dense(12, 100, gen.S_B, (170, 64), dt)
+    C = run_spmm(A, B, dt, out_dtype=TORCH_DT[dt])
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    # one rounding of the fp32 sum to the output format
+    assert rel_err(host_f64(C), ref) <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -11) + 1e-5
+
+
+@pytest.mark.parametrize("dt,N", [("f32", 64), ("bf16", 256), ("f16", 8), ("f32", 1),
+                                  ("bf16", 1), ("f16", 30)])
+@pytest.mark.parametrize("use_plan", [True, False])
+def test_spmm_long_rows(dt, N, use_plan):
+    # rows longer than one chunk go through the chunk blocks and the fixup
+    A = heavy_csr(13, 600, 5000, [4500, 3000, 1025, 1024, 600, 513, 512, 200, 129, 128], dt)
+    B = gen.dense(13, 100, gen.S_B, (5000, N), dt)
+    C = run_spmm(A, B, dt, use_plan=use_plan)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert_close(host_f64(C), ref, dt, "spmm long rows")
+    if use_plan:
+        v, ro, ci = csr_dev(A)
+        p = S.SpmmPlan(ro, S.sort_rows_by_nnz(ro, A.n), ci, A.n)
+        info = p.info()
+        assert info["max_row_nnz"] == 4500 and info["split_rows"] == 6
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [1, 64, 40])
+def test_spmm_integer_values_bitexact(dt, N):
+    A = heavy_csr(14, 300, 900, [800, 530, 140], dt)
+    A = A.with_values(gen.f32_to_storage(
+        np.random.default_rng(1).integers(-3, 4, A.nnz).astype(np.float32), dt), dt)
+    B = gen.dense(14, 100, gen.S_B, (900, N), dt, integer_values=True)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    for kind in ("sorted", "random"):
+        assert np.array_equal(host_f64(run_spmm(A, B, dt, kind)), ref)
+
+
+def test_spmm_identity_returns_b():
+    n = 777
+    eye = gen.CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int16),
+                  np.ones(n, np.float32), "f32")
+    B = gen.dense(15, 100, gen.S_B, (n, 48), "f32")
+    assert np.array_equal(host(run_spmm(eye, B, "f32")), B)
+
+
+def test_spmm_deterministic_and_stream_ordered():
+    A = heavy_csr(16, 500, 3000, [2500, 1200, 700], "bf16")
+    B = gen.dense(16, 100, gen.S_B, (3000, 256), "bf16")
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    Bd = dev(B, "bf16")
+    c1 = S.spmm(v, ro, ri, ci, Bd, A.m)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        c2 = S.spmm(v, ro, ri, ci, Bd, A.m)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+# ----------------------------------------------------------------- SDDMM --
+
+SDDMM_CASES = [
+    # seed, m, n, density, dt, K, kw
+    (1, 37, 53, 0.2, "f32", 64, {}),
+    (2, 64, 70, 0.3, "f16", 24, {"empty_row_frac": 0.3}),
+    (3, 200, 190, 0.05, "bf16", 256, {"shuffle_within_rows": True}),
+    (4, 130, 400, 0.1, "f32", 100, {"col_index_dtype": np.int32}),
+    (5, 90, 33, 0.3, "f16", 2048, {}),
+    (6, 60, 80, 0.3, "bf16", 4104, {}),      # K beyond one register pass
+    (7, 50, 60, 0.2, "f32", 7, {}),          # ragged K: scalar path
+    (8, 40, 41, 0.3, "f16", 1, {}),
+    (9, 300, 700, 0.03, "bf16", 32, {}),
+]
+
+
+def cross_csr(seed, m, n, hot_r, hot_c, dt=None):
+    rng = gen.rng_for(seed, 102, 0)
+    M = gen.cross_mask(rng, m, n, 0.05, hot_r / m, hot_c / n, 0.9)
+    return M
+
+
+def run_sddmm(M, Ad, BT, dt, backend, tau=None, out_dtype=torch.float32):
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, M.n)
+    return S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), backend=backend, tau=tau,
+                   out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("seed,m,n,density,dt,K,kw", SDDMM_CASES)
+@pytest.mark.parametrize("backend,tau", [("sputnik", None), ("structure_aware", None),
+                                         ("structure_aware", 1e-9)])
+def test_sddmm_parity(seed, m, n, density, dt, K, kw, backend, tau):
+    M = gen.random_csr(seed, m, n, density, None, **kw)
+    Ad = gen.dense(seed, 100, gen.S_A, (m, K), dt)
+    BT = gen.dense(seed, 100, gen.S_BT, (n, K), dt)
+    out = run_sddmm(M, Ad, BT, dt, backend, tau)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
+    assert_close(host_f64(out), ref, dt, f"sddmm {backend}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("m,n,K", [(300, 700, 64), (520, 300, 96), (129, 1000, 40)])
+def test_sddmm_structure_aware_cross_mask(dt, m, n, K):
+    M = cross_csr(3, m, n, max(1, m // 15), max(1, n // 15))
+    Ad = gen.dense(3, 100, gen.S_A, (m, K), dt)
+    BT = gen.dense(3, 100, gen.S_BT, (n, K), dt)
+    _, ro, ci = csr_dev(M)
+    plan = S.SddmmPlan(ro, ci, m, n, tau=0.02)
+    info = plan.info()
+    assert info["tiled_nnz"] + info["rest_nnz"] == M.nnz
+    assert info["dense_rows"] > 0 and info["dense_cols"] > 0 and info["tiled_nnz"] > 0
+    ri = S.sort_rows_by_nnz(ro, n)
+    out = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
+    assert_close(host_f64(out), ref, dt, "sddmm tiles")
+    out16 = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan, out_dtype=TORCH_DT[dt])
+    assert rel_err(host_f64(out16), ref) <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -11) + 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_sddmm_backends_bitexact_on_integers(dt):
+    m, n, K = 400, 900, 128
+    M = cross_csr(4, m, n, 30, 60)
+    Ad = gen.dense(4, 100, gen.S_A, (m, K), dt, integer_values=True)
+    BT = gen.dense(4, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
+    for backend, tau in [("sputnik", None), ("structure_aware", None),
+                         ("structure_aware", 1e-9), ("structure_aware", 0.02),
+                         ("structure_aware", 2.0)]:
+        out = run_sddmm(M, Ad, BT, dt, backend, tau)
+        assert np.array_equal(host_f64(out), ref), (backend, tau)
+
+
+def test_sddmm_keeps_f16_subnormals():
+    m, n, K = 20, 30, 64
+    M = gen.random_csr(5, m, n, 0.5, None)
+    Ad = (np.full((m, K), 2.0 ** -20) * np.random.default_rng(0).integers(1, 4, (m, K))).astype(np.float16)
+    BT = np.full((n, K), 1024.0, dtype=np.float16)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, "f16")
+    assert np.all(ref > 0)
+    for backend, tau in [("sputnik", None), ("structure_aware", 1e-9)]:
+        assert_close(host_f64(run_sddmm(M, Ad, BT, "f16", backend, tau)), ref, "f16", backend)
+
+
+def test_sddmm_k0_gives_zeros():
+    M = gen.random_csr(6, 10, 12, 0.5, None)
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, 12)
+    out = S.sddmm(ro, ri, ci, torch.empty((10, 0), device="cuda"),
+                  torch.empty((12, 0), device="cuda"), backend="sputnik")
+    assert torch.count_nonzero(out).item() == 0 and out.numel() == M.nnz
+
+
+# --------------------------------------------------------------- csr_add --
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m,n,density,kw", [
+    (57, 83, 0.25, {"shuffle_within_rows": True, "empty_row_frac": 0.1}),
+    (1000, 3000, 0.02, {}), (40000, 40, 0.05, {"col_index_dtype": np.int32})])
+def test_csr_add_bitexact(dt, m, n, density, kw):
+    A = gen.random_csr(21, m, n, density, dt, **kw)
+    W = gen.dense(21, 100, gen.S_W, (m, n), dt, std=1.0)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, n, index_dtype=torch.int32)
+    Wd = dev(W, dt)
+    out = S.csr_add(v, ro, ri, ci, Wd)
+    assert out.data_ptr() == Wd.data_ptr()
+    ref = oracle.csr_add(A.row_offsets, A.col_idx, A.values, dt, W, dt)
+    assert np.array_equal(host(out).view(np.uint8), ref.view(np.uint8))
+
+
+def test_csr_add_rounds_ties_to_even():
+    A = gen.CSR(1, 4, np.array([0, 4], np.int32), np.array([0, 1, 2, 3], np.int16),
+                np.array([2.0 ** -11, 3 * 2.0 ** -11, -(2.0 ** -12), 2.0 ** -24], np.float16), "f16")
+    W = np.array([[1.0, 1.0, 2.0 ** -14, 2.0 ** -24]], np.float16)
+    v, ro, ci = csr_dev(A)
+    out = S.csr_add(v, ro, dev(np.zeros(1, np.int16)), ci, dev(W))
+    ref = oracle.csr_add(A.row_offsets, A.col_idx, A.values, "f16", W, "f16")
+    assert np.array_equal(host(out).view(np.uint16), ref.view(np.uint16))

@@ -3,7 +3,7 @@ oracle.c (on the CPU), rebuild it, and require that at least one pin fails.
 
 Each mutant below is a single textual change of the kind a careless rewrite
 would make: a dropped term, a wrong sign, a wrong index, a lost tie rule, a
-lost stability guarantee.
+lost stability guarantee.  Every mutant keeps all memory accesses in bounds.
 """
 import shutil
 
@@ -41,8 +41,9 @@ MUTANTS = [
      "  for (int64_t r = m - 1; r >= 0; --r) {\n    for (int64_t p = ro[r]; p < ro[r + 1]; ++p) {\n"
      "      int64_t c = load_idx(col, ct, p);\n      int64_t q = next[c]++;",
      [lambda o: T.test_transpose_matches_scipy(o, *T.CASES[0])]),
-    ("row_idx_ascending", "start[maxc - (ro[r + 1] - ro[r]) + 1] += 1;",
-     "start[(ro[r + 1] - ro[r]) + 1] += 1;",
+    ("row_idx_ties_reversed",
+     "  for (int64_t r = 0; r < m; ++r) {\n    int64_t b = maxc - (ro[r + 1] - ro[r]);",
+     "  for (int64_t r = m - 1; r >= 0; --r) {\n    int64_t b = maxc - (ro[r + 1] - ro[r]);",
      [lambda o: T.test_row_idx_is_stable_descending_sort(o, *T.CASES[1])]),
 ]
 

@@ -1,1 +1,27 @@
+"""Unstructured CSR sparse-dense products on AMD Instinct MI355X (gfx950).
 
+SpMM, SDDMM (general and structure-aware), csr_add and csr_transpose over the
+CSR layout of the spops README (values, int32 row_offsets, int16/int32
+col_idx, nnz-sorted row_idx).  The work runs in hand-written HIP kernels
+behind the C ABI in include/spops.h (libspops.so); this package only
+marshals torch tensors into that ABI.  Nothing here falls back to another
+implementation: calls raise if libspops.so is missing.
+"""
+from .spops import (  # noqa: F401
+    SddmmPlan,
+    SpmmPlan,
+    SpopsError,
+    clear_plan_caches,
+    csr_add,
+    csr_transpose,
+    csr_transpose_workspace,
+    lib,
+    sddmm,
+    sort_rows_by_nnz,
+    sort_rows_workspace,
+    spmm,
+)
+
+__all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
+           "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
+           "sort_rows_workspace"]

@@ -1,0 +1,353 @@
+// api.hip -- the extern "C" entry points declared in include/spops.h.
+// Host-side validation of metadata only, then kernel launches on the
+// caller's stream.  See the header for the meaning of every argument.
+#include <math.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "kernels.h"
+#include "spops.h"
+
+using namespace spops;
+
+struct spops_spmm_plan {
+  SpmmSchedule sch;
+  int64_t rows, nnz;
+  const void* ro;
+  const void* row_idx;
+};
+
+struct spops_sddmm_plan {
+  SddmmPlanDev dev;
+};
+
+namespace {
+
+constexpr double kDefaultTau = 0.04;
+
+bool dtype_ok(int d) { return d == SPOPS_F32 || d == SPOPS_F16 || d == SPOPS_BF16; }
+bool itype_ok(int t) { return t == SPOPS_I16 || t == SPOPS_I32; }
+int elem_bytes(int d) { return d == SPOPS_F32 ? 4 : 2; }
+
+// Structural metadata of a CSR.  Values / row_idx are checked only when the
+// operation uses them.
+spops_status check_csr(const spops_csr* A, bool need_values, bool need_row_idx) {
+  if (!A) return SPOPS_ERR_NULL;
+  if (A->rows < 0 || A->cols < 0 || A->nnz < 0) return SPOPS_ERR_SHAPE;
+  if (A->rows > INT32_MAX - 1 || A->cols > INT32_MAX - 1 || A->nnz > INT32_MAX)
+    return SPOPS_ERR_SHAPE;
+  if (A->nnz > 0 && (A->rows == 0 || A->cols == 0)) return SPOPS_ERR_SHAPE;
+  if (!itype_ok(A->col_type)) return SPOPS_ERR_DTYPE;
+  if (A->col_type == SPOPS_I16 && A->cols > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  if (!A->row_offsets) return SPOPS_ERR_NULL;
+  if (A->nnz > 0 && !A->col_idx) return SPOPS_ERR_NULL;
+  if (need_values) {
+    if (!dtype_ok(A->val_type)) return SPOPS_ERR_DTYPE;
+    if (A->nnz > 0 && !A->values) return SPOPS_ERR_NULL;
+  }
+  if (need_row_idx) {
+    if (!itype_ok(A->row_idx_type)) return SPOPS_ERR_DTYPE;
+    if (A->row_idx_type == SPOPS_I16 && A->rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+    if (A->rows > 0 && !A->row_idx) return SPOPS_ERR_NULL;
+  }
+  return SPOPS_OK;
+}
+
+spops_status from_hip(hipError_t e) { return e == hipSuccess ? SPOPS_OK : SPOPS_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+int spops_abi_version(void) { return SPOPS_ABI_VERSION; }
+
+const char* spops_status_string(spops_status s) {
+  switch (s) {
+    case SPOPS_OK: return "ok";
+    case SPOPS_ERR_NULL: return "a required pointer is NULL";
+    case SPOPS_ERR_SHAPE: return "invalid or inconsistent sizes or leading dimensions";
+    case SPOPS_ERR_DTYPE: return "unknown dtype or unsupported dtype combination";
+    case SPOPS_ERR_INDEX_WIDTH: return "int16 index list cannot address this extent";
+    case SPOPS_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPOPS_ERR_UNSUPPORTED: return "unsupported request";
+    case SPOPS_ERR_PLAN: return "plan was built for a different matrix";
+    case SPOPS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+// ---------------------------------------------------------------- SpMM ---
+
+spops_status spops_spmm_plan_create(const spops_csr* A, void* hip_stream,
+                                    spops_spmm_plan** plan) {
+  if (!plan) return SPOPS_ERR_NULL;
+  *plan = nullptr;
+  spops_status st = check_csr(A, false, true);
+  if (st != SPOPS_OK) return st;
+  spops_spmm_plan* p = new (std::nothrow) spops_spmm_plan();
+  if (!p) return SPOPS_ERR_HIP;
+  p->rows = A->rows;
+  p->nnz = A->nnz;
+  p->ro = A->row_offsets;
+  p->row_idx = A->row_idx;
+  hipError_t e = build_spmm_schedule(A->row_offsets, A->row_idx, A->row_idx_type == SPOPS_I32,
+                                     A->rows, A->nnz, kSpmmSplitLen, &p->sch,
+                                     as_stream(hip_stream));
+  if (e != hipSuccess) {
+    delete p;
+    return SPOPS_ERR_HIP;
+  }
+  *plan = p;
+  return SPOPS_OK;
+}
+
+spops_status spops_spmm_plan_destroy(spops_spmm_plan* plan) {
+  if (!plan) return SPOPS_OK;
+  free_spmm_schedule(&plan->sch);
+  delete plan;
+  return SPOPS_OK;
+}
+
+spops_status spops_spmm_workspace_size(const spops_spmm_plan* plan, int64_t N, size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (N < 0) return SPOPS_ERR_SHAPE;
+  *bytes = (plan && plan->sch.S > 0) ? align256((size_t)plan->sch.P * (size_t)N * 4) : 0;
+  return SPOPS_OK;
+}
+
+spops_status spops_spmm_plan_info(const spops_spmm_plan* plan, int64_t* split_rows,
+                                  int64_t* chunks, int64_t* max_row_nnz) {
+  if (!plan) return SPOPS_ERR_NULL;
+  if (split_rows) *split_rows = plan->sch.S;
+  if (chunks) *chunks = plan->sch.P;
+  if (max_row_nnz) *max_row_nnz = plan->sch.max_row;
+  return SPOPS_OK;
+}
+
+spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, int64_t N,
+                        int64_t ldb, void* C, spops_dtype c_type, int64_t ldc,
+                        const spops_spmm_plan* plan, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  spops_status st = check_csr(A, true, true);
+  if (st != SPOPS_OK) return st;
+  if (!dtype_ok(b_type) || !dtype_ok(c_type)) return SPOPS_ERR_DTYPE;
+  if (b_type != A->val_type) return SPOPS_ERR_DTYPE;
+  if (c_type != SPOPS_F32 && c_type != b_type) return SPOPS_ERR_DTYPE;
+  if (N < 0 || ldb < (N > 0 ? N : 1) || ldc < (N > 0 ? N : 1)) return SPOPS_ERR_SHAPE;
+  if (N == 0 || A->rows == 0) return SPOPS_OK;
+  if (!C) return SPOPS_ERR_NULL;
+  if (A->nnz > 0 && !B) return SPOPS_ERR_NULL;
+  if (plan) {
+    if (plan->rows != A->rows || plan->nnz != A->nnz || plan->ro != A->row_offsets ||
+        plan->row_idx != A->row_idx)
+      return SPOPS_ERR_PLAN;
+    size_t need = 0;
+    spops_spmm_workspace_size(plan, N, &need);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SPOPS_ERR_WORKSPACE;
+  }
+  SpmmArgs a{};
+  a.m = A->rows;
+  a.k = A->cols;
+  a.nnz = A->nnz;
+  a.N = N;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.ro = A->row_offsets;
+  a.col = A->col_idx;
+  a.col_i32 = A->col_type == SPOPS_I32;
+  a.val = A->values;
+  a.row_idx = A->row_idx;
+  a.ri_i32 = A->row_idx_type == SPOPS_I32;
+  a.B = B;
+  a.C = C;
+  a.dtype = b_type;
+  a.out_dtype = c_type;
+  if (plan && plan->sch.P > 0) {
+    a.P = plan->sch.P;
+    a.S = plan->sch.S;
+    a.T = plan->sch.T;
+    a.item_pos = plan->sch.item_pos;
+    a.item_chunk = plan->sch.item_chunk;
+    a.split_pos = plan->sch.split_pos;
+    a.split_start = plan->sch.split_start;
+    a.split_end = plan->sch.split_end;
+    a.partial = (float*)workspace;
+  }
+  return from_hip(launch_spmm(a, as_stream(hip_stream)));
+}
+
+// --------------------------------------------------------------- SDDMM ---
+
+spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hip_stream,
+                                     spops_sddmm_plan** plan) {
+  if (!plan) return SPOPS_ERR_NULL;
+  *plan = nullptr;
+  spops_status st = check_csr(mask, false, false);
+  if (st != SPOPS_OK) return st;
+  if (!(tau > 0.0) || isnan(tau)) tau = kDefaultTau;
+  spops_sddmm_plan* p = new (std::nothrow) spops_sddmm_plan();
+  if (!p) return SPOPS_ERR_HIP;
+  hipError_t e = build_sddmm_plan(mask->rows, mask->cols, mask->nnz, mask->row_offsets,
+                                  mask->col_idx, mask->col_type == SPOPS_I32, tau, &p->dev,
+                                  as_stream(hip_stream));
+  if (e != hipSuccess) {
+    delete p;
+    return SPOPS_ERR_HIP;
+  }
+  *plan = p;
+  return SPOPS_OK;
+}
+
+spops_status spops_sddmm_plan_destroy(spops_sddmm_plan* plan) {
+  if (!plan) return SPOPS_OK;
+  free_sddmm_plan(&plan->dev);
+  delete plan;
+  return SPOPS_OK;
+}
+
+spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_rows,
+                                   int64_t* dense_cols, int64_t* tiled_nnz, int64_t* rest_nnz,
+                                   int64_t* tiles) {
+  if (!plan) return SPOPS_ERR_NULL;
+  if (dense_rows) *dense_rows = plan->dev.n_rows_hot;
+  if (dense_cols) *dense_cols = plan->dev.n_cols_hot;
+  if (tiled_nnz) *tiled_nnz = plan->dev.tiled_nnz;
+  if (rest_nnz) *rest_nnz = plan->dev.rest_nnz;
+  if (tiles) *tiles = plan->dev.tiles;
+  return SPOPS_OK;
+}
+
+spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_t lda,
+                         const void* BT, int64_t ldbt, spops_dtype in_type, void* out_values,
+                         spops_dtype out_type, spops_sddmm_backend backend,
+                         const spops_sddmm_plan* plan, void* hip_stream) {
+  spops_status st = check_csr(mask, false, false);
+  if (st != SPOPS_OK) return st;
+  if (!dtype_ok(in_type) || !dtype_ok(out_type)) return SPOPS_ERR_DTYPE;
+  if (out_type != SPOPS_F32 && out_type != in_type) return SPOPS_ERR_DTYPE;
+  if (backend != SPOPS_SDDMM_STRUCTURE_AWARE && backend != SPOPS_SDDMM_GENERAL)
+    return SPOPS_ERR_UNSUPPORTED;
+  if (K < 0 || lda < (K > 0 ? K : 1) || ldbt < (K > 0 ? K : 1)) return SPOPS_ERR_SHAPE;
+  if (mask->nnz == 0) return SPOPS_OK;
+  if (!out_values) return SPOPS_ERR_NULL;
+  if (K > 0 && (!A || !BT)) return SPOPS_ERR_NULL;
+  hipStream_t s = as_stream(hip_stream);
+
+  SddmmArgs g{};
+  g.m = mask->rows;
+  g.n = mask->cols;
+  g.K = K;
+  g.lda = lda;
+  g.ldbt = ldbt;
+  g.ro = mask->row_offsets;
+  g.pos = nullptr;
+  g.count = mask->nnz;
+  g.col = mask->col_idx;
+  g.col_i32 = mask->col_type == SPOPS_I32;
+  g.A = A;
+  g.BT = BT;
+  g.out = out_values;
+  g.dtype = in_type;
+  g.out_dtype = out_type;
+
+  const bool tiles_ok = in_type != SPOPS_F32 && K > 0 && K % 8 == 0 && lda % 8 == 0 &&
+                        ldbt % 8 == 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
+  if (backend == SPOPS_SDDMM_GENERAL || !tiles_ok) return from_hip(launch_sddmm_general(g, s));
+
+  spops_sddmm_plan* own = nullptr;
+  if (plan) {
+    if (plan->dev.m != mask->rows || plan->dev.n != mask->cols || plan->dev.nnz != mask->nnz ||
+        plan->dev.mask_ro != mask->row_offsets || plan->dev.mask_col != mask->col_idx)
+      return SPOPS_ERR_PLAN;
+  } else {
+    st = spops_sddmm_plan_create(mask, kDefaultTau, hip_stream, &own);
+    if (st != SPOPS_OK) return st;
+    plan = own;
+  }
+  const SddmmPlanDev& P = plan->dev;
+  hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type, s);
+  if (e == hipSuccess && P.rest_nnz > 0) {
+    SddmmArgs r = g;
+    r.ro = P.rest_ro;
+    r.pos = P.rest_pos;
+    r.count = P.rest_nnz;
+    e = launch_sddmm_general(r, s);
+  }
+  if (own) {
+    hipError_t e2 = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = e2;
+    spops_sddmm_plan_destroy(own);
+  }
+  return from_hip(e);
+}
+
+// ------------------------------------------------------------- csr_add ---
+
+spops_status spops_csr_add(const spops_csr* A, void* W, spops_dtype w_type, int64_t ldw,
+                           void* hip_stream) {
+  spops_status st = check_csr(A, true, true);
+  if (st != SPOPS_OK) return st;
+  if (!dtype_ok(w_type)) return SPOPS_ERR_DTYPE;
+  if (w_type != A->val_type) return SPOPS_ERR_DTYPE;
+  if (ldw < (A->cols > 0 ? A->cols : 1)) return SPOPS_ERR_SHAPE;
+  if (A->nnz == 0) return SPOPS_OK;
+  if (!W) return SPOPS_ERR_NULL;
+  return from_hip(launch_csr_add(A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx,
+                                 A->col_type == SPOPS_I32, A->values, W, ldw, w_type,
+                                 as_stream(hip_stream)));
+}
+
+// ------------------------------------------------------- csr_transpose ---
+
+spops_status spops_csr_transpose_workspace_size(int64_t rows, int64_t cols, int64_t nnz,
+                                                size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (rows < 0 || cols < 0 || nnz < 0 || nnz > INT32_MAX) return SPOPS_ERR_SHAPE;
+  *bytes = transpose_workspace_bytes(rows, cols, nnz);
+  return SPOPS_OK;
+}
+
+spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* out_row_offsets,
+                                 void* out_col_idx, spops_itype out_col_type, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  spops_status st = check_csr(A, A && A->values != nullptr, false);
+  if (st != SPOPS_OK) return st;
+  if (!itype_ok(out_col_type)) return SPOPS_ERR_DTYPE;
+  if (out_col_type == SPOPS_I16 && A->rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  if (!out_row_offsets) return SPOPS_ERR_NULL;
+  if (A->nnz > 0 && (!out_col_idx || (A->values && !out_values))) return SPOPS_ERR_NULL;
+  const size_t need = transpose_workspace_bytes(A->rows, A->cols, A->nnz);
+  if (!workspace || workspace_bytes < need) return SPOPS_ERR_WORKSPACE;
+  return from_hip(launch_csr_transpose(
+      A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx, A->col_type == SPOPS_I32,
+      A->values, A->values ? elem_bytes(A->val_type) : 0, out_values, out_row_offsets,
+      out_col_idx, out_col_type == SPOPS_I32, workspace, as_stream(hip_stream)));
+}
+
+// ------------------------------------------------------------ row order ---
+
+spops_status spops_sort_rows_by_nnz_workspace_size(int64_t rows, int64_t cols, size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (rows < 0 || cols < 0 || rows > INT32_MAX - 1 || cols > INT32_MAX - 1) return SPOPS_ERR_SHAPE;
+  *bytes = sort_rows_workspace_bytes(rows, cols);
+  return SPOPS_OK;
+}
+
+spops_status spops_sort_rows_by_nnz(const int32_t* row_offsets, int64_t rows, int64_t cols,
+                                    void* row_idx, spops_itype row_idx_type, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
+  if (rows < 0 || cols < 0 || rows > INT32_MAX - 1 || cols > INT32_MAX - 1) return SPOPS_ERR_SHAPE;
+  if (!itype_ok(row_idx_type)) return SPOPS_ERR_DTYPE;
+  if (row_idx_type == SPOPS_I16 && rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  if (rows == 0) return SPOPS_OK;
+  if (!row_offsets || !row_idx) return SPOPS_ERR_NULL;
+  if (!workspace || workspace_bytes < sort_rows_workspace_bytes(rows, cols))
+    return SPOPS_ERR_WORKSPACE;
+  return from_hip(launch_sort_rows(row_offsets, rows, cols, row_idx, row_idx_type == SPOPS_I32,
+                                   workspace, as_stream(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// common.h -- device helpers shared by the gfx950 kernels of libspops.
+//
+// Element formats: f32 (float), f16 (IEEE binary16, _Float16) and bf16
+// (bfloat16 kept as its 16-bit pattern).  All arithmetic is fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spops {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+// ------------------------------------------------------------ conversions --
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float((uint32_t)x.bits << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// v_cvt_f16_f32 rounds to nearest even and keeps subnormals.
+template <>
+__device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+
+// Round to nearest even on the bit pattern; NaN stays a quiet NaN.
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  bf16_t r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    r.bits = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    r.bits = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+  return r;
+}
+
+// Unpack 16-bit pairs held in one 32-bit word.
+__device__ __forceinline__ float lo_f32(uint32_t w, _Float16*) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hi_f32(uint32_t w, _Float16*) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ float lo_f32(uint32_t w, bf16_t*) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w, bf16_t*) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t bits16(T x) {
+  return __builtin_bit_cast(uint16_t, x);
+}
+template <>
+__device__ __forceinline__ uint16_t bits16<bf16_t>(bf16_t x) { return x.bits; }
+
+// --------------------------------------------------------------- indices --
+
+// Index lists are int16 or int32.  Negative (or >= extent) values are
+// treated as out of range by the callers.
+template <typename I>
+__device__ __forceinline__ int load_index(const I* p, int64_t i) {
+  return (int)p[i];
+}
+
+// ------------------------------------------------------------ wave tools --
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T wave_uniform(T x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64), fixed order:
+// every lane of the group ends up with the same value.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Largest r in [lo, hi) with ro[r] <= p, assuming ro nondecreasing on that
+// range and ro[lo] <= p.  Used to find the row owning position p.
+__device__ __forceinline__ int64_t upper_row(const int32_t* ro, int64_t lo, int64_t hi,
+                                             int64_t p) {
+  // invariant: ro[lo] <= p, answer in [lo, hi)
+  while (hi - lo > 1) {
+    int64_t mid = lo + ((hi - lo) >> 1);
+    if ((int64_t)ro[mid] <= p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace spops

@@ -1,0 +1,72 @@
+// csr_add.hip -- W += A in place for a CSR matrix A and a dense row-major W
+// on gfx950 (spops README, section "Sparse Addition").
+//
+// Each stored entry (r, c, v) is an independent read-modify-write of one
+// element of W: the sum is formed in fp32 and rounded once to W's format.
+// For f16 and bf16 that equals the correctly rounded sum, since an fp32
+// intermediate (24 bits) is at least 2p+1 bits for p = 11 or 8 (Figueroa,
+// "When is double rounding innocuous?", 1995); for f32 it is the single
+// rounding itself.  Entries are spread evenly over lanes (one entry per lane
+// per round, consecutive entries on consecutive lanes), which keeps rows of
+// any length balanced; each lane finds its row by walking forward from the
+// row of the wave's first entry.  Entries are unique within a row, so no two
+// lanes touch the same element.
+#include "common.h"
+#include "kernels.h"
+
+namespace spops {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kRounds = 4;  // entries per lane
+
+template <typename VT, typename IT>
+__global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, int64_t nnz,
+                                                         const int32_t* ro, const IT* col,
+                                                         const VT* val, VT* W, int64_t ldw) {
+  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  const int64_t wb = wave * (kWave * kRounds);
+  if (wb >= nnz) return;
+  int64_t r = wave_uniform((int)upper_row(ro, 0, m, wb));
+  const int lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t p = wb + q * kWave + lane;
+    if (p >= nnz) break;
+    while (r < m - 1 && (int64_t)ro[r + 1] <= p) ++r;
+    const int c = (int)col[p];
+    if ((unsigned)c >= (unsigned)n) continue;
+    VT* w = W + r * ldw + c;
+    *w = from_f32<VT>(to_f32(*w) + to_f32(val[p]));
+  }
+}
+
+template <typename VT>
+hipError_t launch_vt(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
+                     int col_i32, const void* val, void* W, int64_t ldw, hipStream_t s) {
+  const int64_t waves = (nnz + kWave * kRounds - 1) / (kWave * kRounds);
+  const dim3 grid((unsigned)((waves * kWave + kBlock - 1) / kBlock));
+  if (col_i32)
+    hipLaunchKernelGGL((csr_add_kernel<VT, int32_t>), grid, dim3(kBlock), 0, s, m, n, nnz, ro,
+                       (const int32_t*)col, (const VT*)val, (VT*)W, ldw);
+  else
+    hipLaunchKernelGGL((csr_add_kernel<VT, int16_t>), grid, dim3(kBlock), 0, s, m, n, nnz, ro,
+                       (const int16_t*)col, (const VT*)val, (VT*)W, ldw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_csr_add(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
+                          int col_i32, const void* val, void* W, int64_t ldw, int dtype,
+                          hipStream_t s) {
+  if (nnz <= 0 || m <= 0) return hipSuccess;
+  switch (dtype) {
+    case kF32: return launch_vt<float>(m, n, nnz, ro, col, col_i32, val, W, ldw, s);
+    case kF16: return launch_vt<_Float16>(m, n, nnz, ro, col, col_i32, val, W, ldw, s);
+    case kBF16: return launch_vt<bf16_t>(m, n, nnz, ro, col, col_i32, val, W, ldw, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace spops

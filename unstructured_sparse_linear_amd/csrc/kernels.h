@@ -1,0 +1,138 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to libspops).
+// The C ABI layer (api.hip) validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spops {
+
+// Round a byte count up to 256 so sub-buffers carved from one workspace stay
+// aligned for vector access.
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------------ scan --
+// Exclusive prefix sum of n uint32 values (in may equal out).  If `total` is
+// non-null the grand total is stored there (device pointer).
+size_t scan_workspace_bytes(int64_t n);
+hipError_t exclusive_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint32_t* total,
+                              void* ws, hipStream_t s);
+
+// --------------------------------------------------------- csr transpose --
+size_t transpose_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz);
+hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
+                                const void* col, int col_i32, const void* val, int val_bytes,
+                                void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
+                                void* ws, hipStream_t s);
+
+// --------------------------------------------------------- row ordering --
+size_t sort_rows_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_sort_rows(const int32_t* ro, int64_t rows, int64_t cols, void* row_idx,
+                            int row_idx_i32, void* ws, hipStream_t s);
+
+// Stable sort of n keys in [0, 2^bits) with uint32 payload 0..n-1 (the
+// source position).  Results land in sorted_keys / sorted_vals.  Used by the
+// plans.  Workspace from radix_pairs_workspace_bytes.
+size_t radix_pairs_workspace_bytes(int64_t n);
+hipError_t radix_sort_u32_iota(const uint32_t* keys, int64_t n, int bits, uint32_t* sorted_keys,
+                               uint32_t* sorted_vals, void* ws, hipStream_t s);
+
+// ------------------------------------------------------------------ SpMM --
+// Rows with more entries than kSpmmSplitLen are cut by the plan into chunks of
+// kSpmmChunkLen entries, one workgroup per chunk.
+constexpr int32_t kSpmmSplitLen = 128;
+constexpr int32_t kSpmmChunkLen = 512;
+
+struct SpmmArgs {
+  int64_t m, k, nnz, N, ldb, ldc;
+  const int32_t* ro;
+  const void* col;
+  int col_i32;
+  const void* val;
+  const void* row_idx;
+  int ri_i32;
+  const void* B;
+  void* C;
+  int dtype;      // value / B dtype
+  int out_dtype;  // C dtype
+  // row-splitting schedule (P == 0: none)
+  int64_t P;            // number of chunk items of split rows
+  int64_t S;            // number of split rows
+  int32_t T;            // chunk length; rows longer than T are split
+  const int32_t* item_pos;    // [P] position in row_idx of the chunk's row
+  const int32_t* item_chunk;  // [P] chunk number within its row
+  const int32_t* split_pos;   // [S] position in row_idx of each multi-chunk row
+  const int32_t* split_start; // [S] first item of each multi-chunk row
+  const int32_t* split_end;   // [S] one past its last item
+  float* partial;             // [P][N]
+};
+hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
+
+// Row-splitting schedule for SpMM, built on the device.  chunk = T.
+struct SpmmSchedule {
+  int64_t P = 0, S = 0, max_row = 0;
+  int32_t T = 0;
+  int32_t* item_pos = nullptr;
+  int32_t* item_chunk = nullptr;
+  int32_t* split_pos = nullptr;
+  int32_t* split_start = nullptr;
+  int32_t* split_end = nullptr;
+  void* mem = nullptr;  // owning allocation
+};
+hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i32, int64_t m,
+                               int64_t nnz, int32_t T, SpmmSchedule* out, hipStream_t s);
+void free_spmm_schedule(SpmmSchedule* sch);
+
+// ----------------------------------------------------------------- SDDMM --
+struct SddmmArgs {
+  int64_t m, n, K, lda, ldbt;
+  const int32_t* ro;     // row offsets of the entries to compute
+  const int32_t* pos;    // nullable: entry j is mask position pos[j]; else j itself
+  int64_t count;         // entries to compute (== ro[m])
+  const void* col;       // mask column indices (indexed by mask position)
+  int col_i32;
+  const void* A;
+  const void* BT;
+  void* out;             // indexed by mask position
+  int dtype, out_dtype;
+};
+hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s);
+
+// Structure-aware SDDMM plan (device data) and its dense-tile kernel.
+struct SddmmPlanDev {
+  int64_t m = 0, n = 0, nnz = 0;
+  double tau = 0;
+  int64_t n_rows_hot = 0, n_cols_hot = 0;   // dense rows, dense columns
+  int64_t tiled_nnz = 0, rest_nnz = 0, tiles = 0;
+  int64_t tiles_a = 0;        // tiles of region A (dense rows x all columns)
+  int64_t tiles_a_cols = 0;   // tile columns of region A
+  int64_t tiles_b_cols = 0;   // tile columns of region B (other rows x dense columns)
+  int64_t n_rows_cold = 0;    // rows of region B
+  int32_t* hot_rows = nullptr;   // [n_rows_hot]
+  int32_t* cold_rows = nullptr;  // [n_rows_cold]
+  int32_t* hot_cols = nullptr;   // [n_cols_hot]
+  int32_t* tile_start = nullptr; // [tiles+1] entry ranges per tile
+  int32_t* ent_pos = nullptr;    // [tiled_nnz] mask position
+  int32_t* ent_rc = nullptr;     // [tiled_nnz] (local row << 16) | local col
+  int32_t* rest_ro = nullptr;    // [m+1]
+  int32_t* rest_pos = nullptr;   // [rest_nnz]
+  void* mem = nullptr;
+  // identity of the mask it was built for
+  const void* mask_ro = nullptr;
+  const void* mask_col = nullptr;
+};
+hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
+                            const void* col, int col_i32, double tau, SddmmPlanDev* out,
+                            hipStream_t s);
+void free_sddmm_plan(SddmmPlanDev* p);
+hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, int64_t lda,
+                              const void* BT, int64_t ldbt, int dtype, void* out, int out_dtype,
+                              hipStream_t s);
+
+// --------------------------------------------------------------- csr_add --
+hipError_t launch_csr_add(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
+                          int col_i32, const void* val, void* W, int64_t ldw, int dtype,
+                          hipStream_t s);
+
+}  // namespace spops

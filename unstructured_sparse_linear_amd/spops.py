@@ -1,0 +1,368 @@
+"""Python binding of libspops (ctypes).  Argument marshalling only: every step
+of every operation runs in the HIP kernels behind the C ABI in
+include/spops.h; PyTorch provides device memory and the current stream.
+
+The signatures follow the spops README (IST-DASLab), sections "Sparse
+Addition", "Sparse Matrix Multiplication (SpMM)", "Sampled Dense-Dense Matrix
+Multiplication (SDDMM)" and "CSR Transpose"; section "Important Notes" asks
+for contiguous inputs, int32 row offsets and int16 for the other index lists
+(int32 is accepted where 16 bits cannot address the extent).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from collections import OrderedDict
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspops.so")
+
+F32, F16, BF16 = 0, 1, 2
+I16, I32 = 0, 1
+STRUCTURE_AWARE, GENERAL = 0, 1
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_IT = {torch.int16: I16, torch.int32: I32}
+_BACKENDS = {"structure_aware": STRUCTURE_AWARE, "sputnik": GENERAL, "general": GENERAL}
+
+STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "dtype", 4: "index width",
+          5: "workspace", 6: "unsupported", 7: "plan mismatch", 8: "HIP error"}
+
+
+class SpopsError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code} ({msg})")
+        self.code = code
+
+
+class CSRDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("val_type", ctypes.c_int), ("col_type", ctypes.c_int),
+                ("row_idx_type", ctypes.c_int), ("values", ctypes.c_void_p),
+                ("row_offsets", ctypes.c_void_p), ("row_idx", ctypes.c_void_p),
+                ("col_idx", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspops.so; raises if it was not built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libspops.so not found at {LIB_PATH}; build it with "
+                               "`python -m unstructured_sparse_linear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        P = ctypes.POINTER
+        cp = P(CSRDesc)
+        sigs = {
+            "spops_abi_version": ([], i32),
+            "spops_status_string": ([i32], ctypes.c_char_p),
+            "spops_spmm": ([cp, vp, i32, i64, i64, vp, i32, i64, vp, vp, sz, vp], i32),
+            "spops_spmm_plan_create": ([cp, vp, P(vp)], i32),
+            "spops_spmm_plan_destroy": ([vp], i32),
+            "spops_spmm_workspace_size": ([vp, i64, P(sz)], i32),
+            "spops_spmm_plan_info": ([vp, P(i64), P(i64), P(i64)], i32),
+            "spops_sddmm": ([cp, vp, i64, i64, vp, i64, i32, vp, i32, i32, vp, vp], i32),
+            "spops_sddmm_plan_create": ([cp, ctypes.c_double, vp, P(vp)], i32),
+            "spops_sddmm_plan_destroy": ([vp], i32),
+            "spops_sddmm_plan_info": ([vp, P(i64), P(i64), P(i64), P(i64), P(i64)], i32),
+            "spops_csr_add": ([cp, vp, i32, i64, vp], i32),
+            "spops_csr_transpose_workspace_size": ([i64, i64, i64, P(sz)], i32),
+            "spops_csr_transpose": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
+            "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
+            "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
+        }
+        for name, (args, res) in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        msg = lib().spops_status_string(code)
+        raise SpopsError(fn, code, msg.decode() if msg else STATUS.get(code, "?"))
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, dtypes=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+
+
+def _index_type(t: torch.Tensor, name: str, extent: int) -> int:
+    _require(t, name, (torch.int16, torch.int32))
+    if t.dtype == torch.int16 and extent > 32767:
+        raise ValueError(f"{name} is int16 but must address {extent} entries; use int32")
+    return _IT[t.dtype]
+
+
+def csr_desc(values, row_offsets, row_idx, col_idx, m: int, n: int) -> CSRDesc:
+    """Marshal a CSR given as tensors into the C descriptor."""
+    _require(row_offsets, "row_offsets", (torch.int32,))
+    if row_offsets.numel() != m + 1:
+        raise ValueError(f"row_offsets must have m+1 = {m + 1} entries")
+    nnz = col_idx.numel()
+    d = CSRDesc()
+    d.rows, d.cols, d.nnz = m, n, nnz
+    d.col_type = _index_type(col_idx, "col_idx", n)
+    d.row_offsets = row_offsets.data_ptr()
+    d.col_idx = _ptr(col_idx)
+    if values is not None:
+        _require(values, "values", tuple(_DT))
+        if values.numel() != nnz:
+            raise ValueError("values and col_idx must have the same length")
+        d.val_type = _DT[values.dtype]
+        d.values = _ptr(values)
+    if row_idx is not None:
+        d.row_idx_type = _index_type(row_idx, "row_idx", m)
+        if row_idx.numel() != m:
+            raise ValueError(f"row_idx must have m = {m} entries")
+        d.row_idx = _ptr(row_idx)
+    return d
+
+
+# ------------------------------------------------------------- plans -----
+
+class SpmmPlan:
+    """Row-splitting schedule of one CSR pattern (row_offsets + row_idx)."""
+
+    def __init__(self, row_offsets: torch.Tensor, row_idx: torch.Tensor,
+                 col_idx: torch.Tensor, n: int):
+        m = row_offsets.numel() - 1
+        self._keep = (row_offsets, row_idx)
+        d = csr_desc(None, row_offsets, row_idx, col_idx, m, n)
+        h = ctypes.c_void_p()
+        _check("spops_spmm_plan_create", lib().spops_spmm_plan_create(
+            ctypes.byref(d), _stream(row_offsets), ctypes.byref(h)))
+        self.handle = h
+        self._ws = {}
+
+    def info(self):
+        s, c, mx = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check("spops_spmm_plan_info", lib().spops_spmm_plan_info(
+            self.handle, ctypes.byref(s), ctypes.byref(c), ctypes.byref(mx)))
+        return {"split_rows": s.value, "chunks": c.value, "max_row_nnz": mx.value}
+
+    def workspace(self, N: int, device) -> Optional[torch.Tensor]:
+        if N not in self._ws:
+            b = ctypes.c_size_t()
+            _check("spops_spmm_workspace_size",
+                   lib().spops_spmm_workspace_size(self.handle, N, ctypes.byref(b)))
+            self._ws[N] = torch.empty(b.value, dtype=torch.uint8, device=device) \
+                if b.value else None
+        return self._ws[N]
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.spops_spmm_plan_destroy(h)
+            self.handle = None
+
+
+class SddmmPlan:
+    """Dense-row / dense-column detection and entry partition of one mask."""
+
+    def __init__(self, row_offsets: torch.Tensor, col_idx: torch.Tensor, m: int, n: int,
+                 tau: Optional[float] = None):
+        self._keep = (row_offsets, col_idx)
+        d = csr_desc(None, row_offsets, None, col_idx, m, n)
+        h = ctypes.c_void_p()
+        if tau is None:
+            tau = float(os.environ.get("SPOPS_HOT_DENSITY", "0"))
+        _check("spops_sddmm_plan_create", lib().spops_sddmm_plan_create(
+            ctypes.byref(d), ctypes.c_double(tau), _stream(row_offsets), ctypes.byref(h)))
+        self.handle = h
+
+    def info(self):
+        v = [ctypes.c_int64() for _ in range(5)]
+        _check("spops_sddmm_plan_info",
+               lib().spops_sddmm_plan_info(self.handle, *[ctypes.byref(x) for x in v]))
+        keys = ("dense_rows", "dense_cols", "tiled_nnz", "rest_nnz", "tiles")
+        return dict(zip(keys, (x.value for x in v)))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.spops_sddmm_plan_destroy(h)
+            self.handle = None
+
+
+class _PlanCache:
+    def __init__(self, cap: int = 16):
+        self.cap = cap
+        self.d: "OrderedDict[tuple, object]" = OrderedDict()
+
+    def get(self, key, make):
+        if key in self.d:
+            self.d.move_to_end(key)
+            return self.d[key]
+        v = make()
+        self.d[key] = v
+        if len(self.d) > self.cap:
+            self.d.popitem(last=False)
+        return v
+
+    def clear(self):
+        self.d.clear()
+
+
+_spmm_plans = _PlanCache()
+_sddmm_plans = _PlanCache()
+
+
+def _tkey(t: torch.Tensor):
+    return (t.data_ptr(), t.numel(), t.dtype, t._version)
+
+
+def clear_plan_caches():
+    _spmm_plans.clear()
+    _sddmm_plans.clear()
+
+
+# ------------------------------------------------------------ operations --
+
+def spmm(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Tensor,
+         A_col_indices: torch.Tensor, B: torch.Tensor, m: int,
+         out_dtype: torch.dtype = torch.float32, plan: Optional[SpmmPlan] = None,
+         use_plan: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[m x N] = A[m x k] @ B[k x N] (fp32 accumulation)."""
+    _require(B, "B", tuple(_DT))
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    k, N = B.shape
+    if A_val.dtype != B.dtype:
+        raise ValueError("A_val and B must share a dtype")
+    d = csr_desc(A_val, A_row_offsets, A_row_indices, A_col_indices, m, k)
+    if out is None:
+        out = torch.empty((m, N), dtype=out_dtype, device=B.device)
+    else:
+        _require(out, "out", (out_dtype,))
+        if tuple(out.shape) != (m, N):
+            raise ValueError("out has the wrong shape")
+    if plan is None and use_plan:
+        plan = _spmm_plans.get(("spmm", _tkey(A_row_offsets), _tkey(A_row_indices), d.nnz, k),
+                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, k))
+    ws = plan.workspace(N, B.device) if plan is not None else None
+    _check("spops_spmm", lib().spops_spmm(
+        ctypes.byref(d), _ptr(B), _DT[B.dtype], N, N, _ptr(out), _DT[out_dtype], N,
+        plan.handle if plan is not None else None, _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(B)))
+    return out
+
+
+def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
+          out_col_indices: torch.Tensor, A: torch.Tensor, BT: torch.Tensor,
+          backend: str = "structure_aware", out_dtype: torch.dtype = torch.float32,
+          plan: Optional[SddmmPlan] = None, tau: Optional[float] = None,
+          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """values[p] = A[r(p)] . BT[c(p)] at every position of the CSR mask."""
+    if backend not in _BACKENDS:
+        raise ValueError(f"backend must be one of {sorted(_BACKENDS)}")
+    _require(A, "A", tuple(_DT))
+    _require(BT, "BT", tuple(_DT))
+    if A.dim() != 2 or BT.dim() != 2 or A.shape[1] != BT.shape[1] or A.dtype != BT.dtype:
+        raise ValueError("A (m x K) and BT (n x K) must be 2-D with the same K and dtype")
+    m, K = A.shape
+    n = BT.shape[0]
+    d = csr_desc(None, out_row_offsets, out_row_indices, out_col_indices, m, n)
+    nnz = d.nnz
+    if out is None:
+        out = torch.empty(nnz, dtype=out_dtype, device=A.device)
+    b = _BACKENDS[backend]
+    if b == STRUCTURE_AWARE and plan is None and nnz > 0:
+        plan = _sddmm_plans.get(("sddmm", _tkey(out_row_offsets), _tkey(out_col_indices), m, n,
+                                 tau), lambda: SddmmPlan(out_row_offsets, out_col_indices, m, n,
+                                                         tau))
+    _check("spops_sddmm", lib().spops_sddmm(
+        ctypes.byref(d), _ptr(A), K, max(K, 1), _ptr(BT), max(K, 1), _DT[A.dtype], _ptr(out),
+        _DT[out_dtype], b,
+        plan.handle if plan is not None else None, _stream(A)))
+    return out
+
+
+def csr_add(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Tensor,
+            A_col_indices: torch.Tensor, B: torch.Tensor) -> torch.Tensor:
+    """B += A in place (one rounding to B's dtype per entry); returns B."""
+    _require(B, "B", tuple(_DT))
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    m, n = B.shape
+    if A_val.dtype != B.dtype:
+        raise ValueError("A_val and B must share a dtype")
+    d = csr_desc(A_val, A_row_offsets, A_row_indices, A_col_indices, m, n)
+    _check("spops_csr_add", lib().spops_csr_add(ctypes.byref(d), _ptr(B), _DT[B.dtype], n,
+                                                _stream(B)))
+    return B
+
+
+def csr_transpose_workspace(m: int, n: int, nnz: int, device) -> torch.Tensor:
+    b = ctypes.c_size_t()
+    _check("spops_csr_transpose_workspace_size",
+           lib().spops_csr_transpose_workspace_size(m, n, nnz, ctypes.byref(b)))
+    return torch.empty(max(b.value, 1), dtype=torch.uint8, device=device)
+
+
+def csr_transpose(A_val: Optional[torch.Tensor], A_row_offsets: torch.Tensor,
+                  A_col_indices: torch.Tensor, m: int, n: int,
+                  workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
+    """A^T as (values_T, row_offsets_T [n+1] int32, col_idx_T [nnz])."""
+    d = csr_desc(A_val, A_row_offsets, None, A_col_indices, m, n)
+    dev = A_row_offsets.device
+    nnz = d.nnz
+    out_ro = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    oit = torch.int16 if m <= 32767 else torch.int32
+    out_ci = torch.empty(nnz, dtype=oit, device=dev)
+    out_v = torch.empty_like(A_val) if A_val is not None else None
+    if workspace is None:
+        workspace = csr_transpose_workspace(m, n, nnz, dev)
+    _check("spops_csr_transpose", lib().spops_csr_transpose(
+        ctypes.byref(d), _ptr(out_v), out_ro.data_ptr(), _ptr(out_ci), _IT[oit],
+        workspace.data_ptr(), workspace.numel(), _stream(A_row_offsets)))
+    return out_v, out_ro, out_ci
+
+
+def sort_rows_workspace(m: int, n: int, device) -> torch.Tensor:
+    b = ctypes.c_size_t()
+    _check("spops_sort_rows_by_nnz_workspace_size",
+           lib().spops_sort_rows_by_nnz_workspace_size(m, n, ctypes.byref(b)))
+    return torch.empty(max(b.value, 1), dtype=torch.uint8, device=device)
+
+
+def sort_rows_by_nnz(row_offsets: torch.Tensor, n: int,
+                     index_dtype: Optional[torch.dtype] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """row_idx: rows by entry count, most first, ties by ascending row."""
+    _require(row_offsets, "row_offsets", (torch.int32,))
+    m = row_offsets.numel() - 1
+    dt = index_dtype or (torch.int16 if m <= 32767 else torch.int32)
+    if out is None:
+        out = torch.empty(m, dtype=dt, device=row_offsets.device)
+    if workspace is None:
+        workspace = sort_rows_workspace(m, n, row_offsets.device)
+    _check("spops_sort_rows_by_nnz", lib().spops_sort_rows_by_nnz(
+        row_offsets.data_ptr(), m, n, _ptr(out), _IT[out.dtype], workspace.data_ptr(),
+        workspace.numel(), _stream(row_offsets)))
+    return out
