@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSR sparse-dense hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic workload, every
+operation on the GPU through libspops:
+  1. SpMM          C = A @ B                     (row order from row_idx)
+  2. SDDMM         A_d @ BT^T sampled at A's mask (structure-aware backend)
+  3. csr_add       W += A in place
+  4. csr_transpose A^T in CSR
+  5. row order     row_idx of A^T (rows by entry count)
+Plans (SpMM row splitting, SDDMM dense-row/column partition) depend only on
+the sparsity pattern; they are built once before timing (plan once, execute
+many) and their build time is reported separately.
+
+Timing.  Every working set here fits in the 256 MB Infinity Cache, so each
+step starts with an untimed write of a 512 MiB scratch buffer that evicts L2
+and the Infinity Cache; the hot path is then timed with HIP events on the
+stream it runs on.  `value` is algorithmic bytes of the step / mean event time
+of the step (inputs resident in HBM, caches cold).  The wall clock of the K
+steps (barrier + synchronize on both sides, flushes included) is reported too.
+
+Algorithmic bytes per operation (each input read once, each output written
+once; k' / n' = distinct columns touched, m' = rows with entries):
+  SpMM      nnz*(s_v+s_ci) + 4(m+1) + m*s_ri + k'*N*s_B + m*N*s_C
+  SDDMM     nnz*s_ci + 4(m+1) + m*s_ri + m'*K*s_A + n'*K*s_BT + nnz*s_out
+  csr_add   nnz*(s_v+s_ci) + 4(m+1) + m*s_ri + 2*nnz*s_W
+  transpose nnz*(s_v+s_ci) + 4(m+1) + nnz*(s_v+s_ri') + 4(n+1)
+  row order 4(n+1) + n*s_ri'
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FLUSH_BYTES = 512 << 20        # > 256 MB Infinity Cache + 8 x 4 MB L2
+DEFAULT_CONFIG = 2             # the configuration the metric is quoted on
+ESZ = {"f32": 4, "f16": 2, "bf16": 2}
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=DEFAULT_CONFIG,
+                   help="workload 1-5 (2 is the headline configuration)")
+    p.add_argument("--dtype", default=None, help="value dtype override (config 3: f16|bf16)")
+    p.add_argument("--no-flush", action="store_true", help="warm caches (not the metric)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
+    return p.parse_args()
+
+
+def alg_bytes(A, N, K, dt):
+    m, n, nnz = A.m, A.n, A.nnz
+    s_v, s_ci = ESZ[dt], A.col_idx.dtype.itemsize
+    s_ri = 2 if m <= 32767 else 4
+    s_riT = 2 if n <= 32767 else 4
+    col = A.col_idx.astype(np.int64)
+    kp = len(np.unique(col))
+    mp = int(np.count_nonzero(A.row_counts()))
+    return {
+        "spmm": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + kp * N * s_v + m * N * 4,
+        "sddmm": nnz * s_ci + 4 * (m + 1) + m * s_ri + mp * K * s_v + kp * K * s_v + nnz * 4,
+        "csr_add": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + 2 * nnz * s_v,
+        "transpose": nnz * (s_v + s_ci) + 4 * (m + 1) + nnz * (s_v + s_riT) + 4 * (n + 1),
+        "row_order": 4 * (n + 1) + n * s_riT,
+    }
+
+
+def flops(A, N, K):
+    return {"spmm": 2 * A.nnz * N, "sddmm": 2 * A.nnz * K}
+
+
+def kernel_sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "unstructured_sparse_linear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "sddmm": ["sddmm.hip", "sddmm_dense.hip",
+                                                          "common.h"],
+                "csr_add": ["csr_add.hip", "common.h"], "transpose": ["radix.hip", "common.h"],
+                "row_order": ["radix.hip", "common.h"]}
+
+
+def traffic_for(op, config):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(f"config{config}", {}).get(op)
+    if not ent or ent.get("source_sha") != kernel_sources_sha(KERNEL_FILES[op]):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, A, dt, N, K, ops, oracle):
+    """The float64 oracle on the host cores, same workload, one warm-up then
+    the median of 3 runs per operation."""
+    B, Ad, BT, W = w.get("B"), w.get("Ad"), w.get("BT"), w.get("W")
+    ab = alg_bytes(A, N, K, dt)
+    fns = {
+        "spmm": lambda: oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt),
+        "sddmm": lambda: oracle.sddmm(A.row_offsets, A.col_idx, Ad, BT, dt),
+        "csr_add": lambda: oracle.csr_add(A.row_offsets, A.col_idx, A.values, dt, W, dt),
+        "transpose": lambda: oracle.csr_transpose(A.m, A.n, A.row_offsets, A.col_idx, A.values),
+        "row_order": lambda: oracle.row_idx(tro),
+    }
+    _, tro, _ = oracle.csr_transpose(A.m, A.n, A.row_offsets, A.col_idx, None)
+    per, total_s, total_b = {}, 0.0, 0
+    for op in ops:
+        fns[op]()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fns[op]()
+            ts.append(time.perf_counter() - t0)
+        t = float(np.median(ts))
+        per[op] = round(t * 1e3, 3)
+        total_s += t
+        total_b += ab[op]
+    return {"value": round(total_b / total_s / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full workload (all {len(ops)} operations, one pass each), "
+                      "median of 3 after 1 warm-up",
+            "ms_per_op": per, "ms_per_step": round(total_s * 1e3, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards without collectives; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import unstructured_sparse_linear_amd as S
+    from unstructured_sparse_linear_amd import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    S.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    ops = [o for o in args.ops.split(",") if o]
+
+    w = gen.make_config(args.config, dt=args.dtype)
+    A = w.get("A")
+    dt = w.dt
+    N = w.N[-1]
+    K = w.K
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+
+    def to(x, d=None):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    v, ro, ci = to(A.values, dt), to(A.row_offsets), to(A.col_idx)
+    B = to(w.get("B"), dt)
+    Ad, BT = to(w.get("Ad"), dt), to(w.get("BT"), dt)
+    Wd = to(w.get("W"), dt) if "csr_add" in ops else None
+    if args.config == 4 and Wd is not None:
+        A_add = gen.csr_row_slab(A, 0, Wd.shape[0])
+        va, roa, cia = to(A_add.values, dt), to(A_add.row_offsets), to(A_add.col_idx)
+    else:
+        A_add, va, roa, cia = A, v, ro, ci
+    m, n = A.m, A.n
+
+    # plans and row order, once per pattern (not timed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ri = S.sort_rows_by_nnz(ro, n)
+    spmm_plan = S.SpmmPlan(ro, ri, ci, n)
+    torch.cuda.synchronize()
+    t_spmm_plan = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sddmm_plan = S.SddmmPlan(ro, ci, m, n)
+    torch.cuda.synchronize()
+    t_sddmm_plan = time.perf_counter() - t0
+    ri_add = ri if A_add is A else S.sort_rows_by_nnz(roa, n)
+    C = torch.empty((m, N), dtype=torch.float32, device=dev)
+    out = torch.empty(A.nnz, dtype=torch.float32, device=dev)
+    tws = S.csr_transpose_workspace(m, n, A.nnz, dev)
+    sws = S.sort_rows_workspace(n, m, dev)
+    vT = torch.empty_like(v)
+    roT = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    ciT = torch.empty(A.nnz, dtype=torch.int16 if m <= 32767 else torch.int32, device=dev)
+    riT = torch.empty(n, dtype=torch.int16 if n <= 32767 else torch.int32, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    ws = spmm_plan.workspace(N, dev)
+    from unstructured_sparse_linear_amd import spops as SP
+
+    def run_op(op):
+        if op == "spmm":
+            S.spmm(v, ro, ri, ci, B, m, plan=spmm_plan, out=C)
+        elif op == "sddmm":
+            S.sddmm(ro, ri, ci, Ad, BT, plan=sddmm_plan, out=out)
+        elif op == "csr_add":
+            S.csr_add(va, roa, ri_add, cia, Wd)
+        elif op == "transpose":
+            import ctypes
+            d = SP.csr_desc(v, ro, None, ci, m, n)
+            SP._check("spops_csr_transpose", SP.lib().spops_csr_transpose(
+                ctypes.byref(d), vT.data_ptr(), roT.data_ptr(), ciT.data_ptr(),
+                SP._IT[ciT.dtype], tws.data_ptr(), tws.numel(), SP._stream(ro)))
+        elif op == "row_order":
+            S.sort_rows_by_nnz(roT, m, workspace=sws, out=riT)
+    del ws
+
+    stream = torch.cuda.current_stream(dev)
+    nops = len(ops)
+
+    def step(record):
+        if not args.no_flush:
+            flush.fill_(1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] if record else None
+        if record:
+            ev[0].record(stream)
+        for i, op in enumerate(ops):
+            run_op(op)
+            if record:
+                ev[i + 1].record(stream)
+        return ev
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_op = {op: [] for op in ops}
+    step_ms = []
+    for ev in events:
+        for i, op in enumerate(ops):
+            per_op[op].append(ev[i].elapsed_time(ev[i + 1]))
+        step_ms.append(ev[0].elapsed_time(ev[-1]))
+    ab = alg_bytes(A, N, K, dt)
+    if args.config == 4:
+        ab["csr_add"] = alg_bytes(A_add, N, K, dt)["csr_add"]
+    fl = flops(A, N, K)
+    mean_step = float(np.mean(step_ms))
+    total_bytes = sum(ab[o] for o in ops)
+    total_flops = sum(fl.get(o, 0) for o in ops)
+    breakdown = {}
+    for op in ops:
+        t = float(np.mean(per_op[op]))
+        breakdown[op] = {"ms": round(t, 4), "ms_p10": round(float(np.percentile(per_op[op], 10)), 4),
+                         "ms_p90": round(float(np.percentile(per_op[op], 90)), 4),
+                         "alg_bytes": int(ab[op]), "gbps": round(ab[op] / t / 1e6, 1),
+                         "frac_hbm": round(ab[op] / t / 1e6 / HBM_PEAK_GBS, 4)}
+        if op in fl:
+            breakdown[op]["gflops"] = round(fl[op] / t / 1e6, 1)
+    dom = max(ops, key=lambda o: breakdown[o]["ms"])
+    achieved = ab[dom] / breakdown[dom]["ms"] / 1e6
+    traffic = traffic_for(dom, args.config)
+    result = {
+        "metric": "SpMM/SDDMM effective HBM GB/s and GFLOP/s (2*nnz*N), % of HBM roofline",
+        "value": round(total_bytes / mean_step / 1e6, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16-in/f32-acc", "bf16": "bf16-in/f32-acc"}[dt],
+        "data": "synthetic (seeded generators, seed 0)",
+        "config": {"workload": w.name, "config_id": args.config, "m": m, "n": n, "nnz": A.nnz,
+                   "N": N, "K": K, "value_dtype": dt, "ops": ops,
+                   "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)"},
+        "gflops": round(total_flops / mean_step / 1e6, 1),
+        "frac_hbm": round(total_bytes / mean_step / 1e6 / HBM_PEAK_GBS, 4),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "ops_breakdown": breakdown,
+        "plan_ms": {"spmm_schedule_and_row_order": round(t_spmm_plan * 1e3, 2),
+                    "sddmm_partition": round(t_sddmm_plan * 1e3, 2)},
+        "plans": {"spmm": spmm_plan.info(), "sddmm": sddmm_plan.info()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
