@@ -13,11 +13,15 @@ the sparsity pattern; they are built once before timing (plan once, execute
 many) and their build time is reported separately.
 
 Timing.  Every working set here fits in the 256 MB Infinity Cache, so each
-step starts with an untimed write of a 512 MiB scratch buffer that evicts L2
-and the Infinity Cache; the hot path is then timed with HIP events on the
-stream it runs on.  `value` is algorithmic bytes of the step / mean event time
-of the step (inputs resident in HBM, caches cold).  The wall clock of the K
-steps (barrier + synchronize on both sides, flushes included) is reported too.
+timed region starts after an untimed write of a 512 MiB scratch buffer that
+evicts L2 and the Infinity Cache (inputs resident in HBM, caches cold).  The
+step (all operations, in order) is captured once as a HIP graph and replayed,
+so host launch gaps do not count; each replay is bracketed by HIP events on
+its stream.  `value` = algorithmic bytes of the step / mean replay time.  The
+per-operation breakdown times each operation alone, eagerly, right after its
+own flush (the flush keeps the GPU busy while the host enqueues the
+operation, so the events bracket the kernels only).  The wall clock of the K
+graph steps (synchronize on both sides, flushes included) is reported too.
 
 Algorithmic bytes per operation (each input read once, each output written
 once; k' / n' = distinct columns touched, m' = rows with entries):
@@ -57,6 +61,7 @@ def parse():
                    help="workload 1-5 (2 is the headline configuration)")
     p.add_argument("--dtype", default=None, help="value dtype override (config 3: f16|bf16)")
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the metric)")
+    p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
     return p.parse_args()
@@ -226,36 +231,64 @@ def main():
     del ws
 
     stream = torch.cuda.current_stream(dev)
-    nops = len(ops)
 
-    def step(record):
+    def cold():
         if not args.no_flush:
             flush.fill_(1)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] if record else None
-        if record:
-            ev[0].record(stream)
-        for i, op in enumerate(ops):
-            run_op(op)
-            if record:
-                ev[i + 1].record(stream)
-        return ev
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
-        step(False)
+        cold()
+        for op in ops:
+            run_op(op)
+    torch.cuda.synchronize()
+
+    # per-operation cold timing (eager)
+    per_op = {op: [] for op in ops}
+    for _ in range(args.steps):
+        for op in ops:
+            cold()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            run_op(op)
+            e1.record(stream)
+            per_op[op].append((e0, e1))
+    torch.cuda.synchronize()
+    per_op = {op: [a.elapsed_time(b) for a, b in v] for op, v in per_op.items()}
+
+    # the whole step, captured once and replayed
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for op in ops:
+                run_op(op)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+
+    def step():
+        cold()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for op in ops:
+                run_op(op)
+        e1.record(stream)
+        return e0, e1
+
+    step()
     torch.cuda.synchronize()
     events = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        events.append(step(True))
+        events.append(step())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    per_op = {op: [] for op in ops}
-    step_ms = []
-    for ev in events:
-        for i, op in enumerate(ops):
-            per_op[op].append(ev[i].elapsed_time(ev[i + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[-1]))
+    step_ms = [a.elapsed_time(b) for a, b in events]
     ab = alg_bytes(A, N, K, dt)
     if args.config == 4:
         ab["csr_add"] = alg_bytes(A_add, N, K, dt)["csr_add"]
@@ -290,10 +323,14 @@ def main():
         "data": "synthetic (seeded generators, seed 0)",
         "config": {"workload": w.name, "config_id": args.config, "m": m, "n": n, "nnz": A.nnz,
                    "N": N, "K": K, "value_dtype": dt, "ops": ops,
-                   "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)"},
+                   "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)",
+                   "step": "eager" if args.no_graph else "hip graph replay"},
+        "eager_sum_of_ops_ms": round(sum(float(np.mean(v)) for v in per_op.values()), 4),
         "gflops": round(total_flops / mean_step / 1e6, 1),
         "frac_hbm": round(total_bytes / mean_step / 1e6 / HBM_PEAK_GBS, 4),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
+                                round(float(np.percentile(step_ms, 90)), 4)],
         "ops_breakdown": breakdown,
         "plan_ms": {"spmm_schedule_and_row_order": round(t_spmm_plan * 1e3, 2),
                     "sddmm_partition": round(t_sddmm_plan * 1e3, 2)},

@@ -145,7 +145,18 @@ typedef struct spops_sddmm_plan spops_sddmm_plan;
 spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_t lda,
                          const void* BT, int64_t ldbt, spops_dtype in_type, void* out_values,
                          spops_dtype out_type, spops_sddmm_backend backend,
-                         const spops_sddmm_plan* plan, void* hip_stream);
+                         const spops_sddmm_plan* plan, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/* Optional workspace of spops_sddmm.  When BT is larger than one XCD's L2,
+ * the general kernel splits K into slices that run on different XCDs and
+ * sums their fp32 partial products in a fixed order; that needs this many
+ * bytes.  A smaller (or NULL) workspace runs without the split: same
+ * definition, possibly slower.  `plan` as for spops_sddmm (NULL for the
+ * general backend). */
+spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
+                                        spops_sddmm_backend backend,
+                                        const spops_sddmm_plan* plan, size_t* bytes);
 
 /* Finds the clustered rows/columns of the mask and partitions its entries.
  * A row is dense when its entry count is at least tau * cols; a column is

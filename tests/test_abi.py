@@ -89,16 +89,30 @@ def test_spmm_rejects_bad_arguments(L):
 
 def test_sddmm_rejects_bad_arguments(L):
     d = desc(values=None)
-    f = L.spops_sddmm
-    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, FAKE, 2, 0, None, None) == 3  # out bf16, in f16
-    assert f(ctypes.byref(d), FAKE, 8, 4, FAKE, 8, 1, FAKE, 0, 0, None, None) == 2  # lda < K
-    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 9, None, None) == 6  # backend
-    assert f(ctypes.byref(d), None, 8, 8, FAKE, 8, 1, FAKE, 0, 1, None, None) == 1
-    assert f(ctypes.byref(d), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1, None, None) == 1
-    assert f(ctypes.byref(desc(cols=70000, col_type=0)), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 1,
-             None, None) == 4
-    e = desc(nnz=0, col=None)
-    assert f(ctypes.byref(e), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1, None, None) == 0
+
+    def f(dd, A, K, lda, BT, ldbt, it, out, ot, backend):
+        return L.spops_sddmm(ctypes.byref(dd), A, K, lda, BT, ldbt, it, out, ot, backend, None,
+                             None, 0, None)
+    assert f(d, FAKE, 8, 8, FAKE, 8, 1, FAKE, 2, 0) == 3  # out bf16, in f16
+    assert f(d, FAKE, 8, 4, FAKE, 8, 1, FAKE, 0, 0) == 2  # lda < K
+    assert f(d, FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 9) == 6  # backend
+    assert f(d, None, 8, 8, FAKE, 8, 1, FAKE, 0, 1) == 1
+    assert f(d, FAKE, 8, 8, FAKE, 8, 1, None, 0, 1) == 1
+    assert f(desc(cols=70000, col_type=0), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 1) == 4
+    assert f(desc(nnz=0, col=None), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1) == 0
+    b = ctypes.c_size_t()
+    big = desc(rows=4096, cols=4096, nnz=100000)
+    assert L.spops_sddmm_workspace_size(ctypes.byref(big), 2048, 1, 1, None, ctypes.byref(b)) == 0
+    assert b.value == 0                                   # K split off by default
+    os.environ["SPOPS_SDDMM_KSPLIT"] = "8"
+    try:
+        assert L.spops_sddmm_workspace_size(ctypes.byref(big), 2048, 1, 1, None,
+                                            ctypes.byref(b)) == 0
+        assert b.value >= 8 * 100000 * 4                  # 8 K-slices of fp32 partials
+    finally:
+        del os.environ["SPOPS_SDDMM_KSPLIT"]
+    assert L.spops_sddmm_workspace_size(ctypes.byref(desc()), 8, 1, 1, None,
+                                        ctypes.byref(b)) == 0 and b.value == 0
 
 
 def test_csr_add_rejects_bad_arguments(L):

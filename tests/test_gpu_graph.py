@@ -1,0 +1,69 @@
+"""The hot path captured in a HIP graph (through torch.cuda.CUDAGraph) gives,
+on every replay, exactly the results of the same calls run eagerly.  Replays
+are separated by eager work and synchronizations, and each is checked."""
+import numpy as np
+import pytest
+import torch
+
+import unstructured_sparse_linear_amd as S
+from unstructured_sparse_linear_amd import gen
+from helpers import csr_dev, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt,heavy", [("f16", False), ("bf16", True)])
+def test_graph_replays_match_eager(dt, heavy):
+    if heavy:
+        rng = np.random.default_rng(3)
+        counts = np.concatenate([[1500, 700, 300], rng.integers(0, 40, 997)])
+        A = gen.csr_from_row_lists(1000, 3000, [np.sort(rng.choice(3000, int(c), replace=False))
+                                                for c in counts])
+        A = A.with_values(gen.normal(rng, A.nnz, dt), dt)
+    else:
+        A = gen.random_csr(5, 1200, 2600, 0.02, dt)
+    m, n, N, K = A.m, A.n, 256, 128
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, n)
+    B = dev(gen.dense(5, 100, gen.S_B, (n, N), dt), dt)
+    Ad = dev(gen.dense(5, 100, gen.S_A, (m, K), dt), dt)
+    BT = dev(gen.dense(5, 100, gen.S_BT, (n, K), dt), dt)
+    W0 = dev(gen.dense(5, 100, gen.S_W, (m, n), dt), dt)
+    plan = S.SpmmPlan(ro, ri, ci, n)
+    splan = S.SddmmPlan(ro, ci, m, n, tau=0.02)
+    C = torch.empty((m, N), dtype=torch.float32, device="cuda")
+    out = torch.empty(A.nnz, dtype=torch.float32, device="cuda")
+    W = W0.clone()
+    tws = S.csr_transpose_workspace(m, n, A.nnz, "cuda")
+    sws = S.sort_rows_workspace(n, m, "cuda")
+    roT = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    riT = torch.empty(n, dtype=torch.int16, device="cuda")
+
+    def step():
+        S.spmm(v, ro, ri, ci, B, m, plan=plan, out=C)
+        S.sddmm(ro, ri, ci, Ad, BT, plan=splan, out=out)
+        S.csr_add(v, ro, ri, ci, W)
+        _, roT2, _ = S.csr_transpose(v, ro, ci, m, n, workspace=tws)
+        roT.copy_(roT2)
+        S.sort_rows_by_nnz(roT, m, workspace=sws, out=riT)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [C.clone(), out.clone(), W.clone(), roT.clone(), riT.clone()]
+    W.copy_(W0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        W.copy_(W0)
+        C.zero_()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [C, out, W, roT, riT]
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        # unrelated eager work between replays
+        _ = (B.float() @ B.float().T).sum().item()

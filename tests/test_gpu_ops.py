@@ -279,6 +279,23 @@ def test_sddmm_backends_bitexact_on_integers(dt):
         assert np.array_equal(host_f64(out), ref), (backend, tau)
 
 
+@pytest.mark.parametrize("dt,m,n,K", [("f16", 300, 5000, 512), ("bf16", 200, 3000, 1000),
+                                      ("f16", 150, 6000, 2048)])
+@pytest.mark.parametrize("backend", ["sputnik", "structure_aware"])
+def test_sddmm_k_split(dt, m, n, K, backend):
+    # BT larger than one L2: K is split across XCDs and the partials summed
+    M = gen.random_csr(7, m, n, 0.01, None, empty_row_frac=0.1)
+    Ad = gen.dense(7, 100, gen.S_A, (m, K), dt)
+    BT = gen.dense(7, 100, gen.S_BT, (n, K), dt)
+    out = run_sddmm(M, Ad, BT, dt, backend)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
+    assert_close(host_f64(out), ref, dt, "sddmm k-split")
+    Ai = gen.dense(8, 100, gen.S_A, (m, K), dt, integer_values=True)
+    Bi = gen.dense(8, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    refi = oracle.sddmm(M.row_offsets, M.col_idx, Ai, Bi, dt)
+    assert np.array_equal(host_f64(run_sddmm(M, Ai, Bi, dt, backend)), refi)
+
+
 def test_sddmm_keeps_f16_subnormals():
     m, n, K = 20, 30, 64
     M = gen.random_csr(5, m, n, 0.5, None)

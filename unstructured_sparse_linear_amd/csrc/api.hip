@@ -165,6 +165,7 @@ spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, i
   a.C = C;
   a.dtype = b_type;
   a.out_dtype = c_type;
+  if (plan) a.natural = plan->sch.natural;
   if (plan && plan->sch.P > 0) {
     a.P = plan->sch.P;
     a.S = plan->sch.S;
@@ -220,10 +221,36 @@ spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_
   return SPOPS_OK;
 }
 
+// Entries the general kernel handles for this call (all of them, or the
+// plan's remainder) and whether the dense tiles can run.
+static bool sddmm_tiles_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t ldbt,
+                           const void* A, const void* BT) {
+  return in_type != SPOPS_F32 && K > 0 && K % 8 == 0 && lda % 8 == 0 && ldbt % 8 == 0 &&
+         ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
+}
+
+spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
+                                        spops_sddmm_backend backend,
+                                        const spops_sddmm_plan* plan, size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  *bytes = 0;
+  spops_status st = check_csr(mask, false, false);
+  if (st != SPOPS_OK) return st;
+  if (!dtype_ok(in_type)) return SPOPS_ERR_DTYPE;
+  if (K < 0) return SPOPS_ERR_SHAPE;
+  int64_t count = mask->nnz;
+  if (backend == SPOPS_SDDMM_STRUCTURE_AWARE && plan && in_type != SPOPS_F32 && K % 8 == 0)
+    count = plan->dev.rest_nnz;
+  const int64_t ks = sddmm_k_slices(mask->cols, K, in_type);
+  if (ks > 1 && count > 0) *bytes = align256((size_t)(ks * count) * 4);
+  return SPOPS_OK;
+}
+
 spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_t lda,
                          const void* BT, int64_t ldbt, spops_dtype in_type, void* out_values,
                          spops_dtype out_type, spops_sddmm_backend backend,
-                         const spops_sddmm_plan* plan, void* hip_stream) {
+                         const spops_sddmm_plan* plan, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
   spops_status st = check_csr(mask, false, false);
   if (st != SPOPS_OK) return st;
   if (!dtype_ok(in_type) || !dtype_ok(out_type)) return SPOPS_ERR_DTYPE;
@@ -252,10 +279,21 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   g.out = out_values;
   g.dtype = in_type;
   g.out_dtype = out_type;
+  g.ks = 1;
+  g.partial = nullptr;
+  // K split when the workspace allows it (fp32 partials per slice)
+  auto with_split = [&](SddmmArgs x) {
+    const int64_t ks = sddmm_k_slices(mask->cols, K, in_type);
+    if (ks > 1 && workspace && workspace_bytes >= (size_t)(ks * x.count) * 4) {
+      x.ks = ks;
+      x.partial = (float*)workspace;
+    }
+    return x;
+  };
 
-  const bool tiles_ok = in_type != SPOPS_F32 && K > 0 && K % 8 == 0 && lda % 8 == 0 &&
-                        ldbt % 8 == 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
-  if (backend == SPOPS_SDDMM_GENERAL || !tiles_ok) return from_hip(launch_sddmm_general(g, s));
+  const bool tiles_ok = sddmm_tiles_ok(in_type, K, lda, ldbt, A, BT);
+  if (backend == SPOPS_SDDMM_GENERAL || !tiles_ok)
+    return from_hip(launch_sddmm_general(with_split(g), s));
 
   spops_sddmm_plan* own = nullptr;
   if (plan) {
@@ -274,7 +312,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     r.ro = P.rest_ro;
     r.pos = P.rest_pos;
     r.count = P.rest_nnz;
-    e = launch_sddmm_general(r, s);
+    e = launch_sddmm_general(with_split(r), s);
   }
   if (own) {
     hipError_t e2 = hipStreamSynchronize(s);

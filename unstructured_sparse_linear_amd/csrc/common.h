@@ -116,4 +116,24 @@ __device__ __forceinline__ int64_t upper_row(const int32_t* ro, int64_t lo, int6
   return lo;
 }
 
+// Wave-cooperative version of upper_row over [0, m): every lane probes one
+// of 64 evenly spaced offsets per step, so the range shrinks 64-fold per
+// dependent load instead of 2-fold.  All lanes must call it with the same p;
+// all get the same (wave-uniform) answer.
+__device__ __forceinline__ int64_t wave_upper_row(const int32_t* ro, int64_t m, int64_t p) {
+  int64_t lo = 0, hi = m;  // answer in [lo, hi), ro[lo] <= p assumed
+  const int lane = lane_id();
+  while (hi - lo > 1) {
+    const int64_t step = cdiv(hi - lo, kWave);
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool le = idx < hi && (int64_t)ro[idx] <= p;
+    const uint64_t mask = __ballot(le);
+    const int last = mask ? 63 - __builtin_clzll(mask) : 0;
+    lo = lo + (int64_t)last * step;
+    const int64_t nhi = lo + step;
+    hi = nhi < hi ? nhi : hi;
+  }
+  return wave_uniform((int)lo);
+}
+
 }  // namespace spops

@@ -27,18 +27,32 @@ __global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, i
   const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
   const int64_t wb = wave * (kWave * kRounds);
   if (wb >= nnz) return;
-  int64_t r = wave_uniform((int)upper_row(ro, 0, m, wb));
+  int64_t r = wave_upper_row(ro, m, wb);
   const int lane = lane_id();
+  // all loads of W first (positions are distinct), then the stores
+  int64_t off[kRounds];
+  float add[kRounds];
+  VT old[kRounds];
 #pragma unroll
   for (int q = 0; q < kRounds; ++q) {
     const int64_t p = wb + q * kWave + lane;
-    if (p >= nnz) break;
-    while (r < m - 1 && (int64_t)ro[r + 1] <= p) ++r;
-    const int c = (int)col[p];
-    if ((unsigned)c >= (unsigned)n) continue;
-    VT* w = W + r * ldw + c;
-    *w = from_f32<VT>(to_f32(*w) + to_f32(val[p]));
+    off[q] = -1;
+    add[q] = 0.f;
+    if (p < nnz) {
+      while (r < m - 1 && (int64_t)ro[r + 1] <= p) ++r;
+      const int c = (int)col[p];
+      if ((unsigned)c < (unsigned)n) {
+        off[q] = r * ldw + c;
+        add[q] = to_f32(val[p]);
+      }
+    }
   }
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q)
+    if (off[q] >= 0) old[q] = W[off[q]];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q)
+    if (off[q] >= 0) W[off[q]] = from_f32<VT>(to_f32(old[q]) + add[q]);
 }
 
 template <typename VT>

@@ -56,6 +56,7 @@ struct SpmmArgs {
   void* C;
   int dtype;      // value / B dtype
   int out_dtype;  // C dtype
+  int natural;          // 1: whole rows in index order (balanced lengths), 0: row_idx order
   // row-splitting schedule (P == 0: none)
   int64_t P;            // number of chunk items of split rows
   int64_t S;            // number of split rows
@@ -72,6 +73,7 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
 // Row-splitting schedule for SpMM, built on the device.  chunk = T.
 struct SpmmSchedule {
   int64_t P = 0, S = 0, max_row = 0;
+  int natural = 0;  // row lengths balanced enough to keep index order (locality)
   int32_t T = 0;
   int32_t* item_pos = nullptr;
   int32_t* item_chunk = nullptr;
@@ -96,7 +98,14 @@ struct SddmmArgs {
   const void* BT;
   void* out;             // indexed by mask position
   int dtype, out_dtype;
+  // K split across XCDs (ks == 1: none): slice s of K accumulates into
+  // partial[s * count + j], then a fixed-order sum writes out.
+  int64_t ks;
+  float* partial;
 };
+// Number of K slices the general kernel would use, and the fp32 workspace
+// that needs (bytes); 1 / 0 when splitting does not pay.
+int64_t sddmm_k_slices(int64_t n, int64_t K, int dtype);
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s);
 
 // Structure-aware SDDMM plan (device data) and its dense-tile kernel.

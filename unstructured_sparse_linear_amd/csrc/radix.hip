@@ -26,8 +26,6 @@ constexpr int kTile = kThreads * kItems;  // keys per tile
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 
-
-
 // ================================================================= scan ==
 
 // Exclusive scan inside each block of kTile elements; block totals to `sums`.
@@ -71,6 +69,49 @@ __global__ __launch_bounds__(kThreads) void scan_local_kernel(const uint32_t* in
     if (sums) sums[blockIdx.x] = blk;
     if (total && gridDim.x == 1) *total = blk;
   }
+}
+
+// Whole exclusive scan in one workgroup of 1024 threads for n up to 16384:
+// each thread scans a contiguous chunk of at most 16 values.
+constexpr int kSingleThreads = 1024;
+constexpr int64_t kSingleMax = 16384;
+
+__global__ __launch_bounds__(kSingleThreads) void scan_single_kernel(const uint32_t* in,
+                                                                     uint32_t* out, int64_t n,
+                                                                     uint32_t* total) {
+  __shared__ uint32_t wave_tot[kSingleThreads / kWave];
+  const int t = threadIdx.x;
+  constexpr int kPer = kSingleMax / kSingleThreads;
+  const int64_t b0 = (int64_t)t * kPer;
+  uint32_t v[kPer];
+  uint32_t s = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    v[q] = (b0 + q < n) ? in[b0 + q] : 0u;
+    s += v[q];
+  }
+  uint32_t x = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, kWave);
+    if (lane_id() >= o) x += y;
+  }
+  const int w = t / kWave;
+  if (lane_id() == kWave - 1) wave_tot[w] = x;
+  __syncthreads();
+  uint32_t run = 0, blk = 0;
+  for (int i = 0; i < kSingleThreads / kWave; ++i) {
+    const uint32_t wt = wave_tot[i];
+    if (i < w) run += wt;
+    blk += wt;
+  }
+  run += x - s;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (b0 + q < n) out[b0 + q] = run;
+    run += v[q];
+  }
+  if (t == 0 && total) *total = blk;
 }
 
 __global__ __launch_bounds__(kThreads) void scan_add_kernel(uint32_t* out, int64_t n,
@@ -122,6 +163,7 @@ struct ValFromU32 {
 };
 
 // Per-tile digit histogram, stored digit-major: counts[d * ntiles + tile].
+// Thread t takes kItems consecutive keys.
 template <class KS>
 __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n, int shift,
                                                                uint32_t mask, uint32_t* counts,
@@ -130,10 +172,10 @@ __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n,
   const int t = threadIdx.x;
   hist[t] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kTile;
+  const int64_t i0 = (int64_t)blockIdx.x * kTile + (int64_t)t * kItems;
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    int64_t i = base + r * kThreads + t;
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = i0 + q;
     if (i < n) atomicAdd(&hist[(ks(i) >> shift) & mask], 1u);
   }
   __syncthreads();
@@ -324,6 +366,81 @@ hipError_t finish_transpose(const uint32_t* keys, const uint32_t* src, const uin
   return hipGetLastError();
 }
 
+// Row order of up to kBlockSortMax rows in one workgroup: LSD radix sort of
+// 16-bit keys (cols - count) packed above 16-bit row ids, two 8-bit passes
+// through LDS.  Ranks among equal digits come from wave ballots, rounds of
+// 1024 rows are taken in index order, so the sort is stable.
+constexpr int kBlockSortThreads = 1024;
+constexpr int64_t kBlockSortMax = 16384;
+// measured: one workgroup beats the multi-kernel sort only for small counts
+constexpr int64_t kBlockSortUse = 4096;
+
+template <typename OI>
+__global__ __launch_bounds__(kBlockSortThreads) void sort_rows_block_kernel(const int32_t* ro,
+                                                                           int64_t m,
+                                                                           int32_t cols,
+                                                                           OI* out) {
+  constexpr int NW = kBlockSortThreads / kWave;
+  __shared__ uint32_t buf[2][kBlockSortMax];
+  __shared__ uint32_t cnt[NW][kRadix];
+  __shared__ uint32_t base_d[kRadix];
+  const int t = threadIdx.x, w = t / kWave;
+  const uint64_t lt = lanemask_lt();
+  for (int64_t i = t; i < m; i += kBlockSortThreads) {
+    int64_t c = (int64_t)ro[i + 1] - (int64_t)ro[i];
+    c = c < 0 ? 0 : (c > cols ? cols : c);
+    buf[0][i] = ((uint32_t)(cols - c) << 16) | (uint32_t)i;
+  }
+  int cur = 0;
+  for (int shift = 16; shift < 32; shift += 8) {
+    if (t < kRadix) base_d[t] = 0;
+    __syncthreads();
+    for (int64_t i = t; i < m; i += kBlockSortThreads)
+      atomicAdd(&base_d[(buf[cur][i] >> shift) & 0xffu], 1u);
+    __syncthreads();
+    if (t == 0) {
+      uint32_t run = 0;
+      for (int d = 0; d < kRadix; ++d) {
+        const uint32_t c = base_d[d];
+        base_d[d] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int64_t r0 = 0; r0 < m; r0 += kBlockSortThreads) {
+      for (int q = t; q < NW * kRadix; q += kBlockSortThreads) (&cnt[0][0])[q] = 0;
+      __syncthreads();
+      const int64_t i = r0 + t;
+      const bool valid = i < m;
+      const uint32_t item = valid ? buf[cur][i] : 0u;
+      const uint32_t d = (item >> shift) & 0xffu;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      const uint32_t rank = (uint32_t)__popcll(peers & lt);
+      if (valid && rank == 0) cnt[w][d] = (uint32_t)__popcll(peers);
+      __syncthreads();
+      if (t < kRadix) {
+        uint32_t run = base_d[t];
+        for (int ww = 0; ww < NW; ++ww) {
+          const uint32_t c = cnt[ww][t];
+          cnt[ww][t] = run;
+          run += c;
+        }
+        base_d[t] = run;
+      }
+      __syncthreads();
+      if (valid) buf[cur ^ 1][cnt[w][d] + rank] = item;
+      __syncthreads();
+    }
+    cur ^= 1;
+  }
+  for (int64_t i = t; i < m; i += kBlockSortThreads) out[i] = (OI)(buf[cur][i] & 0xffffu);
+}
+
 // row_idx output from the sorted payload
 template <typename OI>
 __global__ __launch_bounds__(256) void store_perm_kernel(const uint32_t* src, int64_t m, OI* out) {
@@ -353,6 +470,11 @@ hipError_t exclusive_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint
   const int64_t nb = cdiv(n, kTile);
   if (nb == 1) {
     hipLaunchKernelGGL(scan_local_kernel, dim3(1), dim3(kThreads), 0, s, in, out, n, nullptr,
+                       total);
+    return hipGetLastError();
+  }
+  if (n <= kSingleMax) {
+    hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kSingleThreads), 0, s, in, out, n,
                        total);
     return hipGetLastError();
   }
@@ -426,6 +548,15 @@ size_t sort_rows_workspace_bytes(int64_t rows, int64_t cols) {
 hipError_t launch_sort_rows(const int32_t* ro, int64_t rows, int64_t cols, void* row_idx,
                             int row_idx_i32, void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (rows <= kBlockSortUse && cols <= 65535) {
+    if (row_idx_i32)
+      hipLaunchKernelGGL(sort_rows_block_kernel<int32_t>, dim3(1), dim3(kBlockSortThreads), 0, s,
+                         ro, rows, (int32_t)cols, (int32_t*)row_idx);
+    else
+      hipLaunchKernelGGL(sort_rows_block_kernel<int16_t>, dim3(1), dim3(kBlockSortThreads), 0, s,
+                         ro, rows, (int32_t)cols, (int16_t*)row_idx);
+    return hipGetLastError();
+  }
   RadixWs R = carve_radix_ws(ws, rows);
   int res = 0;
   const int bits = bit_length((uint64_t)cols);

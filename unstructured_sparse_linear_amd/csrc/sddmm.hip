@@ -14,8 +14,16 @@
 // per instruction, fp32 accumulation) or v_fma_f32; the LPN partial sums are
 // combined with a fixed xor-shuffle tree.
 //
+// K split (optional).  When BT is larger than an XCD's 4 MB L2, K can be cut
+// into ks slices; slice s runs on blocks s, s+ks, ... which the dispatcher
+// places on the same XCD(s), so each L2 only holds its slice of BT.  Each slice
+// writes its partial dot products to a workspace and a second kernel adds the
+// ks partials of every entry in slice order (deterministic).
+//
 // The same kernel runs the remainder of the structure-aware backend, where
 // entry j of a sub-matrix stands for mask position pos[j].
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -77,10 +85,12 @@ __device__ __forceinline__ int64_t mask_pos(const SddmmArgs& a, int64_t j) {
   return a.pos ? (int64_t)a.pos[j] : j;
 }
 
-// Entries per wavefront for a group width.
+// Entries per wavefront for a group width: each group takes 16 entries, or
+// 32 for 64-lane groups, so the row search and the A-row loads of a wave are
+// amortized over enough dot products.
 template <int LPN>
 constexpr int entries_per_wave() {
-  return (kWave / LPN) * 8;
+  return (kWave / LPN) * (LPN == kWave ? 32 : 16);
 }
 
 // Vectorised path.  KV = 16-byte vectors per lane per pass; K is covered in
@@ -92,7 +102,8 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(SddmmArgs a) {
   constexpr int G = kWave / LPN;
   constexpr int E = entries_per_wave<LPN>();
   constexpr int U = 4;
-  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  const int64_t slice = (int64_t)blockIdx.x % a.ks;
+  const int64_t wave = ((int64_t)blockIdx.x / a.ks * kBlock + threadIdx.x) / kWave;
   const int lane = lane_id();
   const int grp = lane / LPN;
   const int gl = lane % LPN;
@@ -107,15 +118,21 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(SddmmArgs a) {
 
   const int64_t m = a.m;
   const int32_t* ro = a.ro;
-  int64_t r = wave_uniform((int)upper_row(ro, 0, m, wb));
+  int64_t r = wave_upper_row(ro, m, wb);
   while (r < m - 1 && (int64_t)ro[r + 1] <= e) ++r;
 
-  const int64_t kvec = a.K / VEC;
+  // this slice's 16-byte vectors of the K axis: [kv0, kv1)
+  const int64_t kvall = a.K / VEC;
+  const int64_t kvper = cdiv(kvall, a.ks);
+  const int64_t kv0 = slice * kvper;
+  const int64_t kv1 = (kv0 + kvper < kvall) ? kv0 + kvper : kvall;
+  const int64_t kvec = kv1 > kv0 ? kv1 - kv0 : 0;
   const int64_t npass = cdiv(kvec, (int64_t)LPN * KV);
-  const VT* A = (const VT*)a.A;
-  const VT* BT = (const VT*)a.BT;
+  const VT* A = (const VT*)a.A + kv0 * VEC;
+  const VT* BT = (const VT*)a.BT + kv0 * VEC;
   const IT* col = (const IT*)a.col;
   OT* out = (OT*)a.out;
+  float* part = a.ks > 1 ? a.partial + slice * a.count : nullptr;
   const int64_t n = a.n;
 
   auto load_slice = [&](const VT* rowp, int64_t pass, uint4* dst) {
@@ -158,8 +175,13 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(SddmmArgs a) {
         for (int u = 0; u < U; ++u) s[u] = group_sum<LPN>(s[u]);
         if (gl == 0) {
 #pragma unroll
-          for (int u = 0; u < U; ++u)
-            out[p[u]] = from_f32<OT>(((unsigned)c[u] < (unsigned)n) ? s[u] : 0.f);
+          for (int u = 0; u < U; ++u) {
+            const float r = ((unsigned)c[u] < (unsigned)n) ? s[u] : 0.f;
+            if (part)
+              part[e + u] = r;
+            else
+              out[p[u]] = from_f32<OT>(r);
+          }
         }
       }
     }
@@ -176,7 +198,13 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(SddmmArgs a) {
         for (int v = 0; v < KV; ++v) s = TR::dot(areg[v], b[v], s);
       }
       s = group_sum<LPN>(s);
-      if (gl == 0) out[p] = from_f32<OT>(((unsigned)c < (unsigned)n) ? s : 0.f);
+      if (gl == 0) {
+        const float r = ((unsigned)c < (unsigned)n) ? s : 0.f;
+        if (part)
+          part[e] = r;
+        else
+          out[p] = from_f32<OT>(r);
+      }
     }
     if (e >= e1) break;
     // next non-empty row
@@ -196,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_scalar_kernel(SddmmArgs a) {
   if (wb >= a.count) return;
   const int64_t we = (wb + E < a.count) ? wb + E : a.count;
   const int64_t m = a.m;
-  int64_t r = wave_uniform((int)upper_row(a.ro, 0, m, wb));
+  int64_t r = wave_upper_row(a.ro, m, wb);
   const VT* A = (const VT*)a.A;
   const VT* BT = (const VT*)a.BT;
   const IT* col = (const IT*)a.col;
@@ -214,28 +242,43 @@ __global__ __launch_bounds__(kBlock) void sddmm_scalar_kernel(SddmmArgs a) {
   }
 }
 
+// out[pos(j)] = sum over slices of partial[s * count + j], slices in order.
+template <typename OT>
+__global__ __launch_bounds__(kBlock) void sddmm_reduce_kernel(SddmmArgs a) {
+  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (j >= a.count) return;
+  float t = 0.f;
+  for (int64_t q = 0; q < a.ks; ++q) t += a.partial[q * a.count + j];
+  ((OT*)a.out)[a.pos ? (int64_t)a.pos[j] : j] = from_f32<OT>(t);
+}
+
 template <typename VT, typename OT, typename IT, int LPN, int KV>
 hipError_t launch_vec(const SddmmArgs& a, hipStream_t s) {
   constexpr int E = entries_per_wave<LPN>();
   const int64_t waves = cdiv(a.count, E);
-  const dim3 grid((unsigned)cdiv(waves * kWave, kBlock));
+  const dim3 grid((unsigned)(cdiv(waves * kWave, kBlock) * a.ks));
   hipLaunchKernelGGL((sddmm_vec_kernel<VT, OT, IT, LPN, KV>), grid, dim3(kBlock), 0, s, a);
+  if (a.ks > 1)
+    hipLaunchKernelGGL(sddmm_reduce_kernel<OT>, dim3((unsigned)cdiv(a.count, kBlock)),
+                       dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename VT, typename OT, typename IT>
-hipError_t launch_typed(const SddmmArgs& a, hipStream_t s) {
+hipError_t launch_typed(SddmmArgs a, hipStream_t s) {
   if (a.count <= 0) return hipSuccess;
   constexpr int VEC = Traits<VT>::vec;
   const bool aligned = a.K > 0 && (a.K % VEC == 0) && (a.lda % VEC == 0) &&
                        (a.ldbt % VEC == 0) && ((uintptr_t)a.A % 16 == 0) &&
                        ((uintptr_t)a.BT % 16 == 0);
   if (!aligned) {
+    a.ks = 1;
     const dim3 grid((unsigned)cdiv(cdiv(a.count, 8) * kWave, kBlock));
     hipLaunchKernelGGL((sddmm_scalar_kernel<VT, OT, IT>), grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
   }
-  const int64_t kvec = a.K / VEC;
+  if (a.ks < 1 || !a.partial) a.ks = 1;
+  const int64_t kvec = cdiv(a.K / VEC, a.ks);
   if (kvec <= 4) return launch_vec<VT, OT, IT, 4, 1>(a, s);
   if (kvec <= 8) return launch_vec<VT, OT, IT, 8, 1>(a, s);
   if (kvec <= 16) return launch_vec<VT, OT, IT, 16, 1>(a, s);
@@ -257,6 +300,20 @@ hipError_t launch_vt(const SddmmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Measured on MI355X, splitting K costs more (one reduction and one output
+// write per slice and entry) than the L2 residency of the slices saves for
+// the shapes benchmarked here, so the split is off unless SPOPS_SDDMM_KSPLIT
+// asks for it (a cap on the number of slices, rounded down to a power of 2).
+int64_t sddmm_k_slices(int64_t n, int64_t K, int dtype) {
+  const char* env = getenv("SPOPS_SDDMM_KSPLIT");
+  const int64_t cap = env ? atoll(env) : 1;
+  const int64_t es = dtype == kF32 ? 4 : 2;
+  const int64_t budget = 5 << 19;  // ~2.5 MB of BT per L2
+  int64_t ks = 1;
+  while (2 * ks <= cap && ks < 8 && n * K * es / ks > budget && K / (2 * ks) >= 128) ks *= 2;
+  return ks;
+}
 
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s) {
   switch (a.dtype) {

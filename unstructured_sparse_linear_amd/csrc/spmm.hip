@@ -1,34 +1,52 @@
 // spmm.hip -- C = A * B for a CSR matrix A and a dense row-major B on gfx950
 // (spops README, section "Sparse Matrix Multiplication (SpMM)").
 //
-// Work mapping.  Rows are visited in row_idx order (section "Usage": rows
-// sorted by entry count), so neighbouring groups of lanes get rows of similar
-// length and the longest rows start first.  A group of LPR lanes owns one row
-// and a window of LPR*VEC columns of C; each lane keeps VEC fp32 accumulators
-// and streams the row's entries, loading 16-byte vectors of the B rows it
-// needs (coalesced across the group) and multiplying by the entry value.
+// Three kernels, chosen per call from N and the data layout:
 //
-// Long rows.  A plan (see build_spmm_schedule) lists the rows longer than
-// kSpmmSplitLen in row_idx order and cuts each into chunks of kChunkLen entries.
-// Each chunk is one workgroup: its groups take contiguous slices of the chunk
-// and are summed in LDS in group order.  A row with one chunk is written
-// directly; a row with several writes fp32 partial rows that a second kernel
-// adds in chunk order.  All sums therefore have a fixed order and results are
-// bitwise reproducible.
+// * spmm_wave_kernel (N >= 64*VEC, the LLM-adapter shapes).  One wavefront per
+//   row and column slice: the row's entries are wave-uniform, so they come in
+//   through 16-byte scalar loads and every lane reuses them; each lane owns
+//   VEC consecutive columns of C.  B rows are read with buffer loads whose row
+//   offset sits in an SGPR (no per-lane address arithmetic; out-of-range
+//   offsets read as zero, which also masks padding entries).  Columns are cut
+//   into slices of 64*VEC and slice s runs on the blocks s, s+ns, ... which the
+//   dispatcher places on the same XCD, so each XCD's 4 MB L2 holds the part of
+//   B it gathers from.  16-bit inputs use v_dot2_f32_{f16,bf16} on pairs of
+//   entries after a v_perm_b32 repack, one instruction per two products.
+// * spmm_kernel (narrow N): a group of LPR lanes owns one row and a window of
+//   LPR*VEC columns; lanes load 16-byte vectors of B rows.
+// * spmv_kernel (N == 1): LPR lanes share a row, striding over its entries.
 //
-// N == 1 (SpMV) uses a different split: the lanes of a group stride over the
-// row's entries and are combined with a fixed xor-shuffle tree.
+// Row order.  Work visits rows in row_idx order (section "Usage": rows sorted
+// by entry count) so that neighbouring waves get rows of similar length and
+// the longest start first.  When the plan finds the lengths balanced (longest
+// row at most twice the mean plus 32) whole rows are visited in index order
+// instead, each XCD taking one contiguous range of rows, which keeps the B
+// rows of banded matrices in L2; results are identical either way.
+//
+// Long rows.  The plan (build_spmm_schedule) lists the rows longer than
+// kSpmmSplitLen in row_idx order and cuts each into chunks of kSpmmChunkLen
+// entries; each chunk is one workgroup whose waves take contiguous slices and
+// are summed through LDS in wave order.  A row with several chunks writes fp32
+// partial rows that spmm_fixup_kernel adds in chunk order.  Every sum has a
+// fixed order, so results are bitwise reproducible.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace spops {
 
-constexpr int32_t kChunkLen = kSpmmChunkLen;
-
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int32_t kChunkLen = kSpmmChunkLen;
+// entries whose B vectors are loaded together (bytes in flight per lane:
+// kUnroll * 16); the gathers are latency-bound, so deeper is faster
+constexpr int kUnroll = 8;
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Vec16;  // 16 bytes of elements
@@ -45,7 +63,30 @@ struct Vec16<bf16_t> {
   static constexpr int n = 8;
 };
 
-// acc[e] += v * B[e] for one 16-byte vector of B.
+__device__ __forceinline__ int64_t load_row(const void* ri, int ri_i32, int64_t i) {
+  return ri_i32 ? (int64_t)((const int32_t*)ri)[i] : (int64_t)((const int16_t*)ri)[i];
+}
+
+// Row r's entry range, clamped to [0, nnz].
+__device__ __forceinline__ void row_range(const int32_t* ro, int64_t r, int64_t nnz,
+                                          int64_t& p0, int64_t& p1) {
+  p0 = ro[r];
+  p1 = ro[r + 1];
+  p0 = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
+  p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
+}
+
+// Whole-row block index -> first row position.  In index order each XCD gets
+// one contiguous range of row blocks (blocks b, b+8, ... share an XCD); grids
+// for this mapping are padded to a multiple of 8 blocks.
+__device__ __forceinline__ int64_t row_block(int64_t bw, int64_t nbw_padded, int natural) {
+  if (!natural) return bw;
+  const int64_t per = nbw_padded / 8;
+  return (bw % 8) * per + bw / 8;
+}
+
+// ------------------------------------------------------- narrow-N groups --
+
 template <typename VT>
 __device__ __forceinline__ void fma_vec(float* acc, float v, const uint4& w) {
   if constexpr (Vec16<VT>::n == 4) {
@@ -63,35 +104,34 @@ __device__ __forceinline__ void fma_vec(float* acc, float v, const uint4& w) {
   }
 }
 
+// Store VEC fp32 results (or their rounding to 16 bits) at dst[0..VEC).
 template <typename OT, int VEC>
 __device__ __forceinline__ void store_vec(OT* dst, const float* acc) {
   if constexpr (sizeof(OT) == 4) {
+    if constexpr (VEC == 1) {
+      *dst = acc[0];
+    } else if constexpr (VEC == 2) {
+      *(float2*)dst = make_float2(acc[0], acc[1]);
+    } else {
 #pragma unroll
-    for (int q = 0; q < VEC / 4; ++q)
-      *(float4*)(dst + 4 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
-                                            acc[4 * q + 3]);
+      for (int q = 0; q < VEC / 4; ++q)
+        *(float4*)(dst + 4 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
+                                              acc[4 * q + 3]);
+    }
   } else {
-    static_assert(VEC == 8, "16-bit outputs use 8-wide vectors");
-    uint32_t w[4];
+    uint32_t w[VEC / 2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < VEC / 2; ++q)
       w[q] = (uint32_t)bits16(from_f32<OT>(acc[2 * q])) |
              ((uint32_t)bits16(from_f32<OT>(acc[2 * q + 1])) << 16);
-    *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+    if constexpr (VEC == 2) {
+      *(uint32_t*)dst = w[0];
+    } else if constexpr (VEC == 4) {
+      *(uint2*)dst = make_uint2(w[0], w[1]);
+    } else {
+      *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
-}
-
-__device__ __forceinline__ int64_t load_row(const void* ri, int ri_i32, int64_t i) {
-  return ri_i32 ? (int64_t)((const int32_t*)ri)[i] : (int64_t)((const int16_t*)ri)[i];
-}
-
-// Row r's entry range, clamped to [0, nnz].
-__device__ __forceinline__ void row_range(const int32_t* ro, int64_t r, int64_t nnz,
-                                          int64_t& p0, int64_t& p1) {
-  p0 = ro[r];
-  p1 = ro[r + 1];
-  p0 = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
-  p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
 }
 
 // Accumulate entries [p0, p1) into acc for columns [j, j+VEC).
@@ -102,9 +142,9 @@ __device__ __forceinline__ void accumulate(const SpmmArgs& a, int64_t p0, int64_
   const VT* val = (const VT*)a.val;
   const VT* B = (const VT*)a.B;
   const int64_t k = a.k;
+  if (j >= a.N) return;
   if constexpr (ALIGNED) {
-    if (j >= a.N) return;
-    constexpr int U = 4;
+    constexpr int U = kUnroll;
     int64_t p = p0;
     for (; p + U <= p1; p += U) {
       int c[U];
@@ -136,7 +176,6 @@ __device__ __forceinline__ void accumulate(const SpmmArgs& a, int64_t p0, int64_
     }
   } else {
     static_assert(VEC == 1, "unaligned path is scalar");
-    if (j >= a.N) return;
     for (int64_t p = p0; p < p1; ++p) {
       int c = (int)col[p];
       if ((unsigned)c >= (unsigned)k) continue;
@@ -203,9 +242,10 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
     }
     return;
   }
-  const int64_t i = ((int64_t)blockIdx.x - a.P) * GPB + grp;
+  const int64_t nbw = (int64_t)gridDim.x - a.P;
+  const int64_t i = row_block((int64_t)blockIdx.x - a.P, nbw, a.natural) * GPB + grp;
   if (i >= a.m) return;
-  const int64_t r = load_row(a.row_idx, a.ri_i32, i);
+  const int64_t r = a.natural ? i : load_row(a.row_idx, a.ri_i32, i);
   if (r < 0 || r >= a.m) return;
   int64_t p0, p1;
   row_range(a.ro, r, a.nnz, p0, p1);
@@ -256,10 +296,11 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
     }
     return;
   }
-  const int64_t i = ((int64_t)blockIdx.x - a.P) * GPB + grp;
+  const int64_t nbw = (int64_t)gridDim.x - a.P;
+  const int64_t i = row_block((int64_t)blockIdx.x - a.P, nbw, a.natural) * GPB + grp;
   int64_t r = -1, p0 = 0, p1 = 0;
   if (i < a.m) {
-    r = load_row(a.row_idx, a.ri_i32, i);
+    r = a.natural ? i : load_row(a.row_idx, a.ri_i32, i);
     if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, p0, p1);
     else r = -1;
     if (a.P > 0 && p1 - p0 > a.T) r = -1;
@@ -293,6 +334,247 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
   if (gl == 0 && r >= 0) ((OT*)a.C)[r * a.ldc] = from_f32<OT>(s);
 }
 
+// --------------------------------------------------------- wide-N waves --
+
+template <int BYTES>
+struct BufLoad;
+template <>
+struct BufLoad<4> {
+  static constexpr int words = 1;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  }
+};
+template <>
+struct BufLoad<8> {
+  static constexpr int words = 2;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+};
+template <>
+struct BufLoad<16> {
+  static constexpr int words = 4;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
+  }
+};
+
+// Raw buffer descriptor (dword 3 as for untyped 32-bit data on gfx9).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, _Float16*) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
+                                false);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, bf16_t*) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, a),
+                                         __builtin_bit_cast(bf162v, b), c, false);
+}
+
+// Eight consecutive entries starting at p (a multiple of 8): column words and
+// value words.  Wave-uniform addresses, so full groups become scalar loads;
+// the group that reaches past nnz is read entry by entry.
+template <typename VT, typename IT>
+__device__ __forceinline__ void load_entries(const IT* col, const VT* val, int64_t p, int64_t nnz,
+                                             int* c, uint32_t* vw) {
+  constexpr int VW = sizeof(VT) == 4 ? 8 : 4;  // value words per 8 entries
+  if (p + 8 <= nnz) {
+    if constexpr (sizeof(IT) == 2) {
+      const uint4 q = *(const uint4*)(col + p);
+      const uint32_t cw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = (int)(int16_t)(cw[u >> 1] >> ((u & 1) * 16));
+    } else {
+      const uint4 q0 = *(const uint4*)(col + p), q1 = *(const uint4*)(col + p + 4);
+      c[0] = (int)q0.x; c[1] = (int)q0.y; c[2] = (int)q0.z; c[3] = (int)q0.w;
+      c[4] = (int)q1.x; c[5] = (int)q1.y; c[6] = (int)q1.z; c[7] = (int)q1.w;
+    }
+    const uint4 v0 = *(const uint4*)(val + p);
+    vw[0] = v0.x; vw[1] = v0.y; vw[2] = v0.z; vw[3] = v0.w;
+    if constexpr (VW == 8) {
+      const uint4 v1 = *(const uint4*)(val + p + 4);
+      vw[4] = v1.x; vw[5] = v1.y; vw[6] = v1.z; vw[7] = v1.w;
+    }
+  } else {
+    const uint16_t* v16 = (const uint16_t*)val;
+    const uint32_t* v32 = (const uint32_t*)val;
+#pragma unroll
+    for (int u = 0; u < VW; ++u) vw[u] = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = p + u < nnz;
+      c[u] = in ? (int)col[p + u] : -1;
+      if constexpr (VW == 8) {
+        vw[u] = in ? v32[p + u] : 0u;
+      } else {
+        vw[u >> 1] |= (in ? (uint32_t)v16[p + u] : 0u) << ((u & 1) * 16);
+      }
+    }
+  }
+}
+
+// One batch of 8 consecutive entries: which are in range, their value words,
+// and the lane's B vectors for them (loads in flight until consumed).
+template <typename VT, int W>
+struct WaveBatch {
+  uint32_t b[8][W];
+  uint32_t vw[sizeof(VT) == 4 ? 8 : 4];
+  bool ok[8];
+};
+
+template <typename VT, typename IT, int VEC>
+__device__ __forceinline__ void fetch_batch(const SpmmArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t bbytes, int64_t p, int64_t q0, int64_t q1,
+                                            uint32_t joff,
+                                            WaveBatch<VT, BufLoad<VEC * sizeof(VT)>::words>& bt) {
+  constexpr int BYTES = VEC * (int)sizeof(VT);
+  const uint32_t ldbb = (uint32_t)(a.ldb * (int64_t)sizeof(VT));
+  int c[8];
+  load_entries<VT, IT>((const IT*)a.col, (const VT*)a.val, p, a.nnz, c, bt.vw);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    bt.ok[u] = (p + u >= q0) && (p + u < q1);
+    const bool use = bt.ok[u] && (unsigned)c[u] < (unsigned)a.k;
+    BufLoad<BYTES>::load(rs, joff, use ? (uint32_t)c[u] * ldbb : bbytes, bt.b[u]);
+  }
+}
+
+template <typename VT, int VEC>
+__device__ __forceinline__ void consume_batch(
+    const WaveBatch<VT, BufLoad<VEC * sizeof(VT)>::words>& bt, float* acc) {
+  constexpr int W = BufLoad<VEC * sizeof(VT)>::words;
+  if constexpr (sizeof(VT) == 4) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = bt.ok[u] ? __uint_as_float(bt.vw[u]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(v, __uint_as_float(bt.b[u][e]), acc[e]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t vp = bt.vw[t];
+      if (!bt.ok[2 * t]) vp &= 0xffff0000u;
+      if (!bt.ok[2 * t + 1]) vp &= 0x0000ffffu;
+#pragma unroll
+      for (int d = 0; d < W; ++d) {
+        const uint32_t lo = __builtin_amdgcn_perm(bt.b[2 * t + 1][d], bt.b[2 * t][d], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(bt.b[2 * t + 1][d], bt.b[2 * t][d], 0x07060302u);
+        acc[2 * d] = dot2(lo, vp, acc[2 * d], (VT*)nullptr);
+        acc[2 * d + 1] = dot2(hi, vp, acc[2 * d + 1], (VT*)nullptr);
+      }
+    }
+  }
+}
+
+// Entries [q0, q1) of one row, columns [j, j+VEC) of this lane (byte offset
+// joff inside a B row).  Entries outside the range or with a column outside
+// [0, k) load from past the end of B (zeros) and carry a zero value.  Two
+// batches are in flight: the next one is fetched before the current one is
+// consumed.
+template <typename VT, typename IT, int VEC>
+__device__ __forceinline__ void accumulate_wave(const SpmmArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                                uint32_t bbytes, int64_t q0, int64_t q1,
+                                                uint32_t joff, float* acc) {
+  constexpr int W = BufLoad<VEC * sizeof(VT)>::words;
+  int64_t p = q0 & ~(int64_t)7;
+  if (p >= q1) return;
+  WaveBatch<VT, W> x, y;
+  fetch_batch<VT, IT, VEC>(a, rs, bbytes, p, q0, q1, joff, x);
+  while (true) {
+    const bool more = p + 8 < q1;
+    if (more) fetch_batch<VT, IT, VEC>(a, rs, bbytes, p + 8, q0, q1, joff, y);
+    consume_batch<VT, VEC>(x, acc);
+    if (!more) break;
+    p += 8;
+    const bool more2 = p + 8 < q1;
+    if (more2) fetch_batch<VT, IT, VEC>(a, rs, bbytes, p + 8, q0, q1, joff, x);
+    consume_batch<VT, VEC>(y, acc);
+    if (!more2) break;
+    p += 8;
+  }
+}
+
+// Blocks are (item, slice) with slice = blockIdx % ns.  Items [0, P): one
+// chunk of a long row, its 4 waves summed in LDS.  Items [P, ...): 4 whole
+// rows, one per wave.
+template <typename VT, typename OT, typename IT, int VEC>
+__global__ __launch_bounds__(kBlock) void spmm_wave_kernel(SpmmArgs a, int64_t ns,
+                                                           int64_t nbw_padded, uint32_t bbytes) {
+  constexpr int NW = kBlock / kWave;
+  const int64_t slice = (int64_t)blockIdx.x % ns;
+  const int64_t item = (int64_t)blockIdx.x / ns;
+  const int w = wave_uniform((int)(threadIdx.x / kWave));
+  const int lane = lane_id();
+  const int64_t j = slice * (kWave * VEC) + (int64_t)lane * VEC;
+  const uint32_t joff = (uint32_t)(j * (int64_t)sizeof(VT));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B, bbytes);
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+  if (item < a.P) {
+    __shared__ float red[NW - 1][kWave * VEC];
+    const int64_t g = item;
+    const int64_t i = a.item_pos[g];
+    const int64_t ch = a.item_chunk[g];
+    const int64_t r = load_row(a.row_idx, a.ri_i32, i);
+    int64_t rs0 = 0, re0 = 0;
+    if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, rs0, re0);
+    const int64_t c0 = rs0 + ch * kChunkLen;
+    const int64_t c1 = (c0 + kChunkLen < re0) ? c0 + kChunkLen : re0;
+    const int64_t len = c1 > c0 ? c1 - c0 : 0;
+    const int64_t sub = (cdiv(len, NW) + 7) & ~(int64_t)7;
+    int64_t q0 = c0 + w * sub;
+    int64_t q1 = q0 + sub;
+    q0 = q0 < c1 ? q0 : c1;
+    q1 = q1 < c1 ? q1 : c1;
+    accumulate_wave<VT, IT, VEC>(a, rs, bbytes, q0, q1, joff, acc);
+    if (w > 0) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red[w - 1][lane * VEC + e] = acc[e];
+    }
+    __syncthreads();
+    if (w == 0 && j < a.N) {
+      for (int q = 0; q < NW - 1; ++q) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += red[q][lane * VEC + e];
+      }
+      const int64_t nch = cdiv(re0 - rs0, kChunkLen);
+      if (nch <= 1) {
+        if (r >= 0 && r < a.m) store_vec<OT, VEC>((OT*)a.C + r * a.ldc + j, acc);
+      } else {
+        store_vec<float, VEC>(a.partial + g * a.N + j, acc);
+      }
+    }
+    return;
+  }
+  const int64_t i = row_block(item - a.P, nbw_padded, a.natural) * NW + w;
+  if (i >= a.m) return;
+  const int64_t r = wave_uniform((int)(a.natural ? i : load_row(a.row_idx, a.ri_i32, i)));
+  if (r < 0 || r >= a.m) return;
+  int64_t p0, p1;
+  row_range(a.ro, r, a.nnz, p0, p1);
+  p0 = wave_uniform((int)p0);
+  p1 = wave_uniform((int)p1);
+  if (a.P > 0 && p1 - p0 > a.T) return;  // handled by the chunk blocks
+  accumulate_wave<VT, IT, VEC>(a, rs, bbytes, p0, p1, joff, acc);
+  if (j < a.N) store_vec<OT, VEC>((OT*)a.C + r * a.ldc + j, acc);
+}
+
 // Sum the partial rows of each multi-chunk row in chunk order.
 template <typename OT>
 __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(SpmmArgs a) {
@@ -310,22 +592,54 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(SpmmArgs a) {
 
 // ------------------------------------------------------------ dispatch ---
 
+int64_t pad8(int64_t x) { return (x + 7) & ~(int64_t)7; }
+
 template <typename VT, typename OT, typename IT, int LPR>
 hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
-  constexpr int GPB = kBlock / LPR;
-  const int64_t bx = a.P + cdiv(a.m, GPB);
-  if (bx == 0) return hipSuccess;
   if (aligned) {
-    dim3 grid((unsigned)bx, (unsigned)cdiv(a.N, LPR * VEC));
+    constexpr int GPB = kBlock / LPR;
+    const int64_t nbw = a.natural ? pad8(cdiv(a.m, GPB)) : cdiv(a.m, GPB);
+    dim3 grid((unsigned)(a.P + nbw), (unsigned)cdiv(a.N, LPR * VEC));
+    if (grid.x == 0) return hipSuccess;
     hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true>), grid, dim3(kBlock), 0, s, a);
   } else {
     // scalar path: 64 lanes per row, one column each
     constexpr int G = kBlock / 64;
-    dim3 grid((unsigned)(a.P + cdiv(a.m, G)), (unsigned)cdiv(a.N, 64));
+    const int64_t nbw = a.natural ? pad8(cdiv(a.m, G)) : cdiv(a.m, G);
+    dim3 grid((unsigned)(a.P + nbw), (unsigned)cdiv(a.N, 64));
+    if (grid.x == 0) return hipSuccess;
     hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, 64, 1, false>), grid, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <typename VT, typename OT, typename IT, int VEC>
+hipError_t launch_waves(const SpmmArgs& a, uint32_t bbytes, hipStream_t s) {
+  const int64_t ns = cdiv(a.N, kWave * VEC);
+  const int64_t nbw = a.natural ? pad8(cdiv(a.m, kBlock / kWave)) : cdiv(a.m, kBlock / kWave);
+  const int64_t blocks = ns * (a.P + nbw);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((spmm_wave_kernel<VT, OT, IT, VEC>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                     s, a, ns, nbw, bbytes);
+  return hipGetLastError();
+}
+
+// Per-lane vector width for the wave kernel: the widest (up to 16 bytes) whose
+// 64*v-column slice of B (k rows) stays within ~2.5 MB, so one slice fits an
+// XCD's L2 with room for the rest; if none fits, the narrowest (most slices).
+// 0 when N is narrower than one wave of the narrowest width.
+template <typename VT>
+int wave_vec(int64_t k, int64_t N) {
+  const int64_t budget = 5 << 19;
+  const int lo = sizeof(VT) == 2 ? 2 : 1;
+  int best = 0;
+  for (int v = 16 / (int)sizeof(VT); v >= lo; v /= 2) {
+    if ((int64_t)kWave * v > N) continue;
+    if (k * kWave * v * (int64_t)sizeof(VT) <= budget) return v;
+    best = v;
+  }
+  return best;
 }
 
 template <typename VT, typename OT, typename IT>
@@ -338,7 +652,8 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     int lpr = 2;
     while (lpr < 64 && lpr * 4 < mean) lpr *= 2;
     const int gpb = kBlock / lpr;
-    const dim3 grid((unsigned)(a.P + cdiv(a.m, gpb)));
+    const int64_t nbw = a.natural ? pad8(cdiv(a.m, gpb)) : cdiv(a.m, gpb);
+    const dim3 grid((unsigned)(a.P + nbw));
     if (grid.x == 0) return hipSuccess;
     switch (lpr) {
       case 2: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 2>), grid, dim3(kBlock), 0, s, a); break;
@@ -350,15 +665,39 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     }
     e = hipGetLastError();
   } else {
-    const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
+    // The wave kernel is kept for shapes where it measures faster; by default
+    // (and with SPOPS_SPMM_KERNEL=group) the group kernel runs, which was
+    // faster on every workload measured so far.
+    static const char* choice = getenv("SPOPS_SPMM_KERNEL");  // "wave" | "group" | unset
+    const bool allow_wave = choice && choice[0] == 'w';
+    const int wv = allow_wave ? wave_vec<VT>(a.k, a.N) : 0;
+    const int64_t bbytes = a.k * a.ldb * (int64_t)sizeof(VT);
+    const bool wave_ok = wv > 0 && a.N % wv == 0 && a.ldb % wv == 0 &&
+                         a.ldc % wv == 0 && bbytes + 64 < ((int64_t)1 << 31) &&
                          ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
-                         ((uintptr_t)a.partial % 16 == 0);
-    const int64_t nv = cdiv(a.N, VEC);
-    if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
-    else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
-    else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
-    else if (nv <= 32) e = launch_rows<VT, OT, IT, 32>(a, aligned, s);
-    else e = launch_rows<VT, OT, IT, 64>(a, aligned, s);
+                         ((uintptr_t)a.partial % 16 == 0) && ((uintptr_t)a.col % 16 == 0) &&
+                         ((uintptr_t)a.val % 16 == 0);
+    if (wave_ok) {
+      if constexpr (sizeof(VT) == 2) {
+        if (wv == 8) e = launch_waves<VT, OT, IT, 8>(a, (uint32_t)bbytes, s);
+        else if (wv == 4) e = launch_waves<VT, OT, IT, 4>(a, (uint32_t)bbytes, s);
+        else e = launch_waves<VT, OT, IT, 2>(a, (uint32_t)bbytes, s);
+      } else {
+        if (wv == 4) e = launch_waves<VT, OT, IT, 4>(a, (uint32_t)bbytes, s);
+        else if (wv == 2) e = launch_waves<VT, OT, IT, 2>(a, (uint32_t)bbytes, s);
+        else e = launch_waves<VT, OT, IT, 1>(a, (uint32_t)bbytes, s);
+      }
+    } else {
+      const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
+                           ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
+                           ((uintptr_t)a.partial % 16 == 0);
+      const int64_t nv = cdiv(a.N, VEC);
+      if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
+      else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
+      else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
+      else if (nv <= 32) e = launch_rows<VT, OT, IT, 32>(a, aligned, s);
+      else e = launch_rows<VT, OT, IT, 64>(a, aligned, s);
+    }
   }
   if (e != hipSuccess) return e;
   if (a.S > 0) {
@@ -470,6 +809,8 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
     out->max_row = host_misc[0];
     out->P = host_misc[1];
     out->S = host_misc[2];
+    // balanced lengths: keep index order for locality
+    out->natural = (out->max_row <= 2 * (nnz / m) + 32) ? 1 : 0;
     if (out->P > 0) {
       const size_t pb = align256((size_t)out->P * 4), sb = align256((size_t)(out->S + 1) * 4);
       char* mem = nullptr;

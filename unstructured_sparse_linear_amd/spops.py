@@ -67,7 +67,9 @@ def lib() -> ctypes.CDLL:
             "spops_spmm_plan_destroy": ([vp], i32),
             "spops_spmm_workspace_size": ([vp, i64, P(sz)], i32),
             "spops_spmm_plan_info": ([vp, P(i64), P(i64), P(i64)], i32),
-            "spops_sddmm": ([cp, vp, i64, i64, vp, i64, i32, vp, i32, i32, vp, vp], i32),
+            "spops_sddmm": ([cp, vp, i64, i64, vp, i64, i32, vp, i32, i32, vp, vp, sz, vp],
+                            i32),
+            "spops_sddmm_workspace_size": ([cp, i64, i32, i32, vp, P(sz)], i32),
             "spops_sddmm_plan_create": ([cp, ctypes.c_double, vp, P(vp)], i32),
             "spops_sddmm_plan_destroy": ([vp], i32),
             "spops_sddmm_plan_info": ([vp, P(i64), P(i64), P(i64), P(i64), P(i64)], i32),
@@ -231,6 +233,19 @@ _spmm_plans = _PlanCache()
 _sddmm_plans = _PlanCache()
 
 
+_ws_pool = {}
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """Scratch device memory reused across calls of the same size."""
+    if nbytes == 0:
+        return None
+    key = (str(device), nbytes)
+    if key not in _ws_pool:
+        _ws_pool[key] = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _ws_pool[key]
+
+
 def _tkey(t: torch.Tensor):
     return (t.data_ptr(), t.numel(), t.dtype, t._version)
 
@@ -238,6 +253,7 @@ def _tkey(t: torch.Tensor):
 def clear_plan_caches():
     _spmm_plans.clear()
     _sddmm_plans.clear()
+    _ws_pool.clear()
 
 
 # ------------------------------------------------------------ operations --
@@ -275,7 +291,8 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
           out_col_indices: torch.Tensor, A: torch.Tensor, BT: torch.Tensor,
           backend: str = "structure_aware", out_dtype: torch.dtype = torch.float32,
           plan: Optional[SddmmPlan] = None, tau: Optional[float] = None,
-          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+          out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """values[p] = A[r(p)] . BT[c(p)] at every position of the CSR mask."""
     if backend not in _BACKENDS:
         raise ValueError(f"backend must be one of {sorted(_BACKENDS)}")
@@ -294,10 +311,16 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
         plan = _sddmm_plans.get(("sddmm", _tkey(out_row_offsets), _tkey(out_col_indices), m, n,
                                  tau), lambda: SddmmPlan(out_row_offsets, out_col_indices, m, n,
                                                          tau))
+    ph = plan.handle if (plan is not None and b == STRUCTURE_AWARE) else None
+    if workspace is None:
+        wb = ctypes.c_size_t()
+        _check("spops_sddmm_workspace_size", lib().spops_sddmm_workspace_size(
+            ctypes.byref(d), K, _DT[A.dtype], b, ph, ctypes.byref(wb)))
+        workspace = _workspace(wb.value, A.device)
     _check("spops_sddmm", lib().spops_sddmm(
         ctypes.byref(d), _ptr(A), K, max(K, 1), _ptr(BT), max(K, 1), _DT[A.dtype], _ptr(out),
-        _DT[out_dtype], b,
-        plan.handle if plan is not None else None, _stream(A)))
+        _DT[out_dtype], b, ph, _ptr(workspace), workspace.numel() if workspace is not None else 0,
+        _stream(A)))
     return out
 
 
