@@ -148,12 +148,14 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
                          const spops_sddmm_plan* plan, void* workspace, size_t workspace_bytes,
                          void* hip_stream);
 
-/* Optional workspace of spops_sddmm.  When BT is larger than one XCD's L2,
- * the general kernel splits K into slices that run on different XCDs and
- * sums their fp32 partial products in a fixed order; that needs this many
- * bytes.  A smaller (or NULL) workspace runs without the split: same
- * definition, possibly slower.  `plan` as for spops_sddmm (NULL for the
- * general backend). */
+/* Optional workspace of spops_sddmm.  The general kernel can split K into
+ * slices that run on different XCDs (so each L2 holds one slice of BT) and
+ * sum their fp32 partial products in a fixed order; when that split is
+ * enabled (environment variable SPOPS_SDDMM_KSPLIT, a cap on the number of
+ * slices) it needs this many bytes.  A smaller (or NULL) workspace runs
+ * without the split: same definition.  The structure-aware backend on 16-bit
+ * inputs needs none.  `plan` as for spops_sddmm (NULL for the general
+ * backend). */
 spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
                                         spops_sddmm_backend backend,
                                         const spops_sddmm_plan* plan, size_t* bytes);

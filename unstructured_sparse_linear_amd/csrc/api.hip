@@ -238,11 +238,11 @@ spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_
   if (st != SPOPS_OK) return st;
   if (!dtype_ok(in_type)) return SPOPS_ERR_DTYPE;
   if (K < 0) return SPOPS_ERR_SHAPE;
-  int64_t count = mask->nnz;
-  if (backend == SPOPS_SDDMM_STRUCTURE_AWARE && plan && in_type != SPOPS_F32 && K % 8 == 0)
-    count = plan->dev.rest_nnz;
+  // the structure-aware path (16-bit inputs, K a multiple of 8) needs none
+  if (backend == SPOPS_SDDMM_STRUCTURE_AWARE && in_type != SPOPS_F32 && K % 8 == 0 && K > 0)
+    return SPOPS_OK;
   const int64_t ks = sddmm_k_slices(mask->cols, K, in_type);
-  if (ks > 1 && count > 0) *bytes = align256((size_t)(ks * count) * 4);
+  if (ks > 1 && mask->nnz > 0) *bytes = align256((size_t)(ks * mask->nnz) * 4);
   return SPOPS_OK;
 }
 
@@ -308,11 +308,24 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   const SddmmPlanDev& P = plan->dev;
   hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type, s);
   if (e == hipSuccess && P.rest_nnz > 0) {
-    SddmmArgs r = g;
-    r.ro = P.rest_ro;
+    SddmmListArgs r{};
+    r.m = mask->rows;
+    r.n = mask->cols;
+    r.K = K;
+    r.lda = lda;
+    r.ldbt = ldbt;
     r.pos = P.rest_pos;
-    r.count = P.rest_nnz;
-    e = launch_sddmm_general(with_split(r), s);
+    r.rows = P.rest_row;
+    r.col = mask->col_idx;
+    r.col_i32 = mask->col_type == SPOPS_I32;
+    r.A = A;
+    r.BT = BT;
+    r.out = out_values;
+    r.dtype = in_type;
+    r.out_dtype = out_type;
+    r.nb = P.nb;
+    for (int b = 0; b <= P.nb; ++b) r.bstart[b] = P.bucket_start[b];
+    e = launch_sddmm_list(r, s);
   }
   if (own) {
     hipError_t e2 = hipStreamSynchronize(s);

@@ -109,6 +109,7 @@ int64_t sddmm_k_slices(int64_t n, int64_t K, int dtype);
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s);
 
 // Structure-aware SDDMM plan (device data) and its dense-tile kernel.
+constexpr int kMaxBuckets = 8;
 struct SddmmPlanDev {
   int64_t m = 0, n = 0, nnz = 0;
   double tau = 0;
@@ -124,8 +125,12 @@ struct SddmmPlanDev {
   int32_t* tile_start = nullptr; // [tiles+1] entry ranges per tile
   int32_t* ent_pos = nullptr;    // [tiled_nnz] mask position
   int32_t* ent_rc = nullptr;     // [tiled_nnz] (local row << 16) | local col
-  int32_t* rest_ro = nullptr;    // [m+1]
-  int32_t* rest_pos = nullptr;   // [rest_nnz]
+  // remainder: entries sorted by (column bucket, row); bucket b holds
+  // columns [b*n/nb, (b+1)*n/nb) and runs on XCD b
+  int nb = 1;
+  int64_t bucket_start[kMaxBuckets + 1] = {};  // host copy, offsets into rest_*
+  int32_t* rest_pos = nullptr;   // [rest_nnz] mask position
+  int32_t* rest_row = nullptr;   // [rest_nnz] row
   void* mem = nullptr;
   // identity of the mask it was built for
   const void* mask_ro = nullptr;
@@ -138,6 +143,24 @@ void free_sddmm_plan(SddmmPlanDev* p);
 hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, int64_t lda,
                               const void* BT, int64_t ldbt, int dtype, void* out, int out_dtype,
                               hipStream_t s);
+
+// General SDDMM over an explicit entry list (the plan's remainder): entry j
+// is mask position pos[j] in row rows[j]; entries of bucket b are
+// [bstart[b], bstart[b+1]) and run on the blocks b, b+nb, ...
+struct SddmmListArgs {
+  int64_t m, n, K, lda, ldbt;
+  const int32_t* pos;
+  const int32_t* rows;
+  const void* col;
+  int col_i32;
+  const void* A;
+  const void* BT;
+  void* out;
+  int dtype, out_dtype;
+  int nb;
+  int64_t bstart[kMaxBuckets + 1];
+};
+hipError_t launch_sddmm_list(const SddmmListArgs& a, hipStream_t s);
 
 // --------------------------------------------------------------- csr_add --
 hipError_t launch_csr_add(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,

@@ -289,6 +289,152 @@ hipError_t launch_typed(SddmmArgs a, hipStream_t s) {
   return launch_vec<VT, OT, IT, 64, 8>(a, s);
 }
 
+// ---------------------------------------------------------- entry lists --
+
+// Entry list (the structure-aware plan's remainder): entry j is mask position
+// pos[j] in row rows[j]; rows ascend inside a bucket.  Bucket b = blockIdx % nb
+// (its blocks share XCD b), so the BT rows gathered by one XCD come from one
+// column range.  Groups of LPN lanes split K as in sddmm_vec_kernel; A's row
+// slice is reloaded only when the row changes.
+template <typename VT, typename OT, typename IT, int LPN, int KV>
+__global__ __launch_bounds__(kBlock) void sddmm_list_kernel(SddmmListArgs a) {
+  using TR = Traits<VT>;
+  constexpr int VEC = TR::vec;
+  constexpr int G = kWave / LPN;
+  constexpr int E = entries_per_wave<LPN>();
+  constexpr int U = 4;
+  const int b = (int)(blockIdx.x % (unsigned)a.nb);
+  const int64_t wave = (int64_t)(blockIdx.x / (unsigned)a.nb) * (kBlock / kWave) +
+                       threadIdx.x / kWave;
+  const int64_t bs = a.bstart[b], be = a.bstart[b + 1];
+  const int64_t wb = bs + wave * E;
+  if (wb >= be) return;
+  const int64_t we = (wb + E < be) ? wb + E : be;
+  const int lane = lane_id();
+  const int grp = lane / LPN;
+  const int gl = lane % LPN;
+  const int64_t per = cdiv(we - wb, G);
+  int64_t e = wb + grp * per;
+  const int64_t e1 = (e + per < we) ? e + per : we;
+  if (e > we) e = we;
+
+  const int64_t kvec = a.K / VEC;
+  const int64_t npass = cdiv(kvec, (int64_t)LPN * KV);
+  const VT* A = (const VT*)a.A;
+  const VT* BT = (const VT*)a.BT;
+  const IT* col = (const IT*)a.col;
+  OT* out = (OT*)a.out;
+  const int64_t n = a.n;
+
+  auto load_slice = [&](const VT* rowp, int64_t pass, uint4* dst) {
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int64_t kv = (pass * KV + v) * LPN + gl;
+      dst[v] = kv < kvec ? *(const uint4*)(rowp + kv * VEC) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  int64_t rcur = -1;
+  uint4 areg[KV];
+  while (e < e1) {
+    if (npass == 1 && e + U <= e1) {
+      int64_t r[U], p[U];
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        r[u] = a.rows[e + u];
+        p[u] = a.pos[e + u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = (int)col[p[u]];
+      if (r[0] == r[U - 1]) {  // rows ascend, so the U entries share a row
+        if (r[0] != rcur) {
+          rcur = r[0];
+          load_slice(A + rcur * a.lda, 0, areg);
+        }
+        uint4 bv[U][KV];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int cc = ((unsigned)c[u] < (unsigned)n) ? c[u] : 0;
+          load_slice(BT + (int64_t)cc * a.ldbt, 0, bv[u]);
+        }
+        float sacc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          sacc[u] = 0.f;
+#pragma unroll
+          for (int v = 0; v < KV; ++v) sacc[u] = TR::dot(areg[v], bv[u][v], sacc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) sacc[u] = group_sum<LPN>(sacc[u]);
+        if (gl == 0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            out[p[u]] = from_f32<OT>(((unsigned)c[u] < (unsigned)n) ? sacc[u] : 0.f);
+        }
+        e += U;
+        continue;
+      }
+    }
+    const int64_t r = a.rows[e];
+    const int64_t p = a.pos[e];
+    const int c = (int)col[p];
+    const int cc = ((unsigned)c < (unsigned)n) ? c : 0;
+    float sacc = 0.f;
+    for (int64_t pass = 0; pass < npass; ++pass) {
+      if (npass > 1 || r != rcur) load_slice(A + r * a.lda, pass, areg);
+      uint4 bv[KV];
+      load_slice(BT + (int64_t)cc * a.ldbt, pass, bv);
+#pragma unroll
+      for (int v = 0; v < KV; ++v) sacc = TR::dot(areg[v], bv[v], sacc);
+    }
+    rcur = npass == 1 ? r : -1;
+    sacc = group_sum<LPN>(sacc);
+    if (gl == 0) out[p] = from_f32<OT>(((unsigned)c < (unsigned)n) ? sacc : 0.f);
+    ++e;
+  }
+}
+
+template <typename VT, typename OT, typename IT, int LPN, int KV>
+hipError_t launch_list(const SddmmListArgs& a, hipStream_t s) {
+  constexpr int E = entries_per_wave<LPN>();
+  int64_t most = 0;
+  for (int b = 0; b < a.nb; ++b) {
+    const int64_t cnt = a.bstart[b + 1] - a.bstart[b];
+    most = cnt > most ? cnt : most;
+  }
+  const int64_t blocks_per_bucket = cdiv(cdiv(most, E), kBlock / kWave);
+  if (blocks_per_bucket == 0) return hipSuccess;
+  hipLaunchKernelGGL((sddmm_list_kernel<VT, OT, IT, LPN, KV>),
+                     dim3((unsigned)(blocks_per_bucket * a.nb)), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename VT, typename OT, typename IT>
+hipError_t launch_list_typed(const SddmmListArgs& a, hipStream_t s) {
+  constexpr int VEC = Traits<VT>::vec;
+  const int64_t kvec = a.K / VEC;
+  if (kvec <= 4) return launch_list<VT, OT, IT, 4, 1>(a, s);
+  if (kvec <= 8) return launch_list<VT, OT, IT, 8, 1>(a, s);
+  if (kvec <= 16) return launch_list<VT, OT, IT, 16, 1>(a, s);
+  if (kvec <= 32) return launch_list<VT, OT, IT, 32, 1>(a, s);
+  if (kvec <= 64) return launch_list<VT, OT, IT, 64, 1>(a, s);
+  if (kvec <= 128) return launch_list<VT, OT, IT, 64, 2>(a, s);
+  if (kvec <= 256) return launch_list<VT, OT, IT, 64, 4>(a, s);
+  return launch_list<VT, OT, IT, 64, 8>(a, s);
+}
+
+template <typename VT>
+hipError_t launch_list_vt(const SddmmListArgs& a, hipStream_t s) {
+  if (a.out_dtype == kF32)
+    return a.col_i32 ? launch_list_typed<VT, float, int32_t>(a, s)
+                     : launch_list_typed<VT, float, int16_t>(a, s);
+  if constexpr (sizeof(VT) == 2)
+    return a.col_i32 ? launch_list_typed<VT, VT, int32_t>(a, s)
+                     : launch_list_typed<VT, VT, int16_t>(a, s);
+  return hipErrorInvalidValue;
+}
+
 template <typename VT>
 hipError_t launch_vt(const SddmmArgs& a, hipStream_t s) {
   if (a.out_dtype == kF32)
@@ -320,6 +466,18 @@ hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s) {
     case kF32: return launch_vt<float>(a, s);
     case kF16: return launch_vt<_Float16>(a, s);
     case kBF16: return launch_vt<bf16_t>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// The list kernel needs 16-byte vectors along K (K, lda, ldbt multiples of
+// the vector width, 16-byte aligned A and BT); the caller checks.
+hipError_t launch_sddmm_list(const SddmmListArgs& a, hipStream_t s) {
+  if (a.nb < 1 || a.nb > kMaxBuckets) return hipErrorInvalidValue;
+  switch (a.dtype) {
+    case kF32: return launch_list_vt<float>(a, s);
+    case kF16: return launch_list_vt<_Float16>(a, s);
+    case kBF16: return launch_list_vt<bf16_t>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -18,6 +18,8 @@
 // the tile's mask positions from an LDS copy of the block.  Every mask entry
 // belongs to exactly one tile or to the remainder, so each output is written
 // once.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -243,12 +245,15 @@ struct ClassifyArgs {
   const uint32_t* row_rank;  // exclusive rank among dense rows
   const int32_t* col_map;    // dense-column index or -1
   int64_t tiles_a, tiles_a_cols, tiles_b_cols, tiles;
+  int nb;                    // column buckets of the remainder
   uint32_t* key;             // [nnz]
-  uint32_t* rc;              // [nnz]
-  uint32_t* rest_cnt;        // [m]
+  uint32_t* rc;              // [nnz] in-tile coordinates, or the row (remainder)
+  uint32_t* rest_total;      // number of remainder entries (accumulated)
 };
 
-// 16 lanes per row: tile key and in-tile coordinates of every entry.
+// 16 lanes per row: tile key and in-tile coordinates of every entry; an
+// entry of neither region gets key tiles + (its column bucket) and keeps its
+// row in rc.
 template <typename IT>
 __global__ void classify_kernel(ClassifyArgs a) {
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
@@ -274,25 +279,33 @@ __global__ void classify_kernel(ClassifyArgs a) {
       key = (uint32_t)(a.tiles_a + (cr / TM) * a.tiles_b_cols + hc / TN);
       rc = ((uint32_t)(cr % TM) << 16) | (uint32_t)(hc % TN);
     } else {
-      key = (uint32_t)a.tiles;
+      key = (uint32_t)(a.tiles + ((int64_t)c * a.nb) / a.n);
+      rc = (uint32_t)r;
       ++rest;
     }
     a.key[p] = key;
     a.rc[p] = rc;
   }
   for (int o = 8; o > 0; o >>= 1) rest += __shfl_xor(rest, o, 16);
-  if (sub == 0) a.rest_cnt[r] = rest;
+  if (sub == 0 && rest) atomicAdd(a.rest_total, rest);
 }
 
-// Tile boundaries (tile_start[t] = first sorted entry with key >= t, for
-// t in [0, tiles+1]) and the gathered in-tile coordinates.
+// All remainder entries into one bucket (keys tiles+b -> tiles).
+__global__ void merge_buckets_kernel(uint32_t* key, int64_t nnz, uint32_t tiles) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p < nnz && key[p] > tiles) key[p] = tiles;
+}
+
+// Key boundaries (tile_start[t] = first sorted entry with key >= t, for
+// t in [0, nkeys]: tiles, then the remainder buckets) and the gathered
+// in-tile coordinates / remainder rows.
 __global__ void tile_bounds_kernel(const uint32_t* skey, const uint32_t* src, const uint32_t* rc,
-                                   int64_t nnz, int64_t tiles, int32_t* tile_start,
+                                   int64_t nnz, int64_t nkeys, int32_t* tile_start,
                                    int32_t* ent_pos, int32_t* ent_rc) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q > nnz) return;
   const int64_t kprev = q == 0 ? -1 : (int64_t)skey[q - 1];
-  const int64_t kcur = q == nnz ? tiles + 1 : (int64_t)skey[q];
+  const int64_t kcur = q == nnz ? nkeys : (int64_t)skey[q];
   for (int64_t k = kprev + 1; k <= kcur; ++k) tile_start[k] = (int32_t)q;
   if (q == nnz) return;
   const uint32_t p = src[q];
@@ -342,7 +355,6 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
   if (e != hipSuccess) return e;
   uint32_t* hot = (uint32_t*)tmp;
   uint32_t* rrank = (uint32_t*)(tmp + mb);
-  uint32_t* rest_cnt = (uint32_t*)(tmp + 2 * mb);
   uint32_t* ccnt = (uint32_t*)(tmp + 3 * mb);
   uint32_t* cflag = (uint32_t*)(tmp + 3 * mb + nb);
   uint32_t* crank = (uint32_t*)(tmp + 3 * mb + 2 * nb);
@@ -395,12 +407,21 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
     out->tiles_b_cols = Hc > 0 ? cdiv(Hc, TN) : 0;
     const int64_t tiles_b = (Hc > 0 && mc > 0) ? cdiv(mc, TM) * out->tiles_b_cols : 0;
     out->tiles = out->tiles_a + tiles_b;
+    // remainder column buckets, one per XCD when there are enough columns
+    // (revisited below once the remainder is counted)
+    out->nb = n >= 1024 ? kMaxBuckets : 1;
+    int forced = 0;
+    if (const char* env = getenv("SPOPS_SDDMM_BUCKETS")) {
+      const int v = atoi(env);
+      out->nb = v < 1 ? 1 : (v > kMaxBuckets ? kMaxBuckets : v);
+      forced = 1;
+    }
     // plan memory
     const size_t b_hot = align256((size_t)(H + 1) * 4), b_cold = align256((size_t)(mc + 1) * 4);
     const size_t b_hc = align256((size_t)(Hc + 1) * 4), b_cm = nb;
-    const size_t b_ts = align256((size_t)(out->tiles + 2) * 4);
+    const size_t b_ts = align256((size_t)(out->tiles + kMaxBuckets + 1) * 4);
     char* mem = nullptr;
-    if ((e = hipMalloc(&mem, b_hot + b_cold + b_hc + b_cm + b_ts + 2 * zb + mb)) != hipSuccess)
+    if ((e = hipMalloc(&mem, b_hot + b_cold + b_hc + b_cm + b_ts + 2 * zb)) != hipSuccess)
       break;
     out->mem = mem;
     out->hot_rows = (int32_t*)mem;
@@ -410,7 +431,6 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
     out->tile_start = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm);
     out->ent_pos = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm + b_ts);
     out->ent_rc = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm + b_ts + zb);
-    out->rest_ro = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm + b_ts + 2 * zb);
     if (m > 0)
       hipLaunchKernelGGL(compact_rows_kernel, dim3(gm), dim3(256), 0, s, hot, rrank, m,
                          out->hot_rows, out->cold_rows);
@@ -424,36 +444,48 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
     }
     if ((e = hipGetLastError()) != hipSuccess) break;
     if (m > 0) {
+      if ((e = hipMemsetAsync(dtot + 2, 0, 4, s)) != hipSuccess) break;
       ClassifyArgs ca{ro,   col,       m,     n,    nnz,      hot, rrank, col_map,
                       out->tiles_a, out->tiles_a_cols, out->tiles_b_cols, out->tiles,
-                      key,  rc,  rest_cnt};
+                      out->nb, key,  rc, dtot + 2};
       if (col_i32)
         hipLaunchKernelGGL(classify_kernel<int32_t>, dim3(gm16), dim3(256), 0, s, ca);
       else
         hipLaunchKernelGGL(classify_kernel<int16_t>, dim3(gm16), dim3(256), 0, s, ca);
       if ((e = hipGetLastError()) != hipSuccess) break;
-      // remainder sub-CSR row offsets
-      if ((e = exclusive_scan_u32(rest_cnt, (uint32_t*)out->rest_ro, m, (uint32_t*)out->rest_ro + m,
-                                  scan_ws, s)) != hipSuccess)
+      if ((e = hipMemcpyAsync(htot + 2, dtot + 2, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
         break;
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
+      // Buckets pay when each remaining row keeps several entries per bucket
+      // (A's row is reloaded once per row and bucket): at least 32 remainder
+      // entries per remaining row on average, else one bucket.
+      if (!forced && out->nb > 1 && (int64_t)htot[2] < 32 * (mc > 0 ? mc : 1)) {
+        out->nb = 1;
+        hipLaunchKernelGGL(merge_buckets_kernel, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s,
+                           key, nnz, (uint32_t)out->tiles);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+      }
     }
+    const int64_t nkeys = out->tiles + out->nb;
     if (nnz > 0) {
-      if ((e = radix_sort_u32_iota(key, nnz, bit_length((uint64_t)out->tiles), skey, src,
+      if ((e = radix_sort_u32_iota(key, nnz, bit_length((uint64_t)(nkeys - 1)), skey, src,
                                    radix_ws, s)) != hipSuccess)
         break;
     }
     hipLaunchKernelGGL(tile_bounds_kernel, dim3((unsigned)cdiv(nnz + 1, 256)), dim3(256), 0, s,
-                       skey, src, rc, nnz, out->tiles, out->tile_start, out->ent_pos,
-                       out->ent_rc);
+                       skey, src, rc, nnz, nkeys, out->tile_start, out->ent_pos, out->ent_rc);
     if ((e = hipGetLastError()) != hipSuccess) break;
-    int32_t tiled = 0;
-    if ((e = hipMemcpyAsync(&tiled, out->tile_start + out->tiles, 4, hipMemcpyDeviceToHost, s)) !=
-        hipSuccess)
+    int32_t bounds[kMaxBuckets + 1] = {};
+    if ((e = hipMemcpyAsync(bounds, out->tile_start + out->tiles, (size_t)(out->nb + 1) * 4,
+                            hipMemcpyDeviceToHost, s)) != hipSuccess)
       break;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
+    const int32_t tiled = bounds[0];
     out->tiled_nnz = tiled;
     out->rest_nnz = nnz - tiled;
+    for (int b = 0; b <= out->nb; ++b) out->bucket_start[b] = bounds[b] - tiled;
     out->rest_pos = out->ent_pos + tiled;
+    out->rest_row = out->ent_rc + tiled;
   } while (0);
   hipFree(tmp);
   if (e != hipSuccess) free_sddmm_plan(out);

@@ -196,19 +196,24 @@ __device__ __forceinline__ void write_out(OT* dst, int64_t j, int64_t N, const f
 
 // Blocks [0, P): one chunk of a long row each.  Blocks [P, ...): kBlock/LPR
 // whole rows each (rows longer than the split length are skipped there).
+// Column windows: window w of LPR*VEC columns runs on blocks w, w+nwin, ...
+// which the dispatcher places on the same XCD(s), so each XCD's L2 serves a
+// fixed slice of B.
 template <typename VT, typename OT, typename IT, int LPR, int VEC, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
+__global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) {
   constexpr int GPB = kBlock / LPR;  // groups per block
   const int grp = threadIdx.x / LPR;
   const int gl = threadIdx.x % LPR;
-  const int64_t j = (int64_t)blockIdx.y * (LPR * VEC) + (int64_t)gl * VEC;
+  const int64_t bx = (int64_t)blockIdx.x / nwin;
+  const int64_t win = (int64_t)blockIdx.x % nwin;
+  const int64_t j = win * (LPR * VEC) + (int64_t)gl * VEC;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  if ((int64_t)blockIdx.x < a.P) {
+  if (bx < a.P) {
     __shared__ float red[GPB > 1 ? GPB - 1 : 1][LPR * VEC];
-    const int64_t g = blockIdx.x;
+    const int64_t g = bx;
     const int64_t i = a.item_pos[g];
     const int64_t ch = a.item_chunk[g];
     const int64_t r = load_row(a.row_idx, a.ri_i32, i);
@@ -242,8 +247,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
     }
     return;
   }
-  const int64_t nbw = (int64_t)gridDim.x - a.P;
-  const int64_t i = row_block((int64_t)blockIdx.x - a.P, nbw, a.natural) * GPB + grp;
+  const int64_t nbw = (int64_t)gridDim.x / nwin - a.P;
+  const int64_t i = row_block(bx - a.P, nbw, a.natural) * GPB + grp;
   if (i >= a.m) return;
   const int64_t r = a.natural ? i : load_row(a.row_idx, a.ri_i32, i);
   if (r < 0 || r >= a.m) return;
@@ -600,16 +605,20 @@ hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
   if (aligned) {
     constexpr int GPB = kBlock / LPR;
     const int64_t nbw = a.natural ? pad8(cdiv(a.m, GPB)) : cdiv(a.m, GPB);
-    dim3 grid((unsigned)(a.P + nbw), (unsigned)cdiv(a.N, LPR * VEC));
-    if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true>), grid, dim3(kBlock), 0, s, a);
+    const int64_t nwin = cdiv(a.N, LPR * VEC);
+    const int64_t blocks = (a.P + nbw) * nwin;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, nwin);
   } else {
     // scalar path: 64 lanes per row, one column each
     constexpr int G = kBlock / 64;
     const int64_t nbw = a.natural ? pad8(cdiv(a.m, G)) : cdiv(a.m, G);
-    dim3 grid((unsigned)(a.P + nbw), (unsigned)cdiv(a.N, 64));
-    if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, 64, 1, false>), grid, dim3(kBlock), 0, s, a);
+    const int64_t nwin = cdiv(a.N, 64);
+    const int64_t blocks = (a.P + nbw) * nwin;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, 64, 1, false>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, nwin);
   }
   return hipGetLastError();
 }
