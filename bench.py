@@ -64,7 +64,22 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
+
+
+def copy_calibration(steps):
+    """Plain device-to-device copies of a known size: what the HBM byte
+    counters read for them calibrates the counters of the real kernels."""
+    import torch
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": steps}))
 
 
 def alg_bytes(A, N, K, dt):
@@ -154,6 +169,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards without collectives; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     import torch
 
     import unstructured_sparse_linear_amd as S
