@@ -291,123 +291,281 @@ hipError_t launch_typed(SddmmArgs a, hipStream_t s) {
 
 // ---------------------------------------------------------- entry lists --
 
+// Cross-lane exchanges without LDS.  For a partner offset o <= 8 a DPP
+// move gives every lane the value of a lane in the other half of its aligned
+// 2o-lane block (o = 1, 2: lane ^ o; o = 4: mirror inside 8 lanes; o = 8:
+// mirror inside 16 lanes).  For o = 16 and 32 gfx950's v_permlane16_swap and
+// v_permlane32_swap swap odd 16-lane rows of x with even rows of y, and the
+// upper 32 lanes of x with the lower 32 of y; adding the two results gives,
+// in the lower half of every 2o-lane block, x summed with its partner lane
+// and, in the upper half, y summed with its partner lane.
+template <int O>
+__device__ __forceinline__ float dpp_partner(float v) {
+  constexpr int ctrl = O == 1 ? 0xB1 : O == 2 ? 0x4E : O == 4 ? 0x141 : 0x140;
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8, "DPP partner offsets are 1, 2, 4, 8");
+  return __uint_as_float(
+      __builtin_amdgcn_update_dpp(0u, __float_as_uint(v), ctrl, 0xF, 0xF, false));
+}
+template <int O>
+__device__ __forceinline__ float swap_sum(float x, float y) {
+  static_assert(O == 16 || O == 32, "swap offsets are 16, 32");
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+// One halving step at offset O: lanes whose bit O is clear keep values
+// [0, H) and add their partner's; the others keep [H, 2H).
+template <int O, int H, int U>
+__device__ __forceinline__ void halve(float (&w)[U], int gl) {
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    if constexpr (O >= 16) {
+      w[j] = swap_sum<O>(w[j], w[j + H]);
+    } else {
+      const bool up = (gl & O) != 0;
+      const float send = up ? w[j] : w[j + H];
+      const float keep = up ? w[j + H] : w[j];
+      w[j] = keep + dpp_partner<O>(send);
+    }
+  }
+}
+template <int O>
+__device__ __forceinline__ float pair_sum(float v) {
+  if constexpr (O >= 16)
+    return swap_sum<O>(v, v);
+  else
+    return v + dpp_partner<O>(v);
+}
+
+// Sum of U values over aligned groups of LPN lanes in log2(LPN) exchange
+// steps instead of U*log2(LPN): log2(U) halving steps at offsets LPN/2,
+// LPN/4, ... leave one value per lane, then pair sums over the remaining
+// LPN/U lanes.  On return lane gl of a group holds the total of value
+// gl / (LPN/U).  The order of additions is fixed for every lane.
+template <int LPN, int U>
+__device__ __forceinline__ float group_sum_multi(const float (&v)[U], int gl) {
+  static_assert(U >= 1 && U <= 4 && U <= LPN && (U & (U - 1)) == 0, "U in {1, 2, 4}, U <= LPN");
+  float w[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) w[j] = v[j];
+  if constexpr (U >= 2) halve<LPN / 2, U / 2>(w, gl);
+  if constexpr (U >= 4) halve<LPN / 4, U / 4>(w, gl);
+  constexpr int S = LPN / U;
+  float t = w[0];
+  if constexpr (S >= 64) t = pair_sum<32>(t);
+  if constexpr (S >= 32) t = pair_sum<16>(t);
+  if constexpr (S >= 16) t = pair_sum<8>(t);
+  if constexpr (S >= 8) t = pair_sum<4>(t);
+  if constexpr (S >= 4) t = pair_sum<2>(t);
+  if constexpr (S >= 2) t = pair_sum<1>(t);
+  return t;
+}
+
 // Entry list (the structure-aware plan's remainder): entry j is mask position
 // pos[j] in row rows[j]; rows ascend inside a bucket.  Bucket b = blockIdx % nb
 // (its blocks share XCD b), so the BT rows gathered by one XCD come from one
-// column range.  Groups of LPN lanes split K as in sddmm_vec_kernel; A's row
-// slice is reloaded only when the row changes.
-template <typename VT, typename OT, typename IT, int LPN, int KV>
-__global__ __launch_bounds__(kBlock) void sddmm_list_kernel(SddmmListArgs a) {
+// column range.
+//
+// A wave takes E consecutive entries of its bucket and first loads one
+// entry's row, position and column per lane, so the loop below issues only
+// operand loads.  The wave is cut into groups of LPN lanes that split K into
+// 16-byte vectors (lane l holds vectors v*LPN + l, so a group's loads of a row
+// are contiguous); group g owns entries [g*E/G, (g+1)*E/G).  A step of a group
+// takes up to U consecutive entries of one row: A's row slice is loaded into
+// registers when the row changes and reused otherwise, the U rows of BT are
+// loaded together, and the U dot products are reduced together.  When K needs
+// more than one pass of LPN*KV vectors, A is reloaded per pass.
+template <typename VT, typename OT, typename IT, int LPN, int KV, int U, int E, bool FULL>
+__global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
+  static_assert(E <= kWave && E % (kWave / LPN) == 0, "one entry per lane");
   using TR = Traits<VT>;
   constexpr int VEC = TR::vec;
   constexpr int G = kWave / LPN;
-  constexpr int E = entries_per_wave<LPN>();
-  constexpr int U = 4;
+  constexpr int EG = E / G;
+  // One wave per workgroup: the wave index is blockIdx, a scalar, so the
+  // loop bounds and the rows derived from it stay in scalar registers.
+  // The grid is a multiple of nb; a wave takes chunks wave, wave + per, ...
   const int b = (int)(blockIdx.x % (unsigned)a.nb);
-  const int64_t wave = (int64_t)(blockIdx.x / (unsigned)a.nb) * (kBlock / kWave) +
-                       threadIdx.x / kWave;
+  const int64_t per = gridDim.x / (unsigned)a.nb;
   const int64_t bs = a.bstart[b], be = a.bstart[b + 1];
+  for (int64_t wave = blockIdx.x / (unsigned)a.nb; bs + wave * E < be; wave += per) {
   const int64_t wb = bs + wave * E;
-  if (wb >= be) return;
-  const int64_t we = (wb + E < be) ? wb + E : be;
+  const int nw = (int)((be - wb < E) ? be - wb : E);
   const int lane = lane_id();
-  const int grp = lane / LPN;
-  const int gl = lane % LPN;
-  const int64_t per = cdiv(we - wb, G);
-  int64_t e = wb + grp * per;
-  const int64_t e1 = (e + per < we) ? e + per : we;
-  if (e > we) e = we;
+  const int g = G == 1 ? 0 : lane / LPN;
+  const int gl = G == 1 ? lane : lane % LPN;
+  const int n = (int)a.n;
+  const IT* col = (const IT*)a.col;
 
+  int my_r = 0, my_p = 0, my_c = -1;
+  if (lane < nw) {
+    my_r = a.rows[wb + lane];
+    my_p = a.pos[wb + lane];
+  }
+  // raw column (validated where it is used, so the first A load below need
+  // not wait for it)
+  if (lane < nw) my_c = (int)col[my_p];
+
+  const int g0 = g * EG;
+  const int g1 = (g0 + EG < nw) ? g0 + EG : nw;  // may be <= g0
   const int64_t kvec = a.K / VEC;
   const int64_t npass = cdiv(kvec, (int64_t)LPN * KV);
   const VT* A = (const VT*)a.A;
   const VT* BT = (const VT*)a.BT;
-  const IT* col = (const IT*)a.col;
   OT* out = (OT*)a.out;
-  const int64_t n = a.n;
+  const bool cache_a = FULL || npass == 1;
 
+  // FULL: K is exactly one pass (kvec == LPN * KV), so no vector is out of
+  // range and the loads of a row differ only by constant offsets.
   auto load_slice = [&](const VT* rowp, int64_t pass, uint4* dst) {
+    if constexpr (FULL) {
+      const uint4* q = (const uint4*)rowp + gl;
 #pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int64_t kv = (pass * KV + v) * LPN + gl;
-      dst[v] = kv < kvec ? *(const uint4*)(rowp + kv * VEC) : make_uint4(0, 0, 0, 0);
+      for (int v = 0; v < KV; ++v) dst[v] = q[v * LPN];
+    } else {
+#pragma unroll
+      for (int v = 0; v < KV; ++v) {
+        const int64_t kv = (pass * KV + v) * LPN + gl;
+        dst[v] = kv < kvec ? *(const uint4*)(rowp + kv * VEC) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // entry q's row, column and position (q is group-uniform)
+  auto fetch = [&](int src, int& r, int& c, int& p) {
+    if constexpr (G == 1) {
+      r = __builtin_amdgcn_readlane(my_r, src);
+      c = __builtin_amdgcn_readlane(my_c, src);
+      p = __builtin_amdgcn_readlane(my_p, src);
+    } else {
+      r = __shfl(my_r, src, 64);
+      c = __shfl(my_c, src, 64);
+      p = __shfl(my_p, src, 64);
     }
   };
 
-  int64_t rcur = -1;
-  uint4 areg[KV];
-  while (e < e1) {
-    if (npass == 1 && e + U <= e1) {
-      int64_t r[U], p[U];
-      int c[U];
+  // The first A row is requested right after the column loads, so its
+  // latency overlaps theirs (vector loads complete in issue order).
+  int rcur = -1;
+  uint4 acur[KV];
+  if (cache_a) {
+    const int r0 = G == 1 ? __builtin_amdgcn_readlane(my_r, 0) : __shfl(my_r, g0, 64);
+    if (g0 < g1) {
+      load_slice(A + (int64_t)r0 * a.lda, 0, acur);
+      rcur = r0;
+    }
+  }
+  int i = g0;
+  while (true) {
+    const bool act = i < g1;
+    if constexpr (G == 1) {
+      if (!act) break;
+    } else {
+      if (__ballot(act) == 0) break;
+    }
+    int r[U], c[U], p[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = i + u;
+      fetch(q < g1 ? q : g0, r[u], c[u], p[u]);
+      if ((unsigned)c[u] >= (unsigned)n) c[u] = -1;
+    }
+    ok[0] = act;
+#pragma unroll
+    for (int u = 1; u < U; ++u) ok[u] = ok[u - 1] && (i + u < g1) && r[u] == r[0];
+    float s[U];
+    uint4 bv[U][KV];
+    if (cache_a) {
+      if (act && r[0] != rcur) {
+        load_slice(A + (int64_t)r[0] * a.lda, 0, acur);
+        rcur = r[0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ok[u]) load_slice(BT + (int64_t)(c[u] >= 0 ? c[u] : 0) * a.ldbt, 0, bv[u]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        r[u] = a.rows[e + u];
-        p[u] = a.pos[e + u];
-      }
+        s[u] = 0.f;
+        if (ok[u]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) c[u] = (int)col[p[u]];
-      if (r[0] == r[U - 1]) {  // rows ascend, so the U entries share a row
-        if (r[0] != rcur) {
-          rcur = r[0];
-          load_slice(A + rcur * a.lda, 0, areg);
+          for (int v = 0; v < KV; ++v) s[u] = TR::dot(acur[v], bv[u][v], s[u]);
         }
-        uint4 bv[U][KV];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) s[u] = 0.f;
+      for (int64_t pass = 0; pass < npass; ++pass) {
+        if (act) load_slice(A + (int64_t)r[0] * a.lda, pass, acur);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ok[u]) load_slice(BT + (int64_t)(c[u] >= 0 ? c[u] : 0) * a.ldbt, pass, bv[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int cc = ((unsigned)c[u] < (unsigned)n) ? c[u] : 0;
-          load_slice(BT + (int64_t)cc * a.ldbt, 0, bv[u]);
+          if (ok[u]) {
+#pragma unroll
+            for (int v = 0; v < KV; ++v) s[u] = TR::dot(acur[v], bv[u][v], s[u]);
+          }
         }
-        float sacc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          sacc[u] = 0.f;
-#pragma unroll
-          for (int v = 0; v < KV; ++v) sacc[u] = TR::dot(areg[v], bv[u][v], sacc[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) sacc[u] = group_sum<LPN>(sacc[u]);
-        if (gl == 0) {
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            out[p[u]] = from_f32<OT>(((unsigned)c[u] < (unsigned)n) ? sacc[u] : 0.f);
-        }
-        e += U;
-        continue;
       }
     }
-    const int64_t r = a.rows[e];
-    const int64_t p = a.pos[e];
-    const int c = (int)col[p];
-    const int cc = ((unsigned)c < (unsigned)n) ? c : 0;
-    float sacc = 0.f;
-    for (int64_t pass = 0; pass < npass; ++pass) {
-      if (npass > 1 || r != rcur) load_slice(A + r * a.lda, pass, areg);
-      uint4 bv[KV];
-      load_slice(BT + (int64_t)cc * a.ldbt, pass, bv);
+    const float t = group_sum_multi<LPN, U>(s, gl);
+    constexpr int SUB = LPN / U;
+    const int uo = gl / SUB;
+    int po = p[0];
+    bool oko = ok[0], cvo = c[0] >= 0;
 #pragma unroll
-      for (int v = 0; v < KV; ++v) sacc = TR::dot(areg[v], bv[v], sacc);
-    }
-    rcur = npass == 1 ? r : -1;
-    sacc = group_sum<LPN>(sacc);
-    if (gl == 0) out[p] = from_f32<OT>(((unsigned)c < (unsigned)n) ? sacc : 0.f);
-    ++e;
+    for (int u = 1; u < U; ++u)
+      if (uo == u) {
+        po = p[u];
+        oko = ok[u];
+        cvo = c[u] >= 0;
+      }
+    if (gl % SUB == 0 && oko) out[po] = from_f32<OT>(cvo ? t : 0.f);
+    int taken = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) taken += ok[u] ? 1 : 0;
+    i += taken;
+  }
   }
 }
 
-template <typename VT, typename OT, typename IT, int LPN, int KV>
-hipError_t launch_list(const SddmmListArgs& a, hipStream_t s) {
-  constexpr int E = entries_per_wave<LPN>();
+template <typename VT, typename OT, typename IT, int LPN, int KV, int U, int E>
+hipError_t launch_list_ue(const SddmmListArgs& a, hipStream_t s) {
   int64_t most = 0;
   for (int b = 0; b < a.nb; ++b) {
     const int64_t cnt = a.bstart[b + 1] - a.bstart[b];
     most = cnt > most ? cnt : most;
   }
-  const int64_t blocks_per_bucket = cdiv(cdiv(most, E), kBlock / kWave);
-  if (blocks_per_bucket == 0) return hipSuccess;
-  hipLaunchKernelGGL((sddmm_list_kernel<VT, OT, IT, LPN, KV>),
-                     dim3((unsigned)(blocks_per_bucket * a.nb)), dim3(kBlock), 0, s, a);
+  // one wave per chunk of E entries, capped so the grid stays well inside
+  // its limits (waves then loop over several chunks)
+  int64_t waves_per_bucket = cdiv(most, E);
+  if (waves_per_bucket == 0) return hipSuccess;
+  const int64_t cap = (int64_t)1 << 22;
+  if (waves_per_bucket * a.nb > cap) waves_per_bucket = cap / a.nb;
+  constexpr int VEC = Traits<VT>::vec;
+  const dim3 grid((unsigned)(waves_per_bucket * a.nb));
+  if (a.K == (int64_t)LPN * KV * VEC)
+    hipLaunchKernelGGL((sddmm_list_kernel<VT, OT, IT, LPN, KV, U, E, true>), grid, dim3(kWave), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((sddmm_list_kernel<VT, OT, IT, LPN, KV, U, E, false>), grid, dim3(kWave),
+                       0, s, a);
   return hipGetLastError();
+}
+
+// U = 4 entries per step and E = 16 entries per wave were the fastest of
+// U in {1, 2, 4} x E in {8, 16, 32, 64} on the config-2, -3 and -5 remainders
+// (MI355X, cold caches).
+template <typename VT, typename OT, typename IT, int LPN, int KV>
+hipError_t launch_list(const SddmmListArgs& a, hipStream_t s) {
+  return launch_list_ue<VT, OT, IT, LPN, KV, 4, 16>(a, s);
 }
 
 template <typename VT, typename OT, typename IT>
