@@ -96,6 +96,25 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with six DPP adds and no
+// LDS traffic: shifts by 1, 2, 4 and 8 lanes inside each 16-lane row (lanes
+// shifted in from outside the row read 0), then lane 15 of rows 0 and 2 is
+// added to rows 1 and 3 (row_bcast:15) and lane 31 to rows 2 and 3
+// (row_bcast:31).  Every lane gets the sum of lanes 0..itself.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v += dpp_u32<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_u32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_u32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_u32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   int l = lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));

@@ -18,9 +18,8 @@ namespace spops {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kRounds = 4;  // entries per lane
 
-template <typename VT, typename IT>
+template <typename VT, typename IT, int kRounds>
 __global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, int64_t nnz,
                                                          const int32_t* ro, const IT* col,
                                                          const VT* val, VT* W, int64_t ldw) {
@@ -55,18 +54,27 @@ __global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, i
     if (off[q] >= 0) W[off[q]] = from_f32<VT>(to_f32(old[q]) + add[q]);
 }
 
-template <typename VT>
-hipError_t launch_vt(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
-                     int col_i32, const void* val, void* W, int64_t ldw, hipStream_t s) {
+template <typename VT, int kRounds>
+hipError_t launch_vtr(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
+                      int col_i32, const void* val, void* W, int64_t ldw, hipStream_t s) {
   const int64_t waves = (nnz + kWave * kRounds - 1) / (kWave * kRounds);
   const dim3 grid((unsigned)((waves * kWave + kBlock - 1) / kBlock));
   if (col_i32)
-    hipLaunchKernelGGL((csr_add_kernel<VT, int32_t>), grid, dim3(kBlock), 0, s, m, n, nnz, ro,
-                       (const int32_t*)col, (const VT*)val, (VT*)W, ldw);
+    hipLaunchKernelGGL((csr_add_kernel<VT, int32_t, kRounds>), grid, dim3(kBlock), 0, s, m, n,
+                       nnz, ro, (const int32_t*)col, (const VT*)val, (VT*)W, ldw);
   else
-    hipLaunchKernelGGL((csr_add_kernel<VT, int16_t>), grid, dim3(kBlock), 0, s, m, n, nnz, ro,
-                       (const int16_t*)col, (const VT*)val, (VT*)W, ldw);
+    hipLaunchKernelGGL((csr_add_kernel<VT, int16_t, kRounds>), grid, dim3(kBlock), 0, s, m, n,
+                       nnz, ro, (const int16_t*)col, (const VT*)val, (VT*)W, ldw);
   return hipGetLastError();
+}
+
+// One entry per lane: the kernel is bound by the latency of its dependent
+// loads (row search, W read), so more waves in flight beat more entries per
+// lane (measured 1, 2, 4, 8 entries per lane on MI355X; 1 was fastest).
+template <typename VT>
+hipError_t launch_vt(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,
+                     int col_i32, const void* val, void* W, int64_t ldw, hipStream_t s) {
+  return launch_vtr<VT, 1>(m, n, nnz, ro, col, col_i32, val, W, ldw, s);
 }
 
 }  // namespace

@@ -43,12 +43,7 @@ __global__ __launch_bounds__(kThreads) void scan_local_kernel(const uint32_t* in
     s += v[i];
   }
   // inclusive scan of per-thread sums inside the wave
-  uint32_t x = s;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane_id() >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_sum(s);
   const int w = t / kWave;
   if (lane_id() == kWave - 1) wave_tot[w] = x;
   __syncthreads();
@@ -71,47 +66,70 @@ __global__ __launch_bounds__(kThreads) void scan_local_kernel(const uint32_t* in
   }
 }
 
-// Whole exclusive scan in one workgroup of 1024 threads for n up to 16384:
-// each thread scans a contiguous chunk of at most 16 values.
+// Whole exclusive scan in one workgroup of 1024 threads for n up to 65536.
+// The array is read in 16 chunks of 4096 values; thread t takes values
+// 4t..4t+3 of every chunk (one 16-byte load each, all issued before any
+// arithmetic), so loads are coalesced and their latencies overlap.  Chunk
+// and wave totals are combined through a 256-entry table in LDS.
 constexpr int kSingleThreads = 1024;
-constexpr int64_t kSingleMax = 16384;
+constexpr int kSingleChunks = 16;
+constexpr int64_t kSingleChunk = kSingleThreads * 4;
+constexpr int64_t kSingleMax = kSingleChunk * kSingleChunks;
 
 __global__ __launch_bounds__(kSingleThreads) void scan_single_kernel(const uint32_t* in,
                                                                      uint32_t* out, int64_t n,
                                                                      uint32_t* total) {
-  __shared__ uint32_t wave_tot[kSingleThreads / kWave];
-  const int t = threadIdx.x;
-  constexpr int kPer = kSingleMax / kSingleThreads;
-  const int64_t b0 = (int64_t)t * kPer;
-  uint32_t v[kPer];
-  uint32_t s = 0;
+  constexpr int NW = kSingleThreads / kWave;
+  __shared__ uint32_t wt[2][NW];  // wave totals of a chunk, double-buffered
+  const int t = threadIdx.x, w = t / kWave, l = lane_id();
+  uint4 v[kSingleChunks];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    v[q] = (b0 + q < n) ? in[b0 + q] : 0u;
-    s += v[q];
+  for (int c = 0; c < kSingleChunks; ++c) {
+    const int64_t b = c * kSingleChunk + (int64_t)t * 4;
+    if (b + 3 < n) {
+      v[c] = *(const uint4*)(in + b);
+    } else {
+      v[c].x = b < n ? in[b] : 0u;
+      v[c].y = b + 1 < n ? in[b + 1] : 0u;
+      v[c].z = b + 2 < n ? in[b + 2] : 0u;
+      v[c].w = 0u;
+    }
   }
-  uint32_t x = s;
+  uint32_t carry = 0;  // total of the chunks before this one (same in every thread)
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane_id() >= o) x += y;
-  }
-  const int w = t / kWave;
-  if (lane_id() == kWave - 1) wave_tot[w] = x;
-  __syncthreads();
-  uint32_t run = 0, blk = 0;
-  for (int i = 0; i < kSingleThreads / kWave; ++i) {
-    const uint32_t wt = wave_tot[i];
-    if (i < w) run += wt;
-    blk += wt;
-  }
-  run += x - s;
+  for (int c = 0; c < kSingleChunks; ++c) {
+    if (c * kSingleChunk >= n) break;
+    const uint32_t s = v[c].x + v[c].y + v[c].z + v[c].w;
+    const uint32_t x = wave_inclusive_sum(s);
+    if (l == kWave - 1) wt[c & 1][w] = x;
+    __syncthreads();
+    uint32_t off = carry, tot = 0;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    if (b0 + q < n) out[b0 + q] = run;
-    run += v[q];
+    for (int ww = 0; ww < NW; ++ww) {
+      const uint32_t q = wt[c & 1][ww];
+      off += ww < w ? q : 0u;
+      tot += q;
+    }
+    uint32_t run = off + x - s;
+    const int64_t b = c * kSingleChunk + (int64_t)t * 4;
+    uint4 o;
+    o.x = run;
+    run += v[c].x;
+    o.y = run;
+    run += v[c].y;
+    o.z = run;
+    run += v[c].z;
+    o.w = run;
+    if (b + 3 < n) {
+      *(uint4*)(out + b) = o;
+    } else {
+      if (b < n) out[b] = o.x;
+      if (b + 1 < n) out[b + 1] = o.y;
+      if (b + 2 < n) out[b + 2] = o.z;
+    }
+    carry += tot;
   }
-  if (t == 0 && total) *total = blk;
+  if (t == 0 && total) *total = carry;
 }
 
 __global__ __launch_bounds__(kThreads) void scan_add_kernel(uint32_t* out, int64_t n,
@@ -198,13 +216,22 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
   base_d[t] = offs[(int64_t)t * ntiles + blockIdx.x];
   const int64_t tbase = (int64_t)blockIdx.x * kTile;
   const uint64_t lt = lanemask_lt();
+  // all keys and payloads of the tile are loaded before the first round
+  uint32_t keys[kItems], pay[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int64_t i = tbase + r * kThreads + t;
+    keys[r] = i < n ? ks(i) : 0u;
+    pay[r] = i < n ? vs(i) : 0u;
+  }
+#pragma unroll
   for (int r = 0; r < kItems; ++r) {
 #pragma unroll
     for (int ww = 0; ww < kThreads / kWave; ++ww) wcnt[ww][t] = 0;
     __syncthreads();
     const int64_t i = tbase + r * kThreads + t;
     const bool valid = i < n;
-    const uint32_t key = valid ? ks(i) : 0u;
+    const uint32_t key = keys[r];
     const uint32_t d = (key >> shift) & mask;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -230,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     if (valid) {
       const uint32_t dst = wcnt[w][d] + rank;
       kout[dst] = key;
-      vout[dst] = vs(i);
+      vout[dst] = pay[r];
     }
     __syncthreads();
   }
@@ -346,6 +373,122 @@ __global__ __launch_bounds__(256) void transpose_finish_kernel(
   }
 }
 
+// Second stage of the two-level transpose.  The entries were stably grouped
+// by coarse column digit c >> SH (one radix pass); workgroup d now orders
+// bucket d by the fine digit c & (F - 1), F = 2^SH <= 512, with a stable
+// counting sort: fine-digit histogram, exclusive scan (which also gives the
+// output row offsets of the bucket's columns), then rounds of 1024 entries in
+// bucket order, each entry's rank among equal fine digits found with wave
+// ballots and per-wave counts.  Rows and values are gathered through the
+// source positions carried by the first pass.
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishWaves = kFinishThreads / kWave;
+constexpr int kMaxFine = 512;
+
+template <typename OI, int VB>
+__global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
+    const uint32_t* keys, const uint32_t* src, const uint32_t* offs, int64_t ntiles,
+    const uint32_t* rows_of, int64_t nnz, int64_t n, int sh, const uint8_t* val, uint8_t* out_val,
+    int32_t* out_ro, OI* out_col) {
+  __shared__ uint32_t base_f[kMaxFine];
+  __shared__ uint32_t wcnt[kFinishWaves][kMaxFine];
+  __shared__ uint32_t wsum[kMaxFine / kWave];
+  const int t = threadIdx.x, w = t / kWave;
+  const int d = blockIdx.x;
+  const int F = 1 << sh;
+  const uint32_t fmask = (uint32_t)F - 1u;
+  const int64_t bs = offs[(int64_t)d * ntiles];
+  const int64_t be = d + 1 < kRadix ? (int64_t)offs[(int64_t)(d + 1) * ntiles] : nnz;
+  const uint64_t lt = lanemask_lt();
+  for (int f = t; f < F; f += kFinishThreads) base_f[f] = 0;
+  __syncthreads();
+  for (int64_t q = bs + t; q < be; q += kFinishThreads) atomicAdd(&base_f[keys[q] & fmask], 1u);
+  __syncthreads();
+  // exclusive scan of the F fine counts (F <= 512: waves 0..7)
+  const int fpad = F < kWave ? kWave : F;
+  uint32_t cnt = 0, inc = 0;
+  if (t < fpad) {
+    cnt = t < F ? base_f[t] : 0u;
+    inc = wave_inclusive_sum(cnt);
+    if (lane_id() == kWave - 1) wsum[w] = inc;
+  }
+  __syncthreads();
+  if (t < F) {
+    uint32_t off = 0;
+    for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+    base_f[t] = off + inc - cnt;
+    const int64_t c = ((int64_t)d << sh) + t;
+    if (c < n) out_ro[c] = (int32_t)(bs + off + inc - cnt);
+  }
+  if (d == 0 && t == 0) out_ro[n] = (int32_t)nnz;
+  __syncthreads();
+  for (int64_t r0 = bs; r0 < be; r0 += kFinishThreads) {
+    for (int k = t; k < kFinishWaves * F; k += kFinishThreads) wcnt[k / F][k % F] = 0;
+    __syncthreads();
+    const int64_t q = r0 + t;
+    const bool valid = q < be;
+    const uint32_t f = valid ? (keys[q] & fmask) : 0u;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < sh; ++b) {
+      const bool bit = (f >> b) & 1u;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const uint32_t rank = (uint32_t)__popcll(peers & lt);
+    if (valid && rank == 0) wcnt[w][f] = (uint32_t)__popcll(peers);
+    __syncthreads();
+    for (int f2 = t; f2 < F; f2 += kFinishThreads) {
+      uint32_t run = base_f[f2];
+#pragma unroll
+      for (int ww = 0; ww < kFinishWaves; ++ww) {
+        const uint32_t c = wcnt[ww][f2];
+        wcnt[ww][f2] = run;
+        run += c;
+      }
+      base_f[f2] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int64_t dst = bs + wcnt[w][f] + rank;
+      const uint32_t p = src[q];
+      out_col[dst] = (OI)rows_of[p];
+      if constexpr (VB == 4) {
+        ((uint32_t*)out_val)[dst] = ((const uint32_t*)val)[p];
+      } else if constexpr (VB == 2) {
+        ((uint16_t*)out_val)[dst] = ((const uint16_t*)val)[p];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <typename OI>
+hipError_t launch_bucket_finish(const uint32_t* keys, const uint32_t* src, const uint32_t* offs,
+                                int64_t ntiles, const uint32_t* rows_of, int64_t nnz, int64_t n,
+                                int sh, const void* val, int vb, void* out_val, int32_t* out_ro,
+                                void* out_col, hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(n, (int64_t)1 << sh));
+  const dim3 blk(kFinishThreads);
+  if (vb == 4)
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 4>), grid, blk, 0, s, keys, src, offs, ntiles,
+                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
+                       (OI*)out_col);
+  else if (vb == 2)
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 2>), grid, blk, 0, s, keys, src, offs, ntiles,
+                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
+                       (OI*)out_col);
+  else
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 0>), grid, blk, 0, s, keys, src, offs, ntiles,
+                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
+                       (OI*)out_col);
+  return hipGetLastError();
+}
+
 template <typename OI>
 hipError_t finish_transpose(const uint32_t* keys, const uint32_t* src, const uint32_t* rows_of,
                             int64_t nnz, int64_t n, const void* val, int vb, void* out_val,
@@ -366,53 +509,177 @@ hipError_t finish_transpose(const uint32_t* keys, const uint32_t* src, const uin
   return hipGetLastError();
 }
 
-// Row order of up to kBlockSortMax rows in one workgroup: LSD radix sort of
-// 16-bit keys (cols - count) packed above 16-bit row ids, two 8-bit passes
-// through LDS.  Ranks among equal digits come from wave ballots, rounds of
-// 1024 rows are taken in index order, so the sort is stable.
+// Row order of up to kBlockSortMax rows in one workgroup of 1024 threads.
+//
+// Usual case, a small spread of row lengths (max - min < 4096): a one-pass
+// stable counting sort on k = max - count.  Wave w owns a contiguous run of
+// rows; it histograms its rows into column w of a [k][wave] table (LDS,
+// 16-bit), the table is scanned in k-major order, and wave w then places its
+// rows in order: a row's slot is its (k, w) base plus the number of earlier
+// lanes of the step with the same k (wave ballots), so equal keys keep row
+// order.  Otherwise: LSD radix sort of 16-bit keys (cols - count) packed above
+// 16-bit row ids, two 8-bit passes through LDS, same ballot ranking.
 constexpr int kBlockSortThreads = 1024;
+constexpr int kBlockSortWaves = kBlockSortThreads / kWave;
 constexpr int64_t kBlockSortMax = 16384;
-// measured: one workgroup beats the multi-kernel sort only for small counts
-constexpr int64_t kBlockSortUse = 4096;
+constexpr int kCountSortRange = 4096;
+// LDS: the counting table (kCountSortRange x 16 x 2 bytes) or the radix
+// buffers (2 x kBlockSortMax + 16 x 256 words); the larger decides.
+constexpr int kBlockSortLdsWords = 2 * (int)kBlockSortMax + kBlockSortWaves * kRadix;
+
+__device__ __forceinline__ int row_len(const int32_t* ro, int64_t i, int32_t cols) {
+  int64_t c = (int64_t)ro[i + 1] - (int64_t)ro[i];
+  return (int)(c < 0 ? 0 : (c > cols ? cols : c));
+}
 
 template <typename OI>
 __global__ __launch_bounds__(kBlockSortThreads) void sort_rows_block_kernel(const int32_t* ro,
                                                                            int64_t m,
                                                                            int32_t cols,
                                                                            OI* out) {
-  constexpr int NW = kBlockSortThreads / kWave;
-  __shared__ uint32_t buf[2][kBlockSortMax];
-  __shared__ uint32_t cnt[NW][kRadix];
+  __shared__ uint32_t lds[kBlockSortLdsWords];
   __shared__ uint32_t base_d[kRadix];
-  const int t = threadIdx.x, w = t / kWave;
+  __shared__ uint32_t wsum[kBlockSortThreads / kWave];
+  __shared__ int red[2][kBlockSortWaves];
+  const int t = threadIdx.x, w = t / kWave, l = lane_id();
   const uint64_t lt = lanemask_lt();
-  for (int64_t i = t; i < m; i += kBlockSortThreads) {
-    int64_t c = (int64_t)ro[i + 1] - (int64_t)ro[i];
-    c = c < 0 ? 0 : (c > cols ? cols : c);
-    buf[0][i] = ((uint32_t)(cols - c) << 16) | (uint32_t)i;
+
+  // Wave w owns rows [r0, r1); lane l keeps the lengths of rows r0 + 64j + l
+  // in registers, so row_offsets is read once.
+  constexpr int RPL = (int)(kBlockSortMax / kBlockSortThreads);  // rows per lane
+  const int64_t chunk = cdiv(cdiv(m, kBlockSortWaves), kWave) * kWave;
+  const int64_t r0 = (int64_t)w * chunk;
+  const int64_t r1 = r0 + chunk < m ? r0 + chunk : m;
+  int len[RPL];
+  int lo = cols, hi = 0;
+#pragma unroll
+  for (int j = 0; j < RPL; ++j) {
+    const int64_t i = r0 + (int64_t)j * kWave + l;
+    len[j] = i < r1 ? row_len(ro, i, cols) : -1;
+    if (len[j] >= 0) {
+      lo = len[j] < lo ? len[j] : lo;
+      hi = len[j] > hi ? len[j] : hi;
+    }
   }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const int lo2 = __shfl_xor(lo, o, 64), hi2 = __shfl_xor(hi, o, 64);
+    lo = lo2 < lo ? lo2 : lo;
+    hi = hi2 > hi ? hi2 : hi;
+  }
+  if (l == 0) {
+    red[0][w] = lo;
+    red[1][w] = hi;
+  }
+  __syncthreads();
+  lo = red[0][0];
+  hi = red[1][0];
+  for (int ww = 1; ww < kBlockSortWaves; ++ww) {
+    lo = red[0][ww] < lo ? red[0][ww] : lo;
+    hi = red[1][ww] > hi ? red[1][ww] : hi;
+  }
+  const int range = hi - lo + 1;
+
+  if (range <= kCountSortRange) {
+    uint16_t* tab = (uint16_t*)lds;  // [k][wave]
+    int bits = 0;
+    while ((1 << bits) < range) ++bits;
+    for (int q = t; q < range * kBlockSortWaves; q += kBlockSortThreads) tab[q] = 0;
+    __syncthreads();
+    // per-wave histograms (leaders of equal-key lane groups add the group size)
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      if (r0 + (int64_t)j * kWave >= r1) break;
+      const bool valid = len[j] >= 0;
+      const uint32_t k = valid ? (uint32_t)(hi - len[j]) : 0u;
+      uint64_t peers = __ballot(valid);
+      for (int x = 0; x < bits; ++x) {
+        const bool bit = (k >> x) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      if (valid && (peers & lt) == 0)
+        tab[k * kBlockSortWaves + w] += (uint16_t)__popcll(peers);
+    }
+    __syncthreads();
+    // exclusive scan of the table in k-major order: wave w owns a contiguous
+    // segment and walks it 64 entries at a time (lane l reads entry j*64 + l,
+    // so the lanes hit consecutive LDS addresses); the first walk only sums.
+    const int total = range * kBlockSortWaves;
+    const int seg = (int)cdiv(cdiv(total, kBlockSortWaves), kWave) * kWave;
+    const int e0 = w * seg;
+    const int e1 = e0 + seg < total ? e0 + seg : total;
+    uint32_t s = 0;
+    for (int e = e0 + l; e < e1; e += kWave) s += tab[e];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (l == 0) wsum[w] = s;
+    __syncthreads();
+    uint32_t carry = 0;
+    for (int ww = 0; ww < w; ++ww) carry += wsum[ww];
+    for (int b = e0; b < e1; b += kWave) {
+      const int e = b + l;
+      const uint32_t c = e < e1 ? tab[e] : 0u;
+      const uint32_t inc = wave_inclusive_sum(c);
+      if (e < e1) tab[e] = (uint16_t)(carry + inc - c);
+      carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+    }
+    __syncthreads();
+    // placement, in row order inside each wave's run
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      if (r0 + (int64_t)j * kWave >= r1) break;
+      const int64_t i = r0 + (int64_t)j * kWave + l;
+      const bool valid = len[j] >= 0;
+      const uint32_t k = valid ? (uint32_t)(hi - len[j]) : 0u;
+      uint64_t peers = __ballot(valid);
+      for (int x = 0; x < bits; ++x) {
+        const bool bit = (k >> x) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      const uint32_t rank = (uint32_t)__popcll(peers & lt);
+      uint32_t base = 0;
+      if (valid) base = tab[k * kBlockSortWaves + w];
+      if (valid) out[base + rank] = (OI)i;
+      if (valid && rank == 0) tab[k * kBlockSortWaves + w] = (uint16_t)(base + __popcll(peers));
+    }
+    return;
+  }
+
+  // wide spread: two 8-bit LSD passes on 16-bit keys
+  uint32_t* const buf0 = lds;
+  uint32_t* const buf1 = lds + kBlockSortMax;
+  uint32_t* const cntf = lds + 2 * kBlockSortMax;  // [wave][digit]
+  for (int64_t i = t; i < m; i += kBlockSortThreads)
+    buf0[i] = ((uint32_t)(cols - row_len(ro, i, cols)) << 16) | (uint32_t)i;
   int cur = 0;
   for (int shift = 16; shift < 32; shift += 8) {
     if (t < kRadix) base_d[t] = 0;
     __syncthreads();
     for (int64_t i = t; i < m; i += kBlockSortThreads)
-      atomicAdd(&base_d[(buf[cur][i] >> shift) & 0xffu], 1u);
+      atomicAdd(&base_d[((cur ? buf1 : buf0)[i] >> shift) & 0xffu], 1u);
     __syncthreads();
-    if (t == 0) {
-      uint32_t run = 0;
-      for (int d = 0; d < kRadix; ++d) {
-        const uint32_t c = base_d[d];
-        base_d[d] = run;
-        run += c;
-      }
+    // exclusive scan of the 256 digit counts by the first four waves
+    if (t < kRadix) {
+      const uint32_t c = base_d[t];
+      const uint32_t inc2 = wave_inclusive_sum(c);
+      if (l == kWave - 1) wsum[w] = inc2;
+      base_d[t] = inc2 - c;
     }
     __syncthreads();
-    for (int64_t r0 = 0; r0 < m; r0 += kBlockSortThreads) {
-      for (int q = t; q < NW * kRadix; q += kBlockSortThreads) (&cnt[0][0])[q] = 0;
+    if (t < kRadix) {
+      uint32_t off = 0;
+      for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+      base_d[t] += off;
+    }
+    __syncthreads();
+    for (int64_t q0 = 0; q0 < m; q0 += kBlockSortThreads) {
+      for (int q = t; q < kBlockSortWaves * kRadix; q += kBlockSortThreads) cntf[q] = 0;
       __syncthreads();
-      const int64_t i = r0 + t;
+      const int64_t i = q0 + t;
       const bool valid = i < m;
-      const uint32_t item = valid ? buf[cur][i] : 0u;
+      const uint32_t item = valid ? (cur ? buf1 : buf0)[i] : 0u;
       const uint32_t d = (item >> shift) & 0xffu;
       uint64_t peers = __ballot(valid);
       for (int b = 0; b < 8; ++b) {
@@ -421,24 +688,24 @@ __global__ __launch_bounds__(kBlockSortThreads) void sort_rows_block_kernel(cons
         peers &= bit ? bal : ~bal;
       }
       const uint32_t rank = (uint32_t)__popcll(peers & lt);
-      if (valid && rank == 0) cnt[w][d] = (uint32_t)__popcll(peers);
+      if (valid && rank == 0) cntf[w * kRadix + d] = (uint32_t)__popcll(peers);
       __syncthreads();
       if (t < kRadix) {
         uint32_t run = base_d[t];
-        for (int ww = 0; ww < NW; ++ww) {
-          const uint32_t c = cnt[ww][t];
-          cnt[ww][t] = run;
+        for (int ww = 0; ww < kBlockSortWaves; ++ww) {
+          const uint32_t c = cntf[ww * kRadix + t];
+          cntf[ww * kRadix + t] = run;
           run += c;
         }
         base_d[t] = run;
       }
       __syncthreads();
-      if (valid) buf[cur ^ 1][cnt[w][d] + rank] = item;
+      if (valid) (cur ? buf0 : buf1)[cntf[w * kRadix + d] + rank] = item;
       __syncthreads();
     }
     cur ^= 1;
   }
-  for (int64_t i = t; i < m; i += kBlockSortThreads) out[i] = (OI)(buf[cur][i] & 0xffffu);
+  for (int64_t i = t; i < m; i += kBlockSortThreads) out[i] = (OI)((cur ? buf1 : buf0)[i] & 0xffffu);
 }
 
 // row_idx output from the sorted payload
@@ -473,7 +740,7 @@ hipError_t exclusive_scan_u32(const uint32_t* in, uint32_t* out, int64_t n, uint
                        total);
     return hipGetLastError();
   }
-  if (n <= kSingleMax) {
+  if (n <= kSingleMax && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0) {
     hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kSingleThreads), 0, s, in, out, n,
                        total);
     return hipGetLastError();
@@ -508,10 +775,60 @@ size_t transpose_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz) {
   return radix_ws_bytes_for(nnz) + align256((size_t)nnz * 4);
 }
 
+// Two-level transpose for up to 2^17 columns: one stable radix pass on the
+// top 8 bits of the column, then one workgroup per coarse bucket orders it by
+// the remaining <= 9 bits (transpose_bucket_kernel).  Five launches: row
+// expansion, digit counts, scan, scatter, bucket finish.
+hipError_t transpose_two_level(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
+                               const void* col, int col_i32, const void* val, int vb,
+                               void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
+                               void* ws, hipStream_t s) {
+  RadixWs R = carve_radix_ws(ws, nnz);
+  uint32_t* rows_of = (uint32_t*)((char*)ws + radix_ws_bytes_for(nnz));
+  const int bits = cols > 1 ? bit_length((uint64_t)(cols - 1)) : 1;
+  const int sh = bits > kRadixBits ? bits - kRadixBits : 0;
+  const int64_t ntiles = cdiv(nnz, kTile);
+  hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
+                     ro, rows, nnz, rows_of);
+  if (col_i32) {
+    KeyFromIndex<int32_t> ks{(const int32_t*)col, (int32_t)(cols - 1)};
+    hipLaunchKernelGGL(radix_count_kernel<KeyFromIndex<int32_t>>, dim3((unsigned)ntiles),
+                       dim3(kThreads), 0, s, ks, nnz, sh, 0xffu, R.counts, ntiles);
+    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((radix_scatter_kernel<KeyFromIndex<int32_t>, ValIota>),
+                       dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, ValIota{}, nnz, sh,
+                       kRadixBits, R.counts, ntiles, R.keys[0], R.vals[0]);
+  } else {
+    KeyFromIndex<int16_t> ks{(const int16_t*)col, (int32_t)(cols - 1)};
+    hipLaunchKernelGGL(radix_count_kernel<KeyFromIndex<int16_t>>, dim3((unsigned)ntiles),
+                       dim3(kThreads), 0, s, ks, nnz, sh, 0xffu, R.counts, ntiles);
+    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((radix_scatter_kernel<KeyFromIndex<int16_t>, ValIota>),
+                       dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, ValIota{}, nnz, sh,
+                       kRadixBits, R.counts, ntiles, R.keys[0], R.vals[0]);
+  }
+  if (out_col_i32)
+    return launch_bucket_finish<int32_t>(R.keys[0], R.vals[0], R.counts, ntiles, rows_of, nnz,
+                                         cols, sh, val, vb, out_val, out_ro, out_col, s);
+  return launch_bucket_finish<int16_t>(R.keys[0], R.vals[0], R.counts, ntiles, rows_of, nnz, cols,
+                                       sh, val, vb, out_val, out_ro, out_col, s);
+}
+
 hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
                                 const void* col, int col_i32, const void* val, int val_bytes,
                                 void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
                                 void* ws, hipStream_t s) {
+  const int vb0 = val ? val_bytes : 0;
+  if (nnz == 0) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(cols + 1, 256)), dim3(256), 0, s,
+                       out_ro, cols + 1, 0);
+    return hipGetLastError();
+  }
+  if (cols <= ((int64_t)1 << (kRadixBits + 9)))
+    return transpose_two_level(rows, cols, nnz, ro, col, col_i32, val, vb0, out_val, out_ro,
+                               out_col, out_col_i32, ws, s);
   RadixWs R = carve_radix_ws(ws, nnz);
   uint32_t* rows_of = (uint32_t*)((char*)ws + radix_ws_bytes_for(nnz));
   const uint32_t* skeys = nullptr;
@@ -548,7 +865,7 @@ size_t sort_rows_workspace_bytes(int64_t rows, int64_t cols) {
 hipError_t launch_sort_rows(const int32_t* ro, int64_t rows, int64_t cols, void* row_idx,
                             int row_idx_i32, void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (rows <= kBlockSortUse && cols <= 65535) {
+  if (rows <= kBlockSortMax && cols <= 65535) {
     if (row_idx_i32)
       hipLaunchKernelGGL(sort_rows_block_kernel<int32_t>, dim3(1), dim3(kBlockSortThreads), 0, s,
                          ro, rows, (int32_t)cols, (int32_t*)row_idx);
