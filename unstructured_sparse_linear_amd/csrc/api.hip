@@ -229,6 +229,14 @@ static bool sddmm_tiles_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t 
          ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
 }
 
+// The entry-list kernel reads 16-byte vectors along K.
+static bool sddmm_list_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t ldbt,
+                          const void* A, const void* BT) {
+  const int64_t v = in_type == SPOPS_F32 ? 4 : 8;
+  return K > 0 && K % v == 0 && lda % v == 0 && ldbt % v == 0 && ((uintptr_t)A % 16 == 0) &&
+         ((uintptr_t)BT % 16 == 0);
+}
+
 spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
                                         spops_sddmm_backend backend,
                                         const spops_sddmm_plan* plan, size_t* bytes) {
@@ -292,15 +300,44 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   };
 
   const bool tiles_ok = sddmm_tiles_ok(in_type, K, lda, ldbt, A, BT);
-  if (backend == SPOPS_SDDMM_GENERAL || !tiles_ok)
-    return from_hip(launch_sddmm_general(with_split(g), s));
+  const bool list_ok = sddmm_list_ok(in_type, K, lda, ldbt, A, BT);
+  SddmmListArgs r{};
+  r.m = mask->rows;
+  r.n = mask->cols;
+  r.K = K;
+  r.lda = lda;
+  r.ldbt = ldbt;
+  r.col = mask->col_idx;
+  r.col_i32 = mask->col_type == SPOPS_I32;
+  r.A = A;
+  r.BT = BT;
+  r.out = out_values;
+  r.dtype = in_type;
+  r.out_dtype = out_type;
+  // the whole mask in CSR order through the entry-list kernel (no plan)
+  auto csr_list = [&]() {
+    r.ro = mask->row_offsets;
+    r.nb = 1;
+    r.bstart[0] = 0;
+    r.bstart[1] = mask->nnz;
+    return launch_sddmm_list(r, s);
+  };
+  const SddmmArgs gs = with_split(g);
+  auto general = [&]() {
+    if (list_ok && gs.ks == 1) return from_hip(csr_list());
+    return from_hip(launch_sddmm_general(gs, s));
+  };
+  if (backend == SPOPS_SDDMM_GENERAL) return general();
+  if (plan && (plan->dev.m != mask->rows || plan->dev.n != mask->cols ||
+               plan->dev.nnz != mask->nnz || plan->dev.mask_ro != mask->row_offsets ||
+               plan->dev.mask_col != mask->col_idx))
+    return SPOPS_ERR_PLAN;
+  // Dense tiles need 16-bit inputs.  Without them the plan's remainder (the
+  // whole mask when it found no tiles) still runs through the entry list.
+  if (!tiles_ok && (!plan || plan->dev.tiles > 0 || !list_ok)) return general();
 
   spops_sddmm_plan* own = nullptr;
-  if (plan) {
-    if (plan->dev.m != mask->rows || plan->dev.n != mask->cols || plan->dev.nnz != mask->nnz ||
-        plan->dev.mask_ro != mask->row_offsets || plan->dev.mask_col != mask->col_idx)
-      return SPOPS_ERR_PLAN;
-  } else {
+  if (!plan) {
     st = spops_sddmm_plan_create(mask, kDefaultTau, hip_stream, &own);
     if (st != SPOPS_OK) return st;
     plan = own;
@@ -308,21 +345,8 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   const SddmmPlanDev& P = plan->dev;
   hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type, s);
   if (e == hipSuccess && P.rest_nnz > 0) {
-    SddmmListArgs r{};
-    r.m = mask->rows;
-    r.n = mask->cols;
-    r.K = K;
-    r.lda = lda;
-    r.ldbt = ldbt;
     r.pos = P.rest_pos;
     r.rows = P.rest_row;
-    r.col = mask->col_idx;
-    r.col_i32 = mask->col_type == SPOPS_I32;
-    r.A = A;
-    r.BT = BT;
-    r.out = out_values;
-    r.dtype = in_type;
-    r.out_dtype = out_type;
     r.nb = P.nb;
     for (int b = 0; b <= P.nb; ++b) r.bstart[b] = P.bucket_start[b];
     e = launch_sddmm_list(r, s);

@@ -149,6 +149,9 @@ hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, i
 // [bstart[b], bstart[b+1]) and run on the blocks b, b+nb, ...
 struct SddmmListArgs {
   int64_t m, n, K, lda, ldbt;
+  // CSR order when ro is set: entry j is mask position j, its row is found in
+  // ro (pos and rows unused, one bucket [0, nnz))
+  const int32_t* ro;
   const int32_t* pos;
   const int32_t* rows;
   const void* col;

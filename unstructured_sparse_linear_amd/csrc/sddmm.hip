@@ -405,7 +405,16 @@ __global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
   const IT* col = (const IT*)a.col;
 
   int my_r = 0, my_p = 0, my_c = -1;
-  if (lane < nw) {
+  if (a.ro) {
+    // CSR order: rows of the wave's first and last entries by a 64-way
+    // search, then each lane's row by binary search between them
+    const int64_t rf = wave_upper_row(a.ro, a.m, wb);
+    const int64_t rl = wave_upper_row(a.ro, a.m, wb + nw - 1);
+    if (lane < nw) {
+      my_p = (int)(wb + lane);
+      my_r = (int)upper_row(a.ro, rf, rl + 1, wb + lane);
+    }
+  } else if (lane < nw) {
     my_r = a.rows[wb + lane];
     my_p = a.pos[wb + lane];
   }
@@ -560,12 +569,16 @@ hipError_t launch_list_ue(const SddmmListArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// U = 4 entries per step and E = 16 entries per wave were the fastest of
-// U in {1, 2, 4} x E in {8, 16, 32, 64} on the config-2, -3 and -5 remainders
-// (MI355X, cold caches).
+// U = 4 entries per step and 16 entries per wave were the fastest of
+// U in {1, 2, 4} x E in {8, 16, 32, 64} on the K = 2048 and K = 256
+// remainders measured (MI355X, cold caches); for K = 32 (8-lane groups) 64
+// entries per wave beat 16.
 template <typename VT, typename OT, typename IT, int LPN, int KV>
 hipError_t launch_list(const SddmmListArgs& a, hipStream_t s) {
-  return launch_list_ue<VT, OT, IT, LPN, KV, 4, 16>(a, s);
+  // 16 entries per wave for 32- and 64-lane groups; narrower groups (small
+  // K) take 64 so that each group still gets several entries
+  constexpr int E = LPN >= 32 ? 16 : kWave;
+  return launch_list_ue<VT, OT, IT, LPN, KV, (LPN < 4 ? LPN : 4), E>(a, s);
 }
 
 template <typename VT, typename OT, typename IT>

@@ -135,6 +135,54 @@ __device__ __forceinline__ void store_vec(OT* dst, const float* acc) {
 }
 
 // Accumulate entries [p0, p1) into acc for columns [j, j+VEC).
+// A wave that owns a whole row (64 lanes per row): every entry is the same
+// in all lanes, so its column and value are moved to scalar registers
+// (readfirstlane) and the B row address is formed with scalar arithmetic; a
+// lane only adds its fixed 32-bit byte offset within the row.
+template <typename VT, typename IT>
+__device__ __forceinline__ void accumulate_wave(const SpmmArgs& a, int64_t p0_, int64_t p1_,
+                                                int64_t j, float* acc) {
+  if (j >= a.N) return;
+  const int p0 = __builtin_amdgcn_readfirstlane((int)p0_);
+  const int p1 = __builtin_amdgcn_readfirstlane((int)p1_);
+  const IT* col = (const IT*)a.col;
+  const VT* val = (const VT*)a.val;
+  const char* B = (const char*)a.B;
+  const int64_t ldb_bytes = a.ldb * (int64_t)sizeof(VT);
+  const uint32_t off = (uint32_t)(j * (int64_t)sizeof(VT));
+  const uint32_t k = (uint32_t)a.k;
+  constexpr int U = kUnroll;
+  int p = p0;
+  for (; p + U <= p1; p += U) {
+    int c[U];
+    float v[U];
+    uint4 b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      c[u] = __builtin_amdgcn_readfirstlane((int)col[p + u]);
+      v[u] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(to_f32(val[p + u]))));
+      if ((uint32_t)c[u] >= k) {
+        c[u] = 0;
+        v[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = *(const uint4*)(B + (int64_t)c[u] * ldb_bytes + off);
+#pragma unroll
+    for (int u = 0; u < U; ++u) fma_vec<VT>(acc, v[u], b[u]);
+  }
+  for (; p < p1; ++p) {
+    int c = __builtin_amdgcn_readfirstlane((int)col[p]);
+    float v = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(to_f32(val[p]))));
+    if ((uint32_t)c >= k) {
+      c = 0;
+      v = 0.f;
+    }
+    const uint4 b = *(const uint4*)(B + (int64_t)c * ldb_bytes + off);
+    fma_vec<VT>(acc, v, b);
+  }
+}
+
 template <typename VT, typename IT, int VEC, bool ALIGNED>
 __device__ __forceinline__ void accumulate(const SpmmArgs& a, int64_t p0, int64_t p1, int64_t j,
                                            float* acc) {
@@ -255,7 +303,10 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   int64_t p0, p1;
   row_range(a.ro, r, a.nnz, p0, p1);
   if (a.P > 0 && p1 - p0 > a.T) return;  // handled by the chunk blocks
-  accumulate<VT, IT, VEC, ALIGNED>(a, p0, p1, j, acc);
+  if constexpr (LPR == kWave && ALIGNED)
+    accumulate_wave<VT, IT>(a, p0, p1, j, acc);
+  else
+    accumulate<VT, IT, VEC, ALIGNED>(a, p0, p1, j, acc);
   write_out<OT, VEC, ALIGNED>((OT*)a.C + r * a.ldc, j, a.N, acc);
 }
 
@@ -700,7 +751,11 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
       const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
                            ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
                            ((uintptr_t)a.partial % 16 == 0);
-      const int64_t nv = cdiv(a.N, VEC);
+      int64_t nv = cdiv(a.N, VEC);
+      {  // TUNING ONLY
+        const char* lp = getenv("SPOPS_SPMM_LPR");
+        if (lp) { const int64_t cap = atoll(lp); if (nv > cap) nv = cap; }
+      }
       if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
       else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
       else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
