@@ -14,8 +14,8 @@
 //
 // Execute: one workgroup per non-empty tile computes the dense TM x TN block
 // A[rows] * BT[cols]^T with v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate),
-// staging 32-wide K slices of the gathered rows through LDS, then writes only
-// the tile's mask positions from an LDS copy of the block.  Every mask entry
+// staging 64-wide K slices of the gathered rows through two LDS stages, then
+// writes only the tile's mask positions from an LDS copy of the block.  Every mask entry
 // belongs to exactly one tile or to the remainder, so each output is written
 // once.
 #include <stdlib.h>
@@ -28,10 +28,14 @@ namespace {
 
 constexpr int TM = 128;       // tile rows
 constexpr int TN = 128;       // tile columns
-constexpr int TK = 32;        // K slice staged per step
+constexpr int TK = 64;        // K slice staged per step
 constexpr int LDK = TK + 8;   // padded LDS row (16-bit elements)
 constexpr int LDC = TN + 4;   // padded LDS row of the fp32 result block
 constexpr int kThreads = 256;
+constexpr int kStage = (TM + TN) * LDK;  // 16-bit elements per LDS stage (A, then BT)
+constexpr int kChunks = TM * TK / 8 / kThreads;  // 16-byte chunks per thread per operand
+static_assert(TM == TN, "A and BT tiles share the staging map");
+static_assert(TM * LDC * 4 <= 2 * kStage * 2, "the fp32 block reuses the LDS stages");
 
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
@@ -64,8 +68,14 @@ __device__ __forceinline__ float16v mfma32(const uint4& a, const uint4& b, float
   }
 }
 
+// One workgroup (4 waves) per tile; wave (wr, wc) computes the 64 x 64
+// quarter (wr, wc) as 2 x 2 MFMA 32x32x16 blocks.  K runs in slices of TK = 64
+// through two LDS stages: while the waves multiply out of one stage, the next
+// slice's gathered rows are already in registers and are stored into the
+// other stage afterwards, so each slice costs one barrier.  After the K loop
+// the fp32 block goes to LDS and only the tile's mask positions are written.
 template <bool BF16, typename OT>
-__global__ __launch_bounds__(kThreads) void sddmm_tile_kernel(TileArgs t) {
+__global__ __launch_bounds__(kThreads, 2) void sddmm_tile_kernel(TileArgs t) {
   const int64_t tile = blockIdx.x;
   const int32_t e0 = t.tile_start[tile], e1 = t.tile_start[tile + 1];
   if (e1 <= e0) return;  // no mask entry in this tile
@@ -91,40 +101,45 @@ __global__ __launch_bounds__(kThreads) void sddmm_tile_kernel(TileArgs t) {
     ccount = t.n_cols_hot;
   }
 
-  __shared__ __attribute__((aligned(16))) char smem[TM * LDC * 4];
-  uint16_t* As = (uint16_t*)smem;            // [TM][LDK]
-  uint16_t* Bs = As + TM * LDK;              // [TN][LDK]
-  float* Cs = (float*)smem;                  // [TM][LDC] (after the K loop)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+  float* Cs = (float*)smem;  // [TM][LDC] after the K loop
 
   const int tid = threadIdx.x;
-  // each thread stages two 16-byte chunks of A and two of BT per K slice:
-  // chunk q = tid + 256*h -> tile row q/4, K offset (q%4)*8
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
-  int srow[2], skc[2];
+  // chunk q = tid + 256*h: tile row q / 8, K offset (q % 8) * 8
+  const uint16_t* ap[kChunks];
+  const uint16_t* bp[kChunks];
+  const int skc = (tid & 7) * 8;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = tid + kThreads * h;
-    srow[h] = q >> 2;
-    skc[h] = (q & 3) * 8;
-    const int64_t ri = tr * TM + srow[h];
-    const int64_t ci = tc * TN + srow[h];
+  for (int h = 0; h < kChunks; ++h) {
+    const int row = (tid >> 3) + h * (kThreads / 8);
+    const int64_t ri = tr * TM + row;
+    const int64_t ci = tc * TN + row;
     ap[h] = ri < rcount ? t.A + (int64_t)rlist[ri] * t.lda : nullptr;
     bp[h] = ci < ccount ? t.BT + (int64_t)(clist ? clist[ci] : ci) * t.ldbt : nullptr;
   }
-  uint4 ra[2], rb[2];
+  uint4 ra[kChunks], rb[kChunks];
   auto fetch = [&](int64_t k0) {
+    const int64_t k = k0 + skc;
+    const bool ok = k < t.K;  // K is a multiple of 8: a chunk is all in or all out
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t k = k0 + skc[h];
-      const bool ok = k < t.K;
+    for (int h = 0; h < kChunks; ++h) {
       ra[h] = (ap[h] && ok) ? *(const uint4*)(ap[h] + k) : make_uint4(0, 0, 0, 0);
       rb[h] = (bp[h] && ok) ? *(const uint4*)(bp[h] + k) : make_uint4(0, 0, 0, 0);
     }
   };
+  auto stash = [&](int stage) {
+    uint16_t* As = smem + stage * kStage;
+    uint16_t* Bs = As + TM * LDK;
+#pragma unroll
+    for (int h = 0; h < kChunks; ++h) {
+      const int row = (tid >> 3) + h * (kThreads / 8);
+      *(uint4*)(As + row * LDK + skc) = ra[h];
+      *(uint4*)(Bs + row * LDK + skc) = rb[h];
+    }
+  };
 
   const int w = tid / kWave, l = lane_id();
-  const int wr = w >> 1, wc = w & 1;  // 2 x 2 waves, 64 x 64 each
+  const int wr = w >> 1, wc = w & 1;
   float16v acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -133,16 +148,15 @@ __global__ __launch_bounds__(kThreads) void sddmm_tile_kernel(TileArgs t) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  const int64_t nst = cdiv(t.K, TK);
   fetch(0);
-  for (int64_t k0 = 0; k0 < t.K; k0 += TK) {
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *(uint4*)(As + srow[h] * LDK + skc[h]) = ra[h];
-      *(uint4*)(Bs + srow[h] * LDK + skc[h]) = rb[h];
-    }
-    __syncthreads();
-    if (k0 + TK < t.K) fetch(k0 + TK);
+  stash(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nst; ++st) {
+    const int stage = (int)(st & 1);
+    if (st + 1 < nst) fetch((st + 1) * TK);
+    const uint16_t* As = smem + stage * kStage;
+    const uint16_t* Bs = As + TM * LDK;
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
       const int kk = ks * 16 + (l >> 5) * 8;
@@ -158,8 +172,9 @@ __global__ __launch_bounds__(kThreads) void sddmm_tile_kernel(TileArgs t) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<BF16>(fa[i], fb[j], acc[i][j]);
     }
+    if (st + 1 < nst) stash(stage ^ 1);
+    __syncthreads();
   }
-  __syncthreads();
   // 32x32 fp32 result layout: lane l holds column l%32; value v sits at row
   // (v/4)*8 + (l/32)*4 + v%4.
 #pragma unroll
