@@ -184,3 +184,46 @@ def to_f64(x: np.ndarray, dt: str) -> np.ndarray:
     if dt == "f32":
         return np.asarray(x, dtype=np.float64)
     return decode(x, dt)
+
+
+# --------------------------------------------------- sparse linear layer --
+#
+# The layer S · X^T (S sparse out x in, X^T dense in x tokens) and its
+# gradients, the pairing the spops README's operations serve for sparse
+# adaptation (csr_add "is used in the RoSA paper"; SDDMM handles RoSA's
+# masks) and that the torchsparsegradutils README describes for sparse_mm
+# (section "Key Features": gradients keep the sparsity of the matrix; its
+# Quick Start multiplies a sparse 2 x 3 matrix into a dense one and calls
+# backward).  Written directly from the stored entries in float64: a loss
+# L = <G, S · X^T> has dL/dS[r][c] = <G[r], X^T[c]> at every stored (r, c)
+# and dL/dX^T = S^T · G.
+
+def _rows_of(row_offsets) -> np.ndarray:
+    ro = np.asarray(row_offsets, dtype=np.int64)
+    return np.repeat(np.arange(len(ro) - 1), np.diff(ro))
+
+
+def sparse_linear_forward(m: int, row_offsets, col_idx, values, val_dt: str, xt,
+                          x_dt: str) -> np.ndarray:
+    """Y^T = S · X^T in float64, one stored entry at a time."""
+    v, x = to_f64(values, val_dt), to_f64(xt, x_dt)
+    r, c = _rows_of(row_offsets), np.asarray(col_idx, dtype=np.int64)
+    yt = np.zeros((m, x.shape[1]), dtype=np.float64)
+    for p in range(len(c)):
+        yt[r[p]] += v[p] * x[c[p]]
+    return yt
+
+
+def sparse_linear_backward(m: int, n: int, row_offsets, col_idx, values, val_dt: str, xt,
+                           dyt, x_dt: str):
+    """(dvalues, dX^T) of L = <dY^T, S · X^T>: dvalues[p] = <dY^T[r], X^T[c]>
+    for stored entry p = (r, c); dX^T[c] = sum over entries (r, c) of
+    v * dY^T[r] (that is S^T · dY^T)."""
+    v, x, g = to_f64(values, val_dt), to_f64(xt, x_dt), to_f64(dyt, x_dt)
+    r, c = _rows_of(row_offsets), np.asarray(col_idx, dtype=np.int64)
+    dv = np.empty(len(c), dtype=np.float64)
+    dxt = np.zeros((n, x.shape[1]), dtype=np.float64)
+    for p in range(len(c)):
+        dv[p] = float(np.dot(g[r[p]], x[c[p]]))
+        dxt[c[p]] += v[p] * g[r[p]]
+    return dv, dxt

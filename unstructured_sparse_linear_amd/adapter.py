@@ -1,0 +1,110 @@
+"""Sparse linear layer with autograd, built from the four CSR operations.
+
+This is the sparse-adaptation pattern the spops README's SDDMM and csr_add
+serve (robust sparse adaptation of a dense weight W by a sparse S): a layer
+computes S·x, training needs the gradients with respect to S's stored values
+and to the input, and the trained S is finally merged into W.  Activations
+are kept feature-major (X^T is in_features x tokens, row-major), which makes
+every step one call into libspops and needs no dense transpose:
+
+    forward    Y^T  = S · X^T                         spmm
+    backward   dS   = dY^T · (X^T)^T sampled at S     sddmm (A = dY^T, BT = X^T)
+               dX^T = S^T · dY^T                      csr_transpose + spmm
+    merge      W   += S                               csr_add
+
+The module only marshals tensors: outputs are allocated here and every value
+is computed by the library's kernels (it raises if libspops.so is missing).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from .spops import (SddmmPlan, SpmmPlan, csr_add, csr_transpose, csr_transpose_workspace,
+                    sddmm, sort_rows_by_nnz, spmm)
+
+
+class SparsePattern:
+    """A CSR sparsity pattern of S (out_features x in_features) and what is
+    derived from it once: the row order, the SpMM / SDDMM plans, and the
+    pattern of S^T with its own row order and plan."""
+
+    def __init__(self, row_offsets: torch.Tensor, col_idx: torch.Tensor,
+                 out_features: int, in_features: int):
+        self.ro, self.ci = row_offsets, col_idx
+        self.m, self.n = out_features, in_features
+        self.nnz = col_idx.numel()
+        dev = row_offsets.device
+        self.ri = sort_rows_by_nnz(row_offsets, in_features)
+        self.spmm_plan = SpmmPlan(row_offsets, self.ri, col_idx, in_features)
+        self.sddmm_plan = SddmmPlan(row_offsets, col_idx, out_features, in_features)
+        self.tws = csr_transpose_workspace(out_features, in_features, self.nnz, dev)
+        _, self.roT, self.ciT = csr_transpose(None, row_offsets, col_idx, out_features,
+                                              in_features, workspace=self.tws)
+        self.riT = sort_rows_by_nnz(self.roT, out_features)
+        self.spmmT_plan = SpmmPlan(self.roT, self.riT, self.ciT, out_features)
+
+    def transposed_values(self, values: torch.Tensor,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Values of S^T in the order of the transposed pattern."""
+        if out is None:
+            out = torch.empty_like(values)
+        csr_transpose(values, self.ro, self.ci, self.m, self.n, workspace=self.tws,
+                      out=(out, self.roT, self.ciT))
+        return out
+
+
+class _SparseLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, values: torch.Tensor, xt: torch.Tensor, pattern: SparsePattern):
+        P = pattern
+        yt = spmm(values, P.ro, P.ri, P.ci, xt, P.m, out_dtype=xt.dtype, plan=P.spmm_plan)
+        ctx.save_for_backward(values, xt)
+        ctx.pattern = P
+        return yt
+
+    @staticmethod
+    def backward(ctx, dyt: torch.Tensor):
+        values, xt = ctx.saved_tensors
+        P = ctx.pattern
+        dyt = dyt.contiguous()
+        dv = dxt = None
+        if ctx.needs_input_grad[0]:
+            dv = sddmm(P.ro, P.ri, P.ci, dyt, xt, plan=P.sddmm_plan, out_dtype=values.dtype)
+        if ctx.needs_input_grad[1]:
+            vt = P.transposed_values(values)
+            dxt = spmm(vt, P.roT, P.riT, P.ciT, dyt, P.n, out_dtype=xt.dtype,
+                       plan=P.spmmT_plan)
+        return dv, dxt, None
+
+
+def sparse_linear(values: torch.Tensor, xt: torch.Tensor, pattern: SparsePattern) -> torch.Tensor:
+    """Y^T = S · X^T with S = (pattern, values); differentiable in values and X^T.
+    values and X^T share a dtype (f32, f16 or bf16); Y^T has that dtype too
+    (fp32 accumulation, one rounding)."""
+    if values.dtype != xt.dtype:
+        raise ValueError("values and X^T must share a dtype")
+    if xt.dim() != 2 or xt.shape[0] != pattern.n:
+        raise ValueError("X^T must be in_features x tokens")
+    return _SparseLinearFn.apply(values, xt, pattern)
+
+
+class SparseAdapter(torch.nn.Module):
+    """A trainable sparse matrix S on a fixed pattern: forward(X^T) = S · X^T;
+    merge_into(W) adds S into a dense out_features x in_features weight."""
+
+    def __init__(self, pattern: SparsePattern, values: torch.Tensor):
+        super().__init__()
+        if values.numel() != pattern.nnz:
+            raise ValueError("one value per stored entry of the pattern")
+        self.pattern = pattern
+        self.values = torch.nn.Parameter(values)
+
+    def forward(self, xt: torch.Tensor) -> torch.Tensor:
+        return sparse_linear(self.values, xt, self.pattern)
+
+    @torch.no_grad()
+    def merge_into(self, W: torch.Tensor) -> torch.Tensor:
+        P = self.pattern
+        return csr_add(self.values.detach(), P.ro, P.ri, P.ci, W)

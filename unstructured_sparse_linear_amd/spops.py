@@ -348,16 +348,32 @@ def csr_transpose_workspace(m: int, n: int, nnz: int, device) -> torch.Tensor:
 
 def csr_transpose(A_val: Optional[torch.Tensor], A_row_offsets: torch.Tensor,
                   A_col_indices: torch.Tensor, m: int, n: int,
-                  workspace: Optional[torch.Tensor] = None
+                  workspace: Optional[torch.Tensor] = None,
+                  out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor,
+                                      torch.Tensor]] = None
                   ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
-    """A^T as (values_T, row_offsets_T [n+1] int32, col_idx_T [nnz])."""
+    """A^T as (values_T, row_offsets_T [n+1] int32, col_idx_T [nnz]); `out`
+    gives preallocated (values_T or None, row_offsets_T, col_idx_T)."""
     d = csr_desc(A_val, A_row_offsets, None, A_col_indices, m, n)
     dev = A_row_offsets.device
     nnz = d.nnz
-    out_ro = torch.empty(n + 1, dtype=torch.int32, device=dev)
     oit = torch.int16 if m <= 32767 else torch.int32
-    out_ci = torch.empty(nnz, dtype=oit, device=dev)
-    out_v = torch.empty_like(A_val) if A_val is not None else None
+    if out is None:
+        out_ro = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        out_ci = torch.empty(nnz, dtype=oit, device=dev)
+        out_v = torch.empty_like(A_val) if A_val is not None else None
+    else:
+        out_v, out_ro, out_ci = out
+        _require(out_ro, "out row_offsets", (torch.int32,))
+        _require(out_ci, "out col_idx", (torch.int16, torch.int32))
+        if out_ro.numel() != n + 1 or out_ci.numel() != nnz or out_ci.dtype != oit:
+            raise ValueError("out arrays have the wrong size or index type")
+        if A_val is not None:
+            if out_v is None:
+                raise ValueError("out values missing")
+            _require(out_v, "out values", (A_val.dtype,))
+            if out_v.numel() != nnz:
+                raise ValueError("out values have the wrong size")
     if workspace is None:
         workspace = csr_transpose_workspace(m, n, nnz, dev)
     _check("spops_csr_transpose", lib().spops_csr_transpose(
