@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
+    p.add_argument("--no-adapter", action="store_true",
+                   help="skip the sparse-layer training step (forward, both gradients, merge)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
@@ -173,6 +175,84 @@ def cpu_baseline(w, A, dt, N, K, ops, oracle):
             "sample": f"the full workload (all {len(ops)} operations, one pass each), "
                       "median of 3 after 1 warm-up",
             "ms_per_op": per, "ms_per_step": round(total_s * 1e3, 3)}
+
+
+def adapter_step(S, w, A, dt, N, dev, flush, args):
+    """One training step of the sparse layer Y^T = S . X^T with S = A (values
+    A.values, pattern A) and X^T = the workload's dense B (k x N): forward,
+    the gradients of the stored values (SDDMM of dY^T and X^T) and of X^T
+    (S^T . dY^T), and the merge W += S; outputs in the input dtype, as the
+    autograd layer produces them.  Captured as a HIP graph, cold caches."""
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+
+    def to(x, d=None):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    m, n = A.m, A.n
+    v, ro, ci = to(A.values, dt), to(A.row_offsets), to(A.col_idx)
+    P = S.SparsePattern(ro, ci, m, n)
+    xt = to(w.get("B"), dt)                   # X^T: in_features x tokens
+    if w.get("Ad").shape != (m, N):
+        return None
+    dyt = to(w.get("Ad"), dt)                 # dY^T: out_features x tokens (synthetic)
+    W = to(w.get("W"), dt) if w.get("W").shape == (m, n) else None
+    yt = torch.empty((m, N), dtype=tdt, device=dev)
+    dv = torch.empty_like(v)
+    vT = torch.empty_like(v)
+    dxt = torch.empty((n, N), dtype=tdt, device=dev)
+
+    def run():
+        S.spmm(v, P.ro, P.ri, P.ci, xt, m, out_dtype=tdt, plan=P.spmm_plan, out=yt)
+        S.sddmm(P.ro, P.ri, P.ci, dyt, xt, plan=P.sddmm_plan, out_dtype=tdt, out=dv)
+        P.transposed_values(v, out=vT)
+        S.spmm(vT, P.roT, P.riT, P.ciT, dyt, n, out_dtype=tdt, plan=P.spmmT_plan, out=dxt)
+        if W is not None:
+            S.csr_add(v, P.ro, P.ri, P.ci, W)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ts = []
+    for _ in range(max(args.steps, 5)):
+        if not args.no_flush:
+            flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t = float(np.mean(ts))
+    s_v, s_ci = ESZ[dt], A.col_idx.dtype.itemsize
+    s_ri, s_riT = (2 if m <= 32767 else 4), (2 if n <= 32767 else 4)
+    kp = len(np.unique(A.col_idx))
+    mp = int(np.count_nonzero(A.row_counts()))
+    nnz = A.nnz
+    parts = {
+        "forward_spmm": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + kp * N * s_v + m * N * s_v,
+        "grad_values_sddmm": nnz * s_ci + 4 * (m + 1) + m * s_ri + mp * N * s_v + kp * N * s_v
+        + nnz * s_v,
+        "transpose": nnz * (s_v + s_ci) + 4 * (m + 1) + nnz * (s_v + s_riT) + 4 * (n + 1),
+        "grad_input_spmm": nnz * (s_v + s_riT) + 4 * (n + 1) + n * s_riT + mp * N * s_v
+        + n * N * s_v,
+    }
+    if W is not None:
+        parts["merge_csr_add"] = nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + 2 * nnz * s_v
+    total = sum(parts.values())
+    return {"ms": round(t, 4), "alg_bytes": int(total), "gbps": round(total / t / 1e6, 1),
+            "frac_hbm": round(total / t / 1e6 / HBM_PEAK_GBS, 4),
+            "steps": list(parts), "tokens": N,
+            "layout": "feature-major (X^T in_features x tokens), outputs in the input dtype",
+            "step": "hip graph replay, cold caches"}
 
 
 def main():
@@ -376,6 +456,8 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if not args.no_adapter:
+        result["next_adapter_step"] = adapter_step(S, w, A, dt, N, dev, flush, args)
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)
