@@ -94,6 +94,7 @@ def alg_bytes(A, N, K, dt):
     mp = int(np.count_nonzero(A.row_counts()))
     return {
         "spmm": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + kp * N * s_v + m * N * 4,
+        "spmv": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + kp * s_v + m * 4,
         "sddmm": nnz * s_ci + 4 * (m + 1) + m * s_ri + mp * K * s_v + kp * K * s_v + nnz * 4,
         "csr_add": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + 2 * nnz * s_v,
         "transpose": nnz * (s_v + s_ci) + 4 * (m + 1) + nnz * (s_v + s_riT) + 4 * (n + 1),
@@ -102,7 +103,7 @@ def alg_bytes(A, N, K, dt):
 
 
 def flops(A, N, K):
-    return {"spmm": 2 * A.nnz * N, "sddmm": 2 * A.nnz * K}
+    return {"spmm": 2 * A.nnz * N, "spmv": 2 * A.nnz, "sddmm": 2 * A.nnz * K}
 
 
 def kernel_sources_sha(files):
@@ -113,18 +114,26 @@ def kernel_sources_sha(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "sddmm": ["sddmm.hip", "sddmm_dense.hip",
+KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "spmv": ["spmm.hip", "common.h"],
+                "sddmm": ["sddmm.hip", "sddmm_dense.hip",
                                                           "common.h"],
                 "csr_add": ["csr_add.hip", "common.h"], "transpose": ["radix.hip", "common.h"],
                 "row_order": ["radix.hip", "common.h"]}
 
 
-def op_kernels(spmm_info, sddmm_info):
+def op_kernels(spmm_info, sddmm_info, m, nnz):
     """Kernels one call of each operation launches (names as in rocprofv3)."""
     spmm = ["spmm_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else [])
+    # N == 1: row blocks through LDS when the plan finds the rows balanced
+    # (longest row <= 2 * mean + 32) and short (<= 128 entries), else a group
+    # of lanes per row
+    mr = spmm_info.get("max_row_nnz", 0)
+    balanced = m > 0 and 0 < mr <= min(128, 2 * (nnz // m) + 32)
+    spmv = (["spmv_stream_kernel"] if balanced and not spmm_info.get("chunks", 0)
+            else ["spmv_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else []))
     sddmm = ((["sddmm_tile_kernel"] if sddmm_info.get("tiles", 0) else [])
              + (["sddmm_list_kernel"] if sddmm_info.get("rest_nnz", 0) else []))
-    return {"spmm": spmm, "sddmm": sddmm or ["sddmm_list_kernel"],
+    return {"spmm": spmm, "spmv": spmv, "sddmm": sddmm or ["sddmm_list_kernel"],
             "csr_add": ["csr_add_kernel"],
             "transpose": ["expand_rows_kernel", "radix_count_kernel", "scan_single_kernel",
                           "radix_scatter_kernel", "transpose_bucket_kernel"],
@@ -149,9 +158,11 @@ def cpu_baseline(w, A, dt, N, K, ops, oracle):
     """The float64 oracle on the host cores, same workload, one warm-up then
     the median of 3 runs per operation."""
     B, Ad, BT, W = w.get("B"), w.get("Ad"), w.get("BT"), w.get("W")
+    B1 = w.get("B1") if "spmv" in ops else None
     ab = alg_bytes(A, N, K, dt)
     fns = {
         "spmm": lambda: oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt),
+        "spmv": lambda: oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B1, dt),
         "sddmm": lambda: oracle.sddmm(A.row_offsets, A.col_idx, Ad, BT, dt),
         "csr_add": lambda: oracle.csr_add(A.row_offsets, A.col_idx, A.values, dt, W, dt),
         "transpose": lambda: oracle.csr_transpose(A.m, A.n, A.row_offsets, A.col_idx, A.values),
@@ -274,6 +285,8 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     ops = [o for o in args.ops.split(",") if o]
+    if args.config == 4 and "spmm" in ops and "spmv" not in ops:
+        ops.insert(ops.index("spmm") + 1, "spmv")  # config 4 names both N = 1 and N = 32
 
     w = gen.make_config(args.config, dt=args.dtype)
     A = w.get("A")
@@ -290,6 +303,7 @@ def main():
 
     v, ro, ci = to(A.values, dt), to(A.row_offsets), to(A.col_idx)
     B = to(w.get("B"), dt)
+    B1 = to(w.get("B1"), dt) if "spmv" in ops else None
     Ad, BT = to(w.get("Ad"), dt), to(w.get("BT"), dt)
     Wd = to(w.get("W"), dt) if "csr_add" in ops else None
     if args.config == 4 and Wd is not None:
@@ -312,6 +326,7 @@ def main():
     t_sddmm_plan = time.perf_counter() - t0
     ri_add = ri if A_add is A else S.sort_rows_by_nnz(roa, n)
     C = torch.empty((m, N), dtype=torch.float32, device=dev)
+    C1 = torch.empty((m, 1), dtype=torch.float32, device=dev)
     out = torch.empty(A.nnz, dtype=torch.float32, device=dev)
     tws = S.csr_transpose_workspace(m, n, A.nnz, dev)
     sws = S.sort_rows_workspace(n, m, dev)
@@ -326,6 +341,8 @@ def main():
     def run_op(op):
         if op == "spmm":
             S.spmm(v, ro, ri, ci, B, m, plan=spmm_plan, out=C)
+        elif op == "spmv":
+            S.spmm(v, ro, ri, ci, B1, m, plan=spmm_plan, out=C1)
         elif op == "sddmm":
             S.sddmm(ro, ri, ci, Ad, BT, plan=sddmm_plan, out=out)
         elif op == "csr_add":
@@ -418,8 +435,8 @@ def main():
     # the dominant kernel: the longer of SpMM and SDDMM (the operations the
     # metric is about; each is one kernel unless long rows are split or the
     # mask has dense tiles, and then its kernels are listed together)
-    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info())
-    gated = [o for o in ops if o in ("spmm", "sddmm")]
+    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.nnz)
+    gated = [o for o in ops if o in ("spmm", "spmv", "sddmm")]
     dom = max(gated or ops, key=lambda o: breakdown[o]["ms"])
     achieved = ab[dom] / breakdown[dom]["ms"] / 1e6
     traffic = traffic_for(dom, args.config)

@@ -205,6 +205,48 @@ def test_spmm_deterministic_and_stream_ordered():
     assert torch.equal(c1, c2)
 
 
+@pytest.mark.parametrize("dt,m,n,density,kw", [
+    ("f32", 5000, 6000, 0.004, {"col_index_dtype": np.int32}),
+    ("f16", 3001, 2000, 0.01, {"empty_row_frac": 0.2}),
+    ("bf16", 700, 900, 0.1, {}),             # ~90 per row: 71 rows per block
+    ("f32", 257, 300, 0.05, {"shuffle_within_rows": True}),
+])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_spmv_row_blocks(dt, m, n, density, kw, offset):
+    # balanced rows with N == 1 run as row blocks streamed through LDS; an
+    # offset of one element makes col/val unaligned for the 4-entry loads
+    A = gen.random_csr(20 + m, m, n, density, dt, **kw)
+    x = gen.dense(20 + m, 100, gen.S_B, (n, 1), dt)
+    v, ro, ci = csr_dev(A)
+    if offset:
+        v = torch.cat([v[:1], v])[1:]
+        ci = torch.cat([ci[:1], ci])[1:]
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    assert 0 < p.info()["max_row_nnz"] <= 128 and p.info()["split_rows"] == 0
+    y = S.spmm(v, ro, ri, ci, dev(x, dt), m, plan=p)
+    ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt)
+    assert_close(host_f64(y), ref, dt, "spmv row blocks")
+
+
+def test_spmv_row_blocks_offsets_changed_after_planning():
+    # a plan made for short rows, then one row rewritten to hold every entry:
+    # the blocks find their range too large for LDS and fall back to a wave
+    # per row, still inside the buffers and still the product
+    m, n = 2000, 3000
+    A = gen.random_csr(31, m, n, 0.005, "f32")
+    x = gen.dense(31, 100, gen.S_B, (n, 1), "f32")
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    ro2 = np.zeros(m + 1, np.int32)
+    ro2[1:] = A.nnz
+    ro.copy_(torch.from_numpy(ro2).to(ro.device))
+    y = S.spmm(v, ro, ri, ci, dev(x, "f32"), m, plan=p)
+    ref = oracle.spmm(m, ro2, A.col_idx, A.values, "f32", x, "f32")
+    assert_close(host_f64(y), ref, "f32", "spmv stale plan")
+
+
 # ----------------------------------------------------------------- SDDMM --
 
 SDDMM_CASES = [

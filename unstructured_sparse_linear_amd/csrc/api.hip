@@ -165,7 +165,10 @@ spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, i
   a.C = C;
   a.dtype = b_type;
   a.out_dtype = c_type;
-  if (plan) a.natural = plan->sch.natural;
+  if (plan) {
+    a.natural = plan->sch.natural;
+    a.max_row = plan->sch.max_row;
+  }
   if (plan && plan->sch.P > 0) {
     a.P = plan->sch.P;
     a.S = plan->sch.S;

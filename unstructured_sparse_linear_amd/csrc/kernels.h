@@ -57,6 +57,7 @@ struct SpmmArgs {
   int dtype;      // value / B dtype
   int out_dtype;  // C dtype
   int natural;          // 1: whole rows in index order (balanced lengths), 0: row_idx order
+  int64_t max_row;      // longest row (from the plan; 0 = unknown)
   // row-splitting schedule (P == 0: none)
   int64_t P;            // number of chunk items of split rows
   int64_t S;            // number of split rows

@@ -32,6 +32,8 @@
 // fixed order, so results are bitwise reproducible.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -390,6 +392,152 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
   if (gl == 0 && r >= 0) ((OT*)a.C)[r * a.ldc] = from_f32<OT>(s);
 }
 
+// N == 1 on balanced rows: a workgroup owns R consecutive rows and streams
+// their entries (one contiguous range of col/val) with coalesced loads, four
+// consecutive entries per lane, into LDS as products val * x[col]; then
+// thread t adds row t's products in stored order.  This is the row-block
+// streaming scheme of Greathouse and Daga ("Efficient Sparse Matrix-Vector
+// Multiplication on GPUs using the CSR Storage Format", SC 2014): every lane
+// is busy whatever the row lengths, and the only dependent load is the x
+// gather.  The host sizes R so that a block's entries take about one round of
+// loads per lane (the kernel is bound by the latency of that round, so many
+// small blocks beat few large ones) and R * (longest row) products fit in the
+// block's LDS (`cap` floats, dynamic); a block whose range is larger anyway
+// (row offsets that do not match the plan) takes a slower wave-per-row path,
+// so no input reaches past the buffers.
+constexpr int kStreamCap = 8192;  // most products per workgroup held in LDS
+constexpr int kStreamQuads = 2;   // groups of four entries per lane per round
+// below this many rows per workgroup (rows longer than kStreamCap / it) the
+// lanes-per-row kernel is used instead
+constexpr int kStreamMinRows = 64;
+
+template <int BYTES>
+struct QuadLoad;
+template <>
+struct QuadLoad<16> {
+  typedef uint4 type;
+};
+template <>
+struct QuadLoad<8> {
+  typedef uint2 type;
+};
+
+// Four consecutive elements from a 4-element-aligned address.
+template <typename T>
+__device__ __forceinline__ void load_quad(const T* p, T (&out)[4]) {
+  typedef typename QuadLoad<4 * sizeof(T)>::type Q;
+  const Q q = *reinterpret_cast<const Q*>(p);
+  __builtin_memcpy(out, &q, sizeof(Q));
+}
+
+template <typename VT, typename OT, typename IT, bool QUAD>
+__global__ __launch_bounds__(kBlock) void spmv_stream_kernel(SpmmArgs a, int32_t R,
+                                                             int32_t cap) {
+  extern __shared__ __align__(16) float prod[];  // cap + 4 floats
+  const IT* col = (const IT*)a.col;
+  const VT* val = (const VT*)a.val;
+  const VT* x = (const VT*)a.B;
+  // entry positions fit in 32 bits (row offsets are int32)
+  const int k = (int)a.k, nnz = (int)a.nnz;
+  const int64_t ldx = a.ldb;
+  const int64_t r0 = row_block(blockIdx.x, gridDim.x, 1) * R;
+  if (r0 >= a.m) return;
+  const int64_t r1 = r0 + R < a.m ? r0 + R : a.m;
+  const int t = threadIdx.x;
+  int base = a.ro[r0], end = a.ro[r1];
+  base = base < 0 ? 0 : (base > nnz ? nnz : base);
+  end = end < base ? base : (end > nnz ? nnz : end);
+  // this thread's row (a clamped row for the idle threads, so the loads need
+  // no branch); the offsets are used only after the products are in LDS
+  const int64_t r = r0 + t;
+  const int64_t rl = r < r1 ? r : r1 - 1;
+  const int o0 = a.ro[rl], o1 = a.ro[rl + 1];
+  // products sit at prod[p - base4]; base4 = base rounded down to a multiple
+  // of four, so each group of four lands on one 16-byte LDS slot
+  const int base4 = base & ~3;
+  if (end - base4 > cap) {
+    // wave per row (not reached with offsets that match the plan)
+    const int w = t / kWave, l = lane_id();
+    for (int64_t rr = r0 + w; rr < r1; rr += kBlock / kWave) {
+      int64_t p0, p1;
+      row_range(a.ro, rr, nnz, p0, p1);
+      float s = 0.f;
+      for (int64_t p = p0 + l; p < p1; p += kWave) {
+        const int c = (int)col[p];
+        if ((unsigned)c < (unsigned)k) s = __builtin_fmaf(to_f32(val[p]), to_f32(x[c * ldx]), s);
+      }
+      s = group_sum<kWave>(s);
+      if (l == 0) ((OT*)a.C)[rr * a.ldc] = from_f32<OT>(s);
+    }
+    return;
+  }
+  // Loads are unconditional at clamped, in-bounds addresses and masked
+  // afterwards, so that all of a lane's loads are in flight together.  x[0]
+  // stands in for an invalid column when x has a row at all.
+  const bool has_x = k > 0;
+  int p_done = base;  // entries below this one are handled by the main loop
+  if constexpr (QUAD) {
+    // groups of four entries [4g, 4g+4) that lie inside the arrays; the first
+    // and last groups may stick out of [base, end)
+    constexpr int U = kStreamQuads;
+    const int gend = min(nnz >> 2, (end + 3) >> 2);
+    const int gbeg = base >> 2;
+    if (gend > gbeg) {
+      p_done = max(base, 4 * gend);
+      for (int g = gbeg + t; g < gend; g += kBlock * U) {
+        IT c[U][4];
+        VT v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int gq = min(g + u * kBlock, gend - 1);
+          load_quad(col + 4 * gq, c[u]);
+          load_quad(val + 4 * gq, v[u]);
+        }
+        float xv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ci = (int)c[u][q];
+            const bool ok = (unsigned)ci < (unsigned)k;
+            const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
+            xv[u][q] = ok ? xl : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // slots before base or from end on are written but never read
+          const int gu = g + u * kBlock;
+          if (gu < gend) {
+            float4 pr;
+            pr.x = to_f32(v[u][0]) * xv[u][0];
+            pr.y = to_f32(v[u][1]) * xv[u][1];
+            pr.z = to_f32(v[u][2]) * xv[u][2];
+            pr.w = to_f32(v[u][3]) * xv[u][3];
+            *reinterpret_cast<float4*>(prod + (4 * gu - base4)) = pr;
+          }
+        }
+      }
+    }
+  }
+  // entries one at a time: everything without the 4-entry loads, else the
+  // at most three past the arrays' last whole group
+  for (int pp = p_done + t; pp < end; pp += kBlock) {
+    const int ci = (int)col[pp];
+    const bool ok = (unsigned)ci < (unsigned)k;
+    const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
+    prod[pp - base4] = ok ? to_f32(val[pp]) * xl : 0.f;
+  }
+  __syncthreads();
+  if (r < r1) {
+    const int q0 = o0 < base ? base : (o0 > end ? end : o0);
+    const int q1 = o1 < q0 ? q0 : (o1 > end ? end : o1);
+    float s = 0.f;
+#pragma unroll 4
+    for (int pp = q0; pp < q1; ++pp) s += prod[pp - base4];
+    ((OT*)a.C)[r * a.ldc] = from_f32<OT>(s);
+  }
+}
+
 // --------------------------------------------------------- wide-N waves --
 
 template <int BYTES>
@@ -706,7 +854,27 @@ template <typename VT, typename OT, typename IT>
 hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
   hipError_t e;
-  if (a.N == 1) {
+  if (a.N == 1 && a.natural && a.P == 0 && a.max_row > 0 &&
+      a.max_row <= kStreamCap / kStreamMinRows) {
+    // balanced rows: stream row blocks through LDS, about one round of
+    // loads per lane per block
+    const int64_t mean = std::max<int64_t>(1, a.nnz / a.m);
+    int64_t R = (int64_t)kBlock * 4 * kStreamQuads / mean;
+    R = std::max<int64_t>(1, std::min<int64_t>({R, (int64_t)kBlock, kStreamCap / a.max_row}));
+    // + 8: the first and last groups of four may stick out of the range
+    const int32_t cap = (int32_t)(R * a.max_row) + 8;
+    const dim3 grid((unsigned)pad8(cdiv(a.m, R)));
+    const size_t lds = (size_t)(cap + 4) * sizeof(float);
+    const bool quad = ((uintptr_t)a.col % (4 * sizeof(IT)) == 0) &&
+                      ((uintptr_t)a.val % (4 * sizeof(VT)) == 0);
+    if (quad)
+      hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, true>), grid, dim3(kBlock), lds, s, a,
+                         (int32_t)R, cap);
+    else
+      hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, false>), grid, dim3(kBlock), lds, s, a,
+                         (int32_t)R, cap);
+    e = hipGetLastError();
+  } else if (a.N == 1) {
     // lanes per row from the mean row length
     const int64_t mean = a.m > 0 ? a.nnz / a.m : 0;
     int lpr = 2;
@@ -751,11 +919,7 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
       const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
                            ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
                            ((uintptr_t)a.partial % 16 == 0);
-      int64_t nv = cdiv(a.N, VEC);
-      {  // TUNING ONLY
-        const char* lp = getenv("SPOPS_SPMM_LPR");
-        if (lp) { const int64_t cap = atoll(lp); if (nv > cap) nv = cap; }
-      }
+      const int64_t nv = cdiv(a.N, VEC);
       if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
       else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
       else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
