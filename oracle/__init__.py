@@ -227,3 +227,54 @@ def sparse_linear_backward(m: int, n: int, row_offsets, col_idx, values, val_dt:
         dv[p] = float(np.dot(g[r[p]], x[c[p]]))
         dxt[c[p]] += v[p] * g[r[p]]
     return dv, dxt
+
+
+# ------------------------------------------------- conjugate gradients --
+# The torchsparsegradutils README lists a CG solver among its built-in
+# iterative solvers ("Built-in Iterative Solvers") and calls a generic sparse
+# solve with it and a tolerance in its usage example ("Generic solve").  The
+# page gives no steps, so this is the method of Hestenes and Stiefel ("Methods
+# of Conjugate Gradients for Solving Linear Systems", J. Res. NBS 49, 1952) in
+# its usual form: residual r = b - A x, search direction p, step
+# alpha = (r.r) / (p.A p), new direction r + beta p with
+# beta = (r_new.r_new) / (r.r).  It stops once the recursively updated
+# residual satisfies ||r|| <= rtol * ||b|| (compared squared) or after
+# max_iter iterations.  Everything is float64; A p is summed entry by entry in
+# stored order.
+
+def csr_matvec(m: int, row_offsets, col_idx, values_f64, x) -> np.ndarray:
+    """y = A x in float64 (one stored entry at a time, stored order)."""
+    r, c = _rows_of(row_offsets), np.asarray(col_idx, dtype=np.int64)
+    return np.bincount(r, weights=np.asarray(values_f64) * np.asarray(x)[c], minlength=m)
+
+
+def cg(m: int, row_offsets, col_idx, values, val_dt: str, b, x0=None, rtol: float = 1e-6,
+       max_iter: int = 1000, history: bool = False):
+    """Solve A x = b for symmetric positive definite A.  Returns
+    (x, iterations, ||r|| / ||b||) and, with history=True, the lists of
+    search directions and residuals of every iteration (for the pins)."""
+    v = to_f64(values, val_dt)
+    b = np.asarray(b, dtype=np.float64).reshape(-1)
+    x = np.zeros(m) if x0 is None else np.asarray(x0, dtype=np.float64).reshape(-1).copy()
+    r = b - csr_matvec(m, row_offsets, col_idx, v, x)
+    p = r.copy()
+    rr, bb = float(r @ r), float(b @ b)
+    thr = rtol * rtol * bb
+    k = 0
+    ps, rs = [p.copy()], [r.copy()]
+    while k < max_iter and rr > thr:
+        q = csr_matvec(m, row_offsets, col_idx, v, p)
+        alpha = rr / float(p @ q)
+        x += alpha * p
+        r -= alpha * q
+        rr_new = float(r @ r)
+        p = r + (rr_new / rr) * p
+        rr = rr_new
+        k += 1
+        if history:
+            ps.append(p.copy())
+            rs.append(r.copy())
+    rel = float(np.sqrt(rr / bb)) if bb > 0 else 0.0
+    if history:
+        return x, k, rel, ps, rs
+    return x, k, rel
