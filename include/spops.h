@@ -8,6 +8,8 @@
  *   spops_csr_add         section "Sparse Addition"
  *   spops_csr_transpose   section "CSR Transpose"
  *   spops_sort_rows_by_nnz  the row_idx list of section "Usage"
+ * and, built on spops_spmm, a conjugate-gradient solver (spops_cg; the
+ * torchsparsegradutils README, section "Built-in Iterative Solvers").
  *
  * Sparse layout (section "Usage"): an m x n matrix with nnz stored entries is
  *   values[nnz]        the stored values (f32, f16 or bf16);
@@ -25,7 +27,8 @@
  *     inside a row.  Element pointers must be aligned to their element size.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
  *     the default stream).  Execute calls never allocate device memory and
- *     never synchronize; plan-creation calls do both and say so.
+ *     never synchronize; plan-creation calls do both and say so, and the
+ *     solver spops_cg synchronizes at its convergence checks.
  *   - Validation reads host-side metadata only (sizes, types, pointers).  On
  *     any error status nothing is launched and no output is written.
  *     Device-resident index data is not validated: indices outside their
@@ -211,6 +214,40 @@ spops_status spops_sort_rows_by_nnz_workspace_size(int64_t rows, int64_t cols, s
 spops_status spops_sort_rows_by_nnz(const int32_t* row_offsets, int64_t rows, int64_t cols,
                                     void* row_idx, spops_itype row_idx_type, void* workspace,
                                     size_t workspace_bytes, void* hip_stream);
+
+/* --------------------------------------------------- conjugate gradients --
+ * Solves A x = b for a symmetric positive definite A with conjugate
+ * gradients.  The torchsparsegradutils README lists a CG solver among its
+ * built-in iterative solvers ("Built-in Iterative Solvers") and calls a
+ * sparse solve with it and a tolerance ("Generic solve"); the page gives no
+ * steps, so the method is that of Hestenes and Stiefel (1952):
+ *   r = b - A x, p = r; per iteration q = A p (the SpMM above with N = 1),
+ *   alpha = r.r / p.q, x += alpha p, r -= alpha q,
+ *   beta = r'.r' / r.r, p = r' + beta p.
+ *   A:  rows x rows CSR, f32 values, row_idx required (as for spops_spmm).
+ *   b:  [rows] f32.  x: [rows] f32, the initial guess on entry, the solution
+ *       on exit.  Vectors are f32; dot products and the scalar steps are
+ *       float64, summed in a fixed order (deterministic).
+ *   Stops after the first iteration whose recursive residual has
+ *   r.r <= rtol^2 * b.b, or after max_iter iterations, or (without writing
+ *   x) when p.q is not positive (A is not positive definite).
+ *   check_every (>= 1): iterations enqueued between two convergence checks;
+ *   each check reads the solver state back and synchronizes hip_stream, so
+ *   this call BLOCKS until it returns.  Iterations enqueued past convergence
+ *   leave x unchanged.
+ *   plan (nullable): spops_spmm_plan_create's plan for A.
+ *   iters_out, rel_resid_out (nullable): iterations done and sqrt(r.r / b.b)
+ *   (0 when b = 0).
+ *   workspace: spops_cg_workspace_size bytes (vectors r, p, q, partial sums,
+ *   solver state, the SpMM's workspace); contents on entry do not matter.
+ *   rtol < 0 or NaN, max_iter < 0, check_every < 1 give SPOPS_ERR_SHAPE;
+ *   rows != cols SPOPS_ERR_SHAPE; values other than f32 SPOPS_ERR_DTYPE. */
+spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* plan,
+                                     size_t* bytes);
+spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, int64_t max_iter,
+                      int64_t check_every, const spops_spmm_plan* plan, void* workspace,
+                      size_t workspace_bytes, int64_t* iters_out, double* rel_resid_out,
+                      void* hip_stream);
 
 #ifdef __cplusplus
 }

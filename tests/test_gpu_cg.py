@@ -1,0 +1,156 @@
+"""GPU conjugate gradients against the float64 oracle.
+
+Element-wise parity on the first iterations (fixed iteration counts, so no
+stopping decision is involved), then convergence: the GPU's stopping
+iteration may differ from the oracle's by one where the two residual norms
+straddle the threshold in their own rounding, so the count is compared to
+within one and the GPU solution's true residual is checked in float64."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unstructured_sparse_linear_amd as S
+from unstructured_sparse_linear_amd import gen
+from helpers import assert_close, csr_dev, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    S.lib()
+    yield
+    S.clear_plan_caches()
+    torch.cuda.synchronize()
+
+
+def spd(seed, n, band=8, draws=4):
+    return gen.banded_spd(np.random.default_rng(seed), np.random.default_rng(seed + 1), n,
+                          band=band, offband_draws=draws)
+
+
+def arrow_spd(seed, n, width):
+    """Diagonally dominant SPD with `width` dense rows and columns (long rows
+    take the SpMV's split-row path)."""
+    rng = np.random.default_rng(seed)
+    rows, cols, vals = [], [], []
+    off = rng.standard_normal((width, n)).astype(np.float32) * 0.01
+    for i in range(width):
+        for j in range(n):
+            if j != i:
+                rows += [i, j]
+                cols += [j, i]
+                vals += [off[i, j], off[i, j]]
+    rows, cols = np.array(rows), np.array(cols)
+    vals = np.array(vals, np.float32)
+    key = rows * n + cols
+    _, first = np.unique(key, return_index=True)       # (i, j) for i, j < width twice
+    rows, cols, vals = rows[first], cols[first], vals[first]
+    absum = np.zeros(n)
+    np.add.at(absum, rows, np.abs(vals.astype(np.float64)))
+    diag = (1.0 + absum).astype(np.float32)
+    return gen.csr_from_coo(n, n, np.concatenate([rows, np.arange(n)]),
+                            np.concatenate([cols, np.arange(n)]),
+                            np.concatenate([vals, diag]), "f32")
+
+
+def solve(A, b, x0=None, **kw):
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    x = None if x0 is None else dev(np.asarray(x0, np.float32))
+    return S.cg(v, ro, ri, ci, dev(np.asarray(b, np.float32)), x=x, **kw)
+
+
+def rhs(seed, n):
+    return np.random.default_rng(seed).standard_normal(n).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed,n,iters,check", [(1, 3000, 5, 2), (2, 777, 3, 1),
+                                                 (3, 12345, 8, 8)])
+def test_cg_first_iterations_match_oracle(seed, n, iters, check):
+    A, b = spd(seed, n), rhs(seed + 10, n)
+    x, k, rel = solve(A, b, rtol=0.0, max_iter=iters, check_every=check)
+    xr, kr, relr = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=0.0,
+                             max_iter=iters)
+    assert k == kr == iters
+    assert_close(host_f64(x), xr, "f32", "cg iterate")
+    assert abs(rel - relr) <= 1e-4 * relr
+
+
+@pytest.mark.parametrize("seed,n,rtol", [(4, 5000, 1e-6), (5, 20000, 1e-5), (6, 1500, 1e-7)])
+def test_cg_converges_like_oracle(seed, n, rtol):
+    A, b = spd(seed, n), rhs(seed + 10, n)
+    x, k, rel = solve(A, b, rtol=rtol, max_iter=500)
+    _, kr, _ = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=rtol,
+                         max_iter=500)
+    assert abs(k - kr) <= 1 and rel <= rtol
+    xg = host_f64(x)
+    r = b.astype(np.float64) - oracle.csr_matvec(n, A.row_offsets, A.col_idx,
+                                                 A.values.astype(np.float64), xg)
+    assert np.linalg.norm(r) <= 2 * rtol * np.linalg.norm(b.astype(np.float64))
+
+
+def test_cg_initial_guess_and_split_rows():
+    n = 3000
+    A = arrow_spd(7, n, 3)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    assert S.SpmmPlan(ro, ri, ci, n).info()["split_rows"] == 3
+    b, x0 = rhs(8, n), rhs(9, n)
+    x, k, rel = S.cg(v, ro, ri, ci, dev(b), x=dev(x0), rtol=0.0, max_iter=4)
+    xr, kr, _ = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, x0=x0, rtol=0.0,
+                          max_iter=4)
+    assert k == kr == 4
+    assert_close(host_f64(x), xr, "f32", "cg iterate with x0")
+
+
+def test_cg_nothing_to_do():
+    n = 500
+    A = spd(10, n)
+    x, k, rel = solve(A, np.zeros(n, np.float32), rtol=1e-6)
+    assert k == 0 and rel == 0.0 and not host_f64(x).any()
+    # an exact start on an integer diagonal system
+    d = np.arange(1, n + 1, dtype=np.float32)
+    D = gen.CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int16), d, "f32")
+    x0 = (np.arange(n) - 200).astype(np.float32)
+    x, k, rel = solve(D, d * x0, x0=x0, rtol=1e-6)
+    assert k == 0 and rel == 0.0 and np.array_equal(host_f64(x), x0.astype(np.float64))
+    # max_iter 0 leaves the guess
+    x, k, _ = solve(A, rhs(11, n), x0=x0, rtol=1e-6, max_iter=0)
+    assert k == 0 and np.array_equal(host_f64(x), x0.astype(np.float64))
+
+
+def test_cg_stops_without_writing_when_not_positive_definite():
+    n = 300
+    D = gen.CSR(n, n, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int16),
+                -np.ones(n, np.float32), "f32")
+    x0 = rhs(12, n)
+    x, k, rel = solve(D, rhs(13, n), x0=x0, rtol=1e-6)
+    assert k == 0 and rel > 1e-6
+    assert np.array_equal(host_f64(x), x0.astype(np.float64))
+
+
+def test_cg_deterministic():
+    n = 8000
+    A, b = spd(14, n), rhs(15, n)
+    x1, k1, r1 = solve(A, b, rtol=1e-6)
+    x2, k2, r2 = solve(A, b, rtol=1e-6, check_every=3)
+    assert k1 == k2 and r1 == r2 and torch.equal(x1, x2)
+
+
+def test_cg_rejects_bad_inputs():
+    A = gen.random_csr(16, 40, 50, 0.1, "f32")
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    with pytest.raises((ValueError, S.SpopsError)):
+        S.cg(v, ro, ri, ci, dev(rhs(17, 50)))                 # not square
+    B = spd(18, 64)
+    v, ro, ci = csr_dev(B)
+    ri = S.sort_rows_by_nnz(ro, B.n)
+    with pytest.raises(ValueError):
+        S.cg(v.half(), ro, ri, ci, dev(rhs(19, 64)))            # f16 values
+    with pytest.raises(S.SpopsError):
+        S.cg(v, ro, ri, ci, dev(rhs(19, 64)), rtol=-1.0)

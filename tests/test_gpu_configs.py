@@ -134,6 +134,22 @@ def test_config4_spmv_spmm():
     check_spmm(A, w.get("B"), "f32")
 
 
+def test_config4_cg():
+    # conjugate gradients on the full banded SPD matrix, b = the SpMV vector
+    w = workload(4)
+    A = w.get("A")
+    b = w.get("B1")[:, 0].astype(np.float32)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    x, k, rel = S.cg(v, ro, ri, ci, dev(b), rtol=1e-6, max_iter=1000)
+    _, kr, _ = oracle.cg(A.m, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=1e-6,
+                         max_iter=1000)
+    assert abs(k - kr) <= 1 and rel <= 1e-6
+    r = b.astype(np.float64) - oracle.csr_matvec(A.m, A.row_offsets, A.col_idx,
+                                                 A.values.astype(np.float64), host_f64(x))
+    assert np.linalg.norm(r) <= 2e-6 * np.linalg.norm(b.astype(np.float64))
+
+
 def test_config4_sddmm_transpose_csr_add():
     w = workload(4)
     A = w.get("A")

@@ -12,6 +12,7 @@ from .spops import (  # noqa: F401
     SddmmPlan,
     SpmmPlan,
     SpopsError,
+    cg,
     clear_plan_caches,
     csr_add,
     csr_transpose,
@@ -25,4 +26,4 @@ from .spops import (  # noqa: F401
 
 __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
-           "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear"]
+           "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg"]

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 
 #include "kernels.h"
@@ -57,6 +58,45 @@ spops_status check_csr(const spops_csr* A, bool need_values, bool need_row_idx) 
 spops_status from_hip(hipError_t e) { return e == hipSuccess ? SPOPS_OK : SPOPS_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Launch arguments of C = A * B for validated inputs.
+SpmmArgs spmm_args(const spops_csr* A, const void* B, spops_dtype b_type, int64_t N, int64_t ldb,
+                   void* C, spops_dtype c_type, int64_t ldc, const spops_spmm_plan* plan,
+                   void* workspace) {
+  SpmmArgs a{};
+  a.m = A->rows;
+  a.k = A->cols;
+  a.nnz = A->nnz;
+  a.N = N;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.ro = A->row_offsets;
+  a.col = A->col_idx;
+  a.col_i32 = A->col_type == SPOPS_I32;
+  a.val = A->values;
+  a.row_idx = A->row_idx;
+  a.ri_i32 = A->row_idx_type == SPOPS_I32;
+  a.B = B;
+  a.C = C;
+  a.dtype = b_type;
+  a.out_dtype = c_type;
+  if (plan) {
+    a.natural = plan->sch.natural;
+    a.max_row = plan->sch.max_row;
+  }
+  if (plan && plan->sch.P > 0) {
+    a.P = plan->sch.P;
+    a.S = plan->sch.S;
+    a.T = plan->sch.T;
+    a.item_pos = plan->sch.item_pos;
+    a.item_chunk = plan->sch.item_chunk;
+    a.split_pos = plan->sch.split_pos;
+    a.split_start = plan->sch.split_start;
+    a.split_end = plan->sch.split_end;
+    a.partial = (float*)workspace;
+  }
+  return a;
+}
 
 }  // namespace
 
@@ -148,38 +188,7 @@ spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, i
     spops_spmm_workspace_size(plan, N, &need);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SPOPS_ERR_WORKSPACE;
   }
-  SpmmArgs a{};
-  a.m = A->rows;
-  a.k = A->cols;
-  a.nnz = A->nnz;
-  a.N = N;
-  a.ldb = ldb;
-  a.ldc = ldc;
-  a.ro = A->row_offsets;
-  a.col = A->col_idx;
-  a.col_i32 = A->col_type == SPOPS_I32;
-  a.val = A->values;
-  a.row_idx = A->row_idx;
-  a.ri_i32 = A->row_idx_type == SPOPS_I32;
-  a.B = B;
-  a.C = C;
-  a.dtype = b_type;
-  a.out_dtype = c_type;
-  if (plan) {
-    a.natural = plan->sch.natural;
-    a.max_row = plan->sch.max_row;
-  }
-  if (plan && plan->sch.P > 0) {
-    a.P = plan->sch.P;
-    a.S = plan->sch.S;
-    a.T = plan->sch.T;
-    a.item_pos = plan->sch.item_pos;
-    a.item_chunk = plan->sch.item_chunk;
-    a.split_pos = plan->sch.split_pos;
-    a.split_start = plan->sch.split_start;
-    a.split_end = plan->sch.split_end;
-    a.partial = (float*)workspace;
-  }
+  const SpmmArgs a = spmm_args(A, B, b_type, N, ldb, C, c_type, ldc, plan, workspace);
   return from_hip(launch_spmm(a, as_stream(hip_stream)));
 }
 
@@ -426,6 +435,74 @@ spops_status spops_sort_rows_by_nnz(const int32_t* row_offsets, int64_t rows, in
     return SPOPS_ERR_WORKSPACE;
   return from_hip(launch_sort_rows(row_offsets, rows, cols, row_idx, row_idx_type == SPOPS_I32,
                                    workspace, as_stream(hip_stream)));
+}
+
+// ---------------------------------------------------- conjugate gradients --
+
+static spops_status check_cg(const spops_csr* A, const spops_spmm_plan* plan) {
+  spops_status st = check_csr(A, true, true);
+  if (st != SPOPS_OK) return st;
+  if (A->rows != A->cols) return SPOPS_ERR_SHAPE;
+  if (A->val_type != SPOPS_F32) return SPOPS_ERR_DTYPE;
+  if (plan && (plan->rows != A->rows || plan->nnz != A->nnz || plan->ro != A->row_offsets ||
+               plan->row_idx != A->row_idx))
+    return SPOPS_ERR_PLAN;
+  return SPOPS_OK;
+}
+
+spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* plan,
+                                     size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  spops_status st = check_cg(A, plan);
+  if (st != SPOPS_OK) return st;
+  size_t sp = 0;
+  spops_spmm_workspace_size(plan, 1, &sp);
+  *bytes = cg_workspace_bytes(A->rows, sp);
+  return SPOPS_OK;
+}
+
+spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, int64_t max_iter,
+                      int64_t check_every, const spops_spmm_plan* plan, void* workspace,
+                      size_t workspace_bytes, int64_t* iters_out, double* rel_resid_out,
+                      void* hip_stream) {
+  spops_status st = check_cg(A, plan);
+  if (st != SPOPS_OK) return st;
+  if (!(rtol >= 0.0) || max_iter < 0 || check_every < 1) return SPOPS_ERR_SHAPE;
+  const int64_t m = A->rows;
+  if (iters_out) *iters_out = 0;
+  if (rel_resid_out) *rel_resid_out = 0.0;
+  if (m == 0) return SPOPS_OK;
+  if (!b || !x) return SPOPS_ERR_NULL;
+  size_t need = 0;
+  spops_cg_workspace_size(A, plan, &need);
+  if (!workspace || workspace_bytes < need) return SPOPS_ERR_WORKSPACE;
+  hipStream_t s = as_stream(hip_stream);
+  const CgBuffers w = carve_cg_workspace(workspace, m);
+  size_t sp = 0;
+  spops_spmm_workspace_size(plan, 1, &sp);
+  // q = A x0, then r = b - q, p = r
+  const SpmmArgs ax = spmm_args(A, x, SPOPS_F32, 1, 1, w.q, SPOPS_F32, 1, plan, w.spmm_ws);
+  hipError_t e = launch_spmm(ax, s);
+  if (e == hipSuccess) e = launch_cg_init(m, (const float*)b, w.q, w, rtol, s);
+  if (e != hipSuccess) return SPOPS_ERR_HIP;
+  const SpmmArgs ap = spmm_args(A, w.p, SPOPS_F32, 1, 1, w.q, SPOPS_F32, 1, plan, w.spmm_ws);
+  CgState h{};
+  int64_t k = 0;
+  for (;;) {
+    if ((e = hipMemcpyAsync(&h, w.st, sizeof(h), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return SPOPS_ERR_HIP;
+    if (h.done || k >= max_iter) break;
+    const int64_t n = std::min<int64_t>(check_every, max_iter - k);
+    for (int64_t j = 0; j < n; ++j, ++k) {
+      if ((e = launch_spmm(ap, s)) != hipSuccess) return SPOPS_ERR_HIP;
+      if ((e = launch_cg_after_product(m, k, (float*)x, w, s)) != hipSuccess)
+        return SPOPS_ERR_HIP;
+    }
+  }
+  if (iters_out) *iters_out = h.iters;
+  if (rel_resid_out) *rel_resid_out = h.bb > 0.0 ? sqrt(h.rr[h.iters & 1] / h.bb) : 0.0;
+  return SPOPS_OK;
 }
 
 }  // extern "C"

@@ -171,4 +171,35 @@ hipError_t launch_csr_add(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, 
                           int col_i32, const void* val, void* W, int64_t ldw, int dtype,
                           hipStream_t s);
 
+// ------------------------------------------------- conjugate gradients --
+// Solver state in device memory (written by the solver's kernels, read by
+// the host at its convergence checks).
+struct CgState {
+  double rr[2];    // r.r after iteration k at rr[k & 1]
+  double bb;       // b.b
+  double thr;      // rtol^2 * b.b
+  int64_t iters;   // iterations completed
+  int32_t done;    // 0 running, 1 converged, 2 stopped (p.q not positive)
+  int32_t pad;
+};
+constexpr int kCgMaxParts = 1024;  // most per-workgroup partial sums
+struct CgBuffers {
+  float *r, *p, *q;        // [m] each
+  double *part0, *part1;   // [kCgMaxParts] each
+  CgState* st;
+  void* spmm_ws;           // the SpMV's own workspace
+};
+// Workspace of the solver for m unknowns and an SpMV workspace of spmm_ws
+// bytes, and its split into buffers (256-byte aligned pieces).
+size_t cg_workspace_bytes(int64_t m, size_t spmm_ws);
+CgBuffers carve_cg_workspace(void* ws, int64_t m);
+int cg_parts(int64_t m);
+// r = b - q (q = A x0), p = r, state for iteration 0.
+hipError_t launch_cg_init(int64_t m, const float* b, const float* q, const CgBuffers& w,
+                          double rtol, hipStream_t s);
+// The rest of iteration k once q = A p is in w.q: p.q, the x / r update, the
+// new direction and the state.
+hipError_t launch_cg_after_product(int64_t m, int64_t k, float* x, const CgBuffers& w,
+                                   hipStream_t s);
+
 }  // namespace spops

@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
             "spops_csr_transpose": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
             "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
             "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
+            "spops_cg_workspace_size": ([cp, vp, P(sz)], i32),
+            "spops_cg": ([cp, vp, vp, ctypes.c_double, i64, i64, vp, vp, sz, P(i64),
+                          P(ctypes.c_double), vp], i32),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -405,3 +408,41 @@ def sort_rows_by_nnz(row_offsets: torch.Tensor, n: int,
         row_offsets.data_ptr(), m, n, _ptr(out), _IT[out.dtype], workspace.data_ptr(),
         workspace.numel(), _stream(row_offsets)))
     return out
+
+
+def cg(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Tensor,
+       A_col_indices: torch.Tensor, b: torch.Tensor, x: Optional[torch.Tensor] = None,
+       rtol: float = 1e-6, max_iter: int = 1000, check_every: int = 8,
+       plan: Optional[SpmmPlan] = None, use_plan: bool = True):
+    """Conjugate gradients for A x = b (A square, symmetric positive definite,
+    f32 values).  `x` (optional) is the initial guess and is overwritten with
+    the solution; without it the solve starts from zero.  Returns
+    (x, iterations, ||r|| / ||b||).  Blocks: the solver reads its state back
+    every `check_every` iterations."""
+    _require(b, "b", (torch.float32,))
+    m = b.numel()
+    if b.dim() != 1:
+        raise ValueError("b must be 1-D")
+    if A_val.dtype != torch.float32:
+        raise ValueError("cg needs f32 values")
+    d = csr_desc(A_val, A_row_offsets, A_row_indices, A_col_indices, m, m)
+    if x is None:
+        x = torch.zeros_like(b)
+    else:
+        _require(x, "x", (torch.float32,))
+        if x.shape != b.shape:
+            raise ValueError("x must have b's shape")
+    if plan is None and use_plan:
+        plan = _spmm_plans.get(("spmm", _tkey(A_row_offsets), _tkey(A_row_indices), d.nnz, m),
+                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, m))
+    ph = plan.handle if plan is not None else None
+    wb = ctypes.c_size_t()
+    _check("spops_cg_workspace_size", lib().spops_cg_workspace_size(
+        ctypes.byref(d), ph, ctypes.byref(wb)))
+    ws = _workspace(wb.value, b.device)
+    its, rel = ctypes.c_int64(), ctypes.c_double()
+    _check("spops_cg", lib().spops_cg(
+        ctypes.byref(d), _ptr(b), _ptr(x), float(rtol), int(max_iter), int(check_every), ph,
+        _ptr(ws), ws.numel() if ws is not None else 0, ctypes.byref(its), ctypes.byref(rel),
+        _stream(b)))
+    return x, int(its.value), float(rel.value)
