@@ -266,6 +266,48 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
             "step": "hip graph replay, cold caches"}
 
 
+def cg_solve(S, w, A, dev, args):
+    """Conjugate gradients on the workload's SPD matrix (A, f32) with b = the
+    SpMV vector, rtol 1e-6, convergence checked every 16 iterations.  Per
+    iteration: one SpMV and three vector kernels (p.q; x and r; p).  The
+    matrix stays in the caches between iterations, as in any solve, so only
+    the first iteration starts cold."""
+    import torch
+
+    if w.dt != "f32" or A.m != A.n or "B1" not in w._builders:
+        return None
+    m = A.m
+    v = torch.from_numpy(A.values).to(dev)
+    ro = torch.from_numpy(A.row_offsets).to(dev)
+    ci = torch.from_numpy(A.col_idx).to(dev)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    plan = S.SpmmPlan(ro, ri, ci, m)
+    b = torch.from_numpy(np.ascontiguousarray(w.get("B1")[:, 0])).to(dev)
+    x = torch.zeros_like(b)
+    S.cg(v, ro, ri, ci, b, x=x.zero_(), rtol=1e-6, max_iter=1000, check_every=16, plan=plan)
+    torch.cuda.synchronize()
+    ts, iters, rel = [], 0, 0.0
+    for _ in range(max(3, min(args.steps, 10))):
+        x.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, iters, rel = S.cg(v, ro, ri, ci, b, x=x, rtol=1e-6, max_iter=1000, check_every=16,
+                             plan=plan)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    t = float(np.median(ts))
+    s_ci = A.col_idx.dtype.itemsize
+    kp = len(np.unique(A.col_idx))
+    spmv = A.nnz * (4 + s_ci) + 4 * (m + 1) + kp * 4 + m * 4
+    per_iter = spmv + 11 * 4 * m          # p.q: 2 reads; x, r: 4 reads 2 writes; p: 2 + 1
+    return {"iterations": iters, "rel_residual": rel, "rtol": 1e-6, "ms": round(t * 1e3, 3),
+            "us_per_iteration": round(t * 1e6 / max(iters, 1), 2),
+            "alg_bytes_per_iteration": int(per_iter),
+            "gbps": round(per_iter * iters / t / 1e9, 1),
+            "frac_hbm": round(per_iter * iters / t / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "host wall clock around the call (it synchronizes at its checks)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -475,6 +517,8 @@ def main():
     }
     if not args.no_adapter:
         result["next_adapter_step"] = adapter_step(S, w, A, dt, N, dev, flush, args)
+    if args.config == 4:
+        result["next_cg"] = cg_solve(S, w, A, dev, args)
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)

@@ -70,9 +70,12 @@ def rhs(seed, n):
 
 @pytest.mark.parametrize("seed,n,iters,check", [(1, 3000, 5, 2), (2, 777, 3, 1),
                                                  (3, 12345, 8, 8)])
-def test_cg_first_iterations_match_oracle(seed, n, iters, check):
+@pytest.mark.parametrize("use_plan", [True, False])
+def test_cg_first_iterations_match_oracle(seed, n, iters, check, use_plan):
+    # with the plan the iterations run as fused row blocks; without it the
+    # direction, SpMV and p.q are separate kernels
     A, b = spd(seed, n), rhs(seed + 10, n)
-    x, k, rel = solve(A, b, rtol=0.0, max_iter=iters, check_every=check)
+    x, k, rel = solve(A, b, rtol=0.0, max_iter=iters, check_every=check, use_plan=use_plan)
     xr, kr, relr = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=0.0,
                              max_iter=iters)
     assert k == kr == iters
@@ -80,10 +83,11 @@ def test_cg_first_iterations_match_oracle(seed, n, iters, check):
     assert abs(rel - relr) <= 1e-4 * relr
 
 
-@pytest.mark.parametrize("seed,n,rtol", [(4, 5000, 1e-6), (5, 20000, 1e-5), (6, 1500, 1e-7)])
-def test_cg_converges_like_oracle(seed, n, rtol):
+@pytest.mark.parametrize("seed,n,rtol,use_plan", [(4, 5000, 1e-6, True), (5, 20000, 1e-5, True),
+                                                  (6, 1500, 1e-7, True), (4, 5000, 1e-6, False)])
+def test_cg_converges_like_oracle(seed, n, rtol, use_plan):
     A, b = spd(seed, n), rhs(seed + 10, n)
-    x, k, rel = solve(A, b, rtol=rtol, max_iter=500)
+    x, k, rel = solve(A, b, rtol=rtol, max_iter=500, use_plan=use_plan)
     _, kr, _ = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=rtol,
                          max_iter=500)
     assert abs(k - kr) <= 1 and rel <= rtol
@@ -133,12 +137,30 @@ def test_cg_stops_without_writing_when_not_positive_definite():
     assert np.array_equal(host_f64(x), x0.astype(np.float64))
 
 
-def test_cg_deterministic():
+@pytest.mark.parametrize("use_plan", [True, False])
+def test_cg_deterministic(use_plan):
     n = 8000
     A, b = spd(14, n), rhs(15, n)
-    x1, k1, r1 = solve(A, b, rtol=1e-6)
-    x2, k2, r2 = solve(A, b, rtol=1e-6, check_every=3)
+    x1, k1, r1 = solve(A, b, rtol=1e-6, use_plan=use_plan)
+    x2, k2, r2 = solve(A, b, rtol=1e-6, check_every=3, use_plan=use_plan)
     assert k1 == k2 and r1 == r2 and torch.equal(x1, x2)
+
+
+def test_cg_int16_columns_and_unaligned_arrays():
+    # n <= 32767 gives int16 columns; an offset of one element takes the
+    # entry-at-a-time loads of the fused row blocks
+    n = 6000
+    A, b = spd(20, n), rhs(21, n)
+    assert A.col_idx.dtype == np.int16
+    v, ro, ci = csr_dev(A)
+    v = torch.cat([v[:1], v])[1:]
+    ci = torch.cat([ci[:1], ci])[1:]
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    x, k, _ = S.cg(v, ro, ri, ci, dev(b), rtol=0.0, max_iter=6)
+    xr, kr, _ = oracle.cg(n, A.row_offsets, A.col_idx, A.values, "f32", b, rtol=0.0,
+                          max_iter=6)
+    assert k == kr == 6
+    assert_close(host_f64(x), xr, "f32", "cg int16 unaligned")
 
 
 def test_cg_rejects_bad_inputs():

@@ -450,6 +450,12 @@ static spops_status check_cg(const spops_csr* A, const spops_spmm_plan* plan) {
   return SPOPS_OK;
 }
 
+// Row-block plan of the fused iteration (ok == false: the library's SpMV).
+static SpmvBlocks cg_blocks(const spops_csr* A, const spops_spmm_plan* plan) {
+  if (!plan) return SpmvBlocks{};
+  return spmv_row_blocks(A->rows, A->nnz, plan->sch.max_row, plan->sch.natural, plan->sch.P);
+}
+
 spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* plan,
                                      size_t* bytes) {
   if (!bytes) return SPOPS_ERR_NULL;
@@ -457,7 +463,8 @@ spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* 
   if (st != SPOPS_OK) return st;
   size_t sp = 0;
   spops_spmm_workspace_size(plan, 1, &sp);
-  *bytes = cg_workspace_bytes(A->rows, sp);
+  const SpmvBlocks sb = cg_blocks(A, plan);
+  *bytes = cg_workspace_bytes(A->rows, sb.ok ? sb.grid : 0, sp);
   return SPOPS_OK;
 }
 
@@ -477,27 +484,46 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
   spops_cg_workspace_size(A, plan, &need);
   if (!workspace || workspace_bytes < need) return SPOPS_ERR_WORKSPACE;
   hipStream_t s = as_stream(hip_stream);
-  const CgBuffers w = carve_cg_workspace(workspace, m);
-  size_t sp = 0;
-  spops_spmm_workspace_size(plan, 1, &sp);
-  // q = A x0, then r = b - q, p = r
+  const SpmvBlocks sb = cg_blocks(A, plan);
+  const CgBuffers w = carve_cg_workspace(workspace, m, sb.ok ? sb.grid : 0);
+  // q = A x0, then r = b - q
   const SpmmArgs ax = spmm_args(A, x, SPOPS_F32, 1, 1, w.q, SPOPS_F32, 1, plan, w.spmm_ws);
   hipError_t e = launch_spmm(ax, s);
-  if (e == hipSuccess) e = launch_cg_init(m, (const float*)b, w.q, w, rtol, s);
+  if (e == hipSuccess) e = launch_cg_init(m, (const float*)b, w, rtol, s);
   if (e != hipSuccess) return SPOPS_ERR_HIP;
-  const SpmmArgs ap = spmm_args(A, w.p, SPOPS_F32, 1, 1, w.q, SPOPS_F32, 1, plan, w.spmm_ws);
+  CgSpmvArgs fa{};
+  fa.m = m;
+  fa.nnz = A->nnz;
+  fa.ro = A->row_offsets;
+  fa.col = A->col_idx;
+  fa.col_i32 = A->col_type == SPOPS_I32;
+  fa.val = (const float*)A->values;
   CgState h{};
   int64_t k = 0;
   for (;;) {
-    if ((e = hipMemcpyAsync(&h, w.st, sizeof(h), hipMemcpyDeviceToHost, s)) != hipSuccess ||
-        (e = hipStreamSynchronize(s)) != hipSuccess)
-      return SPOPS_ERR_HIP;
-    if (h.done || k >= max_iter) break;
+    // the first chunk is enqueued without a check: a start that already
+    // meets the tolerance stops it at its first kernel
+    if (k > 0 || max_iter == 0) {
+      if ((e = launch_cg_record(m, k, w, s)) != hipSuccess ||
+          (e = hipMemcpyAsync(&h, w.st, sizeof(h), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+          (e = hipStreamSynchronize(s)) != hipSuccess)
+        return SPOPS_ERR_HIP;
+      if (h.done || k >= max_iter) break;
+    }
     const int64_t n = std::min<int64_t>(check_every, max_iter - k);
     for (int64_t j = 0; j < n; ++j, ++k) {
-      if ((e = launch_spmm(ap, s)) != hipSuccess) return SPOPS_ERR_HIP;
-      if ((e = launch_cg_after_product(m, k, (float*)x, w, s)) != hipSuccess)
-        return SPOPS_ERR_HIP;
+      if (sb.ok) {
+        fa.k = k;
+        e = launch_cg_fused(fa, sb, (float*)x, w, s);
+      } else {
+        // p sits in the x slots of the (p, r) pairs: leading dimension 2
+        const SpmmArgs ap = spmm_args(A, w.pr[(k + 1) & 1], SPOPS_F32, 1, 2, w.q, SPOPS_F32, 1,
+                                      plan, w.spmm_ws);
+        e = launch_cg_direction(m, k, w, s);
+        if (e == hipSuccess) e = launch_spmm(ap, s);
+        if (e == hipSuccess) e = launch_cg_dot_update(m, k, (float*)x, w, s);
+      }
+      if (e != hipSuccess) return SPOPS_ERR_HIP;
     }
   }
   if (iters_out) *iters_out = h.iters;

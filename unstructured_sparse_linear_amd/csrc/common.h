@@ -155,4 +155,32 @@ __device__ __forceinline__ int64_t wave_upper_row(const int32_t* ro, int64_t m, 
   return wave_uniform((int)lo);
 }
 
+// Whole-row block index -> first row position.  In index order each XCD gets
+// one contiguous range of row blocks (blocks b, b+8, ... share an XCD); grids
+// for this mapping are padded to a multiple of 8 blocks.
+__device__ __forceinline__ int64_t row_block(int64_t bw, int64_t nbw_padded, int natural) {
+  if (!natural) return bw;
+  const int64_t per = nbw_padded / 8;
+  return (bw % 8) * per + bw / 8;
+}
+
+template <int BYTES>
+struct QuadLoad;
+template <>
+struct QuadLoad<16> {
+  typedef uint4 type;
+};
+template <>
+struct QuadLoad<8> {
+  typedef uint2 type;
+};
+
+// Four consecutive elements from a 4-element-aligned address.
+template <typename T>
+__device__ __forceinline__ void load_quad(const T* p, T (&out)[4]) {
+  typedef typename QuadLoad<4 * sizeof(T)>::type Q;
+  const Q q = *reinterpret_cast<const Q*>(p);
+  __builtin_memcpy(out, &q, sizeof(Q));
+}
+
 }  // namespace spops

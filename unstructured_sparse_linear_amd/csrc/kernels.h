@@ -71,6 +71,23 @@ struct SpmmArgs {
 };
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
 
+// N == 1 on balanced rows (the plan found the lengths balanced, no row is
+// split and the longest has at most kStreamCap / kStreamMinRows entries):
+// workgroups of kStreamBlock threads each own R consecutive rows and stream
+// their entries through `cap` floats of LDS (lds_bytes with slack); the grid
+// is padded to a multiple of 8.  ok == false: the other SpMV kernel runs.
+constexpr int kStreamBlock = 256;
+constexpr int kStreamCap = 8192;     // most products per workgroup held in LDS
+constexpr int kStreamQuads = 2;      // groups of four entries per lane per round
+constexpr int kStreamMinRows = 64;
+struct SpmvBlocks {
+  bool ok = false;
+  int32_t R = 0, cap = 0;
+  int64_t grid = 0;
+  size_t lds_bytes = 0;
+};
+SpmvBlocks spmv_row_blocks(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P);
+
 // Row-splitting schedule for SpMM, built on the device.  chunk = T.
 struct SpmmSchedule {
   int64_t P = 0, S = 0, max_row = 0;
@@ -182,24 +199,49 @@ struct CgState {
   int32_t done;    // 0 running, 1 converged, 2 stopped (p.q not positive)
   int32_t pad;
 };
-constexpr int kCgMaxParts = 1024;  // most per-workgroup partial sums
+constexpr int kCgMaxParts = 1024;  // most per-workgroup partial sums of a vector kernel
 struct CgBuffers {
-  float *r, *p, *q;        // [m] each
-  double *part0, *part1;   // [kCgMaxParts] each
+  float2* pr[2];           // [m] each: (p, r) pairs, alternating between iterations
+  float* q;                // [m]
+  double* part_pq;         // partials of p.q (one per SpMV row block when fused)
+  double* part_rr;         // [kCgMaxParts] partials of r.r
   CgState* st;
   void* spmm_ws;           // the SpMV's own workspace
 };
-// Workspace of the solver for m unknowns and an SpMV workspace of spmm_ws
-// bytes, and its split into buffers (256-byte aligned pieces).
-size_t cg_workspace_bytes(int64_t m, size_t spmm_ws);
-CgBuffers carve_cg_workspace(void* ws, int64_t m);
+// Workspace of the solver for m unknowns, npq partials of p.q (the fused
+// SpMV's grid, else 0) and an SpMV workspace of spmm_ws bytes, and its split
+// into buffers (256-byte aligned pieces).
+size_t cg_workspace_bytes(int64_t m, int64_t npq, size_t spmm_ws);
+CgBuffers carve_cg_workspace(void* ws, int64_t m, int64_t npq);
 int cg_parts(int64_t m);
-// r = b - q (q = A x0), p = r, state for iteration 0.
-hipError_t launch_cg_init(int64_t m, const float* b, const float* q, const CgBuffers& w,
-                          double rtol, hipStream_t s);
-// The rest of iteration k once q = A p is in w.q: p.q, the x / r update, the
-// new direction and the state.
-hipError_t launch_cg_after_product(int64_t m, int64_t k, float* x, const CgBuffers& w,
-                                   hipStream_t s);
+// Set-up once q = A x0 is in w.q: r = b - q, state for iteration 0.
+hipError_t launch_cg_init(int64_t m, const float* b, const CgBuffers& w, double rtol,
+                          hipStream_t s);
+// Records r.r and the iteration count k in the state (before a host check).
+hipError_t launch_cg_record(int64_t m, int64_t k, const CgBuffers& w, hipStream_t s);
+// Iteration k around the library's SpMV: direction into the p slots of
+// w.pr[(k+1)&1], then (after q = A p) p.q and the x / r update.
+hipError_t launch_cg_direction(int64_t m, int64_t k, const CgBuffers& w, hipStream_t s);
+hipError_t launch_cg_dot_update(int64_t m, int64_t k, float* x, const CgBuffers& w,
+                                hipStream_t s);
+// Iteration k as row blocks (SpMV fused with the direction and p.q), then
+// the update: two launches.  The CSR (f32 values) comes in `a`; the buffer
+// fields are filled from w.
+struct CgSpmvArgs {
+  int64_t m, nnz, k;
+  const int32_t* ro;
+  const void* col;
+  int col_i32;
+  const float* val;
+  const float2* pr;        // (p_prev, r) pairs read
+  float2* pr_next;         // p written to its x slots
+  float* q;
+  double* part_pq;
+  const double* part_rr;
+  int nparts_rr;
+  CgState* st;
+};
+hipError_t launch_cg_fused(const CgSpmvArgs& a, const SpmvBlocks& sb, float* x,
+                           const CgBuffers& w, hipStream_t s);
 
 }  // namespace spops

@@ -78,15 +78,6 @@ __device__ __forceinline__ void row_range(const int32_t* ro, int64_t r, int64_t 
   p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
 }
 
-// Whole-row block index -> first row position.  In index order each XCD gets
-// one contiguous range of row blocks (blocks b, b+8, ... share an XCD); grids
-// for this mapping are padded to a multiple of 8 blocks.
-__device__ __forceinline__ int64_t row_block(int64_t bw, int64_t nbw_padded, int natural) {
-  if (!natural) return bw;
-  const int64_t per = nbw_padded / 8;
-  return (bw % 8) * per + bw / 8;
-}
-
 // ------------------------------------------------------- narrow-N groups --
 
 template <typename VT>
@@ -405,30 +396,6 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
 // block's LDS (`cap` floats, dynamic); a block whose range is larger anyway
 // (row offsets that do not match the plan) takes a slower wave-per-row path,
 // so no input reaches past the buffers.
-constexpr int kStreamCap = 8192;  // most products per workgroup held in LDS
-constexpr int kStreamQuads = 2;   // groups of four entries per lane per round
-// below this many rows per workgroup (rows longer than kStreamCap / it) the
-// lanes-per-row kernel is used instead
-constexpr int kStreamMinRows = 64;
-
-template <int BYTES>
-struct QuadLoad;
-template <>
-struct QuadLoad<16> {
-  typedef uint4 type;
-};
-template <>
-struct QuadLoad<8> {
-  typedef uint2 type;
-};
-
-// Four consecutive elements from a 4-element-aligned address.
-template <typename T>
-__device__ __forceinline__ void load_quad(const T* p, T (&out)[4]) {
-  typedef typename QuadLoad<4 * sizeof(T)>::type Q;
-  const Q q = *reinterpret_cast<const Q*>(p);
-  __builtin_memcpy(out, &q, sizeof(Q));
-}
 
 template <typename VT, typename OT, typename IT, bool QUAD>
 __global__ __launch_bounds__(kBlock) void spmv_stream_kernel(SpmmArgs a, int32_t R,
@@ -854,25 +821,20 @@ template <typename VT, typename OT, typename IT>
 hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
   hipError_t e;
-  if (a.N == 1 && a.natural && a.P == 0 && a.max_row > 0 &&
-      a.max_row <= kStreamCap / kStreamMinRows) {
-    // balanced rows: stream row blocks through LDS, about one round of
-    // loads per lane per block
-    const int64_t mean = std::max<int64_t>(1, a.nnz / a.m);
-    int64_t R = (int64_t)kBlock * 4 * kStreamQuads / mean;
-    R = std::max<int64_t>(1, std::min<int64_t>({R, (int64_t)kBlock, kStreamCap / a.max_row}));
-    // + 8: the first and last groups of four may stick out of the range
-    const int32_t cap = (int32_t)(R * a.max_row) + 8;
-    const dim3 grid((unsigned)pad8(cdiv(a.m, R)));
-    const size_t lds = (size_t)(cap + 4) * sizeof(float);
+  const SpmvBlocks sb = spmv_row_blocks(a.m, a.nnz, a.max_row, a.natural, a.P);
+  if (a.N == 1 && sb.ok) {
+    // balanced rows: stream row blocks through LDS
+    const int32_t R = sb.R, cap = sb.cap;
+    const dim3 grid((unsigned)sb.grid);
+    const size_t lds = sb.lds_bytes;
     const bool quad = ((uintptr_t)a.col % (4 * sizeof(IT)) == 0) &&
                       ((uintptr_t)a.val % (4 * sizeof(VT)) == 0);
     if (quad)
       hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, true>), grid, dim3(kBlock), lds, s, a,
-                         (int32_t)R, cap);
+                         R, cap);
     else
       hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, false>), grid, dim3(kBlock), lds, s, a,
-                         (int32_t)R, cap);
+                         R, cap);
     e = hipGetLastError();
   } else if (a.N == 1) {
     // lanes per row from the mean row length
@@ -996,6 +958,24 @@ __global__ __launch_bounds__(256) void sched_ends_kernel(const uint32_t* nch, co
 }
 
 }  // namespace
+
+SpmvBlocks spmv_row_blocks(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P) {
+  SpmvBlocks b;
+  if (!(m > 0 && natural && P == 0 && max_row > 0 && max_row <= kStreamCap / kStreamMinRows))
+    return b;
+  // about one round of loads per lane per block, and R * max_row products
+  // must fit the block's LDS
+  const int64_t mean = std::max<int64_t>(1, nnz / m);
+  int64_t R = (int64_t)kStreamBlock * 4 * kStreamQuads / mean;
+  R = std::max<int64_t>(1, std::min<int64_t>({R, (int64_t)kStreamBlock, kStreamCap / max_row}));
+  b.ok = true;
+  b.R = (int32_t)R;
+  // + 8: the first and last groups of four may stick out of the range
+  b.cap = (int32_t)(R * max_row) + 8;
+  b.grid = (cdiv(m, R) + 7) & ~(int64_t)7;
+  b.lds_bytes = (size_t)(b.cap + 4) * sizeof(float);
+  return b;
+}
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
   switch (a.dtype) {
