@@ -181,7 +181,7 @@ def encode(x: np.ndarray, dt: str) -> np.ndarray:
 
 def to_f64(x: np.ndarray, dt: str) -> np.ndarray:
     """Exact float64 view of stored values (own decoders for 16-bit formats)."""
-    if dt == "f32":
+    if dt in ("f32", "f64"):
         return np.asarray(x, dtype=np.float64)
     return decode(x, dt)
 
@@ -278,3 +278,42 @@ def cg(m: int, row_offsets, col_idx, values, val_dt: str, b, x0=None, rtol: floa
     if history:
         return x, k, rel, ps, rs
     return x, k, rel
+
+
+# ------------------------------------------------------------ masked Adam --
+# The SparseAdam page (tensorplay.optim.sparse_adam) describes a masked Adam:
+# only the positions where the gradient is materialized have their first and
+# second moments and their parameter updated; every other position keeps its
+# moments and value, and a materialized gradient of zero still counts.  The
+# page names Adam and its arguments (lr, betas, eps, maximize) but not the
+# update itself, so the step is Adam's (Kingma and Ba, "Adam: A Method for
+# Stochastic Optimization", 2015, Algorithm 1) in the form that paper gives
+# for efficiency at the end of its Section 2, with one step counter t for the
+# whole parameter:
+#   m <- beta1 m + (1 - beta1) g,  v <- beta2 v + (1 - beta2) g^2,
+#   alpha_t = lr sqrt(1 - beta2^t) / (1 - beta1^t),
+#   theta <- theta - alpha_t m / (sqrt(v) + eps)
+# at the materialized positions (g negated when maximizing).  float64
+# throughout; the new parameter is returned in float64 (rounded to the
+# parameter's format by the caller when comparing).
+
+def masked_adam(values, val_dt: str, grad, grad_dt: str, exp_avg, exp_avg_sq, step: int,
+                lr: float, beta1: float, beta2: float, eps: float, maximize: bool = False,
+                positions=None):
+    """One masked Adam step on the CSR value vector.  `grad` holds the
+    gradient of every position (positions=None) or of the listed positions
+    only (unique indices into values).  Returns (values, exp_avg,
+    exp_avg_sq) as new float64 arrays; unlisted positions are copied."""
+    theta = to_f64(values, val_dt).copy()
+    m = np.asarray(exp_avg, dtype=np.float64).copy()
+    v = np.asarray(exp_avg_sq, dtype=np.float64).copy()
+    g = to_f64(grad, grad_dt)
+    idx = np.arange(len(theta)) if positions is None else np.asarray(positions, np.int64)
+    if maximize:
+        g = -g
+    a_t = lr * np.sqrt(1.0 - beta2 ** step) / (1.0 - beta1 ** step)
+    for j, i in enumerate(idx):
+        m[i] = beta1 * m[i] + (1.0 - beta1) * g[j]
+        v[i] = beta2 * v[i] + (1.0 - beta2) * g[j] * g[j]
+        theta[i] = theta[i] - a_t * m[i] / (np.sqrt(v[i]) + eps)
+    return theta, m, v
