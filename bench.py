@@ -65,7 +65,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
     p.add_argument("--no-adapter", action="store_true",
-                   help="skip the sparse-layer training step (forward, both gradients, merge)")
+                   help="skip the sparse-layer training step (forward, both gradients, Adam, merge)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
@@ -192,8 +192,9 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
     """One training step of the sparse layer Y^T = S . X^T with S = A (values
     A.values, pattern A) and X^T = the workload's dense B (k x N): forward,
     the gradients of the stored values (SDDMM of dY^T and X^T) and of X^T
-    (S^T . dY^T), and the merge W += S; outputs in the input dtype, as the
-    autograd layer produces them.  Captured as a HIP graph, cold caches."""
+    (S^T . dY^T), a masked Adam step on the values, and the merge W += S;
+    outputs in the input dtype, as the autograd layer produces them.
+    Captured as a HIP graph, cold caches."""
     import torch
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
 
@@ -216,11 +217,16 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
     vT = torch.empty_like(v)
     dxt = torch.empty((n, N), dtype=tdt, device=dev)
 
+    m1 = torch.zeros(A.nnz, dtype=torch.float32, device=dev)
+    m2 = torch.zeros_like(m1)
+
     def run():
         S.spmm(v, P.ro, P.ri, P.ci, xt, m, out_dtype=tdt, plan=P.spmm_plan, out=yt)
         S.sddmm(P.ro, P.ri, P.ci, dyt, xt, plan=P.sddmm_plan, out_dtype=tdt, out=dv)
         P.transposed_values(v, out=vT)
         S.spmm(vT, P.roT, P.riT, P.ciT, dyt, n, out_dtype=tdt, plan=P.spmmT_plan, out=dxt)
+        # optimizer step on the values (the step number is fixed in the graph)
+        S.masked_adam(v, dv, m1, m2, 1, lr=1e-4)
         if W is not None:
             S.csr_add(v, P.ro, P.ri, P.ci, W)
 
@@ -256,6 +262,7 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
         "grad_input_spmm": nnz * (s_v + s_riT) + 4 * (n + 1) + n * s_riT + mp * N * s_v
         + n * N * s_v,
     }
+    parts["masked_adam"] = nnz * (3 * s_v + 16)
     if W is not None:
         parts["merge_csr_add"] = nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + 2 * nnz * s_v
     total = sum(parts.values())

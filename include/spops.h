@@ -9,7 +9,9 @@
  *   spops_csr_transpose   section "CSR Transpose"
  *   spops_sort_rows_by_nnz  the row_idx list of section "Usage"
  * and, built on spops_spmm, a conjugate-gradient solver (spops_cg; the
- * torchsparsegradutils README, section "Built-in Iterative Solvers").
+ * torchsparsegradutils README, section "Built-in Iterative Solvers"), and a
+ * masked Adam step for trained value vectors (spops_masked_adam; the
+ * SparseAdam page of tensorplay.optim).
  *
  * Sparse layout (section "Usage"): an m x n matrix with nnz stored entries is
  *   values[nnz]        the stored values (f32, f16 or bf16);
@@ -62,7 +64,8 @@ typedef enum spops_status {
   SPOPS_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than the size query returned */
   SPOPS_ERR_UNSUPPORTED = 6,   /* valid request this build does not implement */
   SPOPS_ERR_PLAN = 7,          /* plan built for a different mask */
-  SPOPS_ERR_HIP = 8            /* a HIP runtime call or kernel launch failed */
+  SPOPS_ERR_HIP = 8,           /* a HIP runtime call or kernel launch failed */
+  SPOPS_ERR_ARGUMENT = 9       /* a scalar argument (tolerance, rate, ...) out of its range */
 } spops_status;
 
 typedef enum spops_dtype { SPOPS_F32 = 0, SPOPS_F16 = 1, SPOPS_BF16 = 2 } spops_dtype;
@@ -240,7 +243,7 @@ spops_status spops_sort_rows_by_nnz(const int32_t* row_offsets, int64_t rows, in
  *   (0 when b = 0).
  *   workspace: spops_cg_workspace_size bytes (vectors r, p, q, partial sums,
  *   solver state, the SpMM's workspace); contents on entry do not matter.
- *   rtol < 0 or NaN, max_iter < 0, check_every < 1 give SPOPS_ERR_SHAPE;
+ *   rtol < 0 or NaN, max_iter < 0, check_every < 1 give SPOPS_ERR_ARGUMENT;
  *   rows != cols SPOPS_ERR_SHAPE; values other than f32 SPOPS_ERR_DTYPE. */
 spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* plan,
                                      size_t* bytes);
@@ -248,6 +251,32 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
                       int64_t check_every, const spops_spmm_plan* plan, void* workspace,
                       size_t workspace_bytes, int64_t* iters_out, double* rel_resid_out,
                       void* hip_stream);
+
+/* ----------------------------------------------------------- masked Adam --
+ * One step of the masked Adam of the SparseAdam page (tensorplay.optim):
+ * only the positions where the gradient is materialized update their
+ * moments and their value; a materialized zero still counts.  The step is
+ * Adam's (Kingma and Ba, 2015, in the efficient form of their Section 2):
+ *   m = beta1 m + (1 - beta1) g,  v = beta2 v + (1 - beta2) g^2,
+ *   value -= alpha_t m / (sqrt(v) + eps),
+ *   alpha_t = lr sqrt(1 - beta2^step) / (1 - beta1^step),
+ * with g negated when `maximize` is nonzero.
+ *   values:   [nnz] trained values (val_type f32, f16 or bf16), updated in
+ *             place (fp32 arithmetic, rounded once to val_type).
+ *   exp_avg, exp_avg_sq: [nnz] f32 moments, updated in place (zeros before
+ *             the first step).
+ *   grad:     [ngrad] gradient in val_type.  positions == NULL: every value
+ *             has a gradient entry (ngrad must equal nnz).  Otherwise
+ *             positions[ngrad] (int32) names the value of each entry; they
+ *             must be distinct (a coalesced sparse gradient; duplicates race)
+ *             and those outside [0, nnz) are skipped.
+ *   step:     the step number t >= 1 (the caller counts steps).
+ *   lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0, all finite, else
+ *   SPOPS_ERR_ARGUMENT (step < 1 too). */
+spops_status spops_masked_adam(void* values, spops_dtype val_type, int64_t nnz, const void* grad,
+                               const int32_t* positions, int64_t ngrad, float* exp_avg,
+                               float* exp_avg_sq, int64_t step, double lr, double beta1,
+                               double beta2, double eps, int maximize, void* hip_stream);
 
 #ifdef __cplusplus
 }

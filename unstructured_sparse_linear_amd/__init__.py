@@ -7,7 +7,7 @@ behind the C ABI in include/spops.h (libspops.so); this package only
 marshals torch tensors into that ABI.  Nothing here falls back to another
 implementation: calls raise if libspops.so is missing.
 """
-from .adapter import SparseAdapter, SparsePattern, sparse_linear  # noqa: F401
+from .adapter import MaskedAdam, SparseAdapter, SparsePattern, sparse_linear  # noqa: F401
 from .spops import (  # noqa: F401
     SddmmPlan,
     SpmmPlan,
@@ -18,6 +18,7 @@ from .spops import (  # noqa: F401
     csr_transpose,
     csr_transpose_workspace,
     lib,
+    masked_adam,
     sddmm,
     sort_rows_by_nnz,
     sort_rows_workspace,
@@ -26,4 +27,5 @@ from .spops import (  # noqa: F401
 
 __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
-           "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg"]
+           "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg",
+           "masked_adam", "MaskedAdam"]

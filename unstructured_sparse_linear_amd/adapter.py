@@ -11,6 +11,7 @@ every step one call into libspops and needs no dense transpose:
     backward   dS   = dY^T · (X^T)^T sampled at S     sddmm (A = dY^T, BT = X^T)
                dX^T = S^T · dY^T                      csr_transpose + spmm
     merge      W   += S                               csr_add
+    optimizer  values -= Adam step (masked)           masked_adam (MaskedAdam)
 
 The module only marshals tensors: outputs are allocated here and every value
 is computed by the library's kernels (it raises if libspops.so is missing).
@@ -22,7 +23,7 @@ from typing import Optional
 import torch
 
 from .spops import (SddmmPlan, SpmmPlan, csr_add, csr_transpose, csr_transpose_workspace,
-                    sddmm, sort_rows_by_nnz, spmm)
+                    masked_adam, sddmm, sort_rows_by_nnz, spmm)
 
 
 class SparsePattern:
@@ -108,3 +109,50 @@ class SparseAdapter(torch.nn.Module):
     def merge_into(self, W: torch.Tensor) -> torch.Tensor:
         P = self.pattern
         return csr_add(self.values.detach(), P.ro, P.ri, P.ci, W)
+
+
+class MaskedAdam(torch.optim.Optimizer):
+    """The masked Adam of the SparseAdam page (tensorplay.optim.sparse_adam)
+    for value vectors, each step one launch of the library's kernel
+    (spops_masked_adam).  A dense gradient updates every value; a 1-D sparse
+    COO gradient (coalesced) updates only the values it names, leaving the
+    others and their moments untouched.  Moments are kept in f32."""
+
+    def __init__(self, params, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                 maximize: bool = False):
+        if not (lr >= 0.0 and eps >= 0.0 and 0.0 <= betas[0] < 1.0 and 0.0 <= betas[1] < 1.0):
+            raise ValueError("need lr >= 0, eps >= 0 and betas in [0, 1)")
+        super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps, maximize=maximize))
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if p.dim() != 1 or not p.is_contiguous():
+                    raise ValueError("MaskedAdam trains contiguous 1-D value vectors")
+                st = self.state[p]
+                if not st:
+                    st["step"] = 0
+                    st["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                    st["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32,
+                                                   device=p.device)
+                st["step"] += 1
+                g = p.grad
+                kw = dict(lr=group["lr"], betas=group["betas"], eps=group["eps"],
+                          maximize=group["maximize"])
+                if g.is_sparse:
+                    if not g.is_coalesced():
+                        raise ValueError("sparse gradients must be coalesced")
+                    pos = g.indices()[0].to(torch.int32)
+                    masked_adam(p.data, g.values().contiguous(), st["exp_avg"],
+                                st["exp_avg_sq"], st["step"], positions=pos, **kw)
+                else:
+                    masked_adam(p.data, g.contiguous(), st["exp_avg"], st["exp_avg_sq"],
+                                st["step"], **kw)
+        return loss

@@ -115,6 +115,7 @@ const char* spops_status_string(spops_status s) {
     case SPOPS_ERR_UNSUPPORTED: return "unsupported request";
     case SPOPS_ERR_PLAN: return "plan was built for a different matrix";
     case SPOPS_ERR_HIP: return "HIP runtime error";
+    case SPOPS_ERR_ARGUMENT: return "scalar argument out of range";
   }
   return "unknown status";
 }
@@ -474,7 +475,8 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
                       void* hip_stream) {
   spops_status st = check_cg(A, plan);
   if (st != SPOPS_OK) return st;
-  if (!(rtol >= 0.0) || max_iter < 0 || check_every < 1) return SPOPS_ERR_SHAPE;
+  if (!(rtol >= 0.0) || !isfinite(rtol) || max_iter < 0 || check_every < 1)
+    return SPOPS_ERR_ARGUMENT;
   const int64_t m = A->rows;
   if (iters_out) *iters_out = 0;
   if (rel_resid_out) *rel_resid_out = 0.0;
@@ -529,6 +531,38 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
   if (iters_out) *iters_out = h.iters;
   if (rel_resid_out) *rel_resid_out = h.bb > 0.0 ? sqrt(h.rr[h.iters & 1] / h.bb) : 0.0;
   return SPOPS_OK;
+}
+
+// ----------------------------------------------------------- masked Adam --
+
+spops_status spops_masked_adam(void* values, spops_dtype val_type, int64_t nnz, const void* grad,
+                               const int32_t* positions, int64_t ngrad, float* exp_avg,
+                               float* exp_avg_sq, int64_t step, double lr, double beta1,
+                               double beta2, double eps, int maximize, void* hip_stream) {
+  if (!dtype_ok(val_type)) return SPOPS_ERR_DTYPE;
+  if (nnz < 0 || ngrad < 0 || nnz > INT32_MAX || ngrad > INT32_MAX) return SPOPS_ERR_SHAPE;
+  if (!positions && ngrad != nnz) return SPOPS_ERR_SHAPE;
+  if (step < 1 || !(lr >= 0.0) || !isfinite(lr) || !(beta1 >= 0.0 && beta1 < 1.0) ||
+      !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0) || !isfinite(eps))
+    return SPOPS_ERR_ARGUMENT;
+  if (ngrad == 0) return SPOPS_OK;
+  if (!values || !grad || !exp_avg || !exp_avg_sq) return SPOPS_ERR_NULL;
+  AdamArgs a{};
+  a.nnz = nnz;
+  a.ngrad = ngrad;
+  a.positions = positions;
+  a.values = values;
+  a.grad = grad;
+  a.exp_avg = exp_avg;
+  a.exp_avg_sq = exp_avg_sq;
+  a.beta1 = (float)beta1;
+  a.beta2 = (float)beta2;
+  a.one_minus_beta1 = (float)(1.0 - beta1);
+  a.one_minus_beta2 = (float)(1.0 - beta2);
+  a.alpha_t = (float)(lr * sqrt(1.0 - pow(beta2, (double)step)) / (1.0 - pow(beta1, (double)step)));
+  a.eps = (float)eps;
+  a.maximize = maximize ? 1 : 0;
+  return from_hip(launch_masked_adam(a, val_type, as_stream(hip_stream)));
 }
 
 }  // extern "C"

@@ -244,4 +244,18 @@ struct CgSpmvArgs {
 hipError_t launch_cg_fused(const CgSpmvArgs& a, const SpmvBlocks& sb, float* x,
                            const CgBuffers& w, hipStream_t s);
 
+// ------------------------------------------------------------ masked Adam --
+struct AdamArgs {
+  int64_t nnz;             // length of values / exp_avg / exp_avg_sq
+  int64_t ngrad;           // gradient entries
+  const int32_t* positions;  // [ngrad] value index of each gradient entry, or null (j -> j)
+  void* values;
+  const void* grad;        // [ngrad], values' dtype
+  float* exp_avg;
+  float* exp_avg_sq;
+  float beta1, beta2, one_minus_beta1, one_minus_beta2, alpha_t, eps;
+  int maximize;
+};
+hipError_t launch_masked_adam(const AdamArgs& a, int dtype, hipStream_t s);
+
 }  // namespace spops

@@ -28,7 +28,8 @@ _IT = {torch.int16: I16, torch.int32: I32}
 _BACKENDS = {"structure_aware": STRUCTURE_AWARE, "sputnik": GENERAL, "general": GENERAL}
 
 STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "dtype", 4: "index width",
-          5: "workspace", 6: "unsupported", 7: "plan mismatch", 8: "HIP error"}
+          5: "workspace", 6: "unsupported", 7: "plan mismatch", 8: "HIP error",
+          9: "argument out of range"}
 
 
 class SpopsError(RuntimeError):
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
             "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
             "spops_cg_workspace_size": ([cp, vp, P(sz)], i32),
+            "spops_masked_adam": ([vp, i32, i64, vp, vp, i64, vp, vp, i64, ctypes.c_double,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_double, i32, vp],
+                                  i32),
             "spops_cg": ([cp, vp, vp, ctypes.c_double, i64, i64, vp, vp, sz, P(i64),
                           P(ctypes.c_double), vp], i32),
         }
@@ -446,3 +450,31 @@ def cg(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Te
         _ptr(ws), ws.numel() if ws is not None else 0, ctypes.byref(its), ctypes.byref(rel),
         _stream(b)))
     return x, int(its.value), float(rel.value)
+
+
+def masked_adam(values: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor,
+                exp_avg_sq: torch.Tensor, step: int, lr: float = 1e-3, betas=(0.9, 0.999),
+                eps: float = 1e-8, maximize: bool = False,
+                positions: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One masked Adam step, in place on `values`, `exp_avg` and `exp_avg_sq`
+    (f32 moments).  `grad` covers every value (positions=None) or the
+    distinct int32 `positions` only.  Returns `values`."""
+    _require(values, "values", tuple(_DT))
+    _require(grad, "grad", (values.dtype,))
+    _require(exp_avg, "exp_avg", (torch.float32,))
+    _require(exp_avg_sq, "exp_avg_sq", (torch.float32,))
+    n = values.numel()
+    if exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError("moments must match values")
+    if positions is None:
+        if grad.numel() != n:
+            raise ValueError("grad must cover every value when positions is None")
+    else:
+        _require(positions, "positions", (torch.int32,))
+        if positions.numel() != grad.numel():
+            raise ValueError("positions and grad must have the same length")
+    _check("spops_masked_adam", lib().spops_masked_adam(
+        _ptr(values), _DT[values.dtype], n, _ptr(grad), _ptr(positions), grad.numel(),
+        _ptr(exp_avg), _ptr(exp_avg_sq), int(step), float(lr), float(betas[0]),
+        float(betas[1]), float(eps), int(bool(maximize)), _stream(values)))
+    return values
