@@ -317,3 +317,77 @@ def masked_adam(values, val_dt: str, grad, grad_dt: str, exp_avg, exp_avg_sq, st
         v[i] = beta2 * v[i] + (1.0 - beta2) * g[j] * g[j]
         theta[i] = theta[i] - a_t * m[i] / (np.sqrt(v[i]) + eps)
     return theta, m, v
+
+
+# ------------------------------------------------- delta-compressed rows --
+# The UST news page (section "Formatos menos comuns") converts a matrix to a
+# 2-bit delta-compressed format: rows stay a dense level, and inside a row
+# the column coordinates are stored as differences (2 bits each) instead of
+# indices; its MACKO experiment (section "Performance") runs SpMV on that
+# format for low sparsity, with padding that stops at the end of each row.
+# The page shows no layout, so this is the reading taken:
+#   * each stored entry carries a 2-bit code d: its column is the previous
+#     entry's column + d + 1 (the first entry of a row counts from column -1);
+#   * a gap larger than 4 is bridged by zero-valued padding entries, each 4
+#     columns after the previous entry, until the rest of the gap is <= 4;
+#   * nothing is padded after a row's last entry (empty rows stay empty);
+#   * enc_offsets[m+1] (int32) delimit the rows in the encoded stream; codes
+#     are packed 16 per uint32, entry e in bits 2(e mod 16)..2(e mod 16)+1 of
+#     word e // 16; values keep the matrix's format.
+# Columns inside a row must be distinct; they are taken in ascending order.
+
+def delta_encode(m: int, n: int, row_offsets, col_idx, values, val_dt: str):
+    """CSR -> (enc_offsets[m+1] int32, codes uint32[ceil(E/16)], enc_values[E])
+    with values in the storage convention of val_dt (padding = +0).
+
+    Per row, with columns sorted and c_{-1} = -1, entry k has the gap
+    g = c_k - c_{k-1} >= 1; it is preceded by p = (g - 1) // 4 padding
+    entries (code 3, four columns each) and carries code g - 1 - 4p."""
+    ro = np.asarray(row_offsets, np.int64)
+    ci = np.asarray(col_idx, np.int64)
+    vals = np.asarray(values)
+    rows = _rows_of(ro)
+    order = np.lexsort((ci, rows))            # by row, then column
+    c, v, r = ci[order], vals[order], rows[order]
+    prev = np.empty_like(c)
+    prev[1:] = c[:-1]
+    first = np.ones(len(c), bool)
+    first[1:] = r[1:] != r[:-1]
+    prev[first] = -1
+    gap = c - prev
+    pad = (gap - 1) // 4
+    # position of each entry in the encoded stream: its paddings come first
+    pos = np.cumsum(pad + 1) - 1
+    E = int(pos[-1]) + 1 if len(pos) else 0
+    code = np.full(E, 3, np.uint32)
+    code[pos] = (gap - 1 - 4 * pad).astype(np.uint32)
+    ev = np.zeros(E, dtype=vals.dtype)
+    ev[pos] = v
+    per_row = np.bincount(r, weights=pad + 1, minlength=m).astype(np.int64)
+    enc_off = np.concatenate([[0], np.cumsum(per_row)]).astype(np.int32)
+    words = np.zeros((E + 15) // 16, np.uint32)
+    shifts = (2 * (np.arange(E) % 16)).astype(np.uint32)
+    np.bitwise_or.at(words, np.arange(E) // 16, code << shifts)
+    return enc_off, words, ev
+
+
+def delta_decode(m: int, enc_offsets, codes, enc_values):
+    """Encoded rows -> CSR (row_offsets, col_idx int64, values) holding every
+    encoded entry, padding zeros included: a column is the running sum of
+    (code + 1) along its row, starting from -1."""
+    eo = np.asarray(enc_offsets, np.int64)
+    words = np.asarray(codes, np.uint32)
+    E = int(eo[-1])
+    e = np.arange(E)
+    code = (words[e // 16] >> (2 * (e % 16)).astype(np.uint32)) & np.uint32(3)
+    run = np.cumsum(code.astype(np.int64) + 1)
+    row_start = np.repeat(eo[:-1], np.diff(eo))
+    before = np.concatenate([[0], run])[row_start]     # steps taken before the row
+    cols = run - before - 1
+    return eo.astype(np.int32), cols, np.asarray(enc_values)
+
+
+def delta_spmv(m: int, enc_offsets, codes, enc_values, val_dt: str, x, x_dt: str) -> np.ndarray:
+    """y = A x in float64 for A in the delta format, from the decoded entries."""
+    eo, cols, ev = delta_decode(m, enc_offsets, codes, enc_values)
+    return csr_matvec(m, eo, cols, to_f64(ev, val_dt), to_f64(np.asarray(x).reshape(-1), x_dt))
