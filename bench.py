@@ -315,6 +315,56 @@ def cg_solve(S, w, A, dev, args):
             "timing": "host wall clock around the call (it synchronizes at its checks)"}
 
 
+def delta_spmv_bench(S, dev, flush, args):
+    """SpMV on the 2-bit delta-coded rows against CSR SpMV, same matrix: the
+    8192 x 8192 size of the UST page's MACKO experiment at 50% and 90%
+    density, f16 values, cold caches, HIP events around each call."""
+    import torch
+    from unstructured_sparse_linear_amd import gen
+
+    out = {}
+    for density in (0.5, 0.9):
+        A = gen.random_csr(20, 8192, 8192, density, "f16")
+        v = torch.from_numpy(A.values).to(dev)
+        ro = torch.from_numpy(A.row_offsets).to(dev)
+        ci = torch.from_numpy(A.col_idx).to(dev)
+        x = torch.from_numpy(gen.dense(20, 100, gen.S_B, (8192,), "f16")).to(dev)
+        D = S.delta_encode(v, ro, ci, A.m, A.n)
+        ri = S.sort_rows_by_nnz(ro, A.n)
+        plan = S.SpmmPlan(ro, ri, ci, A.n)
+        y = torch.empty(A.m, dtype=torch.float32, device=dev)
+        y2 = torch.empty((A.m, 1), dtype=torch.float32, device=dev)
+        x2 = x.reshape(-1, 1)
+        runs = {"delta": lambda: S.delta_spmv(D, x, out=y),
+                "csr": lambda: S.spmm(v, ro, ri, ci, x2, A.m, plan=plan, out=y2)}
+        words = (D.entries + 15) // 16
+        byts = {"delta": D.entries * 2 + 4 * words + 4 * (A.m + 1) + 2 * A.n + 4 * A.m,
+                "csr": A.nnz * 4 + 4 * (A.m + 1) + 2 * A.m + 2 * A.n + 4 * A.m}
+        res = {}
+        for name, fn in runs.items():
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(max(args.steps, 5)):
+                if not args.no_flush:
+                    flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            t = float(np.mean(ts))
+            res[name] = {"ms": round(t, 4), "alg_bytes": int(byts[name]),
+                         "gbps": round(byts[name] / t / 1e6, 1),
+                         "frac_hbm": round(byts[name] / t / 1e6 / HBM_PEAK_GBS, 4)}
+        res["nnz"] = A.nnz
+        res["encoded_entries"] = D.entries
+        out[f"density_{density}"] = res
+        del D, v, ro, ci
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -526,6 +576,8 @@ def main():
         result["next_adapter_step"] = adapter_step(S, w, A, dt, N, dev, flush, args)
     if args.config == 4:
         result["next_cg"] = cg_solve(S, w, A, dev, args)
+    if args.config == DEFAULT_CONFIG and not args.no_adapter:
+        result["next_delta_spmv"] = delta_spmv_bench(S, dev, flush, args)
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)

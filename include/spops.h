@@ -11,7 +11,9 @@
  * and, built on spops_spmm, a conjugate-gradient solver (spops_cg; the
  * torchsparsegradutils README, section "Built-in Iterative Solvers"), and a
  * masked Adam step for trained value vectors (spops_masked_adam; the
- * SparseAdam page of tensorplay.optim).
+ * SparseAdam page of tensorplay.optim), and rows with 2-bit delta-coded
+ * columns with their SpMV (spops_delta_*; the UST news page, sections
+ * "Formatos menos comuns" and "Performance").
  *
  * Sparse layout (section "Usage"): an m x n matrix with nnz stored entries is
  *   values[nnz]        the stored values (f32, f16 or bf16);
@@ -65,7 +67,8 @@ typedef enum spops_status {
   SPOPS_ERR_UNSUPPORTED = 6,   /* valid request this build does not implement */
   SPOPS_ERR_PLAN = 7,          /* plan built for a different mask */
   SPOPS_ERR_HIP = 8,           /* a HIP runtime call or kernel launch failed */
-  SPOPS_ERR_ARGUMENT = 9       /* a scalar argument (tolerance, rate, ...) out of its range */
+  SPOPS_ERR_ARGUMENT = 9,      /* a scalar argument (tolerance, rate, ...) out of its range */
+  SPOPS_ERR_INDEX_ORDER = 10   /* columns not strictly ascending inside a row, or out of range */
 } spops_status;
 
 typedef enum spops_dtype { SPOPS_F32 = 0, SPOPS_F16 = 1, SPOPS_BF16 = 2 } spops_dtype;
@@ -277,6 +280,41 @@ spops_status spops_masked_adam(void* values, spops_dtype val_type, int64_t nnz, 
                                const int32_t* positions, int64_t ngrad, float* exp_avg,
                                float* exp_avg_sq, int64_t step, double lr, double beta1,
                                double beta2, double eps, int maximize, void* hip_stream);
+
+/* ------------------------------------------------------ delta-coded rows --
+ * The 2-bit delta-compressed row format of the UST news page (section
+ * "Formatos menos comuns": rows dense, column coordinates stored as 2-bit
+ * differences; section "Performance": its MACKO SpMV for low sparsity, with
+ * padding that stops at the end of each row).  Layout:
+ *   enc_offsets[rows+1] (int32): row r owns encoded entries
+ *     [enc_offsets[r], enc_offsets[r+1]);  E = enc_offsets[rows].
+ *   codes[ceil(E/16)] (uint32): entry e has the 2-bit code in bits
+ *     2(e mod 16)..2(e mod 16)+1 of codes[e/16]; its column is the previous
+ *     entry's column + code + 1, starting from -1 at each row.
+ *   enc_values[16 ceil(E/16)]: the values (val_type); entries that bridge a
+ *     gap above 4 columns are zero-valued padding entries (code 3, four
+ *     columns each); the tail after E is zero.  Nothing is padded after a
+ *     row's last stored entry.
+ * Building it takes two calls: spops_delta_size writes enc_offsets and
+ * returns E (it synchronizes); the caller allocates codes and enc_values;
+ * spops_delta_encode fills them.  The CSR's columns must be strictly
+ * ascending inside each row and in [0, cols) (SPOPS_ERR_INDEX_ORDER from
+ * spops_delta_size otherwise). */
+spops_status spops_delta_size_workspace(int64_t rows, size_t* bytes);
+spops_status spops_delta_size(const spops_csr* A, int32_t* enc_offsets, int64_t* enc_entries,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+/* Fills codes and enc_values (A->values required, same dtype) for the
+ * enc_offsets / E that spops_delta_size returned for A. */
+spops_status spops_delta_encode(const spops_csr* A, const int32_t* enc_offsets,
+                                int64_t enc_entries, uint32_t* codes, void* enc_values,
+                                void* hip_stream);
+/* y = A x for A in the delta format (rows x cols):
+ *   x: [cols] in val_type;  y: [rows], y_type SPOPS_F32 or val_type (one
+ *   rounding of the fp32 sum).  fp32 accumulation; deterministic. */
+spops_status spops_delta_spmv(int64_t rows, int64_t cols, const int32_t* enc_offsets,
+                              int64_t enc_entries, const uint32_t* codes, const void* enc_values,
+                              spops_dtype val_type, const void* x, void* y, spops_dtype y_type,
+                              void* hip_stream);
 
 #ifdef __cplusplus
 }

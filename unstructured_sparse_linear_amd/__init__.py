@@ -11,8 +11,11 @@ from .adapter import MaskedAdam, SparseAdapter, SparsePattern, sparse_linear  # 
 from .spops import (  # noqa: F401
     SddmmPlan,
     SpmmPlan,
+    DeltaMatrix,
     SpopsError,
     cg,
+    delta_encode,
+    delta_spmv,
     clear_plan_caches,
     csr_add,
     csr_transpose,
@@ -28,4 +31,4 @@ from .spops import (  # noqa: F401
 __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
            "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg",
-           "masked_adam", "MaskedAdam"]
+           "masked_adam", "MaskedAdam", "DeltaMatrix", "delta_encode", "delta_spmv"]

@@ -116,6 +116,7 @@ const char* spops_status_string(spops_status s) {
     case SPOPS_ERR_PLAN: return "plan was built for a different matrix";
     case SPOPS_ERR_HIP: return "HIP runtime error";
     case SPOPS_ERR_ARGUMENT: return "scalar argument out of range";
+    case SPOPS_ERR_INDEX_ORDER: return "columns not strictly ascending in a row, or out of range";
   }
   return "unknown status";
 }
@@ -563,6 +564,70 @@ spops_status spops_masked_adam(void* values, spops_dtype val_type, int64_t nnz, 
   a.eps = (float)eps;
   a.maximize = maximize ? 1 : 0;
   return from_hip(launch_masked_adam(a, val_type, as_stream(hip_stream)));
+}
+
+// ------------------------------------------------------ delta-coded rows --
+
+spops_status spops_delta_size_workspace(int64_t rows, size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (rows < 0 || rows > INT32_MAX - 1) return SPOPS_ERR_SHAPE;
+  *bytes = delta_size_workspace_bytes(rows);
+  return SPOPS_OK;
+}
+
+spops_status spops_delta_size(const spops_csr* A, int32_t* enc_offsets, int64_t* enc_entries,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  spops_status st = check_csr(A, false, false);
+  if (st != SPOPS_OK) return st;
+  if (!enc_offsets || !enc_entries) return SPOPS_ERR_NULL;
+  // every count and offset must fit int32: at most one padding entry per 4
+  // columns of each row on top of the stored entries
+  if ((double)A->nnz + (double)A->rows * (double)((A->cols + 3) / 4) > (double)INT32_MAX)
+    return SPOPS_ERR_SHAPE;
+  if (!workspace || workspace_bytes < delta_size_workspace_bytes(A->rows))
+    return SPOPS_ERR_WORKSPACE;
+  hipStream_t s = as_stream(hip_stream);
+  uint32_t tb[2] = {0, 0};
+  hipError_t e = launch_delta_size(A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx,
+                                   A->col_type == SPOPS_I32, enc_offsets, workspace, tb, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return SPOPS_ERR_HIP;
+  if (tb[1]) return SPOPS_ERR_INDEX_ORDER;
+  *enc_entries = (int64_t)tb[0];
+  return SPOPS_OK;
+}
+
+spops_status spops_delta_encode(const spops_csr* A, const int32_t* enc_offsets,
+                                int64_t enc_entries, uint32_t* codes, void* enc_values,
+                                void* hip_stream) {
+  spops_status st = check_csr(A, true, false);
+  if (st != SPOPS_OK) return st;
+  if (!enc_offsets) return SPOPS_ERR_NULL;
+  if (enc_entries < 0 || enc_entries > INT32_MAX) return SPOPS_ERR_SHAPE;
+  if (enc_entries > 0 && (!codes || !enc_values)) return SPOPS_ERR_NULL;
+  if (A->rows == 0) return SPOPS_OK;
+  return from_hip(launch_delta_encode(A->rows, A->nnz, A->row_offsets, A->col_idx,
+                                      A->col_type == SPOPS_I32, A->values, A->val_type,
+                                      enc_offsets, enc_entries, codes, enc_values,
+                                      as_stream(hip_stream)));
+}
+
+spops_status spops_delta_spmv(int64_t rows, int64_t cols, const int32_t* enc_offsets,
+                              int64_t enc_entries, const uint32_t* codes, const void* enc_values,
+                              spops_dtype val_type, const void* x, void* y, spops_dtype y_type,
+                              void* hip_stream) {
+  if (!dtype_ok(val_type) || !dtype_ok(y_type)) return SPOPS_ERR_DTYPE;
+  if (y_type != SPOPS_F32 && y_type != val_type) return SPOPS_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || rows > INT32_MAX - 1 || enc_entries < 0 ||
+      enc_entries > INT32_MAX)
+    return SPOPS_ERR_SHAPE;
+  if (rows == 0) return SPOPS_OK;
+  if (!enc_offsets || !y) return SPOPS_ERR_NULL;
+  if (enc_entries > 0 && cols == 0) return SPOPS_ERR_SHAPE;
+  if (enc_entries > 0 && (!codes || !enc_values || !x)) return SPOPS_ERR_NULL;
+  if (((uintptr_t)enc_values % 16) != 0) return SPOPS_ERR_SHAPE;
+  return from_hip(launch_delta_spmv(rows, cols, enc_offsets, codes, enc_values, val_type,
+                                    enc_entries, x, y, y_type, as_stream(hip_stream)));
 }
 
 }  // extern "C"

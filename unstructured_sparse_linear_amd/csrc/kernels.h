@@ -258,4 +258,19 @@ struct AdamArgs {
 };
 hipError_t launch_masked_adam(const AdamArgs& a, int dtype, hipStream_t s);
 
+// ------------------------------------------------- delta-coded rows --
+size_t delta_size_workspace_bytes(int64_t m);
+// Encoded row lengths -> enc_offsets[m+1]; copies enc_offsets[m] and a flag
+// (columns not strictly ascending / out of range) to total_and_bad[0..1]
+// (host memory; valid after the stream synchronizes).
+hipError_t launch_delta_size(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
+                             const void* col, int col_i32, int32_t* enc_offsets, void* ws,
+                             uint32_t* total_and_bad, hipStream_t s);
+hipError_t launch_delta_encode(int64_t m, int64_t nnz, const int32_t* ro, const void* col,
+                               int col_i32, const void* val, int dtype, const int32_t* eo,
+                               int64_t total, uint32_t* codes, void* out, hipStream_t s);
+hipError_t launch_delta_spmv(int64_t m, int64_t n, const int32_t* eo, const uint32_t* codes,
+                             const void* val, int dtype, int64_t total, const void* x, void* y,
+                             int y_dtype, hipStream_t s);
+
 }  // namespace spops

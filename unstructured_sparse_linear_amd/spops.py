@@ -29,7 +29,7 @@ _BACKENDS = {"structure_aware": STRUCTURE_AWARE, "sputnik": GENERAL, "general": 
 
 STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "dtype", 4: "index width",
           5: "workspace", 6: "unsupported", 7: "plan mismatch", 8: "HIP error",
-          9: "argument out of range"}
+          9: "argument out of range", 10: "column order"}
 
 
 class SpopsError(RuntimeError):
@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
             "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
             "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
             "spops_cg_workspace_size": ([cp, vp, P(sz)], i32),
+            "spops_delta_size_workspace": ([i64, P(sz)], i32),
+            "spops_delta_size": ([cp, vp, P(i64), vp, sz, vp], i32),
+            "spops_delta_encode": ([cp, vp, i64, vp, vp, vp], i32),
+            "spops_delta_spmv": ([i64, i64, vp, i64, vp, vp, i32, vp, vp, i32, vp], i32),
             "spops_masked_adam": ([vp, i32, i64, vp, vp, i64, vp, vp, i64, ctypes.c_double,
                                    ctypes.c_double, ctypes.c_double, ctypes.c_double, i32, vp],
                                   i32),
@@ -478,3 +482,55 @@ def masked_adam(values: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor,
         _ptr(exp_avg), _ptr(exp_avg_sq), int(step), float(lr), float(betas[0]),
         float(betas[1]), float(eps), int(bool(maximize)), _stream(values)))
     return values
+
+
+class DeltaMatrix:
+    """A matrix in the 2-bit delta-coded row format (see include/spops.h):
+    enc_offsets[m+1] int32, codes[ceil(E/16)] (int32 storage of the uint32
+    words), values[16 ceil(E/16)] in the matrix dtype."""
+
+    def __init__(self, m: int, n: int, enc_offsets: torch.Tensor, codes: torch.Tensor,
+                 values: torch.Tensor, entries: int):
+        self.m, self.n = m, n
+        self.enc_offsets, self.codes, self.values, self.entries = (enc_offsets, codes, values,
+                                                                   entries)
+
+
+def delta_encode(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_col_indices: torch.Tensor,
+                 m: int, n: int) -> DeltaMatrix:
+    """CSR (columns strictly ascending in each row) -> DeltaMatrix.  Two
+    library calls: the encoded size (synchronizes), then the encoding."""
+    _require(A_val, "A_val", tuple(_DT))
+    d = csr_desc(A_val, A_row_offsets, None, A_col_indices, m, n)
+    dev = A_row_offsets.device
+    wb = ctypes.c_size_t()
+    _check("spops_delta_size_workspace", lib().spops_delta_size_workspace(m, ctypes.byref(wb)))
+    ws = _workspace(wb.value, dev)
+    eo = torch.empty(m + 1, dtype=torch.int32, device=dev)
+    E = ctypes.c_int64()
+    _check("spops_delta_size", lib().spops_delta_size(
+        ctypes.byref(d), _ptr(eo), ctypes.byref(E), _ptr(ws), wb.value, _stream(A_row_offsets)))
+    words = (E.value + 15) // 16
+    codes = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(words, 1) * 16, dtype=A_val.dtype, device=dev)
+    _check("spops_delta_encode", lib().spops_delta_encode(
+        ctypes.byref(d), _ptr(eo), E.value, _ptr(codes), _ptr(vals), _stream(A_row_offsets)))
+    return DeltaMatrix(m, n, eo, codes, vals, E.value)
+
+
+def delta_spmv(D: DeltaMatrix, x: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = A x for A in the delta format (fp32 accumulation)."""
+    _require(x, "x", (D.values.dtype,))
+    if x.numel() != D.n:
+        raise ValueError("x must have n entries")
+    if out is None:
+        out = torch.empty(D.m, dtype=out_dtype, device=x.device)
+    else:
+        _require(out, "out", (out_dtype,))
+        if out.numel() != D.m:
+            raise ValueError("out must have m entries")
+    _check("spops_delta_spmv", lib().spops_delta_spmv(
+        D.m, D.n, _ptr(D.enc_offsets), D.entries, _ptr(D.codes), _ptr(D.values),
+        _DT[D.values.dtype], _ptr(x), _ptr(out), _DT[out_dtype], _stream(x)))
+    return out
