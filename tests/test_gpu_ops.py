@@ -229,6 +229,33 @@ def test_spmv_row_blocks(dt, m, n, density, kw, offset):
     assert_close(host_f64(y), ref, dt, "spmv row blocks")
 
 
+@pytest.mark.parametrize("dt,m,n,density", [("f32", 300, 5000, 0.1), ("f16", 129, 8192, 0.5),
+                                             ("bf16", 64, 3000, 0.9)])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_spmv_balanced_long_rows(dt, m, n, density, offset):
+    # balanced rows longer than the row-block limit: a workgroup per row; the
+    # plan's split of long rows is not used and must not be fixed up
+    A = gen.random_csr(40 + m, m, n, density, dt)
+    x = gen.dense(40 + m, 100, gen.S_B, (n, 1), dt)
+    v, ro, ci = csr_dev(A)
+    if offset:
+        v = torch.cat([v[:1], v])[1:]
+        ci = torch.cat([ci[:1], ci])[1:]
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    info = p.info()
+    assert info["max_row_nnz"] > 128 and info["split_rows"] > 0
+    y = S.spmm(v, ro, ri, ci, dev(x, dt), m, plan=p)
+    ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt)
+    assert_close(host_f64(y), ref, dt, "spmv long rows")
+    Ai = A.with_values(gen.f32_to_storage(
+        np.random.default_rng(2).integers(-3, 4, A.nnz).astype(np.float32), dt), dt)
+    xi = gen.dense(40 + m, 100, gen.S_B, (n, 1), dt, integer_values=True)
+    yi = S.spmm(dev(Ai.values, dt), ro, ri, ci, dev(xi, dt), m, plan=p)
+    assert np.array_equal(host_f64(yi),
+                          oracle.spmm(m, A.row_offsets, A.col_idx, Ai.values, dt, xi, dt))
+
+
 def test_spmv_row_blocks_offsets_changed_after_planning():
     # a plan made for short rows, then one row rewritten to hold every entry:
     # the blocks find their range too large for LDS and fall back to a wave

@@ -22,8 +22,13 @@
 // wave turns the per-lane step totals into each lane's starting column with
 // a DPP prefix sum, and the lane gathers x at its columns and accumulates in
 // fp32.  A row spans as many 1024-entry wave rounds as it needs; the column
-// carries over between rounds.  Entries whose decoded column is outside
-// [0, n) (codes that do not belong to a valid matrix) are skipped.
+// carries over between rounds, and the next round's word and values are
+// loaded while a round is computed.  When x fits (48 KiB) each workgroup
+// first copies it into LDS, so the gathers are LDS reads; workgroups then
+// loop over rows.  Entries whose decoded column is outside [0, n) (codes
+// that do not belong to a valid matrix) are skipped.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -156,54 +161,88 @@ __device__ __forceinline__ void load16(const VT* p, float (&v)[16]) {
   }
 }
 
-template <typename VT, typename OT>
+// x in LDS when it fits this many bytes (then every gather is an LDS read
+// and the next round's loads can be in flight while a round is computed)
+constexpr int64_t kDeltaXLds = 48 * 1024;
+// most workgroups; each copies x into its LDS once and loops over rows
+constexpr int64_t kDeltaMaxBlocks = 1024;
+
+template <typename VT, typename OT, bool XLDS>
 __global__ __launch_bounds__(kBlock) void delta_spmv_kernel(int64_t m, int64_t n,
                                                             const int32_t* eo,
                                                             const uint32_t* codes, const VT* val,
                                                             int64_t total, const VT* x, OT* y) {
-  const int64_t r = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-  const int l = lane_id();
-  if (r >= m) return;
-  int64_t e0 = eo[r], e1 = eo[r + 1];
-  e0 = e0 < 0 ? 0 : (e0 > total ? total : e0);
-  e1 = e1 < e0 ? e0 : (e1 > total ? total : e1);
-  float acc = 0.f;
-  int64_t colc = -1;  // column before the first entry of this round
-  for (int64_t wb = e0 >> 4; wb * 16 < e1; wb += kWave) {
-    const int64_t w = wb + l;
-    const int64_t eb = w * 16;  // first entry of this lane's word
-    const bool any = eb < e1;
-    // the word and its 16 values (the value array is padded to whole words)
-    const int64_t wl = any ? w : e0 >> 4;
-    const uint32_t word = codes[wl];
-    float v[16];
-    load16(val + wl * 16, v);
-    // column steps of this lane's entries that belong to the row
-    uint32_t step[16];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t e = eb + j;
-      step[j] = (any && e >= e0 && e < e1) ? ((word >> (2 * j)) & 3u) + 1u : 0u;
-      tot += step[j];
-    }
-    const uint32_t incl = wave_inclusive_sum(tot);
-    // columns, then all 16 gathers at clamped addresses, then the products
-    int64_t c = colc + (int64_t)(incl - tot);
-    float xv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      c += step[j];
-      const bool ok = step[j] != 0 && c < n;
-      xv[j] = to_f32(x[ok ? c : 0]);
-      v[j] = ok ? v[j] : 0.f;  // entries of other rows
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(v[j], xv[j], acc);
-    colc += (int64_t)wave_last(incl);
+  extern __shared__ __align__(16) unsigned char xs_raw[];
+  const VT* xr = x;
+  if constexpr (XLDS) {
+    VT* xs = (VT*)xs_raw;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock) xs[i] = x[i];
+    __syncthreads();
+    xr = xs;
   }
-  acc = group_sum<kWave>(acc);
-  if (l == 0) y[r] = from_f32<OT>(acc);
+  const int l = lane_id();
+  for (int64_t r = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave; r < m;
+       r += (int64_t)gridDim.x * kWaves) {
+    int64_t e0 = eo[r], e1 = eo[r + 1];
+    e0 = e0 < 0 ? 0 : (e0 > total ? total : e0);
+    e1 = e1 < e0 ? e0 : (e1 > total ? total : e1);
+    float acc0 = 0.f, acc1 = 0.f;
+    int64_t colc = -1;  // column before the first entry of this round
+    const int64_t wfirst = e0 >> 4;
+    // round 0's word and values; later rounds are loaded one round ahead
+    // (the value array is padded to whole words; lanes past the row load
+    // the row's first word)
+    int64_t w = wfirst + l;
+    uint32_t word = 0;
+    float v[16];
+    {
+      const int64_t wl = w * 16 < e1 ? w : wfirst;
+      if (e0 < e1) {
+        word = codes[wl];
+        load16(val + wl * 16, v);
+      }
+    }
+    for (int64_t wb = wfirst; wb * 16 < e1; wb += kWave, w += kWave) {
+      const int64_t eb = w * 16;  // first entry of this lane's word
+      const bool any = eb < e1;
+      uint32_t nword = 0;
+      float nv[16];
+      const int64_t wn = w + kWave;
+      if ((wb + kWave) * 16 < e1) {
+        const int64_t wl = wn * 16 < e1 ? wn : wfirst;
+        nword = codes[wl];
+        load16(val + wl * 16, nv);
+      }
+      // column steps of this lane's entries that belong to the row
+      uint32_t step[16];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t e = eb + j;
+        step[j] = (any && e >= e0 && e < e1) ? ((word >> (2 * j)) & 3u) + 1u : 0u;
+        tot += step[j];
+      }
+      const uint32_t incl = wave_inclusive_sum(tot);
+      int64_t c = colc + (int64_t)(incl - tot);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        c += step[j];
+        const bool ok = step[j] != 0 && c < n;
+        const float xv = to_f32(xr[ok ? c : 0]);
+        const float vv = ok ? v[j] : 0.f;  // entries of other rows
+        if (j & 1)
+          acc1 = __builtin_fmaf(vv, xv, acc1);
+        else
+          acc0 = __builtin_fmaf(vv, xv, acc0);
+      }
+      colc += (int64_t)wave_last(incl);
+      word = nword;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = nv[j];
+    }
+    float acc = group_sum<kWave>(acc0 + acc1);
+    if (l == 0) y[r] = from_f32<OT>(acc);
+  }
 }
 
 template <typename IT>
@@ -238,17 +277,27 @@ hipError_t encode_vt(int64_t m, int64_t nnz, const int32_t* ro, const void* col,
   return hipGetLastError();
 }
 
+template <typename VT, typename OT>
+void spmv_launch(int64_t m, int64_t n, const int32_t* eo, const uint32_t* codes, const void* val,
+                 int64_t total, const void* x, void* y, hipStream_t s) {
+  const dim3 grid((unsigned)std::min<int64_t>(cdiv(m, kWaves), kDeltaMaxBlocks));
+  const int64_t xbytes = n * (int64_t)sizeof(VT);
+  if (xbytes <= kDeltaXLds)
+    hipLaunchKernelGGL((delta_spmv_kernel<VT, OT, true>), grid, dim3(kBlock), (size_t)xbytes, s,
+                       m, n, eo, codes, (const VT*)val, total, (const VT*)x, (OT*)y);
+  else
+    hipLaunchKernelGGL((delta_spmv_kernel<VT, OT, false>), grid, dim3(kBlock), 0, s, m, n, eo,
+                       codes, (const VT*)val, total, (const VT*)x, (OT*)y);
+}
+
 template <typename VT>
 hipError_t spmv_vt(int64_t m, int64_t n, const int32_t* eo, const uint32_t* codes,
                    const void* val, int64_t total, const void* x, void* y, int y_dtype,
                    hipStream_t s) {
-  const dim3 grid((unsigned)cdiv(m, kWaves));
   if (y_dtype == kF32)
-    hipLaunchKernelGGL((delta_spmv_kernel<VT, float>), grid, dim3(kBlock), 0, s, m, n, eo, codes,
-                       (const VT*)val, total, (const VT*)x, (float*)y);
+    spmv_launch<VT, float>(m, n, eo, codes, val, total, x, y, s);
   else
-    hipLaunchKernelGGL((delta_spmv_kernel<VT, VT>), grid, dim3(kBlock), 0, s, m, n, eo, codes,
-                       (const VT*)val, total, (const VT*)x, (VT*)y);
+    spmv_launch<VT, VT>(m, n, eo, codes, val, total, x, y, s);
   return hipGetLastError();
 }
 

@@ -505,6 +505,77 @@ __global__ __launch_bounds__(kBlock) void spmv_stream_kernel(SpmmArgs a, int32_t
   }
 }
 
+// N == 1 on balanced long rows (every row above the row-block limit): one
+// workgroup per row, rows in index order with one contiguous range per XCD.
+// Lanes stream the row's entries with the same clamped 4-entry loads as the
+// row-block kernel and keep two fp32 sums; the workgroup adds its lanes'
+// sums in a fixed order.
+template <typename VT, typename OT, typename IT, bool QUAD>
+__global__ __launch_bounds__(kBlock) void spmv_row_kernel(SpmmArgs a) {
+  __shared__ float red[kBlock / kWave];
+  const IT* col = (const IT*)a.col;
+  const VT* val = (const VT*)a.val;
+  const VT* x = (const VT*)a.B;
+  const int k = (int)a.k, nnz = (int)a.nnz;
+  const int64_t ldx = a.ldb;
+  const int64_t r = row_block(blockIdx.x, gridDim.x, 1);
+  if (r >= a.m) return;
+  const int t = threadIdx.x;
+  int base = a.ro[r], end = a.ro[r + 1];
+  base = base < 0 ? 0 : (base > nnz ? nnz : base);
+  end = end < base ? base : (end > nnz ? nnz : end);
+  const bool has_x = k > 0;
+  float acc0 = 0.f, acc1 = 0.f;
+  int p_done = base;
+  if constexpr (QUAD) {
+    constexpr int U = kStreamQuads;
+    const int gend = min(nnz >> 2, (end + 3) >> 2);
+    const int gbeg = base >> 2;
+    if (gend > gbeg) {
+      p_done = max(base, 4 * gend);
+      for (int g = gbeg + t; g < gend; g += kBlock * U) {
+        IT c[U][4];
+        VT v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int gq = min(g + u * kBlock, gend - 1);
+          load_quad(col + 4 * gq, c[u]);
+          load_quad(val + 4 * gq, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int gu = g + u * kBlock;
+            const int pp = 4 * gu + q;
+            const int ci = (int)c[u][q];
+            const bool ok = gu < gend && pp >= base && pp < end && (unsigned)ci < (unsigned)k;
+            const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
+            const float pr = ok ? to_f32(v[u][q]) * xl : 0.f;
+            if (q & 1)
+              acc1 += pr;
+            else
+              acc0 += pr;
+          }
+      }
+    }
+  }
+  for (int pp = p_done + t; pp < end; pp += kBlock) {
+    const int ci = (int)col[pp];
+    const bool ok = (unsigned)ci < (unsigned)k;
+    const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
+    acc0 += ok ? to_f32(val[pp]) * xl : 0.f;
+  }
+  float s = group_sum<kWave>(acc0 + acc1);
+  if (lane_id() == 0) red[t / kWave] = s;
+  __syncthreads();
+  if (t == 0) {
+    float tot = red[0];
+    for (int w = 1; w < kBlock / kWave; ++w) tot += red[w];
+    ((OT*)a.C)[r * a.ldc] = from_f32<OT>(tot);
+  }
+}
+
 // --------------------------------------------------------- wide-N waves --
 
 template <int BYTES>
@@ -822,6 +893,7 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
   hipError_t e;
   const SpmvBlocks sb = spmv_row_blocks(a.m, a.nnz, a.max_row, a.natural, a.P);
+  bool whole_rows = false;  // every row written by one workgroup (no fixup)
   if (a.N == 1 && sb.ok) {
     // balanced rows: stream row blocks through LDS
     const int32_t R = sb.R, cap = sb.cap;
@@ -835,6 +907,18 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, false>), grid, dim3(kBlock), lds, s, a,
                          R, cap);
+    e = hipGetLastError();
+  } else if (a.N == 1 && a.natural && a.max_row > kStreamCap / kStreamMinRows) {
+    // balanced long rows: a workgroup per row (the plan's row splits are not
+    // used, so there is nothing to fix up)
+    whole_rows = true;
+    const dim3 grid((unsigned)pad8(a.m));
+    const bool quad = ((uintptr_t)a.col % (4 * sizeof(IT)) == 0) &&
+                      ((uintptr_t)a.val % (4 * sizeof(VT)) == 0);
+    if (quad)
+      hipLaunchKernelGGL((spmv_row_kernel<VT, OT, IT, true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((spmv_row_kernel<VT, OT, IT, false>), grid, dim3(kBlock), 0, s, a);
     e = hipGetLastError();
   } else if (a.N == 1) {
     // lanes per row from the mean row length
@@ -890,7 +974,7 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     }
   }
   if (e != hipSuccess) return e;
-  if (a.S > 0) {
+  if (a.S > 0 && !whole_rows) {
     dim3 grid((unsigned)a.S, (unsigned)cdiv(a.N, kBlock));
     hipLaunchKernelGGL(spmm_fixup_kernel<OT>, grid, dim3(kBlock), 0, s, a);
     e = hipGetLastError();
