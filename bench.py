@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
     p.add_argument("--no-adapter", action="store_true",
                    help="skip the sparse-layer training step (forward, both gradients, Adam, merge)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the copy and gather rate measurements")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
@@ -365,6 +367,78 @@ def delta_spmv_bench(S, dev, flush, args):
     return out
 
 
+def measure_ceilings(dev, flush):
+    """Rates that bound the gather-shaped kernels, measured with the
+    measurement library (libspops_ceilings.so): a plain 256 MiB device copy
+    after a cache flush, and row gathers (16-byte lanes, a wave per row, 8
+    rows in flight per lane) of 1 KiB and 4 KiB rows at random indices, from
+    a 2 MiB slice per XCD (L2-resident) and from one 16 MiB source shared by
+    all XCDs (Infinity Cache), warm, 5 back-to-back launches."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "unstructured_sparse_linear_amd", "libspops_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    f = L.spops_ceil_gather
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    ts = []
+    for _ in range(5):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    out["copy_gbps"] = round(2 * (256 << 20) / float(np.median(ts)) / 1e6, 1)
+    del a, b
+    src = torch.empty(16 << 20, dtype=torch.uint8, device=dev)
+    src.fill_(3)
+    blocks = 2048
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(0)
+    for rb in (1024, 4096):
+        per_wave = 64 if rb == 1024 else 16
+        waves = blocks * 4
+        for sliced, label in ((1, "l2"), (0, "ic")):
+            rows = (2 << 20) // rb if sliced else (16 << 20) // rb
+            idx = torch.from_numpy(rng.integers(0, rows, waves * per_wave).astype(np.int32)).to(dev)
+            args = (src.data_ptr(), rows, rb, sliced, idx.data_ptr(), per_wave, blocks,
+                    sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+            assert f(*args) == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                f(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 5
+            out[f"gather_{label}_{rb // 1024}kib_gbps"] = round(waves * per_wave * rb / t / 1e6, 1)
+    return out
+
+
+def gathered_bytes(op, A, N, K, dt):
+    """Bytes the operation gathers on chip (one operand row segment per
+    stored entry) and the size of one gathered segment."""
+    s = ESZ[dt]
+    if op in ("spmm", "spmv"):
+        n_ = N if op == "spmm" else 1
+        return A.nnz * n_ * s, min(n_ * s, 1024)
+    if op == "sddmm":
+        return A.nnz * K * s, K * s
+    return 0, 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -572,6 +646,17 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if not args.no_ceilings:
+        ceil = measure_ceilings(dev, flush)
+        result["ceilings"] = ceil
+        gb, seg = gathered_bytes(dom, A, N if dom != "spmv" else 1, K, dt)
+        if gb:
+            key = f"gather_l2_{4 if seg > 2048 else 1}kib_gbps"
+            rate = gb / breakdown[dom]["ms"] / 1e6
+            result["roofline"]["gathered_bytes_per_launch"] = int(gb)
+            result["roofline"]["gather_rate_gbps"] = round(rate, 1)
+            result["roofline"]["gather_ceiling"] = key
+            result["roofline"]["frac_of_gather_ceiling"] = round(rate / ceil[key], 4)
     if not args.no_adapter:
         result["next_adapter_step"] = adapter_step(S, w, A, dt, N, dev, flush, args)
     if args.config == 4:

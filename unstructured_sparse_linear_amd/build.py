@@ -18,6 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "spops")
 LIB = os.path.join(HERE, "libspops.so")
+CEILINGS_LIB = os.path.join(HERE, "libspops_ceilings.so")
 ARCH = os.environ.get("SPOPS_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [
@@ -59,7 +60,24 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
+    build_ceilings(verbose)
     return LIB
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """The benchmark's measurement kernels (gather rates), a library of their
+    own that libspops does not link."""
+    src = os.path.join(HERE, "ceilings", "ceilings.hip")
+    obj = _compile(src)
+    tmp = CEILINGS_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, CEILINGS_LIB)
+    if verbose:
+        print(f"built {CEILINGS_LIB}", file=sys.stderr)
+    return CEILINGS_LIB
 
 
 if __name__ == "__main__":
