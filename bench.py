@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
     p.add_argument("--no-adapter", action="store_true",
                    help="skip the sparse-layer training step (forward, both gradients, Adam, merge)")
+    p.add_argument("--records", default=None,
+                   help="also write one JSON record per operation to this file (JSONL)")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the copy and gather rate measurements")
     p.add_argument("--copy-calibration", action="store_true",
@@ -184,7 +186,7 @@ def cpu_baseline(w, A, dt, N, K, ops, oracle):
         total_s += t
         total_b += ab[op]
     return {"value": round(total_b / total_s / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the full workload (all {len(ops)} operations, one pass each), "
                       "median of 3 after 1 warm-up",
             "ms_per_op": per, "ms_per_step": round(total_s * 1e3, 3)}
@@ -439,6 +441,60 @@ def gathered_bytes(op, A, N, K, dt):
     return 0, 0
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def write_records(path, result, args, A, dt, N, K, ab, fl):
+    """One record per operation with the fields of the measurement plan:
+    times (cold median / p10 / p90, warm), rates against the nominal HBM
+    peak and the measured copy rate, counter traffic where committed for
+    these kernel sources, the plan time and the CPU oracle's time.  Accuracy
+    fields stay null here: parity is checked by the tests, not the bench."""
+    copy = (result.get("ceilings") or {}).get("copy_gbps")
+    cpu = result.get("cpu_baseline") or {}
+    plans = result["plans"]
+    with open(path, "a") as f:
+        for op, b in result["ops_breakdown"].items():
+            t = b["ms"]
+            traffic = traffic_for(op, args.config) if op in KERNEL_FILES else None
+            rec = {
+                "config": args.config, "workload": result["config"]["workload"], "op": op,
+                "dtype": dt, "out_dtype": "f32" if op in ("spmm", "spmv", "sddmm") else dt,
+                "backend": "structure_aware" if op == "sddmm" else None,
+                "tau": None if op != "sddmm" else "default",
+                "m": A.m, "n": A.n,
+                "N_or_K": {"spmm": N, "spmv": 1, "sddmm": K}.get(op),
+                "nnz": A.nnz, "alg_bytes": b["alg_bytes"], "flops": fl.get(op),
+                "t_med_us": round(t * 1e3, 2), "t_p10_us": round(b["ms_p10"] * 1e3, 2),
+                "t_p90_us": round(b["ms_p90"] * 1e3, 2),
+                "t_warm_med_us": round(b["ms_warm"] * 1e3, 2),
+                "plan_us": (round(result["plan_ms"]["sddmm_partition"] * 1e3, 1) if op == "sddmm"
+                            else round(result["plan_ms"]["spmm_schedule_and_row_order"] * 1e3, 1)
+                            if op in ("spmm", "spmv") else None),
+                "gbps_alg": b["gbps"], "gflops": b.get("gflops"),
+                "frac_hbm_nominal": b["frac_hbm"],
+                "frac_hbm_copy": round(b["gbps"] / copy, 4) if copy else None,
+                "hbm_bytes_counters": traffic,
+                "refetch": round(traffic / b["alg_bytes"], 2) if traffic else None,
+                "mfma_busy": None,
+                "oracle_s": (cpu.get("ms_per_op", {}).get(op, 0) / 1e3) if cpu else None,
+                "oracle_threads": cpu.get("cores"), "cpu_model": cpu_model() if cpu else None,
+                "max_rel_err": None, "normwise_err": None, "bitexact_idx": None,
+                "seed": 0,
+                "kernel_sources_sha": kernel_sources_sha(KERNEL_FILES.get(op, ["common.h"])),
+                "plan": plans["sddmm"] if op == "sddmm" else plans["spmm"],
+            }
+            f.write(json.dumps(rec) + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -558,6 +614,21 @@ def main():
     torch.cuda.synchronize()
     per_op = {op: [a.elapsed_time(b) for a, b in v] for op, v in per_op.items()}
 
+    # per-operation warm timing: 10 back-to-back calls between two events
+    # (no flush, so the working set sits in the Infinity Cache), 3 times
+    warm = {}
+    for op in ops:
+        reps = []
+        for _ in range(3):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(10):
+                run_op(op)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / 10)
+        warm[op] = float(np.median(reps))
+
     # the whole step, captured once and replayed
     graph = None
     if not args.no_graph:
@@ -605,6 +676,7 @@ def main():
                          "frac_hbm": round(ab[op] / t / 1e6 / HBM_PEAK_GBS, 4)}
         if op in fl:
             breakdown[op]["gflops"] = round(fl[op] / t / 1e6, 1)
+        breakdown[op]["ms_warm"] = round(warm[op], 4)
     # the dominant kernel: the longer of SpMM and SDDMM (the operations the
     # metric is about; each is one kernel unless long rows are split or the
     # mask has dense tiles, and then its kernels are listed together)
@@ -666,6 +738,8 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)
+    if args.records:
+        write_records(args.records, result, args, A, dt, N, K, ab, fl)
     print(json.dumps(result))
 
 
