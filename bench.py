@@ -62,6 +62,10 @@ def parse():
     p.add_argument("--dtype", default=None, help="value dtype override (config 3: f16|bf16)")
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the metric)")
     p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
+    p.add_argument("--serial-step", action="store_true",
+                   help="capture the step on one stream (no overlap of independent operations)")
+    p.add_argument("--streams", type=int, default=2, choices=(1, 2, 3),
+                   help="streams the step graph spreads independent operations over")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ops", default="spmm,sddmm,csr_add,transpose,row_order")
     p.add_argument("--no-adapter", action="store_true",
@@ -630,12 +634,33 @@ def main():
         warm[op] = float(np.median(reps))
 
     # the whole step, captured once and replayed
+    # Independent operations run on separate streams inside the graph (fork
+    # from the capturing stream, join at the end of the step): with two
+    # streams the two gather-bound products share one and the short
+    # launch-bound operations (csr_add, transpose, then the row order of A^T,
+    # which needs the transpose) take the other; with three, SpMM and SDDMM
+    # get one each.  Default stream priorities.
     graph = None
+    side_ops = [o for o in ops if o in ("csr_add", "transpose", "row_order")]
+    main_ops = [o for o in ops if o not in side_ops]
+    nstreams = 1 if args.serial_step or not side_ops or not main_ops else args.streams
+    lanes = ([ops] if nstreams == 1 else [main_ops, side_ops] if nstreams == 2
+             else [[o] for o in main_ops] + [side_ops])
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
+        extra = [torch.cuda.Stream(device=dev) for _ in lanes[1:]]
         with torch.cuda.graph(graph):
-            for op in ops:
+            cur = torch.cuda.current_stream(dev)
+            for st in extra:
+                st.wait_stream(cur)
+            for st, lane_ops in zip(extra, lanes[1:]):
+                with torch.cuda.stream(st):
+                    for op in lane_ops:
+                        run_op(op)
+            for op in lanes[0]:
                 run_op(op)
+            for st in extra:
+                cur.wait_stream(st)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream(dev)
 
@@ -701,7 +726,8 @@ def main():
         "config": {"workload": w.name, "config_id": args.config, "m": m, "n": n, "nnz": A.nnz,
                    "N": N, "K": K, "value_dtype": dt, "ops": ops,
                    "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)",
-                   "step": "eager" if args.no_graph else "hip graph replay"},
+                   "step": "eager" if args.no_graph else
+                   "hip graph replay, streams: " + " | ".join("+".join(x) for x in lanes)},
         "eager_sum_of_ops_ms": round(sum(float(np.mean(v)) for v in per_op.values()), 4),
         "gflops": round(total_flops / mean_step / 1e6, 1),
         "frac_hbm": round(total_bytes / mean_step / 1e6 / HBM_PEAK_GBS, 4),
