@@ -67,3 +67,70 @@ def test_graph_replays_match_eager(dt, heavy):
             assert torch.equal(a, b), f"replay {rep} differs"
         # unrelated eager work between replays
         _ = (B.float() @ B.float().T).sum().item()
+
+
+def test_graph_replays_of_the_next_rows_match_eager():
+    # delta-coded SpMV, a masked Adam step and the sparse layer's training
+    # step (forward, both gradients, merge) on two streams, captured once and
+    # replayed; each replay is compared with the same sequence run eagerly
+    # from the same state
+    dt = "f16"
+    A = gen.random_csr(7, 700, 900, 0.3, dt)
+    m, n, T = A.m, A.n, 64
+    v, ro, ci = csr_dev(A)
+    D = S.delta_encode(v, ro, ci, m, n)
+    x = dev(gen.dense(7, 100, gen.S_B1, (n,), dt), dt)
+    y = torch.empty(m, dtype=torch.float32, device="cuda")
+    P = S.SparsePattern(ro, ci, m, n)
+    xt = dev(gen.dense(7, 100, gen.S_B, (n, T), dt), dt)
+    dyt = dev(gen.dense(7, 100, gen.S_A, (m, T), dt), dt)
+    W0 = dev(gen.dense(7, 100, gen.S_W, (m, n), dt), dt)
+    th0 = v.clone()
+    yt = torch.empty((m, T), dtype=torch.float16, device="cuda")
+    dv = torch.empty_like(v)
+    vT = torch.empty_like(v)
+    dxt = torch.empty((n, T), dtype=torch.float16, device="cuda")
+    th, W = th0.clone(), W0.clone()
+    m1 = torch.zeros(A.nnz, dtype=torch.float32, device="cuda")
+    m2 = torch.zeros_like(m1)
+    side = torch.cuda.Stream()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            S.delta_spmv(D, x, out=y)
+        S.spmm(th, P.ro, P.ri, P.ci, xt, m, out_dtype=torch.float16, plan=P.spmm_plan, out=yt)
+        S.sddmm(P.ro, P.ri, P.ci, dyt, xt, plan=P.sddmm_plan, out_dtype=torch.float16, out=dv)
+        P.transposed_values(th, out=vT)
+        S.spmm(vT, P.roT, P.riT, P.ciT, dyt, n, out_dtype=torch.float16, plan=P.spmmT_plan,
+               out=dxt)
+        S.masked_adam(th, dv, m1, m2, 3, lr=1e-3)
+        S.csr_add(th, P.ro, P.ri, P.ci, W)
+        cur.wait_stream(side)
+
+    def reset():
+        th.copy_(th0)
+        W.copy_(W0)
+        m1.zero_()
+        m2.zero_()
+        for t in (y, yt, dv, vT, dxt):
+            t.zero_()
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, yt, dv, vT, dxt, th, W, m1, m2)]
+    reset()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((y, yt, dv, vT, dxt, th, W, m1, m2), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (xt.float() @ xt.float().T).sum().item()
