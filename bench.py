@@ -376,8 +376,9 @@ def delta_spmv_bench(S, dev, flush, args):
 def measure_ceilings(dev, flush):
     """Rates that bound the gather-shaped kernels, measured with the
     measurement library (libspops_ceilings.so): a plain 256 MiB device copy
-    after a cache flush, and row gathers (16-byte lanes, a wave per row, 8
-    rows in flight per lane) of 1 KiB and 4 KiB rows at random indices, from
+    after a cache flush, and row gathers (16-byte lanes, a wave per row and
+    half a wave per 512-byte row, 8 rows in flight per lane) of 512 B, 1 KiB
+    and 4 KiB rows at random indices, from
     a 2 MiB slice per XCD (L2-resident) and from one 16 MiB source shared by
     all XCDs (Infinity Cache), warm, 5 back-to-back launches."""
     import ctypes
@@ -412,8 +413,8 @@ def measure_ceilings(dev, flush):
     blocks = 2048
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     rng = np.random.default_rng(0)
-    for rb in (1024, 4096):
-        per_wave = 64 if rb == 1024 else 16
+    for rb in (512, 1024, 4096):
+        per_wave = {512: 128, 1024: 64, 4096: 16}[rb]
         waves = blocks * 4
         for sliced, label in ((1, "l2"), (0, "ic")):
             rows = (2 << 20) // rb if sliced else (16 << 20) // rb
@@ -429,7 +430,8 @@ def measure_ceilings(dev, flush):
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / 5
-            out[f"gather_{label}_{rb // 1024}kib_gbps"] = round(waves * per_wave * rb / t / 1e6, 1)
+            name = f"{rb // 1024}kib" if rb >= 1024 else f"{rb}b"
+            out[f"gather_{label}_{name}_gbps"] = round(waves * per_wave * rb / t / 1e6, 1)
     return out
 
 
@@ -749,7 +751,8 @@ def main():
         result["ceilings"] = ceil
         gb, seg = gathered_bytes(dom, A, N if dom != "spmv" else 1, K, dt)
         if gb:
-            key = f"gather_l2_{4 if seg > 2048 else 1}kib_gbps"
+            key = ("gather_l2_4kib_gbps" if seg > 2048 else "gather_l2_1kib_gbps" if seg > 512
+                   else "gather_l2_512b_gbps")
             rate = gb / breakdown[dom]["ms"] / 1e6
             result["roofline"]["gathered_bytes_per_launch"] = int(gb)
             result["roofline"]["gather_rate_gbps"] = round(rate, 1)
