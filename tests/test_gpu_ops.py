@@ -139,7 +139,11 @@ def test_spmm_any_row_order_same_bits(kind):
     A = gen.random_csr(11, 400, 300, 0.05, "f16")
     B = gen.dense(11, 100, gen.S_B, (300, 64), "f16")
     ref = run_spmm(A, B, "f16", "sorted")
-    assert torch.equal(run_spmm(A, B, "f16", kind), ref)
+    C = run_spmm(A, B, "f16", kind)
+    diff = C != ref
+    rows = torch.nonzero(diff.any(1)).flatten().tolist()
+    assert not diff.any(), (f"{int(diff.sum())} elements differ in rows {rows[:8]}, "
+                            f"nan {int(torch.isnan(C).sum())}/{int(torch.isnan(ref).sum())}")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -167,6 +171,18 @@ def test_spmm_long_rows(dt, N, use_plan):
         p = S.SpmmPlan(ro, S.sort_rows_by_nnz(ro, A.n), ci, A.n)
         info = p.info()
         assert info["max_row_nnz"] == 4500 and info["split_rows"] == 6
+
+
+@pytest.mark.parametrize("dt,N", [("f32", 64), ("bf16", 256), ("f16", 24), ("f32", 8)])
+def test_spmm_pointer_load_path(monkeypatch, dt, N):
+    # the group kernel's path for operands of 2 GiB and more (pointer loads,
+    # per-lane metadata), selected here by its switch
+    monkeypatch.setenv("SPOPS_SPMM_NOBUF", "1")
+    A = heavy_csr(15, 300, 2000, [1500, 700, 130, 129], dt)
+    B = gen.dense(15, 100, gen.S_B, (2000, N), dt)
+    C = run_spmm(A, B, dt)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert_close(host_f64(C), ref, dt, "spmm pointer-load path")
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])

@@ -13,8 +13,13 @@
 //   dispatcher places on the same XCD, so each XCD's 4 MB L2 holds the part of
 //   B it gathers from.  16-bit inputs use v_dot2_f32_{f16,bf16} on pairs of
 //   entries after a v_perm_b32 repack, one instruction per two products.
-// * spmm_kernel (narrow N): a group of LPR lanes owns one row and a window of
-//   LPR*VEC columns; lanes load 16-byte vectors of B rows.
+// * spmm_kernel (the default for N > 1): a group of LPR lanes owns one row
+//   and a window of LPR*VEC columns; lanes load 16-byte vectors of B rows.
+//   The entries' columns and values are loaded once per group (a few lanes
+//   load a batch of 8, the rest fetch them with ds_bpermute) and B, col_idx
+//   and values are read through buffer resources, whose range check turns
+//   padding entries into loads of zero that touch no memory.  LPR is halved
+//   while one window's share of B would overflow an XCD's L2.
 // * spmv_kernel (N == 1): LPR lanes share a row, striding over its entries.
 //
 // Row order.  Work visits rows in row_idx order (section "Usage": rows sorted
@@ -235,13 +240,199 @@ __device__ __forceinline__ void write_out(OT* dst, int64_t j, int64_t N, const f
   }
 }
 
+// ------------------------------------------------------- buffer loads --
+
+template <int BYTES>
+struct BufLoad;
+template <>
+struct BufLoad<4> {
+  static constexpr int words = 1;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  }
+};
+template <>
+struct BufLoad<8> {
+  static constexpr int words = 2;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+};
+template <>
+struct BufLoad<16> {
+  static constexpr int words = 4;
+  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                              uint32_t* w) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
+  }
+};
+
+// Raw buffer descriptor (dword 3 as for untyped 32-bit data on gfx9).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, _Float16*) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
+                                false);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, bf16_t*) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, a),
+                                         __builtin_bit_cast(bf162v, b), c, false);
+}
+
+
+// Group path with buffer loads (B, col_idx and values each under 2 GiB).
+// Entries go in batches of 8.  The group's lanes share a batch's metadata:
+// lane gl loads column and value of entry p + (gl mod W) (W = min(LPR, 8);
+// groups of 4 lanes load two entries each), turns the column into a byte
+// offset into B, and the other lanes fetch offsets and values with
+// ds_bpermute.  Entries outside [q0, q1) and columns outside [0, k) get an
+// offset past the end of the buffer, which reads zeros without touching
+// memory, and a zero value; so every load is unconditional and the loop has
+// no branch but its exit.  The next batch's metadata is requested after this
+// batch's B vectors and arrives while they are consumed.
+constexpr uint32_t kOob = 0x80000000u;  // past the end of any buffer this path takes
+
+template <int LPR>
+struct BatchMeta {
+  static constexpr int W = LPR < 8 ? LPR : 8;  // lanes holding metadata
+  static constexpr int T = 8 / W;              // entries per holding lane
+  uint32_t c[T];    // column (raw bits of IT)
+  uint32_t raw[T];  // value bits (fp32, or the 16-bit value)
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t buf_load_elem(__amdgpu_buffer_rsrc_t rs, uint32_t i) {
+  if constexpr (sizeof(T) == 2)
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, i * 2u, 0, 0);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4u, 0, 0);
+}
+
+template <typename VT, typename IT, int LPR>
+__device__ __forceinline__ void load_meta(__amdgpu_buffer_rsrc_t crs, __amdgpu_buffer_rsrc_t vrs,
+                                          int p, int gl, BatchMeta<LPR>& m) {
+  using M = BatchMeta<LPR>;
+#pragma unroll
+  for (int t = 0; t < M::T; ++t) {
+    const uint32_t e = (uint32_t)(p + gl % M::W + M::W * t);
+    m.c[t] = buf_load_elem<IT>(crs, e);
+    m.raw[t] = buf_load_elem<VT>(vrs, e);
+  }
+}
+
+template <typename VT>
+struct GroupBatch {
+  static constexpr int NV = sizeof(VT) == 2 ? 4 : 8;  // 16-bit values go in pairs
+  uint4 b[8];
+  uint32_t v[NV];
+};
+
+// Check the batch at entry p (metadata in m) and request its B vectors.
+template <typename VT, typename IT, int LPR>
+__device__ __forceinline__ void issue_group(__amdgpu_buffer_rsrc_t brs, int64_t k, uint32_t ldbb,
+                                            const BatchMeta<LPR>& m, int p, int q1, int gl,
+                                            int lb4, uint32_t joff, GroupBatch<VT>& x) {
+  using M = BatchMeta<LPR>;
+  uint32_t off[M::T], vb[M::T];
+#pragma unroll
+  for (int t = 0; t < M::T; ++t) {
+    const int c = sizeof(IT) == 2 ? (int)(int16_t)m.c[t] : (int)m.c[t];
+    const bool ok = p + gl % M::W + M::W * t < q1 && (unsigned)c < (unsigned)k;
+    off[t] = ok ? (uint32_t)c * ldbb : kOob;
+    vb[t] = ok ? m.raw[t] : 0u;
+    if constexpr (sizeof(VT) == 2) {
+      // even lanes pack their value with the next lane's: one v_dot2 pair
+      const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)vb[t], 0xF5, 0xF, 0xF, false);
+      vb[t] |= nb << 16;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t o =
+        (uint32_t)__builtin_amdgcn_ds_bpermute(lb4 + 4 * (u % M::W), (int)off[u / M::W]);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, o + joff, 0, 0);
+    x.b[u] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+#pragma unroll
+  for (int q = 0; q < GroupBatch<VT>::NV; ++q) {
+    const int e = sizeof(VT) == 2 ? 2 * q : q;  // first entry of the pair / the entry
+    x.v[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(lb4 + 4 * (e % M::W), (int)vb[e / M::W]);
+  }
+}
+
+template <typename VT>
+__device__ __forceinline__ void consume_group(const GroupBatch<VT>& x, float* acc) {
+  if constexpr (sizeof(VT) == 4) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = __uint_as_float(x.v[u]);
+      acc[0] = __builtin_fmaf(v, __uint_as_float(x.b[u].x), acc[0]);
+      acc[1] = __builtin_fmaf(v, __uint_as_float(x.b[u].y), acc[1]);
+      acc[2] = __builtin_fmaf(v, __uint_as_float(x.b[u].z), acc[2]);
+      acc[3] = __builtin_fmaf(v, __uint_as_float(x.b[u].w), acc[3]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w0[4] = {x.b[2 * t].x, x.b[2 * t].y, x.b[2 * t].z, x.b[2 * t].w};
+      const uint32_t w1[4] = {x.b[2 * t + 1].x, x.b[2 * t + 1].y, x.b[2 * t + 1].z,
+                              x.b[2 * t + 1].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = __builtin_amdgcn_perm(w1[d], w0[d], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(w1[d], w0[d], 0x07060302u);
+        acc[2 * d] = dot2(lo, x.v[t], acc[2 * d], (VT*)nullptr);
+        acc[2 * d + 1] = dot2(hi, x.v[t], acc[2 * d + 1], (VT*)nullptr);
+      }
+    }
+  }
+}
+
+// Buffer resources of the group path.
+struct GroupBufs {
+  __amdgpu_buffer_rsrc_t b, c, v;
+};
+
+// Entries [q0, q1) of one row into this lane's 16 bytes of columns (byte
+// offset joff within a B row).  lb4: 4 x the wave lane of the group's lane 0.
+template <typename VT, typename IT, int LPR>
+__device__ __forceinline__ void accumulate_buf(const SpmmArgs& a, const GroupBufs& rs,
+                                               uint32_t ldbb, int q0, int q1, int gl, int lb4,
+                                               uint32_t joff, float* acc) {
+  if (q0 >= q1) return;
+  BatchMeta<LPR> m;
+  load_meta<VT, IT, LPR>(rs.c, rs.v, q0, gl, m);
+  for (int p = q0; p < q1; p += 8) {
+    GroupBatch<VT> x;
+    issue_group<VT, IT, LPR>(rs.b, a.k, ldbb, m, p, q1, gl, lb4, joff, x);
+    __builtin_amdgcn_sched_barrier(0);
+    load_meta<VT, IT, LPR>(rs.c, rs.v, p + 8, gl, m);
+    __builtin_amdgcn_sched_barrier(0);
+    consume_group<VT>(x, acc);
+  }
+}
+
 // Blocks [0, P): one chunk of a long row each.  Blocks [P, ...): kBlock/LPR
 // whole rows each (rows longer than the split length are skipped there).
 // Column windows: window w of LPR*VEC columns runs on blocks w, w+nwin, ...
 // which the dispatcher places on the same XCD(s), so each XCD's L2 serves a
 // fixed slice of B.
-template <typename VT, typename OT, typename IT, int LPR, int VEC, bool ALIGNED>
+// BUF: B, col_idx and values are read through buffer resources (each under
+// 2 GiB) with the group-shared metadata of accumulate_buf.
+template <typename VT, typename OT, typename IT, int LPR, int VEC, bool ALIGNED, bool BUF>
 __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) {
+  static_assert(!BUF || (ALIGNED && VEC * sizeof(VT) == 16), "buffer path loads 16 bytes");
   constexpr int GPB = kBlock / LPR;  // groups per block
   const int grp = threadIdx.x / LPR;
   const int gl = threadIdx.x % LPR;
@@ -251,6 +442,14 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  // buffer path: lanes past column N read column 0 (results not stored)
+  const uint32_t ldbb = (uint32_t)(a.ldb * (int64_t)sizeof(VT));
+  const uint32_t joff = (uint32_t)((j < a.N ? j : 0) * (int64_t)sizeof(VT));
+  const int lb4 = (int)((threadIdx.x % kWave) / LPR * LPR * 4);
+  GroupBufs brs;
+  brs.b = make_rsrc(a.B, BUF ? (uint32_t)(a.k * a.ldb * (int64_t)sizeof(VT)) : 0u);
+  brs.c = make_rsrc(a.col, BUF ? (uint32_t)(a.nnz * (int64_t)sizeof(IT)) : 0u);
+  brs.v = make_rsrc(a.val, BUF ? (uint32_t)(a.nnz * (int64_t)sizeof(VT)) : 0u);
 
   if (bx < a.P) {
     __shared__ float red[GPB > 1 ? GPB - 1 : 1][LPR * VEC];
@@ -268,7 +467,10 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
     int64_t q1 = q0 + sub;
     q0 = q0 < c1 ? q0 : c1;
     q1 = q1 < c1 ? q1 : c1;
-    accumulate<VT, IT, VEC, ALIGNED>(a, q0, q1, j, acc);
+    if constexpr (BUF)
+      accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)q0, (int)q1, gl, lb4, joff, acc);
+    else
+      accumulate<VT, IT, VEC, ALIGNED>(a, q0, q1, j, acc);
     if (grp > 0) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) red[grp - 1][gl * VEC + e] = acc[e];
@@ -296,7 +498,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   int64_t p0, p1;
   row_range(a.ro, r, a.nnz, p0, p1);
   if (a.P > 0 && p1 - p0 > a.T) return;  // handled by the chunk blocks
-  if constexpr (LPR == kWave && ALIGNED)
+  if constexpr (BUF)
+    accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)p0, (int)p1, gl, lb4, joff, acc);
+  else if constexpr (LPR == kWave && ALIGNED)
     accumulate_wave<VT, IT>(a, p0, p1, j, acc);
   else
     accumulate<VT, IT, VEC, ALIGNED>(a, p0, p1, j, acc);
@@ -578,54 +782,6 @@ __global__ __launch_bounds__(kBlock) void spmv_row_kernel(SpmmArgs a) {
 
 // --------------------------------------------------------- wide-N waves --
 
-template <int BYTES>
-struct BufLoad;
-template <>
-struct BufLoad<4> {
-  static constexpr int words = 1;
-  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                              uint32_t* w) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
-  }
-};
-template <>
-struct BufLoad<8> {
-  static constexpr int words = 2;
-  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                              uint32_t* w) {
-    auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
-    w[0] = v[0];
-    w[1] = v[1];
-  }
-};
-template <>
-struct BufLoad<16> {
-  static constexpr int words = 4;
-  __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                              uint32_t* w) {
-    auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
-    w[0] = v[0];
-    w[1] = v[1];
-    w[2] = v[2];
-    w[3] = v[3];
-  }
-};
-
-// Raw buffer descriptor (dword 3 as for untyped 32-bit data on gfx9).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, _Float16*) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
-                                false);
-}
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, bf16_t*) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, a),
-                                         __builtin_bit_cast(bf162v, b), c, false);
-}
-
 // Eight consecutive entries starting at p (a multiple of 8): column words and
 // value words.  Wave-uniform addresses, so full groups become scalar loads;
 // the group that reaches past nnz is read entry by entry.
@@ -845,8 +1001,18 @@ hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
     const int64_t nwin = cdiv(a.N, LPR * VEC);
     const int64_t blocks = (a.P + nbw) * nwin;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true>), dim3((unsigned)blocks),
-                       dim3(kBlock), 0, s, a, nwin);
+    // SPOPS_SPMM_NOBUF=1 selects the pointer-load path, which otherwise only
+    // runs for operands of 2 GiB and more (read per call, for tests)
+    const char* noBuf = getenv("SPOPS_SPMM_NOBUF");
+    const int64_t esz = sizeof(VT) > sizeof(IT) ? sizeof(VT) : sizeof(IT);
+    const bool buf = !(noBuf && noBuf[0] == '1') && a.k * a.ldb * (int64_t)sizeof(VT) < ((int64_t)1 << 31) &&
+                     (a.nnz + 64) * esz < ((int64_t)1 << 31);
+    if (buf)
+      hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true, true>), dim3((unsigned)blocks),
+                         dim3(kBlock), 0, s, a, nwin);
+    else
+      hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true, false>),
+                         dim3((unsigned)blocks), dim3(kBlock), 0, s, a, nwin);
   } else {
     // scalar path: 64 lanes per row, one column each
     constexpr int G = kBlock / 64;
@@ -854,7 +1020,7 @@ hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
     const int64_t nwin = cdiv(a.N, 64);
     const int64_t blocks = (a.P + nbw) * nwin;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, 64, 1, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, 64, 1, false, false>), dim3((unsigned)blocks),
                        dim3(kBlock), 0, s, a, nwin);
   }
   return hipGetLastError();
@@ -965,7 +1131,14 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
       const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
                            ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
                            ((uintptr_t)a.partial % 16 == 0);
-      const int64_t nv = cdiv(a.N, VEC);
+      // lanes per row: enough for N (at most a wave), then halved (not below
+      // 16) while the B columns one window reads exceed an XCD's 4 MB L2, so
+      // that the windows the dispatcher spreads over the XCDs stay cached
+      int64_t nv = cdiv(a.N, VEC);
+      int64_t lpr = 4;
+      while (lpr < 64 && lpr < nv) lpr *= 2;
+      while (lpr > 16 && a.k * lpr * 16 > ((int64_t)4 << 20)) lpr /= 2;
+      nv = lpr;
       if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
       else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
       else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);

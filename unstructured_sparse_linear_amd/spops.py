@@ -226,12 +226,16 @@ class _PlanCache:
         self.cap = cap
         self.d: "OrderedDict[tuple, object]" = OrderedDict()
 
-    def get(self, key, make):
+    def get(self, key, make, keep=()):
+        """The plan cached under key, or a new one from make().  The tensors
+        the key was made from (keep) are held with the plan: while they live
+        no other tensor can take their address, so a key built from data
+        pointers (and version counters) never matches a different tensor."""
         if key in self.d:
             self.d.move_to_end(key)
-            return self.d[key]
+            return self.d[key][0]
         v = make()
-        self.d[key] = v
+        self.d[key] = (v, tuple(keep))
         if len(self.d) > self.cap:
             self.d.popitem(last=False)
         return v
@@ -289,7 +293,8 @@ def spmm(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.
             raise ValueError("out has the wrong shape")
     if plan is None and use_plan:
         plan = _spmm_plans.get(("spmm", _tkey(A_row_offsets), _tkey(A_row_indices), d.nnz, k),
-                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, k))
+                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, k),
+                               (A_row_offsets, A_row_indices))
     ws = plan.workspace(N, B.device) if plan is not None else None
     _check("spops_spmm", lib().spops_spmm(
         ctypes.byref(d), _ptr(B), _DT[B.dtype], N, N, _ptr(out), _DT[out_dtype], N,
@@ -321,7 +326,8 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
     if b == STRUCTURE_AWARE and plan is None and nnz > 0:
         plan = _sddmm_plans.get(("sddmm", _tkey(out_row_offsets), _tkey(out_col_indices), m, n,
                                  tau), lambda: SddmmPlan(out_row_offsets, out_col_indices, m, n,
-                                                         tau))
+                                                         tau),
+                                (out_row_offsets, out_col_indices))
     ph = plan.handle if (plan is not None and b == STRUCTURE_AWARE) else None
     if workspace is None:
         wb = ctypes.c_size_t()
@@ -442,7 +448,8 @@ def cg(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Te
             raise ValueError("x must have b's shape")
     if plan is None and use_plan:
         plan = _spmm_plans.get(("spmm", _tkey(A_row_offsets), _tkey(A_row_indices), d.nnz, m),
-                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, m))
+                               lambda: SpmmPlan(A_row_offsets, A_row_indices, A_col_indices, m),
+                               (A_row_offsets, A_row_indices))
     ph = plan.handle if plan is not None else None
     wb = ctypes.c_size_t()
     _check("spops_cg_workspace_size", lib().spops_cg_workspace_size(
