@@ -16,7 +16,7 @@
 // * spmm_kernel (the default for N > 1): a group of LPR lanes owns one row
 //   and a window of LPR*VEC columns; lanes load 16-byte vectors of B rows.
 //   The entries' columns and values are loaded once per group (a few lanes
-//   load a batch of 8, the rest fetch them with ds_bpermute) and B, col_idx
+//   load a batch of 8, the rest fetch them with ds_swizzle) and B, col_idx
 //   and values are read through buffer resources, whose range check turns
 //   padding entries into loads of zero that touch no memory.  LPR is halved
 //   while one window's share of B would overflow an XCD's L2.
@@ -38,6 +38,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -296,7 +297,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, bf16_t*) 
 // lane gl loads column and value of entry p + (gl mod W) (W = min(LPR, 8);
 // groups of 4 lanes load two entries each), turns the column into a byte
 // offset into B, and the other lanes fetch offsets and values with
-// ds_bpermute.  Entries outside [q0, q1) and columns outside [0, k) get an
+// ds_swizzle.  Entries outside [q0, q1) and columns outside [0, k) get an
 // offset past the end of the buffer, which reads zeros without touching
 // memory, and a zero value; so every load is unconditional and the loop has
 // no branch but its exit.  The next batch's metadata is requested after this
@@ -331,6 +332,22 @@ __device__ __forceinline__ void load_meta(__amdgpu_buffer_rsrc_t crs, __amdgpu_b
   }
 }
 
+// Value of lane src (< W) of this lane's group, by ds_swizzle in bit-mask
+// mode: within each half-wave, lane i reads lane (i & and_mask) | src, the
+// and-mask keeping the bits that number the group.  Groups of 64 lanes work
+// as two halves whose lanes 0..W-1 hold the same metadata.
+template <int LPR, int SRC>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t v) {
+  constexpr int kAnd = LPR >= 32 ? 0 : (31 & ~(LPR - 1));
+  static_assert(SRC < (LPR < 32 ? LPR : 32), "source lane outside the group");
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, kAnd | (SRC << 5));
+}
+
+template <int LPR, int W, int U>
+struct Bcast {  // entry U of a batch: lane U mod W, slot U / W
+  __device__ static uint32_t get(const uint32_t* x) { return group_bcast<LPR, U % W>(x[U / W]); }
+};
+
 template <typename VT>
 struct GroupBatch {
   static constexpr int NV = sizeof(VT) == 2 ? 4 : 8;  // 16-bit values go in pairs
@@ -339,10 +356,18 @@ struct GroupBatch {
 };
 
 // Check the batch at entry p (metadata in m) and request its B vectors.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 template <typename VT, typename IT, int LPR>
 __device__ __forceinline__ void issue_group(__amdgpu_buffer_rsrc_t brs, int64_t k, uint32_t ldbb,
                                             const BatchMeta<LPR>& m, int p, int q1, int gl,
-                                            int lb4, uint32_t joff, GroupBatch<VT>& x) {
+                                            uint32_t joff, GroupBatch<VT>& x) {
   using M = BatchMeta<LPR>;
   uint32_t off[M::T], vb[M::T];
 #pragma unroll
@@ -357,18 +382,16 @@ __device__ __forceinline__ void issue_group(__amdgpu_buffer_rsrc_t brs, int64_t 
       vb[t] |= nb << 16;
     }
   }
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const uint32_t o =
-        (uint32_t)__builtin_amdgcn_ds_bpermute(lb4 + 4 * (u % M::W), (int)off[u / M::W]);
+  static_for<8>([&](auto u) {
+    const uint32_t o = Bcast<LPR, M::W, decltype(u)::value>::get(off);
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, o + joff, 0, 0);
     x.b[u] = make_uint4(v[0], v[1], v[2], v[3]);
-  }
-#pragma unroll
-  for (int q = 0; q < GroupBatch<VT>::NV; ++q) {
-    const int e = sizeof(VT) == 2 ? 2 * q : q;  // first entry of the pair / the entry
-    x.v[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(lb4 + 4 * (e % M::W), (int)vb[e / M::W]);
-  }
+  });
+  static_for<GroupBatch<VT>::NV>([&](auto q) {
+    // the entry (32-bit values) or the first entry of the pair (16-bit)
+    constexpr int e = sizeof(VT) == 2 ? 2 * decltype(q)::value : decltype(q)::value;
+    x.v[q] = Bcast<LPR, M::W, e>::get(vb);
+  });
 }
 
 template <typename VT>
@@ -405,17 +428,17 @@ struct GroupBufs {
 };
 
 // Entries [q0, q1) of one row into this lane's 16 bytes of columns (byte
-// offset joff within a B row).  lb4: 4 x the wave lane of the group's lane 0.
+// offset joff within a B row).
 template <typename VT, typename IT, int LPR>
 __device__ __forceinline__ void accumulate_buf(const SpmmArgs& a, const GroupBufs& rs,
-                                               uint32_t ldbb, int q0, int q1, int gl, int lb4,
+                                               uint32_t ldbb, int q0, int q1, int gl,
                                                uint32_t joff, float* acc) {
   if (q0 >= q1) return;
   BatchMeta<LPR> m;
   load_meta<VT, IT, LPR>(rs.c, rs.v, q0, gl, m);
   for (int p = q0; p < q1; p += 8) {
     GroupBatch<VT> x;
-    issue_group<VT, IT, LPR>(rs.b, a.k, ldbb, m, p, q1, gl, lb4, joff, x);
+    issue_group<VT, IT, LPR>(rs.b, a.k, ldbb, m, p, q1, gl, joff, x);
     __builtin_amdgcn_sched_barrier(0);
     load_meta<VT, IT, LPR>(rs.c, rs.v, p + 8, gl, m);
     __builtin_amdgcn_sched_barrier(0);
@@ -445,7 +468,6 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   // buffer path: lanes past column N read column 0 (results not stored)
   const uint32_t ldbb = (uint32_t)(a.ldb * (int64_t)sizeof(VT));
   const uint32_t joff = (uint32_t)((j < a.N ? j : 0) * (int64_t)sizeof(VT));
-  const int lb4 = (int)((threadIdx.x % kWave) / LPR * LPR * 4);
   GroupBufs brs;
   brs.b = make_rsrc(a.B, BUF ? (uint32_t)(a.k * a.ldb * (int64_t)sizeof(VT)) : 0u);
   brs.c = make_rsrc(a.col, BUF ? (uint32_t)(a.nnz * (int64_t)sizeof(IT)) : 0u);
@@ -468,7 +490,7 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
     q0 = q0 < c1 ? q0 : c1;
     q1 = q1 < c1 ? q1 : c1;
     if constexpr (BUF)
-      accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)q0, (int)q1, gl, lb4, joff, acc);
+      accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)q0, (int)q1, gl, joff, acc);
     else
       accumulate<VT, IT, VEC, ALIGNED>(a, q0, q1, j, acc);
     if (grp > 0) {
@@ -499,7 +521,7 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   row_range(a.ro, r, a.nnz, p0, p1);
   if (a.P > 0 && p1 - p0 > a.T) return;  // handled by the chunk blocks
   if constexpr (BUF)
-    accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)p0, (int)p1, gl, lb4, joff, acc);
+    accumulate_buf<VT, IT, LPR>(a, brs, ldbb, (int)p0, (int)p1, gl, joff, acc);
   else if constexpr (LPR == kWave && ALIGNED)
     accumulate_wave<VT, IT>(a, p0, p1, j, acc);
   else
@@ -983,8 +1005,18 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(SpmmArgs a) {
   const int64_t r = load_row(a.row_idx, a.ri_i32, i);
   if (r < 0 || r >= a.m) return;
   const int64_t g0 = a.split_start[s], g1 = a.split_end[s];
+  const float* pj = a.partial + j;
   float t = 0.f;
-  for (int64_t g = g0; g < g1; ++g) t += a.partial[g * a.N + j];
+  int64_t g = g0;
+  for (; g + 4 <= g1; g += 4) {  // four loads in flight, added in chunk order
+    const float v0 = pj[g * a.N], v1 = pj[(g + 1) * a.N], v2 = pj[(g + 2) * a.N],
+                v3 = pj[(g + 3) * a.N];
+    t += v0;
+    t += v1;
+    t += v2;
+    t += v3;
+  }
+  for (; g < g1; ++g) t += pj[g * a.N];
   ((OT*)a.C)[r * a.ldc + j] = from_f32<OT>(t);
 }
 
