@@ -78,6 +78,19 @@ __device__ __forceinline__ int load_index(const I* p, int64_t i) {
   return (int)p[i];
 }
 
+// --------------------------------------------------------- buffer loads --
+
+// Raw buffer resource over `bytes` bytes at p (dword 3 as for untyped 32-bit
+// data on gfx9).  Loads at offsets at or past `bytes` return zeros without a
+// memory access, which the kernels use to mask entries without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// An offset past the end of every buffer the kernels read this way (each is
+// under 2 GiB).
+constexpr uint32_t kOob = 0x80000000u;
+
 // ------------------------------------------------------------ wave tools --
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

@@ -276,11 +276,6 @@ struct BufLoad<16> {
   }
 };
 
-// Raw buffer descriptor (dword 3 as for untyped 32-bit data on gfx9).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, _Float16*) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
@@ -302,7 +297,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, bf16_t*) 
 // memory, and a zero value; so every load is unconditional and the loop has
 // no branch but its exit.  The next batch's metadata is requested after this
 // batch's B vectors and arrives while they are consumed.
-constexpr uint32_t kOob = 0x80000000u;  // past the end of any buffer this path takes
 
 template <int LPR>
 struct BatchMeta {
