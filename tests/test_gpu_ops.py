@@ -90,6 +90,20 @@ def test_transpose_bitexact(seed, m, n, density, dt, kw):
     assert np.array_equal(host(vT).view(np.uint8), ev.view(np.uint8))
 
 
+@pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (1, 3, 4)])
+def test_transpose_bitexact_16_byte_records(monkeypatch, seed, m, n, density, dt, kw):
+    # the first pass's 16-byte records (used when row numbers do not fit
+    # above the fine column digit), selected here by their switch
+    monkeypatch.setenv("SPOPS_TRANSPOSE_REC16", "1")
+    test_transpose_bitexact(seed, m, n, density, dt, kw)
+    vT = None
+    A = gen.random_csr(seed, m, n, density, dt, **kw)
+    v, ro, ci = csr_dev(A)
+    _, roT, ciT = S.csr_transpose(vT, ro, ci, m, n)
+    _, ero, eci = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx)
+    assert np.array_equal(host(roT), ero) and np.array_equal(host(ciT), eci)
+
+
 def test_transpose_pattern_only_and_twice():
     A = gen.random_csr(9, 700, 900, 0.03, "f32")
     v, ro, ci = csr_dev(A)

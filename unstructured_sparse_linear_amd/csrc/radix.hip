@@ -13,6 +13,10 @@
 // the digit bits) plus per-wave digit counts in LDS, so no atomics decide
 // any position and the output is deterministic.  No kernel waits on another
 // block, so no launch order assumptions are made.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -180,6 +184,20 @@ struct ValFromU32 {
   __device__ uint32_t operator()(int64_t i) const { return p[i]; }
 };
 
+// Second payload of a scatter: none, or the raw bits of a 2- or 4-byte value.
+struct NoPay {
+  __device__ uint32_t operator()(int64_t) const { return 0u; }
+};
+template <int VB>
+struct ValBits {  // VB == 0: no values (zero bits)
+  const void* p;
+  __device__ uint32_t operator()(int64_t i) const {
+    if constexpr (VB == 4) return ((const uint32_t*)p)[i];
+    else if constexpr (VB == 2) return (uint32_t)((const uint16_t*)p)[i];
+    else return 0u;
+  }
+};
+
 // Per-tile digit histogram, stored digit-major: counts[d * ntiles + tile].
 // Thread t takes kItems consecutive keys.
 template <class KS>
@@ -204,10 +222,15 @@ __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n,
 // then thread order == index order).  In a round each wave finds the lanes
 // holding the same digit with ballots; the lowest such lane publishes the
 // count; digit offsets per wave then follow from the running per-digit base.
-template <class KS, class VS>
+// RB != 0: a second payload VS2 too, and each entry goes out as one record
+// at kout (an array of n records), one store per entry: RB = 16, {key, pay,
+// pay2, 0}; RB = 8, {pay << shift | key's bits below shift, pay2} (pay below
+// 2^(32 - shift)).
+template <class KS, class VS, class VS2, int RB>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     KS ks, VS vs, int64_t n, int shift, int nbits, const uint32_t* offs, int64_t ntiles,
-    uint32_t* kout, uint32_t* vout) {
+    uint32_t* kout, uint32_t* vout, VS2 vs2) {
+  constexpr bool kTwo = RB != 0;
   __shared__ uint32_t base_d[kRadix];
   __shared__ uint32_t wcnt[kThreads / kWave][kRadix];
   const int t = threadIdx.x;
@@ -217,12 +240,13 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
   const int64_t tbase = (int64_t)blockIdx.x * kTile;
   const uint64_t lt = lanemask_lt();
   // all keys and payloads of the tile are loaded before the first round
-  uint32_t keys[kItems], pay[kItems];
+  uint32_t keys[kItems], pay[kItems], pay2[kTwo ? kItems : 1];
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const int64_t i = tbase + r * kThreads + t;
     keys[r] = i < n ? ks(i) : 0u;
     pay[r] = i < n ? vs(i) : 0u;
+    if constexpr (kTwo) pay2[r] = i < n ? vs2(i) : 0u;
   }
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
@@ -256,8 +280,15 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     __syncthreads();
     if (valid) {
       const uint32_t dst = wcnt[w][d] + rank;
-      kout[dst] = key;
-      vout[dst] = pay[r];
+      if constexpr (RB == 16) {
+        ((uint4*)kout)[dst] = make_uint4(key, pay[r], pay2[r], 0u);
+      } else if constexpr (RB == 8) {
+        ((uint2*)kout)[dst] =
+            make_uint2((pay[r] << shift) | (key & ((1u << shift) - 1u)), pay2[r]);
+      } else {
+        kout[dst] = key;
+        vout[dst] = pay[r];
+      }
     }
     __syncthreads();
   }
@@ -323,13 +354,13 @@ hipError_t radix_sort_iota(KS0 ks0, int64_t n, int bits, const RadixWs& R, int* 
     hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
     if (e != hipSuccess) return e;
     if (cur < 0) {
-      hipLaunchKernelGGL((radix_scatter_kernel<KS0, ValIota>), dim3(ntiles), dim3(kThreads), 0,
-                         s, ks0, ValIota{}, n, shift, nb, R.counts, ntiles, R.keys[dst],
-                         R.vals[dst]);
+      hipLaunchKernelGGL((radix_scatter_kernel<KS0, ValIota, NoPay, 0>), dim3(ntiles),
+                         dim3(kThreads), 0, s, ks0, ValIota{}, n, shift, nb, R.counts, ntiles,
+                         R.keys[dst], R.vals[dst], NoPay{});
     } else {
-      hipLaunchKernelGGL((radix_scatter_kernel<KeyFromU32, ValFromU32>), dim3(ntiles),
+      hipLaunchKernelGGL((radix_scatter_kernel<KeyFromU32, ValFromU32, NoPay, 0>), dim3(ntiles),
                          dim3(kThreads), 0, s, KeyFromU32{R.keys[cur]}, ValFromU32{R.vals[cur]},
-                         n, shift, nb, R.counts, ntiles, R.keys[dst], R.vals[dst]);
+                         n, shift, nb, R.counts, ntiles, R.keys[dst], R.vals[dst], NoPay{});
     }
     cur = dst;
     dst ^= 1;
@@ -375,42 +406,90 @@ __global__ __launch_bounds__(256) void transpose_finish_kernel(
 
 // Second stage of the two-level transpose.  The entries were stably grouped
 // by coarse column digit c >> SH (one radix pass); workgroup d now orders
-// bucket d by the fine digit c & (F - 1), F = 2^SH <= 512, with a stable
-// counting sort: fine-digit histogram, exclusive scan (which also gives the
-// output row offsets of the bucket's columns), then rounds of 1024 entries in
-// bucket order, each entry's rank among equal fine digits found with wave
-// ballots and per-wave counts.  Rows and values are gathered through the
-// source positions carried by the first pass.
+// bucket d by the fine digit c & (F - 1), F = 2^SH <= 512, stably.  The
+// bucket is cut into one contiguous slice per wave.  Each wave counts the
+// fine digits of its slice (its own row of an LDS table); one pass over the
+// table gives, per digit, the count in earlier slices, and a scan over the
+// digit totals gives the bucket's output row offsets.  Then every wave walks
+// its slice in rounds of 64 entries with no further barrier: an entry's rank
+// among equal digits of the round comes from wave ballots, its destination
+// is digit base + earlier slices + the wave's running count, and the first
+// lane of each digit advances that count.  The first pass wrote each
+// entry's column, row and value bits as one 16-byte record, so the slice is
+// read sequentially, four rounds ahead of their use.
 constexpr int kFinishThreads = 1024;
 constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kMaxFine = 512;
 
-template <typename OI, int VB>
+// Records as the first pass wrote them (RB = 8 or 16 bytes, see
+// radix_scatter_kernel): fine digit, row and value bits of each entry.
+template <int RB>
+struct Rec;
+template <>
+struct Rec<16> {
+  uint4 r;
+  __device__ uint32_t fine(uint32_t fmask, int) const { return r.x & fmask; }
+  __device__ uint32_t row(int) const { return r.y; }
+  __device__ uint32_t bits() const { return r.z; }
+};
+template <>
+struct Rec<8> {
+  uint2 r;
+  __device__ uint32_t fine(uint32_t fmask, int) const { return r.x & fmask; }
+  __device__ uint32_t row(int sh) const { return r.x >> sh; }
+  __device__ uint32_t bits() const { return r.y; }
+};
+
+template <typename OI, int VB, int RB>
 __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
-    const uint32_t* keys, const uint32_t* src, const uint32_t* offs, int64_t ntiles,
-    const uint32_t* rows_of, int64_t nnz, int64_t n, int sh, const uint8_t* val, uint8_t* out_val,
-    int32_t* out_ro, OI* out_col) {
+    const Rec<RB>* rec, const uint32_t* offs, int64_t ntiles, int64_t nnz, int64_t n, int sh,
+    uint8_t* out_val, int32_t* out_ro, OI* out_col) {
   __shared__ uint32_t base_f[kMaxFine];
   __shared__ uint32_t wcnt[kFinishWaves][kMaxFine];
   __shared__ uint32_t wsum[kMaxFine / kWave];
-  const int t = threadIdx.x, w = t / kWave;
+  const int t = threadIdx.x, w = t / kWave, lane = lane_id();
   const int d = blockIdx.x;
   const int F = 1 << sh;
   const uint32_t fmask = (uint32_t)F - 1u;
   const int64_t bs = offs[(int64_t)d * ntiles];
   const int64_t be = d + 1 < kRadix ? (int64_t)offs[(int64_t)(d + 1) * ntiles] : nnz;
   const uint64_t lt = lanemask_lt();
-  for (int f = t; f < F; f += kFinishThreads) base_f[f] = 0;
+  for (int k = t; k < kFinishWaves * F; k += kFinishThreads) wcnt[k / F][k % F] = 0;
   __syncthreads();
-  for (int64_t q = bs + t; q < be; q += kFinishThreads) atomicAdd(&base_f[keys[q] & fmask], 1u);
+  // this wave's slice [s0, s1) of the bucket
+  const int64_t len = be - bs;
+  const int64_t L = cdiv(len, (int64_t)kFinishWaves);
+  const int64_t s0 = bs + (w * L < len ? w * L : len);
+  const int64_t s1 = bs + ((w + 1) * L < len ? (w + 1) * L : len);
+  // per-slice digit counts, eight key loads in flight per lane
+  for (int64_t q = s0 + lane; q < s1; q += 8 * kWave) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t qi = q + (int64_t)i * kWave;
+      kk[i] = rec[qi < s1 ? qi : s1 - 1].r.x;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q + (int64_t)i * kWave < s1) atomicAdd(&wcnt[w][kk[i] & fmask], 1u);
+  }
   __syncthreads();
-  // exclusive scan of the F fine counts (F <= 512: waves 0..7)
+  // per digit: counts of earlier slices; digit totals scanned over digits
   const int fpad = F < kWave ? kWave : F;
   uint32_t cnt = 0, inc = 0;
   if (t < fpad) {
-    cnt = t < F ? base_f[t] : 0u;
+    if (t < F) {
+      uint32_t run = 0;
+#pragma unroll
+      for (int ww = 0; ww < kFinishWaves; ++ww) {
+        const uint32_t c = wcnt[ww][t];
+        wcnt[ww][t] = run;
+        run += c;
+      }
+      cnt = run;
+    }
     inc = wave_inclusive_sum(cnt);
-    if (lane_id() == kWave - 1) wsum[w] = inc;
+    if (lane == kWave - 1) wsum[w] = inc;
   }
   __syncthreads();
   if (t < F) {
@@ -422,43 +501,43 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
   }
   if (d == 0 && t == 0) out_ro[n] = (int32_t)nnz;
   __syncthreads();
-  for (int64_t r0 = bs; r0 < be; r0 += kFinishThreads) {
-    for (int k = t; k < kFinishWaves * F; k += kFinishThreads) wcnt[k / F][k % F] = 0;
-    __syncthreads();
-    const int64_t q = r0 + t;
-    const bool valid = q < be;
-    const uint32_t f = valid ? (keys[q] & fmask) : 0u;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < sh; ++b) {
-      const bool bit = (f >> b) & 1u;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    const uint32_t rank = (uint32_t)__popcll(peers & lt);
-    if (valid && rank == 0) wcnt[w][f] = (uint32_t)__popcll(peers);
-    __syncthreads();
-    for (int f2 = t; f2 < F; f2 += kFinishThreads) {
-      uint32_t run = base_f[f2];
+  if (s0 >= s1) return;
+  // rounds of 64 entries, taken four at a time: the records of the next four
+  // rounds are requested before the current four are ranked and written
+  constexpr int kSub = 4;
+  auto clampq = [&](int64_t q) { return q < s1 ? q : s0; };
+  Rec<RB> cur[kSub];
 #pragma unroll
-      for (int ww = 0; ww < kFinishWaves; ++ww) {
-        const uint32_t c = wcnt[ww][f2];
-        wcnt[ww][f2] = run;
-        run += c;
+  for (int j = 0; j < kSub; ++j) cur[j] = rec[clampq(s0 + j * kWave + lane)];
+  for (int64_t qb = s0; qb < s1; qb += kSub * kWave) {
+    Rec<RB> nxt[kSub];
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) nxt[j] = rec[clampq(qb + (kSub + j) * kWave + lane)];
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      const bool valid = qb + j * kWave + lane < s1;
+      const uint32_t f = valid ? cur[j].fine(fmask, sh) : 0u;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < sh; ++b) {
+        const bool bit = (f >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
       }
-      base_f[f2] = run;
-    }
-    __syncthreads();
-    if (valid) {
-      const int64_t dst = bs + wcnt[w][f] + rank;
-      const uint32_t p = src[q];
-      out_col[dst] = (OI)rows_of[p];
-      if constexpr (VB == 4) {
-        ((uint32_t*)out_val)[dst] = ((const uint32_t*)val)[p];
-      } else if constexpr (VB == 2) {
-        ((uint16_t*)out_val)[dst] = ((const uint16_t*)val)[p];
+      const uint32_t rank = (uint32_t)__popcll(peers & lt);
+      const uint32_t before = wcnt[w][f];
+      if (valid) {
+        const int64_t dst = bs + base_f[f] + before + rank;
+        out_col[dst] = (OI)cur[j].row(sh);
+        if constexpr (VB == 4) {
+          ((uint32_t*)out_val)[dst] = cur[j].bits();
+        } else if constexpr (VB == 2) {
+          ((uint16_t*)out_val)[dst] = (uint16_t)cur[j].bits();
+        }
+        if (rank == 0) wcnt[w][f] = before + (uint32_t)__popcll(peers);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) cur[j] = nxt[j];
   }
 }
 
@@ -467,25 +546,22 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, in
   if (i < n) p[i] = v;
 }
 
-template <typename OI>
-hipError_t launch_bucket_finish(const uint32_t* keys, const uint32_t* src, const uint32_t* offs,
-                                int64_t ntiles, const uint32_t* rows_of, int64_t nnz, int64_t n,
-                                int sh, const void* val, int vb, void* out_val, int32_t* out_ro,
-                                void* out_col, hipStream_t s) {
+template <typename OI, int RB>
+hipError_t launch_bucket_finish(const void* rec, const uint32_t* offs, int64_t ntiles,
+                                int64_t nnz, int64_t n, int sh, int vb, void* out_val,
+                                int32_t* out_ro, void* out_col, hipStream_t s) {
   const dim3 grid((unsigned)cdiv(n, (int64_t)1 << sh));
   const dim3 blk(kFinishThreads);
+  const Rec<RB>* r = (const Rec<RB>*)rec;
   if (vb == 4)
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 4>), grid, blk, 0, s, keys, src, offs, ntiles,
-                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
-                       (OI*)out_col);
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 4, RB>), grid, blk, 0, s, r, offs, ntiles,
+                       nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   else if (vb == 2)
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 2>), grid, blk, 0, s, keys, src, offs, ntiles,
-                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
-                       (OI*)out_col);
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 2, RB>), grid, blk, 0, s, r, offs, ntiles,
+                       nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   else
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 0>), grid, blk, 0, s, keys, src, offs, ntiles,
-                       rows_of, nnz, n, sh, (const uint8_t*)val, (uint8_t*)out_val, out_ro,
-                       (OI*)out_col);
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 0, RB>), grid, blk, 0, s, r, offs, ntiles,
+                       nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   return hipGetLastError();
 }
 
@@ -790,30 +866,50 @@ hipError_t transpose_two_level(int64_t rows, int64_t cols, int64_t nnz, const in
   const int64_t ntiles = cdiv(nnz, kTile);
   hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
                      ro, rows, nnz, rows_of);
+  // first pass: columns with their rows and value bits, one record per entry
+  // over the key and payload buffers of the workspace (which lie back to
+  // back and hold at least 16 bytes per entry): 8 bytes while the row
+  // numbers fit above the fine digit, else 16
+  uint32_t* rec = R.keys[0];
+  // (SPOPS_TRANSPOSE_REC16=1, read per call, selects 16 for its test)
+  const char* r16 = getenv("SPOPS_TRANSPOSE_REC16");
+  const bool rec8 = rows <= ((int64_t)1 << (32 - sh)) && !(r16 && r16[0] == '1');
+  auto scatter = [&](auto ks, auto rb) -> hipError_t {
+    using KS = decltype(ks);
+    constexpr int RB = decltype(rb)::value;
+    hipLaunchKernelGGL(radix_count_kernel<KS>, dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks,
+                       nnz, sh, 0xffu, R.counts, ntiles);
+    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
+    if (e != hipSuccess) return e;
+    const ValFromU32 rowpay{rows_of};
+    if (vb == 4)
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<4>, RB>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<4>{val});
+    else if (vb == 2)
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<2>, RB>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<2>{val});
+    else
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<0>, RB>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<0>{nullptr});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (out_col_i32)
+      return launch_bucket_finish<int32_t, RB>(rec, R.counts, ntiles, nnz, cols, sh, vb, out_val,
+                                               out_ro, out_col, s);
+    return launch_bucket_finish<int16_t, RB>(rec, R.counts, ntiles, nnz, cols, sh, vb, out_val,
+                                             out_ro, out_col, s);
+  };
+  using R8 = std::integral_constant<int, 8>;
+  using R16 = std::integral_constant<int, 16>;
   if (col_i32) {
-    KeyFromIndex<int32_t> ks{(const int32_t*)col, (int32_t)(cols - 1)};
-    hipLaunchKernelGGL(radix_count_kernel<KeyFromIndex<int32_t>>, dim3((unsigned)ntiles),
-                       dim3(kThreads), 0, s, ks, nnz, sh, 0xffu, R.counts, ntiles);
-    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((radix_scatter_kernel<KeyFromIndex<int32_t>, ValIota>),
-                       dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, ValIota{}, nnz, sh,
-                       kRadixBits, R.counts, ntiles, R.keys[0], R.vals[0]);
-  } else {
-    KeyFromIndex<int16_t> ks{(const int16_t*)col, (int32_t)(cols - 1)};
-    hipLaunchKernelGGL(radix_count_kernel<KeyFromIndex<int16_t>>, dim3((unsigned)ntiles),
-                       dim3(kThreads), 0, s, ks, nnz, sh, 0xffu, R.counts, ntiles);
-    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((radix_scatter_kernel<KeyFromIndex<int16_t>, ValIota>),
-                       dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, ValIota{}, nnz, sh,
-                       kRadixBits, R.counts, ntiles, R.keys[0], R.vals[0]);
+    const KeyFromIndex<int32_t> ks{(const int32_t*)col, (int32_t)(cols - 1)};
+    return rec8 ? scatter(ks, R8{}) : scatter(ks, R16{});
   }
-  if (out_col_i32)
-    return launch_bucket_finish<int32_t>(R.keys[0], R.vals[0], R.counts, ntiles, rows_of, nnz,
-                                         cols, sh, val, vb, out_val, out_ro, out_col, s);
-  return launch_bucket_finish<int16_t>(R.keys[0], R.vals[0], R.counts, ntiles, rows_of, nnz, cols,
-                                       sh, val, vb, out_val, out_ro, out_col, s);
+  const KeyFromIndex<int16_t> ks{(const int16_t*)col, (int32_t)(cols - 1)};
+  return rec8 ? scatter(ks, R8{}) : scatter(ks, R16{});
 }
 
 hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
