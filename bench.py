@@ -638,13 +638,15 @@ def main():
     # the whole step, captured once and replayed
     # Independent operations run on separate streams inside the graph (fork
     # from the capturing stream, join at the end of the step): with two
-    # streams the two gather-bound products share one and the short
-    # launch-bound operations (csr_add, transpose, then the row order of A^T,
-    # which needs the transpose) take the other; with three, SpMM and SDDMM
-    # get one each.  Default stream priorities.
+    # streams the two gather-bound products share one, longest (by the cold
+    # times just measured) first, and the short launch-bound operations
+    # (csr_add, transpose, then the row order of A^T, which needs the
+    # transpose) take the other; with three, SpMM and SDDMM get one each.
+    # Default stream priorities.
     graph = None
     side_ops = [o for o in ops if o in ("csr_add", "transpose", "row_order")]
-    main_ops = [o for o in ops if o not in side_ops]
+    main_ops = sorted([o for o in ops if o not in side_ops],
+                      key=lambda o: -float(np.median(per_op[o])))
     nstreams = 1 if args.serial_step or not side_ops or not main_ops else args.streams
     lanes = ([ops] if nstreams == 1 else [main_ops, side_ops] if nstreams == 2
              else [[o] for o in main_ops] + [side_ops])
