@@ -129,6 +129,21 @@ KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "spmv": ["spmm.hip", "common.h
                 "row_order": ["radix.hip", "common.h"]}
 
 
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "mfma_busy.json")
+
+
+def mfma_busy_for(op, config):
+    """MFMA busy fraction of the structure-aware SDDMM's tile kernel from the
+    committed counter run (profiles/mfma_busy.json), while the kernel sources
+    still match the ones it was taken on; else None."""
+    if op != "sddmm" or not os.path.exists(MFMA_COUNTERS):
+        return None
+    ent = json.load(open(MFMA_COUNTERS)).get(f"config{config}")
+    if not ent or ent.get("source_sha") != kernel_sources_sha(KERNEL_FILES[op]):
+        return None
+    return ent.get("mfma_busy_frac")
+
+
 def op_kernels(spmm_info, sddmm_info, m, nnz):
     """Kernels one call of each operation launches (names as in rocprofv3)."""
     spmm = ["spmm_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else [])
@@ -490,7 +505,7 @@ def write_records(path, result, args, A, dt, N, K, ab, fl):
                 "frac_hbm_copy": round(b["gbps"] / copy, 4) if copy else None,
                 "hbm_bytes_counters": traffic,
                 "refetch": round(traffic / b["alg_bytes"], 2) if traffic else None,
-                "mfma_busy": None,
+                "mfma_busy": mfma_busy_for(op, args.config),
                 "oracle_s": (cpu.get("ms_per_op", {}).get(op, 0) / 1e3) if cpu else None,
                 "oracle_threads": cpu.get("cores"), "cpu_model": cpu_model() if cpu else None,
                 "max_rel_err": None, "normwise_err": None, "bitexact_idx": None,

@@ -252,10 +252,11 @@ _ws_pool = {}
 
 
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """Scratch device memory reused across calls of the same size."""
+    """Scratch device memory reused across calls of the same size on the same
+    stream (calls on one stream run in order, so they never overlap)."""
     if nbytes == 0:
         return None
-    key = (str(device), nbytes)
+    key = (str(device), nbytes, torch.cuda.current_stream(device).cuda_stream)
     if key not in _ws_pool:
         _ws_pool[key] = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return _ws_pool[key]
