@@ -349,7 +349,7 @@ struct GroupBatch {
   uint32_t v[NV];
 };
 
-// Check the batch at entry p (metadata in m) and request its B vectors.
+// f(integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (N > 0) {
@@ -358,6 +358,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Check the batch at entry p (metadata in m) and request its B vectors.
 template <typename VT, typename IT, int LPR>
 __device__ __forceinline__ void issue_group(__amdgpu_buffer_rsrc_t brs, int64_t k, uint32_t ldbb,
                                             const BatchMeta<LPR>& m, int p, int q1, int gl,
