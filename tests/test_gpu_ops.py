@@ -187,6 +187,18 @@ def test_spmm_long_rows(dt, N, use_plan):
         assert info["max_row_nnz"] == 4500 and info["split_rows"] == 6
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_spmm_many_column_windows(dt):
+    # k = 9000 rows of B with N = 2048: 16-lane groups, 16 windows of 128
+    # columns, which the XCDs take two at a time in sequence; long rows
+    # exercise the chunk blocks under the same mapping
+    A = heavy_csr(16, 200, 9000, [3000, 1200, 700, 513, 129], dt)
+    B = gen.dense(16, 100, gen.S_B, (9000, 2048), dt)
+    C = run_spmm(A, B, dt)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert_close(host_f64(C), ref, dt, "spmm 16 windows")
+
+
 @pytest.mark.parametrize("dt,N", [("f32", 64), ("bf16", 256), ("f16", 24), ("f32", 8)])
 def test_spmm_pointer_load_path(monkeypatch, dt, N):
     # the group kernel's path for operands of 2 GiB and more (pointer loads,

@@ -454,8 +454,20 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
   constexpr int GPB = kBlock / LPR;  // groups per block
   const int grp = threadIdx.x / LPR;
   const int gl = threadIdx.x % LPR;
-  const int64_t bx = (int64_t)blockIdx.x / nwin;
-  const int64_t win = (int64_t)blockIdx.x % nwin;
+  // Window w runs on the XCD(s) w mod 8 (block b is on XCD b mod 8).  With
+  // more than 8 windows (a multiple of 8), XCD x takes its windows x, x + 8,
+  // ... one after the other rather than interleaved, so its L2 holds one
+  // window's share of B at a time.
+  const int64_t nblk = (int64_t)gridDim.x / nwin;  // blocks per window
+  int64_t bx, win;
+  if (nwin > 8 && nwin % 8 == 0) {
+    const int64_t k = (int64_t)blockIdx.x / 8;
+    win = (int64_t)blockIdx.x % 8 + 8 * (k / nblk);
+    bx = k % nblk;
+  } else {
+    bx = (int64_t)blockIdx.x / nwin;
+    win = (int64_t)blockIdx.x % nwin;
+  }
   const int64_t j = win * (LPR * VEC) + (int64_t)gl * VEC;
   float acc[VEC];
 #pragma unroll
@@ -507,7 +519,7 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
     }
     return;
   }
-  const int64_t nbw = (int64_t)gridDim.x / nwin - a.P;
+  const int64_t nbw = nblk - a.P;
   const int64_t i = row_block(bx - a.P, nbw, a.natural) * GPB + grp;
   if (i >= a.m) return;
   const int64_t r = a.natural ? i : load_row(a.row_idx, a.ri_i32, i);
