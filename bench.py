@@ -144,7 +144,20 @@ def mfma_busy_for(op, config):
     return ent.get("mfma_busy_frac")
 
 
-def op_kernels(spmm_info, sddmm_info, m, nnz):
+def transpose_kernels(n, nnz):
+    """Kernels of one csr_transpose (up to 2^17 columns: count with row
+    expansion, a scan of the count table above 128 tiles of 2048 entries,
+    scatter, bucket finish; wider: full LSD passes)."""
+    if n > 1 << 17:
+        return ["expand_rows_kernel", "radix_count_kernel", "scan_*", "radix_scatter_kernel",
+                "transpose_finish_kernel"]
+    tiles = -(-nnz // 2048)
+    scan = ([] if tiles <= 128 else ["scan_single_kernel"] if tiles * 256 <= 65536
+            else ["scan_local_kernel", "scan_add_kernel"])
+    return ["transpose_count_kernel"] + scan + ["radix_scatter_kernel", "transpose_bucket_kernel"]
+
+
+def op_kernels(spmm_info, sddmm_info, m, n, nnz):
     """Kernels one call of each operation launches (names as in rocprofv3)."""
     spmm = ["spmm_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else [])
     # N == 1: row blocks through LDS when the plan finds the rows balanced
@@ -158,8 +171,7 @@ def op_kernels(spmm_info, sddmm_info, m, nnz):
              + (["sddmm_list_kernel"] if sddmm_info.get("rest_nnz", 0) else []))
     return {"spmm": spmm, "spmv": spmv, "sddmm": sddmm or ["sddmm_list_kernel"],
             "csr_add": ["csr_add_kernel"],
-            "transpose": ["expand_rows_kernel", "radix_count_kernel", "scan_single_kernel",
-                          "radix_scatter_kernel", "transpose_bucket_kernel"],
+            "transpose": transpose_kernels(n, nnz),
             "row_order": ["sort_rows_block_kernel"]}
 
 
@@ -724,7 +736,7 @@ def main():
     # the dominant kernel: the longer of SpMM and SDDMM (the operations the
     # metric is about; each is one kernel unless long rows are split or the
     # mask has dense tiles, and then its kernels are listed together)
-    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.nnz)
+    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.n, A.nnz)
     gated = [o for o in ops if o in ("spmm", "spmv", "sddmm")]
     dom = max(gated or ops, key=lambda o: breakdown[o]["ms"])
     achieved = ab[dom] / breakdown[dom]["ms"] / 1e6

@@ -81,13 +81,40 @@ TRANSPOSE_CASES = [
 
 @pytest.mark.parametrize("seed,m,n,density,dt,kw", TRANSPOSE_CASES)
 def test_transpose_bitexact(seed, m, n, density, dt, kw):
-    A = gen.random_csr(seed, m, n, density, dt, **kw)
+    check_transpose_exact(gen.random_csr(seed, m, n, density, dt, **kw))
+
+
+def check_transpose_exact(A):
     v, ro, ci = csr_dev(A)
-    vT, roT, ciT = S.csr_transpose(v, ro, ci, m, n)
-    ev, ero, eci = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx, A.values)
+    vT, roT, ciT = S.csr_transpose(v, ro, ci, A.m, A.n)
+    ev, ero, eci = oracle.csr_transpose(A.m, A.n, A.row_offsets, A.col_idx, A.values)
     assert np.array_equal(host(roT), ero)
     assert np.array_equal(host(ciT), eci)
     assert np.array_equal(host(vT).view(np.uint8), ev.view(np.uint8))
+
+
+def exact_nnz_csr(seed, m, n, nnz, dt):
+    """CSR with exactly nnz entries spread over the rows at random."""
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(nnz, np.full(m, 1.0 / m))
+    rows = [np.sort(rng.choice(n, int(c), replace=False)) for c in counts]
+    A = gen.csr_from_row_lists(m, n, rows)
+    return A.with_values(gen.normal(rng, A.nnz, dt), dt)
+
+
+@pytest.mark.parametrize("nnz", [128 * 2048, 128 * 2048 + 1])
+def test_transpose_single_pass_tile_limit(nnz):
+    # 128 tiles of 2048 entries is the most whose scatter derives its own
+    # offsets from the count table; one entry more takes the scan
+    check_transpose_exact(exact_nnz_csr(11, 2048, 3000, nnz, "bf16"))
+
+
+@pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (0, 3, 4, 5)])
+def test_transpose_bitexact_scan_path(monkeypatch, seed, m, n, density, dt, kw):
+    # small inputs through the scan between count and scatter, selected by
+    # its switch
+    monkeypatch.setenv("SPOPS_TRANSPOSE_SCAN", "1")
+    test_transpose_bitexact(seed, m, n, density, dt, kw)
 
 
 @pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (1, 3, 4)])

@@ -218,6 +218,47 @@ __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n,
   counts[(int64_t)t * ntiles + blockIdx.x] = hist[t];
 }
 
+// First pass of the two-level transpose: the digit counts of tile b (blocks
+// b < ntiles) and, for rows [b*rpb, (b+1)*rpb), the row owning every stored
+// position (rows_of), so no separate launch expands the row offsets.  TM: counts stored tile-major, counts[tile * kRadix + d] (the
+// layout radix_scatter_kernel reads when it derives its own offsets), else
+// digit-major like radix_count_kernel.
+template <class KS, bool TM>
+__global__ __launch_bounds__(kThreads) void transpose_count_kernel(
+    KS ks, int64_t n, int shift, uint32_t mask, uint32_t* counts, int64_t ntiles,
+    const int32_t* __restrict__ ro, int64_t m, int64_t rpb, uint32_t* __restrict__ rows_of) {
+  __shared__ uint32_t hist[kRadix];
+  __shared__ int32_t rol[kThreads + 1];  // the block's row offsets
+  const int t = threadIdx.x;
+  const bool tile = blockIdx.x < ntiles;
+  hist[t] = 0;
+  const int64_t i0 = (int64_t)blockIdx.x * kTile + (int64_t)t * kItems;
+  uint32_t key[kItems];
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) key[q] = tile && i0 + q < n ? ks(i0 + q) : 0u;
+  // rpb <= kThreads: the rpb + 1 offsets are read in one round
+  const int64_t r0 = (int64_t)blockIdx.x * rpb;
+  const int nr = (int)(r0 >= m ? 0 : (m - r0 < rpb ? m - r0 : rpb));
+  if (t <= nr) rol[t] = ro[r0 + t];
+  if (t == 0 && nr == kThreads) rol[kThreads] = ro[r0 + kThreads];
+  __syncthreads();
+  // one wave per row (loop bounds are wave-uniform)
+  const int w = t / kWave, lane = lane_id();
+  for (int j = w; j < nr; j += kThreads / kWave) {
+    int64_t p0 = rol[j], p1 = rol[j + 1];
+    p0 = p0 < 0 ? 0 : p0;
+    p1 = p1 > n ? n : p1;
+    for (int64_t p = p0 + lane; p < p1; p += kWave) rows_of[p] = (uint32_t)(r0 + j);
+  }
+  __syncthreads();
+  if (!tile) return;
+#pragma unroll
+  for (int q = 0; q < kItems; ++q)
+    if (i0 + q < n) atomicAdd(&hist[(key[q] >> shift) & mask], 1u);
+  __syncthreads();
+  counts[TM ? (int64_t)blockIdx.x * kRadix + t : (int64_t)t * ntiles + blockIdx.x] = hist[t];
+}
+
 // Stable scatter.  Keys of a tile are taken in rounds of kThreads (round-major,
 // then thread order == index order).  In a round each wave finds the lanes
 // holding the same digit with ballots; the lowest such lane publishes the
@@ -226,17 +267,25 @@ __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n,
 // at kout (an array of n records), one store per entry: RB = 16, {key, pay,
 // pay2, 0}; RB = 8, {pay << shift | key's bits below shift, pay2} (pay below
 // 2^(32 - shift)).
-template <class KS, class VS, class VS2, int RB>
+//
+// SELF (single pass, ntiles <= kSelfMaxTiles): `offs` holds the raw digit
+// counts, tile-major, and every workgroup derives its own offsets from the
+// whole table: base of digit d in tile b = (entries of all digits below d) +
+// (entries of digit d in tiles below b).  Workgroup 0 also stores the digit
+// starts to bstart[0..kRadix), which replaces the scan launch.
+constexpr int64_t kSelfMaxTiles = 128;
+
+template <class KS, class VS, class VS2, int RB, bool SELF = false>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     KS ks, VS vs, int64_t n, int shift, int nbits, const uint32_t* offs, int64_t ntiles,
-    uint32_t* kout, uint32_t* vout, VS2 vs2) {
+    uint32_t* kout, uint32_t* vout, VS2 vs2, uint32_t* bstart = nullptr) {
   constexpr bool kTwo = RB != 0;
   __shared__ uint32_t base_d[kRadix];
   __shared__ uint32_t wcnt[kThreads / kWave][kRadix];
   const int t = threadIdx.x;
   const int w = t / kWave;
   const uint32_t mask = (1u << nbits) - 1u;
-  base_d[t] = offs[(int64_t)t * ntiles + blockIdx.x];
+  if constexpr (!SELF) base_d[t] = offs[(int64_t)t * ntiles + blockIdx.x];
   const int64_t tbase = (int64_t)blockIdx.x * kTile;
   const uint64_t lt = lanemask_lt();
   // all keys and payloads of the tile are loaded before the first round
@@ -247,6 +296,53 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     keys[r] = i < n ? ks(i) : 0u;
     pay[r] = i < n ? vs(i) : 0u;
     if constexpr (kTwo) pay2[r] = i < n ? vs2(i) : 0u;
+  }
+  if constexpr (SELF) {
+    // thread t sums digits 4*(t % 64) .. +3 over tiles t/64, t/64 + 4, ...
+    // (16-byte loads, up to 32 per thread, all in flight together), split
+    // into tiles below this one and all tiles; the four phases meet in LDS.
+    __shared__ uint4 part[2 * 4 * kWave];  // [pre, all][phase][lane]
+    const int q = t % kWave, ph = t / kWave;
+    constexpr int kLoads = (int)(kSelfMaxTiles / 4);
+    uint4 c[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int64_t tl = ph + 4 * j;
+      c[j] = tl < ntiles ? ((const uint4*)offs)[tl * (kRadix / 4) + q] : make_uint4(0, 0, 0, 0);
+    }
+    uint4 pre = make_uint4(0, 0, 0, 0), tot = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      tot.x += c[j].x;
+      tot.y += c[j].y;
+      tot.z += c[j].z;
+      tot.w += c[j].w;
+      if (ph + 4 * j < (int64_t)blockIdx.x) {
+        pre.x += c[j].x;
+        pre.y += c[j].y;
+        pre.z += c[j].z;
+        pre.w += c[j].w;
+      }
+    }
+    part[ph * kWave + q] = pre;
+    part[(4 + ph) * kWave + q] = tot;
+    __syncthreads();
+    // thread t now owns digit t
+    const uint32_t* pw = (const uint32_t*)part;
+    uint32_t dpre = 0, dtot = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      dpre += pw[(p * kWave + t / 4) * 4 + t % 4];
+      dtot += pw[((4 + p) * kWave + t / 4) * 4 + t % 4];
+    }
+    const uint32_t inc = wave_inclusive_sum(dtot);
+    if (lane_id() == kWave - 1) wcnt[0][w] = inc;
+    __syncthreads();
+    uint32_t below = inc - dtot;
+    for (int ww = 0; ww < w; ++ww) below += wcnt[0][ww];
+    base_d[t] = below + dpre;
+    if (blockIdx.x == 0) bstart[t] = below;
+    __syncthreads();
   }
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
@@ -406,7 +502,8 @@ __global__ __launch_bounds__(256) void transpose_finish_kernel(
 
 // Second stage of the two-level transpose.  The entries were stably grouped
 // by coarse column digit c >> SH (one radix pass); workgroup d now orders
-// bucket d by the fine digit c & (F - 1), F = 2^SH <= 512, stably.  The
+// bucket d by the fine digit c & (F - 1), F = 2^SH <= 512, stably; bucket d
+// starts at bstart[d * bstride] and ends where bucket d + 1 starts.  The
 // bucket is cut into one contiguous slice per wave.  Each wave counts the
 // fine digits of its slice (its own row of an LDS table); one pass over the
 // table gives, per digit, the count in earlier slices, and a scan over the
@@ -442,7 +539,7 @@ struct Rec<8> {
 
 template <typename OI, int VB, int RB>
 __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
-    const Rec<RB>* rec, const uint32_t* offs, int64_t ntiles, int64_t nnz, int64_t n, int sh,
+    const Rec<RB>* rec, const uint32_t* bstart, int64_t bstride, int64_t nnz, int64_t n, int sh,
     uint8_t* out_val, int32_t* out_ro, OI* out_col) {
   __shared__ uint32_t base_f[kMaxFine];
   __shared__ uint32_t wcnt[kFinishWaves][kMaxFine];
@@ -451,8 +548,8 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
   const int d = blockIdx.x;
   const int F = 1 << sh;
   const uint32_t fmask = (uint32_t)F - 1u;
-  const int64_t bs = offs[(int64_t)d * ntiles];
-  const int64_t be = d + 1 < kRadix ? (int64_t)offs[(int64_t)(d + 1) * ntiles] : nnz;
+  const int64_t bs = bstart[(int64_t)d * bstride];
+  const int64_t be = d + 1 < kRadix ? (int64_t)bstart[(int64_t)(d + 1) * bstride] : nnz;
   const uint64_t lt = lanemask_lt();
   for (int k = t; k < kFinishWaves * F; k += kFinishThreads) wcnt[k / F][k % F] = 0;
   __syncthreads();
@@ -547,20 +644,20 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, in
 }
 
 template <typename OI, int RB>
-hipError_t launch_bucket_finish(const void* rec, const uint32_t* offs, int64_t ntiles,
+hipError_t launch_bucket_finish(const void* rec, const uint32_t* bstart, int64_t bstride,
                                 int64_t nnz, int64_t n, int sh, int vb, void* out_val,
                                 int32_t* out_ro, void* out_col, hipStream_t s) {
   const dim3 grid((unsigned)cdiv(n, (int64_t)1 << sh));
   const dim3 blk(kFinishThreads);
   const Rec<RB>* r = (const Rec<RB>*)rec;
   if (vb == 4)
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 4, RB>), grid, blk, 0, s, r, offs, ntiles,
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 4, RB>), grid, blk, 0, s, r, bstart, bstride,
                        nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   else if (vb == 2)
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 2, RB>), grid, blk, 0, s, r, offs, ntiles,
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 2, RB>), grid, blk, 0, s, r, bstart, bstride,
                        nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   else
-    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 0, RB>), grid, blk, 0, s, r, offs, ntiles,
+    hipLaunchKernelGGL((transpose_bucket_kernel<OI, 0, RB>), grid, blk, 0, s, r, bstart, bstride,
                        nnz, n, sh, (uint8_t*)out_val, out_ro, (OI*)out_col);
   return hipGetLastError();
 }
@@ -848,24 +945,34 @@ hipError_t radix_sort_u32_iota(const uint32_t* keys, int64_t n, int bits, uint32
 size_t transpose_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz) {
   (void)rows;
   (void)cols;
-  return radix_ws_bytes_for(nnz) + align256((size_t)nnz * 4);
+  // radix buffers, rows_of, and the coarse bucket starts of the single-pass
+  // first stage
+  return radix_ws_bytes_for(nnz) + align256((size_t)nnz * 4) + align256(kRadix * 4);
 }
 
 // Two-level transpose for up to 2^17 columns: one stable radix pass on the
 // top 8 bits of the column, then one workgroup per coarse bucket orders it by
-// the remaining <= 9 bits (transpose_bucket_kernel).  Five launches: row
-// expansion, digit counts, scan, scatter, bucket finish.
+// the remaining <= 9 bits (transpose_bucket_kernel).  The first launch counts
+// digits per tile and expands the row offsets into rows_of.  Up to
+// kSelfMaxTiles tiles the scatter derives its own offsets from the count
+// table (three launches); beyond that an exclusive scan of the table runs
+// between count and scatter.
 hipError_t transpose_two_level(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
                                const void* col, int col_i32, const void* val, int vb,
                                void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
                                void* ws, hipStream_t s) {
   RadixWs R = carve_radix_ws(ws, nnz);
   uint32_t* rows_of = (uint32_t*)((char*)ws + radix_ws_bytes_for(nnz));
+  uint32_t* bstart = rows_of + align256((size_t)nnz * 4) / 4;
   const int bits = cols > 1 ? bit_length((uint64_t)(cols - 1)) : 1;
   const int sh = bits > kRadixBits ? bits - kRadixBits : 0;
   const int64_t ntiles = cdiv(nnz, kTile);
-  hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
-                     ro, rows, nnz, rows_of);
+  // the count launch also expands row offsets, at most 256 rows per workgroup
+  const int64_t cgrid = ntiles > cdiv(rows, (int64_t)256) ? ntiles : cdiv(rows, (int64_t)256);
+  const int64_t rpb = cdiv(rows, cgrid);
+  // (SPOPS_TRANSPOSE_SCAN=1, read per call, forces the scan path for its test)
+  const char* fs = getenv("SPOPS_TRANSPOSE_SCAN");
+  const bool self = ntiles <= kSelfMaxTiles && !(fs && fs[0] == '1');
   // first pass: columns with their rows and value bits, one record per entry
   // over the key and payload buffers of the workspace (which lie back to
   // back and hold at least 16 bytes per entry): 8 bytes while the row
@@ -874,42 +981,51 @@ hipError_t transpose_two_level(int64_t rows, int64_t cols, int64_t nnz, const in
   // (SPOPS_TRANSPOSE_REC16=1, read per call, selects 16 for its test)
   const char* r16 = getenv("SPOPS_TRANSPOSE_REC16");
   const bool rec8 = rows <= ((int64_t)1 << (32 - sh)) && !(r16 && r16[0] == '1');
-  auto scatter = [&](auto ks, auto rb) -> hipError_t {
+  auto scatter = [&](auto ks, auto rb, auto sf) -> hipError_t {
     using KS = decltype(ks);
     constexpr int RB = decltype(rb)::value;
-    hipLaunchKernelGGL(radix_count_kernel<KS>, dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks,
-                       nnz, sh, 0xffu, R.counts, ntiles);
-    hipError_t e = exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
-    if (e != hipSuccess) return e;
+    constexpr bool SELF = decltype(sf)::value;
+    hipLaunchKernelGGL((transpose_count_kernel<KS, SELF>), dim3((unsigned)cgrid), dim3(kThreads),
+                       0, s, ks, nnz, sh, 0xffu, R.counts, ntiles, ro, rows, rpb, rows_of);
+    if constexpr (!SELF) {
+      hipError_t e =
+          exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
+      if (e != hipSuccess) return e;
+    }
     const ValFromU32 rowpay{rows_of};
     if (vb == 4)
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<4>, RB>),
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<4>, RB, SELF>),
                          dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<4>{val});
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<4>{val}, bstart);
     else if (vb == 2)
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<2>, RB>),
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<2>, RB, SELF>),
                          dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<2>{val});
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<2>{val}, bstart);
     else
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<0>, RB>),
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<0>, RB, SELF>),
                          dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<0>{nullptr});
-    e = hipGetLastError();
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<0>{nullptr},
+                         bstart);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const uint32_t* bs = SELF ? bstart : R.counts;
+    const int64_t bstride = SELF ? 1 : ntiles;
     if (out_col_i32)
-      return launch_bucket_finish<int32_t, RB>(rec, R.counts, ntiles, nnz, cols, sh, vb, out_val,
+      return launch_bucket_finish<int32_t, RB>(rec, bs, bstride, nnz, cols, sh, vb, out_val,
                                                out_ro, out_col, s);
-    return launch_bucket_finish<int16_t, RB>(rec, R.counts, ntiles, nnz, cols, sh, vb, out_val,
+    return launch_bucket_finish<int16_t, RB>(rec, bs, bstride, nnz, cols, sh, vb, out_val,
                                              out_ro, out_col, s);
   };
-  using R8 = std::integral_constant<int, 8>;
-  using R16 = std::integral_constant<int, 16>;
-  if (col_i32) {
-    const KeyFromIndex<int32_t> ks{(const int32_t*)col, (int32_t)(cols - 1)};
-    return rec8 ? scatter(ks, R8{}) : scatter(ks, R16{});
-  }
-  const KeyFromIndex<int16_t> ks{(const int16_t*)col, (int32_t)(cols - 1)};
-  return rec8 ? scatter(ks, R8{}) : scatter(ks, R16{});
+  auto pick = [&](auto ks) -> hipError_t {
+    using R8 = std::integral_constant<int, 8>;
+    using R16 = std::integral_constant<int, 16>;
+    using Y = std::true_type;
+    using N = std::false_type;
+    if (self) return rec8 ? scatter(ks, R8{}, Y{}) : scatter(ks, R16{}, Y{});
+    return rec8 ? scatter(ks, R8{}, N{}) : scatter(ks, R16{}, N{});
+  };
+  if (col_i32) return pick(KeyFromIndex<int32_t>{(const int32_t*)col, (int32_t)(cols - 1)});
+  return pick(KeyFromIndex<int16_t>{(const int16_t*)col, (int32_t)(cols - 1)});
 }
 
 hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
