@@ -76,6 +76,8 @@ TRANSPOSE_CASES = [
     (6, 40000, 7, 0.2, "f16", {}),       # rows > 32767: int32 transposed indices
     (7, 50, 50, 0.0, "f32", {}),         # no entries
     (8, 1, 1, 1.0, "f32", {}),
+    # more than 2^17 columns: full LSD passes instead of the two-level sort
+    (9, 200, 300000, 0.001, "f32", {"col_index_dtype": np.int32}),
 ]
 
 

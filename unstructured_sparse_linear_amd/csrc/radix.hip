@@ -9,9 +9,10 @@
 // Sorting is least-significant-digit radix with 8-bit digits, in three
 // kernels per pass: per-tile digit counts, one exclusive scan over the
 // digit-major count table, and a stable scatter.  Inside a tile the rank of
-// each key among equal digits is found with wave ballots (64-lane match on
-// the digit bits) plus per-wave digit counts in LDS, so no atomics decide
-// any position and the output is deterministic.  No kernel waits on another
+// each key among equal digits is found from a 64-lane match (the lanes of a
+// wave holding the same digit, as a bit mask) plus per-wave digit counts in
+// LDS, so no atomic's ordering decides any position and the output is
+// deterministic.  No kernel waits on another
 // block, so no launch order assumptions are made.
 #include <stdlib.h>
 
@@ -198,6 +199,35 @@ struct ValBits {  // VB == 0: no values (zero bits)
   }
 };
 
+// Lanes of the wave whose (valid) digit equals this lane's, as a bit mask.
+// Two equivalent ways, chosen per call for speed: when at least a quarter
+// of the lanes share lane 0's digit (clustered keys, where LDS atomics on
+// one address would serialize) one ballot per digit bit; otherwise every
+// valid lane ORs its bit into its digit's 64-bit mask in LDS (`match`, this
+// wave's row, all zero on entry and on return), reads the mask back and
+// clears it -- one wave's LDS operations complete in issue order, so each
+// read sees all of the call's ORs and each clear follows all of its reads.
+__device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d, int nbits,
+                                                uint64_t* match, uint64_t lanebit) {
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)d);
+  if (__popcll(__ballot(valid && d == d0)) >= kWave / 4) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    return valid ? peers : 0;
+  }
+  uint64_t peers = 0;
+  if (valid) {
+    atomicOr((unsigned long long*)&match[d], (unsigned long long)lanebit);
+    peers = match[d];
+    match[d] = 0;
+  }
+  return peers;
+}
+
 // Per-tile digit histogram, stored digit-major: counts[d * ntiles + tile].
 // Thread t takes kItems consecutive keys.
 template <class KS>
@@ -252,16 +282,25 @@ __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
   }
   __syncthreads();
   if (!tile) return;
+  // lanes sharing lane 0's digit add once through their lowest lane (keys
+  // of a tile are often clustered, and LDS atomics on one address serialize)
+  const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int q = 0; q < kItems; ++q)
-    if (i0 + q < n) atomicAdd(&hist[(key[q] >> shift) & mask], 1u);
+  for (int q = 0; q < kItems; ++q) {
+    const bool v = i0 + q < n;
+    const uint32_t d = (key[q] >> shift) & mask;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)d);
+    const uint64_t same = __ballot(v && d == d0);
+    if (v && d == d0 && (same & lt) == 0) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+    if (v && d != d0) atomicAdd(&hist[d], 1u);
+  }
   __syncthreads();
   counts[TM ? (int64_t)blockIdx.x * kRadix + t : (int64_t)t * ntiles + blockIdx.x] = hist[t];
 }
 
 // Stable scatter.  Keys of a tile are taken in rounds of kThreads (round-major,
 // then thread order == index order).  In a round each wave finds the lanes
-// holding the same digit with ballots; the lowest such lane publishes the
+// holding the same digit (digit_peers); the lowest such lane publishes the
 // count; digit offsets per wave then follow from the running per-digit base.
 // RB != 0: a second payload VS2 too, and each entry goes out as one record
 // at kout (an array of n records), one store per entry: RB = 16, {key, pay,
@@ -282,12 +321,17 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
   constexpr bool kTwo = RB != 0;
   __shared__ uint32_t base_d[kRadix];
   __shared__ uint32_t wcnt[kThreads / kWave][kRadix];
+  // per wave and digit: the lanes of the current round holding it
+  __shared__ uint64_t match[kThreads / kWave][kRadix];
   const int t = threadIdx.x;
   const int w = t / kWave;
   const uint32_t mask = (1u << nbits) - 1u;
   if constexpr (!SELF) base_d[t] = offs[(int64_t)t * ntiles + blockIdx.x];
+#pragma unroll
+  for (int ww = 0; ww < kThreads / kWave; ++ww) match[ww][t] = 0;
   const int64_t tbase = (int64_t)blockIdx.x * kTile;
   const uint64_t lt = lanemask_lt();
+  const uint64_t lanebit = lt + 1;
   // all keys and payloads of the tile are loaded before the first round
   uint32_t keys[kItems], pay[kItems], pay2[kTwo ? kItems : 1];
 #pragma unroll
@@ -353,12 +397,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     const bool valid = i < n;
     const uint32_t key = keys[r];
     const uint32_t d = (key >> shift) & mask;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
+    const uint64_t peers = digit_peers(valid, d, nbits, match[w], lanebit);
     const uint32_t rank = (uint32_t)__popcll(peers & lt);
     if (valid && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
     __syncthreads();
@@ -509,7 +548,7 @@ __global__ __launch_bounds__(256) void transpose_finish_kernel(
 // table gives, per digit, the count in earlier slices, and a scan over the
 // digit totals gives the bucket's output row offsets.  Then every wave walks
 // its slice in rounds of 64 entries with no further barrier: an entry's rank
-// among equal digits of the round comes from wave ballots, its destination
+// among equal digits of the round comes from digit_peers, its destination
 // is digit base + earlier slices + the wave's running count, and the first
 // lane of each digit advances that count.  The first pass wrote each
 // entry's column, row and value bits as one 16-byte record, so the slice is
@@ -544,6 +583,8 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
   __shared__ uint32_t base_f[kMaxFine];
   __shared__ uint32_t wcnt[kFinishWaves][kMaxFine];
   __shared__ uint32_t wsum[kMaxFine / kWave];
+  // per wave and fine digit: the lanes of the current round holding it
+  __shared__ uint64_t match[kFinishWaves][kMaxFine];
   const int t = threadIdx.x, w = t / kWave, lane = lane_id();
   const int d = blockIdx.x;
   const int F = 1 << sh;
@@ -551,7 +592,11 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
   const int64_t bs = bstart[(int64_t)d * bstride];
   const int64_t be = d + 1 < kRadix ? (int64_t)bstart[(int64_t)(d + 1) * bstride] : nnz;
   const uint64_t lt = lanemask_lt();
-  for (int k = t; k < kFinishWaves * F; k += kFinishThreads) wcnt[k / F][k % F] = 0;
+  const uint64_t lanebit = lt + 1;
+  for (int k = t; k < kFinishWaves * F; k += kFinishThreads) {
+    wcnt[k / F][k % F] = 0;
+    match[k / F][k % F] = 0;
+  }
   __syncthreads();
   // this wave's slice [s0, s1) of the bucket
   const int64_t len = be - bs;
@@ -614,12 +659,7 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
     for (int j = 0; j < kSub; ++j) {
       const bool valid = qb + j * kWave + lane < s1;
       const uint32_t f = valid ? cur[j].fine(fmask, sh) : 0u;
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < sh; ++b) {
-        const bool bit = (f >> b) & 1u;
-        const uint64_t bal = __ballot(bit);
-        peers &= bit ? bal : ~bal;
-      }
+      const uint64_t peers = digit_peers(valid, f, sh, match[w], lanebit);
       const uint32_t rank = (uint32_t)__popcll(peers & lt);
       const uint32_t before = wcnt[w][f];
       if (valid) {
