@@ -59,6 +59,21 @@ def test_sort_rows_bitexact(m, n, density, kw):
     assert np.array_equal(host(ri), oracle.row_idx(A.row_offsets))
 
 
+@pytest.mark.parametrize("m,n,lengths", [
+    # more than 16384 rows: LSD radix passes (two launches per pass up to
+    # 128 tiles of 2048 rows, else with a scan between count and scatter)
+    (30000, 6000, [5999, 3000, 3000, 700, 129]),
+    (20000, 200000, [150000, 70000, 129]),
+    (300000, 50, [49, 49, 17]),
+])
+def test_sort_rows_many_rows(m, n, lengths):
+    A = heavy_csr(3, m, n, lengths, "f32")
+    for it in (torch.int32, None):
+        ri = S.sort_rows_by_nnz(dev(A.row_offsets), A.n, index_dtype=it)
+        want = oracle.row_idx(A.row_offsets, np.int32 if it is torch.int32 else None)
+        assert np.array_equal(host(ri), want)
+
+
 def test_sort_rows_heavy_and_int32_output():
     A = heavy_csr(2, 2000, 5000, [4096 - 1, 3000, 3000, 700, 129], "f32")
     ri = S.sort_rows_by_nnz(dev(A.row_offsets), A.n, index_dtype=torch.int32)

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
   // rpb <= kThreads: the rpb + 1 offsets are read in one round
   const int64_t r0 = (int64_t)blockIdx.x * rpb;
   const int nr = (int)(r0 >= m ? 0 : (m - r0 < rpb ? m - r0 : rpb));
-  if (t <= nr) rol[t] = ro[r0 + t];
+  if (nr > 0 && t <= nr) rol[t] = ro[r0 + t];  // (nr == 0: no offset is read)
   if (t == 0 && nr == kThreads) rol[kThreads] = ro[r0 + kThreads];
   __syncthreads();
   // one wave per row (loop bounds are wave-uniform)
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
 // counts, tile-major, and every workgroup derives its own offsets from the
 // whole table: base of digit d in tile b = (entries of all digits below d) +
 // (entries of digit d in tiles below b).  Workgroup 0 also stores the digit
-// starts to bstart[0..kRadix), which replaces the scan launch.
+// starts to bstart[0..kRadix) (if given), which replaces the scan launch.
 constexpr int64_t kSelfMaxTiles = 128;
 
 template <class KS, class VS, class VS2, int RB, bool SELF = false>
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     uint32_t below = inc - dtot;
     for (int ww = 0; ww < w; ++ww) below += wcnt[0][ww];
     base_d[t] = below + dpre;
-    if (blockIdx.x == 0) bstart[t] = below;
+    if (blockIdx.x == 0 && bstart) bstart[t] = below;
     __syncthreads();
   }
 #pragma unroll
@@ -468,7 +468,9 @@ int bit_length(uint64_t v) {
 }
 
 // Sorts n keys (all < 2^bits) stably; the first pass reads `ks0` and produces
-// payload iota.  Returns the buffer index holding the result.
+// payload iota.  Returns the buffer index holding the result.  Up to
+// kSelfMaxTiles tiles a pass is two launches (count, then a scatter that
+// derives its own offsets), else three (count, scan, scatter).
 template <class KS0>
 hipError_t radix_sort_iota(KS0 ks0, int64_t n, int bits, const RadixWs& R, int* result,
                            hipStream_t s) {
@@ -476,9 +478,33 @@ hipError_t radix_sort_iota(KS0 ks0, int64_t n, int bits, const RadixWs& R, int* 
   if (bits < 1) bits = 1;
   int cur = -1;  // -1: source functor; else buffer index holding current keys
   int dst = 0;
+  const bool self = ntiles <= kSelfMaxTiles;
   for (int shift = 0; shift < bits; shift += kRadixBits) {
     const int nb = (bits - shift) < kRadixBits ? (bits - shift) : kRadixBits;
     const uint32_t mask = (1u << nb) - 1u;
+    if (self) {
+      // count (clustered lanes added once) and a scatter that derives its
+      // own offsets: two launches per pass
+      if (cur < 0) {
+        hipLaunchKernelGGL((transpose_count_kernel<KS0, true>), dim3(ntiles), dim3(kThreads), 0,
+                           s, ks0, n, shift, mask, R.counts, ntiles, nullptr, 0, 0, nullptr);
+        hipLaunchKernelGGL((radix_scatter_kernel<KS0, ValIota, NoPay, 0, true>), dim3(ntiles),
+                           dim3(kThreads), 0, s, ks0, ValIota{}, n, shift, nb, R.counts, ntiles,
+                           R.keys[dst], R.vals[dst], NoPay{}, nullptr);
+      } else {
+        const KeyFromU32 kc{R.keys[cur]};
+        hipLaunchKernelGGL((transpose_count_kernel<KeyFromU32, true>), dim3(ntiles),
+                           dim3(kThreads), 0, s, kc, n, shift, mask, R.counts, ntiles, nullptr, 0,
+                           0, nullptr);
+        hipLaunchKernelGGL((radix_scatter_kernel<KeyFromU32, ValFromU32, NoPay, 0, true>),
+                           dim3(ntiles), dim3(kThreads), 0, s, kc, ValFromU32{R.vals[cur]}, n,
+                           shift, nb, R.counts, ntiles, R.keys[dst], R.vals[dst], NoPay{},
+                           nullptr);
+      }
+      cur = dst;
+      dst ^= 1;
+      continue;
+    }
     if (cur < 0) {
       hipLaunchKernelGGL(radix_count_kernel<KS0>, dim3(ntiles), dim3(kThreads), 0, s, ks0, n,
                          shift, mask, R.counts, ntiles);
@@ -982,6 +1008,89 @@ hipError_t radix_sort_u32_iota(const uint32_t* keys, int64_t n, int bits, uint32
   return hipMemcpyAsync(sorted_vals, R.vals[res], (size_t)n * 4, hipMemcpyDeviceToDevice, s);
 }
 
+// Stable two-level sort of n entries by key (< nkeys <= 2^17): one radix
+// pass on the top 8 key bits, then one workgroup per coarse bucket orders it
+// by the remaining <= 9 bits (transpose_bucket_kernel), which writes the
+// entries' payloads to out_col (and value bits to out_val) in key order and
+// the key boundaries to out_ro[0..nkeys].  Payload: the row of each stored
+// position (rows_of, expanded from the row offsets `ro` of `rows` rows by
+// the count launch) or, with ro == nullptr, the entry's own index.  Up to
+// kSelfMaxTiles tiles the scatter derives its own offsets from the count
+// table (three launches); beyond that an exclusive scan of the table runs
+// between count and scatter.  Workspace: radix buffers (records), rows_of,
+// bucket starts.
+template <class KS>
+hipError_t two_level_sort(KS ks, int64_t n, int64_t nkeys, const int32_t* ro, int64_t rows,
+                          const void* val, int vb, void* out_val, int32_t* out_ro,
+                          void* out_col, int out_col_i32, void* ws, hipStream_t s) {
+  RadixWs R = carve_radix_ws(ws, n);
+  uint32_t* rows_of = (uint32_t*)((char*)ws + radix_ws_bytes_for(n));
+  uint32_t* bstart = rows_of + align256((size_t)n * 4) / 4;
+  const int bits = nkeys > 1 ? bit_length((uint64_t)(nkeys - 1)) : 1;
+  const int sh = bits > kRadixBits ? bits - kRadixBits : 0;
+  const int64_t ntiles = cdiv(n, kTile);
+  const int64_t erows = ro ? rows : 0;  // rows to expand
+  const int64_t pay_max = ro ? rows : n;  // payloads are below this
+  // the count launch also expands row offsets, at most 256 rows per workgroup
+  const int64_t cgrid = ntiles > cdiv(erows, (int64_t)256) ? ntiles : cdiv(erows, (int64_t)256);
+  const int64_t rpb = cdiv(erows, cgrid);
+  // (SPOPS_TRANSPOSE_SCAN=1, read per call, forces the scan path for its test)
+  const char* fs = getenv("SPOPS_TRANSPOSE_SCAN");
+  const bool self = ntiles <= kSelfMaxTiles && !(fs && fs[0] == '1');
+  // first pass: keys with their payloads and value bits, one record per
+  // entry over the key and payload buffers of the workspace (which lie back
+  // to back and hold at least 16 bytes per entry): 8 bytes while the
+  // payloads fit above the fine digit, else 16
+  uint32_t* rec = R.keys[0];
+  // (SPOPS_TRANSPOSE_REC16=1, read per call, selects 16 for its test)
+  const char* r16 = getenv("SPOPS_TRANSPOSE_REC16");
+  const bool rec8 = pay_max <= ((int64_t)1 << (32 - sh)) && !(r16 && r16[0] == '1');
+  auto scatter = [&](auto vs, auto rb, auto sf) -> hipError_t {
+    using VS = decltype(vs);
+    constexpr int RB = decltype(rb)::value;
+    constexpr bool SELF = decltype(sf)::value;
+    hipLaunchKernelGGL((transpose_count_kernel<KS, SELF>), dim3((unsigned)cgrid), dim3(kThreads),
+                       0, s, ks, n, sh, 0xffu, R.counts, ntiles, ro, erows, rpb, rows_of);
+    if constexpr (!SELF) {
+      hipError_t e =
+          exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
+      if (e != hipSuccess) return e;
+    }
+    if (vb == 4)
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, VS, ValBits<4>, RB, SELF>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, vs, n, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<4>{val}, bstart);
+    else if (vb == 2)
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, VS, ValBits<2>, RB, SELF>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, vs, n, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<2>{val}, bstart);
+    else
+      hipLaunchKernelGGL((radix_scatter_kernel<KS, VS, ValBits<0>, RB, SELF>),
+                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, vs, n, sh,
+                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<0>{nullptr},
+                         bstart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint32_t* bs = SELF ? bstart : R.counts;
+    const int64_t bstride = SELF ? 1 : ntiles;
+    if (out_col_i32)
+      return launch_bucket_finish<int32_t, RB>(rec, bs, bstride, n, nkeys, sh, vb, out_val,
+                                               out_ro, out_col, s);
+    return launch_bucket_finish<int16_t, RB>(rec, bs, bstride, n, nkeys, sh, vb, out_val,
+                                             out_ro, out_col, s);
+  };
+  auto pick = [&](auto vs) -> hipError_t {
+    using R8 = std::integral_constant<int, 8>;
+    using R16 = std::integral_constant<int, 16>;
+    using Y = std::true_type;
+    using N = std::false_type;
+    if (self) return rec8 ? scatter(vs, R8{}, Y{}) : scatter(vs, R16{}, Y{});
+    return rec8 ? scatter(vs, R8{}, N{}) : scatter(vs, R16{}, N{});
+  };
+  if (ro) return pick(ValFromU32{rows_of});
+  return pick(ValIota{});
+}
+
 size_t transpose_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz) {
   (void)rows;
   (void)cols;
@@ -990,82 +1099,17 @@ size_t transpose_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz) {
   return radix_ws_bytes_for(nnz) + align256((size_t)nnz * 4) + align256(kRadix * 4);
 }
 
-// Two-level transpose for up to 2^17 columns: one stable radix pass on the
-// top 8 bits of the column, then one workgroup per coarse bucket orders it by
-// the remaining <= 9 bits (transpose_bucket_kernel).  The first launch counts
-// digits per tile and expands the row offsets into rows_of.  Up to
-// kSelfMaxTiles tiles the scatter derives its own offsets from the count
-// table (three launches); beyond that an exclusive scan of the table runs
-// between count and scatter.
+// Transpose for up to 2^17 columns: the two-level sort of the stored entries
+// by column, payload the entry's row.
 hipError_t transpose_two_level(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
                                const void* col, int col_i32, const void* val, int vb,
                                void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
                                void* ws, hipStream_t s) {
-  RadixWs R = carve_radix_ws(ws, nnz);
-  uint32_t* rows_of = (uint32_t*)((char*)ws + radix_ws_bytes_for(nnz));
-  uint32_t* bstart = rows_of + align256((size_t)nnz * 4) / 4;
-  const int bits = cols > 1 ? bit_length((uint64_t)(cols - 1)) : 1;
-  const int sh = bits > kRadixBits ? bits - kRadixBits : 0;
-  const int64_t ntiles = cdiv(nnz, kTile);
-  // the count launch also expands row offsets, at most 256 rows per workgroup
-  const int64_t cgrid = ntiles > cdiv(rows, (int64_t)256) ? ntiles : cdiv(rows, (int64_t)256);
-  const int64_t rpb = cdiv(rows, cgrid);
-  // (SPOPS_TRANSPOSE_SCAN=1, read per call, forces the scan path for its test)
-  const char* fs = getenv("SPOPS_TRANSPOSE_SCAN");
-  const bool self = ntiles <= kSelfMaxTiles && !(fs && fs[0] == '1');
-  // first pass: columns with their rows and value bits, one record per entry
-  // over the key and payload buffers of the workspace (which lie back to
-  // back and hold at least 16 bytes per entry): 8 bytes while the row
-  // numbers fit above the fine digit, else 16
-  uint32_t* rec = R.keys[0];
-  // (SPOPS_TRANSPOSE_REC16=1, read per call, selects 16 for its test)
-  const char* r16 = getenv("SPOPS_TRANSPOSE_REC16");
-  const bool rec8 = rows <= ((int64_t)1 << (32 - sh)) && !(r16 && r16[0] == '1');
-  auto scatter = [&](auto ks, auto rb, auto sf) -> hipError_t {
-    using KS = decltype(ks);
-    constexpr int RB = decltype(rb)::value;
-    constexpr bool SELF = decltype(sf)::value;
-    hipLaunchKernelGGL((transpose_count_kernel<KS, SELF>), dim3((unsigned)cgrid), dim3(kThreads),
-                       0, s, ks, nnz, sh, 0xffu, R.counts, ntiles, ro, rows, rpb, rows_of);
-    if constexpr (!SELF) {
-      hipError_t e =
-          exclusive_scan_u32(R.counts, R.counts, ntiles * kRadix, nullptr, R.scan_ws, s);
-      if (e != hipSuccess) return e;
-    }
-    const ValFromU32 rowpay{rows_of};
-    if (vb == 4)
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<4>, RB, SELF>),
-                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<4>{val}, bstart);
-    else if (vb == 2)
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<2>, RB, SELF>),
-                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<2>{val}, bstart);
-    else
-      hipLaunchKernelGGL((radix_scatter_kernel<KS, ValFromU32, ValBits<0>, RB, SELF>),
-                         dim3((unsigned)ntiles), dim3(kThreads), 0, s, ks, rowpay, nnz, sh,
-                         kRadixBits, R.counts, ntiles, rec, nullptr, ValBits<0>{nullptr},
-                         bstart);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const uint32_t* bs = SELF ? bstart : R.counts;
-    const int64_t bstride = SELF ? 1 : ntiles;
-    if (out_col_i32)
-      return launch_bucket_finish<int32_t, RB>(rec, bs, bstride, nnz, cols, sh, vb, out_val,
-                                               out_ro, out_col, s);
-    return launch_bucket_finish<int16_t, RB>(rec, bs, bstride, nnz, cols, sh, vb, out_val,
-                                             out_ro, out_col, s);
-  };
-  auto pick = [&](auto ks) -> hipError_t {
-    using R8 = std::integral_constant<int, 8>;
-    using R16 = std::integral_constant<int, 16>;
-    using Y = std::true_type;
-    using N = std::false_type;
-    if (self) return rec8 ? scatter(ks, R8{}, Y{}) : scatter(ks, R16{}, Y{});
-    return rec8 ? scatter(ks, R8{}, N{}) : scatter(ks, R16{}, N{});
-  };
-  if (col_i32) return pick(KeyFromIndex<int32_t>{(const int32_t*)col, (int32_t)(cols - 1)});
-  return pick(KeyFromIndex<int16_t>{(const int16_t*)col, (int32_t)(cols - 1)});
+  if (col_i32)
+    return two_level_sort(KeyFromIndex<int32_t>{(const int32_t*)col, (int32_t)(cols - 1)}, nnz,
+                          cols, ro, rows, val, vb, out_val, out_ro, out_col, out_col_i32, ws, s);
+  return two_level_sort(KeyFromIndex<int16_t>{(const int16_t*)col, (int32_t)(cols - 1)}, nnz,
+                        cols, ro, rows, val, vb, out_val, out_ro, out_col, out_col_i32, ws, s);
 }
 
 hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
@@ -1126,6 +1170,8 @@ hipError_t launch_sort_rows(const int32_t* ro, int64_t rows, int64_t cols, void*
                          ro, rows, (int32_t)cols, (int16_t*)row_idx);
     return hipGetLastError();
   }
+  // LSD passes over the key cols - count (not the two-level sort: the keys
+  // crowd just below cols, which would put every row in one coarse bucket)
   RadixWs R = carve_radix_ws(ws, rows);
   int res = 0;
   const int bits = bit_length((uint64_t)cols);
