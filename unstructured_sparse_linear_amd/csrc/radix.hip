@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
   uint32_t key[kItems];
 #pragma unroll
   for (int q = 0; q < kItems; ++q) key[q] = tile && i0 + q < n ? ks(i0 + q) : 0u;
-  // rpb <= kThreads: the rpb + 1 offsets are read in one round
+  // rpb <= kThreads: the rpb + 1 offsets are read in one round (rpb <=
+  // kExpandRows as launched)
   const int64_t r0 = (int64_t)blockIdx.x * rpb;
   const int nr = (int)(r0 >= m ? 0 : (m - r0 < rpb ? m - r0 : rpb));
   if (nr > 0 && t <= nr) rol[t] = ro[r0 + t];  // (nr == 0: no offset is read)
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
 // (entries of digit d in tiles below b).  Workgroup 0 also stores the digit
 // starts to bstart[0..kRadix) (if given), which replaces the scan launch.
 constexpr int64_t kSelfMaxTiles = 128;
+constexpr int64_t kExpandRows = 32;  // most rows one count workgroup expands
 
 template <class KS, class VS, class VS2, int RB, bool SELF = false>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
@@ -1031,8 +1033,10 @@ hipError_t two_level_sort(KS ks, int64_t n, int64_t nkeys, const int32_t* ro, in
   const int64_t ntiles = cdiv(n, kTile);
   const int64_t erows = ro ? rows : 0;  // rows to expand
   const int64_t pay_max = ro ? rows : n;  // payloads are below this
-  // the count launch also expands row offsets, at most 256 rows per workgroup
-  const int64_t cgrid = ntiles > cdiv(erows, (int64_t)256) ? ntiles : cdiv(erows, (int64_t)256);
+  // the count launch also expands row offsets, at most kExpandRows rows per
+  // workgroup (eight per wave), extra workgroups beyond the tiles only expand
+  const int64_t cgrid =
+      ntiles > cdiv(erows, kExpandRows) ? ntiles : cdiv(erows, kExpandRows);
   const int64_t rpb = cdiv(erows, cgrid);
   // (SPOPS_TRANSPOSE_SCAN=1, read per call, forces the scan path for its test)
   const char* fs = getenv("SPOPS_TRANSPOSE_SCAN");
