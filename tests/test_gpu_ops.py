@@ -93,6 +93,7 @@ TRANSPOSE_CASES = [
     (8, 1, 1, 1.0, "f32", {}),
     # more than 2^17 columns: full LSD passes instead of the two-level sort
     (9, 200, 300000, 0.001, "f32", {"col_index_dtype": np.int32}),
+    (10, 1, 5000, 0.5, "bf16", {}),      # one long row, expanded by one wave
 ]
 
 
@@ -126,7 +127,7 @@ def test_transpose_single_pass_tile_limit(nnz):
     check_transpose_exact(exact_nnz_csr(11, 2048, 3000, nnz, "bf16"))
 
 
-@pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (0, 3, 4, 5)])
+@pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (0, 3, 4, 5, 9)])
 def test_transpose_bitexact_scan_path(monkeypatch, seed, m, n, density, dt, kw):
     # small inputs through the scan between count and scatter, selected by
     # its switch
