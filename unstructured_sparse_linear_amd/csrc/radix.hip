@@ -248,11 +248,12 @@ __global__ __launch_bounds__(kThreads) void radix_count_kernel(KS ks, int64_t n,
   counts[(int64_t)t * ntiles + blockIdx.x] = hist[t];
 }
 
-// First pass of the two-level transpose: the digit counts of tile b (blocks
-// b < ntiles) and, for rows [b*rpb, (b+1)*rpb), the row owning every stored
-// position (rows_of), so no separate launch expands the row offsets.  TM: counts stored tile-major, counts[tile * kRadix + d] (the
-// layout radix_scatter_kernel reads when it derives its own offsets), else
-// digit-major like radix_count_kernel.
+// Digit counts of tile b (workgroups b < ntiles) and, when row offsets `ro`
+// of m rows are given (the transpose's first pass), the row owning every
+// stored position of rows [b*rpb, (b+1)*rpb) (rows_of), so no separate launch
+// expands the row offsets.  TM: counts stored tile-major,
+// counts[tile * kRadix + d] (the layout radix_scatter_kernel reads when it
+// derives its own offsets), else digit-major like radix_count_kernel.
 template <class KS, bool TM>
 __global__ __launch_bounds__(kThreads) void transpose_count_kernel(
     KS ks, int64_t n, int shift, uint32_t mask, uint32_t* counts, int64_t ntiles,
@@ -946,7 +947,8 @@ __global__ __launch_bounds__(kBlockSortThreads) void sort_rows_block_kernel(cons
     }
     cur ^= 1;
   }
-  for (int64_t i = t; i < m; i += kBlockSortThreads) out[i] = (OI)((cur ? buf1 : buf0)[i] & 0xffffu);
+  for (int64_t i = t; i < m; i += kBlockSortThreads)
+    out[i] = (OI)((cur ? buf1 : buf0)[i] & 0xffffu);
 }
 
 // row_idx output from the sorted payload
