@@ -200,32 +200,25 @@ struct ValBits {  // VB == 0: no values (zero bits)
 };
 
 // Lanes of the wave whose (valid) digit equals this lane's, as a bit mask.
-// Two equivalent ways, chosen per call for speed: when at least a quarter
-// of the lanes share lane 0's digit (clustered keys, where LDS atomics on
-// one address would serialize) one ballot per digit bit; otherwise every
-// valid lane ORs its bit into its digit's 64-bit mask in LDS (`match`, this
-// wave's row, all zero on entry and on return), reads the mask back and
-// clears it -- one wave's LDS operations complete in issue order, so each
-// read sees all of the call's ORs and each clear follows all of its reads.
-__device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d, int nbits,
-                                                uint64_t* match, uint64_t lanebit) {
+// Lanes holding lane 0's digit take it from one ballot; every other valid
+// lane ORs its bit into its digit's 64-bit mask in LDS (`match`, this wave's
+// row, all zero on entry and on return), reads the mask back and clears it
+// -- one wave's LDS operations complete in issue order, so each read sees all
+// of the call's ORs and each clear follows all of its reads.  Clustered keys
+// (where LDS atomics on one address would serialize) mostly share lane 0's
+// digit, so the LDS traffic is left to the scattered rest.
+__device__ __forceinline__ uint64_t digit_peers(bool valid, uint32_t d, uint64_t* match,
+                                                uint64_t lanebit) {
   const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)d);
-  if (__popcll(__ballot(valid && d == d0)) >= kWave / 4) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    return valid ? peers : 0;
-  }
+  const bool first = valid && d == d0;
+  const uint64_t same = __ballot(first);
   uint64_t peers = 0;
-  if (valid) {
+  if (valid && !first) {
     atomicOr((unsigned long long*)&match[d], (unsigned long long)lanebit);
     peers = match[d];
     match[d] = 0;
   }
-  return peers;
+  return first ? same : peers;
 }
 
 // Per-tile digit histogram, stored digit-major: counts[d * ntiles + tile].
@@ -400,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     const bool valid = i < n;
     const uint32_t key = keys[r];
     const uint32_t d = (key >> shift) & mask;
-    const uint64_t peers = digit_peers(valid, d, nbits, match[w], lanebit);
+    const uint64_t peers = digit_peers(valid, d, match[w], lanebit);
     const uint32_t rank = (uint32_t)__popcll(peers & lt);
     if (valid && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
     __syncthreads();
@@ -688,7 +681,7 @@ __global__ __launch_bounds__(kFinishThreads) void transpose_bucket_kernel(
     for (int j = 0; j < kSub; ++j) {
       const bool valid = qb + j * kWave + lane < s1;
       const uint32_t f = valid ? cur[j].fine(fmask, sh) : 0u;
-      const uint64_t peers = digit_peers(valid, f, sh, match[w], lanebit);
+      const uint64_t peers = digit_peers(valid, f, match[w], lanebit);
       const uint32_t rank = (uint32_t)__popcll(peers & lt);
       const uint32_t before = wcnt[w][f];
       if (valid) {
