@@ -172,7 +172,12 @@ def op_kernels(spmm_info, sddmm_info, m, n, nnz):
     return {"spmm": spmm, "spmv": spmv, "sddmm": sddmm or ["sddmm_list_kernel"],
             "csr_add": ["csr_add_kernel"],
             "transpose": transpose_kernels(n, nnz),
-            "row_order": ["sort_rows_block_kernel"]}
+            # the row order of A^T (n rows, keys up to m)
+            "row_order": (["sort_rows_block_kernel"] if n <= 16384 and m <= 65535
+                          else ["transpose_count_kernel", "radix_scatter_kernel",
+                                "store_perm_kernel"] if -(-n // 2048) <= 128
+                          else ["radix_count_kernel", "scan_*", "radix_scatter_kernel",
+                                "store_perm_kernel"])}
 
 
 def traffic_for(op, config):
