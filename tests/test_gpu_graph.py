@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import unstructured_sparse_linear_amd as S
 from unstructured_sparse_linear_amd import gen
 from helpers import csr_dev, dev
@@ -67,6 +68,49 @@ def test_graph_replays_match_eager(dt, heavy):
             assert torch.equal(a, b), f"replay {rep} differs"
         # unrelated eager work between replays
         _ = (B.float() @ B.float().T).sum().item()
+
+
+@pytest.mark.parametrize("m,n,density", [
+    (300, 40000, 0.01),    # row order of 40000 rows: radix passes, no scan
+    (3000, 3000, 0.04),    # transpose of ~360 K entries: scan between count and scatter
+    (50, 300000, 0.002),   # > 2^17 columns: full LSD transpose; row order with scans
+])
+def test_graph_replays_of_radix_paths(m, n, density):
+    A = gen.random_csr(7, m, n, density, "f32")
+    v, ro, ci = csr_dev(A)
+    tws = S.csr_transpose_workspace(m, n, A.nnz, "cuda")
+    sws = S.sort_rows_workspace(n, m, "cuda")
+    it = torch.int16 if m <= 32767 else torch.int32
+    vT = torch.empty(A.nnz, dtype=torch.float32, device="cuda")
+    roT = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    ciT = torch.empty(A.nnz, dtype=it, device="cuda")
+    riT = torch.empty(n, dtype=torch.int16 if n <= 32767 else torch.int32, device="cuda")
+
+    def step():
+        S.csr_transpose(v, ro, ci, m, n, workspace=tws, out=(vT, roT, ciT))
+        S.sort_rows_by_nnz(roT, m, workspace=sws, out=riT)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [vT.clone(), roT.clone(), ciT.clone(), riT.clone()]
+    ev, ero, eci = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx, A.values)
+    assert np.array_equal(ref[1].cpu().numpy(), ero)
+    assert np.array_equal(ref[2].cpu().numpy(), eci)
+    assert np.array_equal(ref[0].cpu().numpy().view(np.uint8), ev.view(np.uint8))
+    assert np.array_equal(ref[3].cpu().numpy(), oracle.row_idx(ero))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (vT, roT, ciT, riT):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([vT, roT, ciT, riT], ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (v.float() * 2).sum().item()
 
 
 def test_graph_replays_of_the_next_rows_match_eager():
