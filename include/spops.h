@@ -101,6 +101,33 @@ typedef struct spops_csr {
 int spops_abi_version(void);
 const char* spops_status_string(spops_status status);
 
+/* Process-wide switches, read by every later call (0 = the default for all).
+ * They select alternative code paths for tests and tuning; results are the
+ * same definition whatever they hold.
+ *   SPOPS_OPT_SPMM_POINTER_LOADS    nonzero: SpMM reads its operands through
+ *       plain pointers (the path otherwise taken for operands of 2 GiB and
+ *       more).
+ *   SPOPS_OPT_TRANSPOSE_FORCE_SCAN  nonzero: csr_transpose scans its count
+ *       table even for inputs whose scatter could derive its own offsets.
+ *   SPOPS_OPT_TRANSPOSE_WIDE_RECORDS  nonzero: csr_transpose's first pass
+ *       writes 16-byte records even where 8-byte ones fit.
+ *   SPOPS_OPT_SDDMM_BUCKETS  1..8: column buckets of the structure-aware
+ *       remainder in plans built afterwards (0: chosen per mask).
+ *   SPOPS_OPT_SDDMM_SPLITS   1..16: K splits of the structure-aware dense
+ *       tiles (0: chosen per plan and K); changes spops_sddmm_workspace_size.
+ * spops_set_option returns SPOPS_ERR_UNSUPPORTED for an unknown option and
+ * SPOPS_ERR_ARGUMENT for a negative value.  Calls running concurrently with
+ * a change may see either value. */
+typedef enum spops_option {
+  SPOPS_OPT_SPMM_POINTER_LOADS = 0,
+  SPOPS_OPT_TRANSPOSE_FORCE_SCAN = 1,
+  SPOPS_OPT_TRANSPOSE_WIDE_RECORDS = 2,
+  SPOPS_OPT_SDDMM_BUCKETS = 3,
+  SPOPS_OPT_SDDMM_SPLITS = 4
+} spops_option;
+spops_status spops_set_option(spops_option option, int64_t value);
+spops_status spops_get_option(spops_option option, int64_t* value);
+
 /* ------------------------------------------------------------------ SpMM --
  * Section "Sparse Matrix Multiplication (SpMM)": C = A * B.
  *   A:  rows x cols CSR with values; row_idx required.
@@ -138,17 +165,25 @@ spops_status spops_spmm_plan_info(const spops_spmm_plan* plan, int64_t* split_ro
 /* ----------------------------------------------------------------- SDDMM --
  * Section "Sampled Dense-Dense Matrix Multiplication (SDDMM)":
  *   out[p] = sum_k A[r][k] * BT[c][k]  for every stored position p = (r, c)
- *   of `mask` (values ignored; row_idx required), in the mask's CSR order.
+ *   of `mask` (values and row_idx not used), in the mask's CSR order.
  *   A:  mask->rows x K dense, leading dim lda >= K.
  *   BT: mask->cols x K dense (B transposed), leading dim ldbt >= K.
  *   A and BT share in_type; out_type is SPOPS_F32 or in_type.
  *   backend SPOPS_SDDMM_GENERAL: one kernel for any pattern; `plan` ignored.
  *   backend SPOPS_SDDMM_STRUCTURE_AWARE: runs the rows and columns where the
  *   mask's entries cluster as dense tiles on the matrix cores and the rest
- *   with the general kernel; needs a plan for this mask.  With plan == NULL
- *   a temporary plan is built and freed inside the call (that call then
- *   allocates and synchronizes).  Both backends compute the same values up
- *   to fp32 summation order. */
+ *   with the general kernel.  The partition comes from `plan` (see
+ *   spops_sddmm_plan_create); with plan == NULL it is built inside the call,
+ *   on the stream, in the caller's workspace, with the default density
+ *   threshold (slower than reusing a plan, but it neither allocates nor
+ *   synchronizes, so it can be captured in a HIP graph).  The dense tiles
+ *   need 16-bit inputs, K a multiple of 8, lda and ldbt multiples of 8 and
+ *   16-byte aligned A and BT; other calls run the general kernel (with a
+ *   plan that found no tiles, over the plan's column buckets).
+ *   workspace: spops_sddmm_workspace_size bytes (NULL when that is 0),
+ *   256-byte aligned; its contents on entry do not matter.  Too small:
+ *   SPOPS_ERR_WORKSPACE.  Both backends compute the same values up to fp32
+ *   summation order. */
 typedef struct spops_sddmm_plan spops_sddmm_plan;
 
 spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_t lda,
@@ -157,14 +192,13 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
                          const spops_sddmm_plan* plan, void* workspace, size_t workspace_bytes,
                          void* hip_stream);
 
-/* Optional workspace of spops_sddmm.  The general kernel can split K into
- * slices that run on different XCDs (so each L2 holds one slice of BT) and
- * sum their fp32 partial products in a fixed order; when that split is
- * enabled (environment variable SPOPS_SDDMM_KSPLIT, a cap on the number of
- * slices) it needs this many bytes.  A smaller (or NULL) workspace runs
- * without the split: same definition.  The structure-aware backend on 16-bit
- * inputs needs none.  `plan` as for spops_sddmm (NULL for the general
- * backend). */
+/* Workspace of spops_sddmm for this mask, K, input type, backend and plan:
+ *   general backend, or inputs the dense tiles cannot take: 0;
+ *   structure-aware with a plan: fp32 partial sums when the plan splits K
+ *     across workgroups (S splits x entries in tiles x 4 bytes; 0 without
+ *     a split);
+ *   structure-aware without a plan: the plan built inside the call (a few
+ *     int32 arrays of the mask's sizes and entry count). */
 spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
                                         spops_sddmm_backend backend,
                                         const spops_sddmm_plan* plan, size_t* bytes);
@@ -174,7 +208,7 @@ spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_
  * dense when, over the remaining rows, its count is at least tau * rows.
  * tau <= 0 selects the default.  tau > 1 disables the dense tiles (all
  * entries go to the general kernel).  Allocates, synchronizes.  Valid while
- * the mask's row_offsets / col_idx / row_idx contents are unchanged. */
+ * the mask's row_offsets / col_idx contents are unchanged. */
 spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hip_stream,
                                      spops_sddmm_plan** plan);
 spops_status spops_sddmm_plan_destroy(spops_sddmm_plan* plan);
@@ -190,7 +224,7 @@ spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_
  * every other element of W keeps its bits.  w_type == A->val_type; the sum
  * is formed in fp32 and rounded once to w_type (nearest-even), which equals
  * the correctly rounded sum for f32, f16 and bf16.  W is A->rows x A->cols
- * with leading dim ldw >= A->cols.  row_idx required. */
+ * with leading dim ldw >= A->cols.  row_idx is not used (may be NULL). */
 spops_status spops_csr_add(const spops_csr* A, void* W, spops_dtype w_type, int64_t ldw,
                            void* hip_stream);
 

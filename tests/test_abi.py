@@ -100,19 +100,54 @@ def test_sddmm_rejects_bad_arguments(L):
     assert f(d, FAKE, 8, 8, FAKE, 8, 1, None, 0, 1) == 1
     assert f(desc(cols=70000, col_type=0), FAKE, 8, 8, FAKE, 8, 1, FAKE, 0, 1) == 4
     assert f(desc(nnz=0, col=None), FAKE, 8, 8, FAKE, 8, 1, None, 0, 1) == 0
+
+
+def test_sddmm_workspace_size_contract(L):
     b = ctypes.c_size_t()
-    big = desc(rows=4096, cols=4096, nnz=100000)
-    assert L.spops_sddmm_workspace_size(ctypes.byref(big), 2048, 1, 1, None, ctypes.byref(b)) == 0
-    assert b.value == 0                                   # K split off by default
-    os.environ["SPOPS_SDDMM_KSPLIT"] = "8"
-    try:
-        assert L.spops_sddmm_workspace_size(ctypes.byref(big), 2048, 1, 1, None,
+
+    def ws(d, K, it, backend, plan=None):
+        assert L.spops_sddmm_workspace_size(ctypes.byref(d), K, it, backend, plan,
                                             ctypes.byref(b)) == 0
-        assert b.value >= 8 * 100000 * 4                  # 8 K-slices of fp32 partials
-    finally:
-        del os.environ["SPOPS_SDDMM_KSPLIT"]
-    assert L.spops_sddmm_workspace_size(ctypes.byref(desc()), 8, 1, 1, None,
-                                        ctypes.byref(b)) == 0 and b.value == 0
+        return b.value
+    big = desc(rows=4096, cols=11008, nnz=450000, values=None)
+    assert ws(big, 2048, 1, 1) == 0                      # general backend: none
+    assert ws(big, 2048, 0, 0) == 0                      # f32: no dense tiles, none
+    assert ws(big, 2044, 1, 0) == 0                      # K not a multiple of 8: none
+    assert ws(big, 0, 1, 0) == 0
+    assert ws(desc(nnz=0, col=None, values=None), 64, 1, 0) == 0
+    # without a plan the structure-aware call builds one in the workspace: at
+    # least the entry arrays (position, in-tile coordinates, sort keys)
+    need = ws(big, 2048, 1, 0)
+    assert need >= 4 * 450000 * 4
+    assert ws(big, 2048, 2, 0) == need                   # same for bf16 and any K
+    assert ws(big, 64, 1, 0) == need
+    assert L.spops_sddmm_workspace_size(ctypes.byref(big), 2048, 1, 7, None,
+                                        ctypes.byref(b)) == 6
+    assert L.spops_sddmm_workspace_size(ctypes.byref(big), -1, 1, 0, None,
+                                        ctypes.byref(b)) == 2
+    # an execute call without a plan and with too little workspace is refused
+    # before anything is launched
+    f = L.spops_sddmm
+    args = (FAKE, 2048, 2048, FAKE, 2048, 1, FAKE, 0, 0, None)
+    assert f(ctypes.byref(big), *args, None, 0, None) == 5
+    assert f(ctypes.byref(big), *args, FAKE, need - 1, None) == 5
+    assert f(ctypes.byref(big), *args, FAKE + 16, need, None) == 5   # not 256-byte aligned
+
+
+def test_options_round_trip(L):
+    v = ctypes.c_int64()
+    for opt in range(5):
+        assert L.spops_get_option(opt, ctypes.byref(v)) == 0 and v.value == 0
+        assert L.spops_set_option(opt, 3) == 0
+        assert L.spops_get_option(opt, ctypes.byref(v)) == 0 and v.value == 3
+        assert L.spops_set_option(opt, 0) == 0
+    assert L.spops_set_option(5, 1) == 6 and L.spops_set_option(-1, 1) == 6
+    assert L.spops_set_option(0, -1) == 9
+    assert L.spops_get_option(0, None) == 1
+    assert S.set_option("sddmm_splits", 4) == 0
+    with S.option("sddmm_splits", 2):
+        assert L.spops_get_option(4, ctypes.byref(v)) == 0 and v.value == 2
+    assert S.set_option("sddmm_splits", 0) == 4
 
 
 def test_csr_add_rejects_bad_arguments(L):
@@ -120,6 +155,9 @@ def test_csr_add_rejects_bad_arguments(L):
     assert f(ctypes.byref(desc()), FAKE, 1, 4, None) == 3     # W dtype != values dtype
     assert f(ctypes.byref(desc()), FAKE, 0, 3, None) == 2     # ldw < cols
     assert f(ctypes.byref(desc()), None, 0, 4, None) == 1
+    # row_idx is not used by csr_add: its absence is not an error
+    assert f(ctypes.byref(desc(ri=None, ri_type=9)), None, 0, 4, None) == 1
+    assert f(ctypes.byref(desc(ri=None, nnz=0, col=None, values=None)), None, 0, 4, None) == 0
 
 
 def test_transpose_and_sort_reject_bad_arguments(L):

@@ -178,3 +178,51 @@ def test_graph_replays_of_the_next_rows_match_eager():
         for a, b in zip((y, yt, dv, vT, dxt, th, W, m1, m2), ref):
             assert torch.equal(a, b), f"replay {rep} differs"
         _ = (xt.float() @ xt.float().T).sum().item()
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_graph_replays_sddmm_without_plan(dt):
+    # structure-aware SDDMM with no plan: the partition is built inside the
+    # call on the stream, in the caller's workspace, so the whole call can be
+    # captured; each replay must give the oracle's values (integer data:
+    # exact) and the eager result
+    m, n, K = 2100, 900, 136
+    M = gen.cross_mask(gen.rng_for(12, 102, 0), m, n, 0.05, 264 / m, 290 / n, 0.9)
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, n)
+    Ad = dev(gen.dense(12, 100, gen.S_A, (m, K), dt, integer_values=True), dt)
+    BT = dev(gen.dense(12, 100, gen.S_BT, (n, K), dt, integer_values=True), dt)
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, host_bits(Ad, dt), host_bits(BT, dt), dt)
+    out = torch.empty(M.nnz, dtype=torch.float32, device="cuda")
+    import ctypes
+    from unstructured_sparse_linear_amd import spops as SP
+    d = SP.csr_desc(None, ro, ri, ci, m, n)
+    b = ctypes.c_size_t()
+    assert SP.lib().spops_sddmm_workspace_size(ctypes.byref(d), K, SP._DT[Ad.dtype], 0, None,
+                                               ctypes.byref(b)) == 0
+    assert b.value > 0
+    ws = torch.empty(b.value, dtype=torch.uint8, device="cuda")
+    S.sddmm(ro, ri, ci, Ad, BT, use_plan=False, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert np.array_equal(eager.double().cpu().numpy(), ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.sddmm(ro, ri, ci, Ad, BT, use_plan=False, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        ws.fill_(0xAB)  # the plan must not depend on what the workspace held
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        _ = (Ad.float() @ BT.float().T).sum().item()
+
+
+def host_bits(t, dt):
+    """Device tensor -> host array in the generators' storage convention."""
+    t = t.cpu()
+    if dt == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

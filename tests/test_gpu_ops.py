@@ -128,23 +128,23 @@ def test_transpose_single_pass_tile_limit(nnz):
 
 
 @pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (0, 3, 4, 5, 9)])
-def test_transpose_bitexact_scan_path(monkeypatch, seed, m, n, density, dt, kw):
+def test_transpose_bitexact_scan_path(seed, m, n, density, dt, kw):
     # small inputs through the scan between count and scatter, selected by
     # its switch
-    monkeypatch.setenv("SPOPS_TRANSPOSE_SCAN", "1")
-    test_transpose_bitexact(seed, m, n, density, dt, kw)
+    with S.option("transpose_force_scan", 1):
+        test_transpose_bitexact(seed, m, n, density, dt, kw)
 
 
 @pytest.mark.parametrize("seed,m,n,density,dt,kw", [TRANSPOSE_CASES[i] for i in (1, 3, 4)])
-def test_transpose_bitexact_16_byte_records(monkeypatch, seed, m, n, density, dt, kw):
+def test_transpose_bitexact_16_byte_records(seed, m, n, density, dt, kw):
     # the first pass's 16-byte records (used when row numbers do not fit
     # above the fine column digit), selected here by their switch
-    monkeypatch.setenv("SPOPS_TRANSPOSE_REC16", "1")
-    test_transpose_bitexact(seed, m, n, density, dt, kw)
-    vT = None
-    A = gen.random_csr(seed, m, n, density, dt, **kw)
-    v, ro, ci = csr_dev(A)
-    _, roT, ciT = S.csr_transpose(vT, ro, ci, m, n)
+    with S.option("transpose_wide_records", 1):
+        test_transpose_bitexact(seed, m, n, density, dt, kw)
+        vT = None
+        A = gen.random_csr(seed, m, n, density, dt, **kw)
+        v, ro, ci = csr_dev(A)
+        _, roT, ciT = S.csr_transpose(vT, ro, ci, m, n)
     _, ero, eci = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx)
     assert np.array_equal(host(roT), ero) and np.array_equal(host(ciT), eci)
 
@@ -245,13 +245,13 @@ def test_spmm_many_column_windows(dt):
 
 
 @pytest.mark.parametrize("dt,N", [("f32", 64), ("bf16", 256), ("f16", 24), ("f32", 8)])
-def test_spmm_pointer_load_path(monkeypatch, dt, N):
+def test_spmm_pointer_load_path(dt, N):
     # the group kernel's path for operands of 2 GiB and more (pointer loads,
     # per-lane metadata), selected here by its switch
-    monkeypatch.setenv("SPOPS_SPMM_NOBUF", "1")
     A = heavy_csr(15, 300, 2000, [1500, 700, 130, 129], dt)
     B = gen.dense(15, 100, gen.S_B, (2000, N), dt)
-    C = run_spmm(A, B, dt)
+    with S.option("spmm_pointer_loads", 1):
+        C = run_spmm(A, B, dt)
     ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
     assert_close(host_f64(C), ref, dt, "spmm pointer-load path")
 
@@ -384,15 +384,20 @@ def cross_csr(seed, m, n, hot_r, hot_c, dt=None):
 
 
 def run_sddmm(M, Ad, BT, dt, backend, tau=None, out_dtype=torch.float32):
+    """backend "structure_aware_inline": the structure-aware backend without a
+    plan (the library partitions the mask inside the call)."""
     _, ro, ci = csr_dev(M)
     ri = S.sort_rows_by_nnz(ro, M.n)
-    return S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), backend=backend, tau=tau,
-                   out_dtype=out_dtype)
+    inline = backend == "structure_aware_inline"
+    return S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt),
+                   backend="structure_aware" if inline else backend, tau=tau,
+                   out_dtype=out_dtype, use_plan=not inline)
 
 
 @pytest.mark.parametrize("seed,m,n,density,dt,K,kw", SDDMM_CASES)
 @pytest.mark.parametrize("backend,tau", [("sputnik", None), ("structure_aware", None),
-                                         ("structure_aware", 1e-9)])
+                                         ("structure_aware", 1e-9),
+                                         ("structure_aware_inline", None)])
 def test_sddmm_parity(seed, m, n, density, dt, K, kw, backend, tau):
     M = gen.random_csr(seed, m, n, density, None, **kw)
     Ad = gen.dense(seed, 100, gen.S_A, (m, K), dt)
@@ -435,21 +440,50 @@ def test_sddmm_backends_bitexact_on_integers(dt):
         assert np.array_equal(host_f64(out), ref), (backend, tau)
 
 
-@pytest.mark.parametrize("dt,m,n,K", [("f16", 300, 5000, 512), ("bf16", 200, 3000, 1000),
-                                      ("f16", 150, 6000, 2048)])
-@pytest.mark.parametrize("backend", ["sputnik", "structure_aware"])
-def test_sddmm_k_split(dt, m, n, K, backend):
-    # BT larger than one L2: K is split across XCDs and the partials summed
-    M = gen.random_csr(7, m, n, 0.01, None, empty_row_frac=0.1)
-    Ad = gen.dense(7, 100, gen.S_A, (m, K), dt)
-    BT = gen.dense(7, 100, gen.S_BT, (n, K), dt)
-    out = run_sddmm(M, Ad, BT, dt, backend)
+# masks with many 256 x 256 dense tiles and ragged edges: region A with two
+# tile rows (the second partly filled), region B with a partial last tile
+# column, K with a partial last 64-wide slice
+TILE_CASES = [("f16", 3000, 1300, 200, 300, 300), ("bf16", 2100, 900, 264, 400, 290),
+              ("f16", 700, 3000, 2048, 280, 100)]
+
+
+@pytest.mark.parametrize("dt,m,n,K,hr,hc", TILE_CASES)
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 8])
+def test_sddmm_tiles_split_k(dt, m, n, K, hr, hc, splits):
+    # the dense tiles with K split across workgroups (fixed-order sum of the
+    # partials) and without, against the oracle; bit-exact on integer data
+    M = cross_csr(9, m, n, hr, hc)
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, n)
+    plan = S.SddmmPlan(ro, ci, m, n)
+    info = plan.info()
+    assert info["tiles"] >= 4 and info["tiled_nnz"] + info["rest_nnz"] == M.nnz
+    Ad = gen.dense(9, 100, gen.S_A, (m, K), dt)
+    BT = gen.dense(9, 100, gen.S_BT, (n, K), dt)
+    Ai = gen.dense(10, 100, gen.S_A, (m, K), dt, integer_values=True)
+    Bi = gen.dense(10, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    with S.option("sddmm_splits", splits):
+        out = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan)
+        outi = S.sddmm(ro, ri, ci, dev(Ai, dt), dev(Bi, dt), plan=plan)
+        out16 = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan,
+                        out_dtype=TORCH_DT[dt])
     ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
-    assert_close(host_f64(out), ref, dt, "sddmm k-split")
-    Ai = gen.dense(8, 100, gen.S_A, (m, K), dt, integer_values=True)
-    Bi = gen.dense(8, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    assert_close(host_f64(out), ref, dt, f"sddmm tiles, {splits} splits")
+    assert rel_err(host_f64(out16), ref) <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -11) + 1e-5
     refi = oracle.sddmm(M.row_offsets, M.col_idx, Ai, Bi, dt)
-    assert np.array_equal(host_f64(run_sddmm(M, Ai, Bi, dt, backend)), refi)
+    assert np.array_equal(host_f64(outi), refi)
+
+
+@pytest.mark.parametrize("dt,m,n,K,hr,hc", TILE_CASES[:2])
+def test_sddmm_inline_plan_matches_plan(dt, m, n, K, hr, hc):
+    # without a plan the partition is built in the call's workspace; on
+    # integer data every path gives the oracle's values exactly
+    M = cross_csr(11, m, n, hr, hc)
+    Ai = gen.dense(11, 100, gen.S_A, (m, K), dt, integer_values=True)
+    Bi = gen.dense(11, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    refi = oracle.sddmm(M.row_offsets, M.col_idx, Ai, Bi, dt)
+    for backend in ("structure_aware_inline", "structure_aware", "sputnik"):
+        assert np.array_equal(host_f64(run_sddmm(M, Ai, Bi, dt, backend)), refi), backend
 
 
 def test_sddmm_keeps_f16_subnormals():

@@ -22,7 +22,9 @@ from .spops import (  # noqa: F401
     csr_transpose_workspace,
     lib,
     masked_adam,
+    option,
     sddmm,
+    set_option,
     sort_rows_by_nnz,
     sort_rows_workspace,
     spmm,
@@ -31,4 +33,5 @@ from .spops import (  # noqa: F401
 __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
            "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg",
-           "masked_adam", "MaskedAdam", "DeltaMatrix", "delta_encode", "delta_spmv"]
+           "masked_adam", "MaskedAdam", "DeltaMatrix", "delta_encode", "delta_spmv",
+           "option", "set_option"]

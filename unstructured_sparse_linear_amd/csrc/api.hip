@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <new>
 
 #include "kernels.h"
@@ -22,6 +23,15 @@ struct spops_spmm_plan {
 struct spops_sddmm_plan {
   SddmmPlanDev dev;
 };
+
+namespace spops {
+namespace {
+std::atomic<int64_t> g_options[kOptCount];
+}  // namespace
+int64_t option(int o) {
+  return (o >= 0 && o < kOptCount) ? g_options[o].load(std::memory_order_relaxed) : 0;
+}
+}  // namespace spops
 
 namespace {
 
@@ -103,6 +113,20 @@ SpmmArgs spmm_args(const spops_csr* A, const void* B, spops_dtype b_type, int64_
 extern "C" {
 
 int spops_abi_version(void) { return SPOPS_ABI_VERSION; }
+
+spops_status spops_set_option(spops_option opt, int64_t value) {
+  if ((int)opt < 0 || (int)opt >= kOptCount) return SPOPS_ERR_UNSUPPORTED;
+  if (value < 0) return SPOPS_ERR_ARGUMENT;
+  g_options[(int)opt].store(value, std::memory_order_relaxed);
+  return SPOPS_OK;
+}
+
+spops_status spops_get_option(spops_option opt, int64_t* value) {
+  if (!value) return SPOPS_ERR_NULL;
+  if ((int)opt < 0 || (int)opt >= kOptCount) return SPOPS_ERR_UNSUPPORTED;
+  *value = g_options[(int)opt].load(std::memory_order_relaxed);
+  return SPOPS_OK;
+}
 
 const char* spops_status_string(spops_status s) {
   switch (s) {
@@ -196,6 +220,11 @@ spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, i
 
 // --------------------------------------------------------------- SDDMM ---
 
+static void free_sddmm_plan_mem(SddmmPlanDev* p) {
+  if (p->mem) hipFree(p->mem);
+  *p = SddmmPlanDev{};
+}
+
 spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hip_stream,
                                      spops_sddmm_plan** plan) {
   if (!plan) return SPOPS_ERR_NULL;
@@ -205,10 +234,21 @@ spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hi
   if (!(tau > 0.0) || isnan(tau)) tau = kDefaultTau;
   spops_sddmm_plan* p = new (std::nothrow) spops_sddmm_plan();
   if (!p) return SPOPS_ERR_HIP;
-  hipError_t e = build_sddmm_plan(mask->rows, mask->cols, mask->nnz, mask->row_offsets,
-                                  mask->col_idx, mask->col_type == SPOPS_I32, tau, &p->dev,
-                                  as_stream(hip_stream));
+  hipStream_t s = as_stream(hip_stream);
+  const int64_t m = mask->rows, n = mask->cols, nnz = mask->nnz;
+  void* mem = nullptr;
+  void* scratch = nullptr;
+  hipError_t e = hipMalloc(&mem, sddmm_plan_bytes(m, n, nnz));
+  if (e == hipSuccess) e = hipMalloc(&scratch, sddmm_plan_scratch_bytes(m, n, nnz));
+  if (e == hipSuccess)
+    e = enqueue_sddmm_plan(m, n, nnz, mask->row_offsets, mask->col_idx,
+                           mask->col_type == SPOPS_I32, tau, mem, scratch, &p->dev, s);
+  if (e == hipSuccess) e = fetch_sddmm_plan_counts(&p->dev, s);  // synchronizes s
+  else if (scratch) hipStreamSynchronize(s);
+  if (scratch) hipFree(scratch);
+  p->dev.mem = mem;
   if (e != hipSuccess) {
+    free_sddmm_plan_mem(&p->dev);
     delete p;
     return SPOPS_ERR_HIP;
   }
@@ -218,7 +258,7 @@ spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hi
 
 spops_status spops_sddmm_plan_destroy(spops_sddmm_plan* plan) {
   if (!plan) return SPOPS_OK;
-  free_sddmm_plan(&plan->dev);
+  free_sddmm_plan_mem(&plan->dev);
   delete plan;
   return SPOPS_OK;
 }
@@ -227,19 +267,23 @@ spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_
                                    int64_t* dense_cols, int64_t* tiled_nnz, int64_t* rest_nnz,
                                    int64_t* tiles) {
   if (!plan) return SPOPS_ERR_NULL;
-  if (dense_rows) *dense_rows = plan->dev.n_rows_hot;
-  if (dense_cols) *dense_cols = plan->dev.n_cols_hot;
-  if (tiled_nnz) *tiled_nnz = plan->dev.tiled_nnz;
-  if (rest_nnz) *rest_nnz = plan->dev.rest_nnz;
-  if (tiles) *tiles = plan->dev.tiles;
+  const SddmmPlanScalars& h = plan->dev.h;
+  if (dense_rows) *dense_rows = h.H;
+  if (dense_cols) *dense_cols = h.Hc;
+  if (tiled_nnz) *tiled_nnz = h.tiled;
+  if (rest_nnz) *rest_nnz = h.rest;
+  if (tiles) *tiles = h.tiles;
   return SPOPS_OK;
 }
 
-// Entries the general kernel handles for this call (all of them, or the
-// plan's remainder) and whether the dense tiles can run.
+// The dense tiles need 16-bit inputs, K a multiple of 8 and 16-byte rows
+// (MFMA operands are 8 consecutive K elements).
+static bool sddmm_tiles_possible(spops_dtype in_type, int64_t K) {
+  return in_type != SPOPS_F32 && K > 0 && K % 8 == 0;
+}
 static bool sddmm_tiles_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t ldbt,
                            const void* A, const void* BT) {
-  return in_type != SPOPS_F32 && K > 0 && K % 8 == 0 && lda % 8 == 0 && ldbt % 8 == 0 &&
+  return sddmm_tiles_possible(in_type, K) && lda % 8 == 0 && ldbt % 8 == 0 &&
          ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
 }
 
@@ -251,6 +295,13 @@ static bool sddmm_list_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t l
          ((uintptr_t)BT % 16 == 0);
 }
 
+// Workspace of a structure-aware call without a plan: the plan built inside
+// the call (its arrays, then its temporaries).
+static size_t sddmm_inline_plan_bytes(const spops_csr* mask) {
+  return align256(sddmm_plan_bytes(mask->rows, mask->cols, mask->nnz)) +
+         sddmm_plan_scratch_bytes(mask->rows, mask->cols, mask->nnz);
+}
+
 spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
                                         spops_sddmm_backend backend,
                                         const spops_sddmm_plan* plan, size_t* bytes) {
@@ -259,12 +310,16 @@ spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_
   spops_status st = check_csr(mask, false, false);
   if (st != SPOPS_OK) return st;
   if (!dtype_ok(in_type)) return SPOPS_ERR_DTYPE;
+  if (backend != SPOPS_SDDMM_STRUCTURE_AWARE && backend != SPOPS_SDDMM_GENERAL)
+    return SPOPS_ERR_UNSUPPORTED;
   if (K < 0) return SPOPS_ERR_SHAPE;
-  // the structure-aware path (16-bit inputs, K a multiple of 8) needs none
-  if (backend == SPOPS_SDDMM_STRUCTURE_AWARE && in_type != SPOPS_F32 && K % 8 == 0 && K > 0)
+  if (backend != SPOPS_SDDMM_STRUCTURE_AWARE || !sddmm_tiles_possible(in_type, K) ||
+      mask->nnz == 0)
     return SPOPS_OK;
-  const int64_t ks = sddmm_k_slices(mask->cols, K, in_type);
-  if (ks > 1 && mask->nnz > 0) *bytes = align256((size_t)(ks * mask->nnz) * 4);
+  if (plan)
+    *bytes = sddmm_split_bytes(plan->dev, sddmm_tile_schedule(plan->dev, K));
+  else
+    *bytes = sddmm_inline_plan_bytes(mask);
   return SPOPS_OK;
 }
 
@@ -283,35 +338,11 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   if (mask->nnz == 0) return SPOPS_OK;
   if (!out_values) return SPOPS_ERR_NULL;
   if (K > 0 && (!A || !BT)) return SPOPS_ERR_NULL;
+  if (plan && backend == SPOPS_SDDMM_STRUCTURE_AWARE &&
+      (plan->dev.m != mask->rows || plan->dev.n != mask->cols || plan->dev.nnz != mask->nnz ||
+       plan->dev.mask_ro != mask->row_offsets || plan->dev.mask_col != mask->col_idx))
+    return SPOPS_ERR_PLAN;
   hipStream_t s = as_stream(hip_stream);
-
-  SddmmArgs g{};
-  g.m = mask->rows;
-  g.n = mask->cols;
-  g.K = K;
-  g.lda = lda;
-  g.ldbt = ldbt;
-  g.ro = mask->row_offsets;
-  g.pos = nullptr;
-  g.count = mask->nnz;
-  g.col = mask->col_idx;
-  g.col_i32 = mask->col_type == SPOPS_I32;
-  g.A = A;
-  g.BT = BT;
-  g.out = out_values;
-  g.dtype = in_type;
-  g.out_dtype = out_type;
-  g.ks = 1;
-  g.partial = nullptr;
-  // K split when the workspace allows it (fp32 partials per slice)
-  auto with_split = [&](SddmmArgs x) {
-    const int64_t ks = sddmm_k_slices(mask->cols, K, in_type);
-    if (ks > 1 && workspace && workspace_bytes >= (size_t)(ks * x.count) * 4) {
-      x.ks = ks;
-      x.partial = (float*)workspace;
-    }
-    return x;
-  };
 
   const bool tiles_ok = sddmm_tiles_ok(in_type, K, lda, ldbt, A, BT);
   const bool list_ok = sddmm_list_ok(in_type, K, lda, ldbt, A, BT);
@@ -328,48 +359,82 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   r.out = out_values;
   r.dtype = in_type;
   r.out_dtype = out_type;
-  // the whole mask in CSR order through the entry-list kernel (no plan)
-  auto csr_list = [&]() {
-    r.ro = mask->row_offsets;
-    r.nb = 1;
-    r.bstart[0] = 0;
-    r.bstart[1] = mask->nnz;
+  // the whole mask in CSR order: the entry-list kernel, or the scalar kernel
+  // when K or the operands do not allow 16-byte vectors
+  auto general = [&]() {
+    if (list_ok) {
+      r.ro = mask->row_offsets;
+      r.nb = 1;
+      r.bstart[0] = 0;
+      r.bstart[1] = mask->nnz;
+      return from_hip(launch_sddmm_list(r, s));
+    }
+    SddmmArgs g{};
+    g.m = mask->rows;
+    g.n = mask->cols;
+    g.K = K;
+    g.lda = lda;
+    g.ldbt = ldbt;
+    g.ro = mask->row_offsets;
+    g.count = mask->nnz;
+    g.col = mask->col_idx;
+    g.col_i32 = mask->col_type == SPOPS_I32;
+    g.A = A;
+    g.BT = BT;
+    g.out = out_values;
+    g.dtype = in_type;
+    g.out_dtype = out_type;
+    return from_hip(launch_sddmm_general(g, s));
+  };
+  // the plan's remainder through the entry-list kernel, bucket by bucket
+  auto remainder = [&](const SddmmPlanDev& P) {
+    r.pos = P.ent_pos;
+    r.rows = P.ent_rc;
+    if (P.host_ok) {
+      if (P.h.rest == 0) return hipSuccess;
+      r.nb = P.h.nb;
+      for (int b = 0; b <= P.h.nb; ++b) r.bstart[b] = P.bucket_start[b];
+    } else {
+      r.nb = P.nb_max;
+      r.bstart_dev = P.key_start + P.rest_key;
+      r.max_bucket = mask->nnz;
+    }
     return launch_sddmm_list(r, s);
   };
-  const SddmmArgs gs = with_split(g);
-  auto general = [&]() {
-    if (list_ok && gs.ks == 1) return from_hip(csr_list());
-    return from_hip(launch_sddmm_general(gs, s));
-  };
   if (backend == SPOPS_SDDMM_GENERAL) return general();
-  if (plan && (plan->dev.m != mask->rows || plan->dev.n != mask->cols ||
-               plan->dev.nnz != mask->nnz || plan->dev.mask_ro != mask->row_offsets ||
-               plan->dev.mask_col != mask->col_idx))
-    return SPOPS_ERR_PLAN;
-  // Dense tiles need 16-bit inputs.  Without them the plan's remainder (the
-  // whole mask when it found no tiles) still runs through the entry list.
-  if (!tiles_ok && (!plan || plan->dev.tiles > 0 || !list_ok)) return general();
-
-  spops_sddmm_plan* own = nullptr;
+  if (!tiles_ok) {
+    // 32-bit or unaligned inputs: the plan's remainder still runs where the
+    // plan found no tiles (its remainder is then the whole mask)
+    if (plan && plan->dev.host_ok && plan->dev.h.tiles == 0 && list_ok)
+      return from_hip(remainder(plan->dev));
+    return general();
+  }
   if (!plan) {
-    st = spops_sddmm_plan_create(mask, kDefaultTau, hip_stream, &own);
-    if (st != SPOPS_OK) return st;
-    plan = own;
+    // plan built here, in the caller's workspace, on the stream: no
+    // allocation, no synchronization
+    const size_t need = sddmm_inline_plan_bytes(mask);
+    if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)
+      return SPOPS_ERR_WORKSPACE;
+    SddmmPlanDev P;
+    char* ws = (char*)workspace;
+    hipError_t e = enqueue_sddmm_plan(
+        mask->rows, mask->cols, mask->nnz, mask->row_offsets, mask->col_idx,
+        mask->col_type == SPOPS_I32, kDefaultTau, ws,
+        ws + align256(sddmm_plan_bytes(mask->rows, mask->cols, mask->nnz)), &P, s);
+    if (e == hipSuccess)
+      e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type,
+                             sddmm_tile_schedule(P, K), nullptr, s);
+    if (e == hipSuccess) e = remainder(P);
+    return from_hip(e);
   }
   const SddmmPlanDev& P = plan->dev;
-  hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type, s);
-  if (e == hipSuccess && P.rest_nnz > 0) {
-    r.pos = P.rest_pos;
-    r.rows = P.rest_row;
-    r.nb = P.nb;
-    for (int b = 0; b <= P.nb; ++b) r.bstart[b] = P.bucket_start[b];
-    e = launch_sddmm_list(r, s);
-  }
-  if (own) {
-    hipError_t e2 = hipStreamSynchronize(s);
-    if (e == hipSuccess) e = e2;
-    spops_sddmm_plan_destroy(own);
-  }
+  const SddmmTileSched sched = sddmm_tile_schedule(P, K);
+  const size_t need = sddmm_split_bytes(P, sched);
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
+    return SPOPS_ERR_WORKSPACE;
+  hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type,
+                                    sched, (float*)workspace, s);
+  if (e == hipSuccess) e = remainder(P);
   return from_hip(e);
 }
 
@@ -377,7 +442,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
 
 spops_status spops_csr_add(const spops_csr* A, void* W, spops_dtype w_type, int64_t ldw,
                            void* hip_stream) {
-  spops_status st = check_csr(A, true, true);
+  spops_status st = check_csr(A, true, false);
   if (st != SPOPS_OK) return st;
   if (!dtype_ok(w_type)) return SPOPS_ERR_DTYPE;
   if (w_type != A->val_type) return SPOPS_ERR_DTYPE;

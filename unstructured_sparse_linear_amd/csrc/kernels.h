@@ -37,6 +37,11 @@ hipError_t launch_sort_rows(const int32_t* ro, int64_t rows, int64_t cols, void*
 size_t radix_pairs_workspace_bytes(int64_t n);
 hipError_t radix_sort_u32_iota(const uint32_t* keys, int64_t n, int bits, uint32_t* sorted_keys,
                                uint32_t* sorted_vals, void* ws, hipStream_t s);
+// The same sort leaving its results in the workspace: *sorted_keys and
+// *sorted_vals point into ws (no copies).
+hipError_t radix_sort_u32_iota_ptrs(const uint32_t* keys, int64_t n, int bits, void* ws,
+                                    const uint32_t** sorted_keys, const uint32_t** sorted_vals,
+                                    hipStream_t s);
 
 // ------------------------------------------------------------------ SpMM --
 // Rows with more entries than kSpmmSplitLen are cut by the plan into chunks of
@@ -105,66 +110,96 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
 void free_spmm_schedule(SpmmSchedule* sch);
 
 // ----------------------------------------------------------------- SDDMM --
+// Scalar kernel of the general backend, for K, leading dimensions or
+// pointers that do not allow 16-byte vectors along K (mask in CSR order).
 struct SddmmArgs {
   int64_t m, n, K, lda, ldbt;
-  const int32_t* ro;     // row offsets of the entries to compute
-  const int32_t* pos;    // nullable: entry j is mask position pos[j]; else j itself
-  int64_t count;         // entries to compute (== ro[m])
-  const void* col;       // mask column indices (indexed by mask position)
+  const int32_t* ro;     // mask row offsets
+  int64_t count;         // mask entries (== ro[m])
+  const void* col;       // mask column indices
   int col_i32;
   const void* A;
   const void* BT;
-  void* out;             // indexed by mask position
+  void* out;             // [count], CSR order
   int dtype, out_dtype;
-  // K split across XCDs (ks == 1: none): slice s of K accumulates into
-  // partial[s * count + j], then a fixed-order sum writes out.
-  int64_t ks;
-  float* partial;
 };
-// Number of K slices the general kernel would use, and the fp32 workspace
-// that needs (bytes); 1 / 0 when splitting does not pay.
-int64_t sddmm_k_slices(int64_t n, int64_t K, int dtype);
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s);
 
-// Structure-aware SDDMM plan (device data) and its dense-tile kernel.
+// Structure-aware SDDMM plan.  Dense tiles are kSddmmTM x kSddmmTN blocks of
+// gathered rows x gathered columns; tile t's entries carry the keys 2t and
+// 2t + 1 (upper and lower half of its rows), the remainder the keys
+// rest_key + column bucket.
 constexpr int kMaxBuckets = 8;
+constexpr int kSddmmTM = 128;
+constexpr int kSddmmTN = 128;
+
+// Counts the plan kernels write to device memory.
+struct SddmmPlanScalars {
+  int32_t H;             // dense rows
+  int32_t mc;            // the other rows
+  int32_t Hc;            // dense columns (counted over the other rows)
+  int32_t tiles_a;       // tiles of region A (dense rows x all columns)
+  int32_t tiles_b_cols;  // tile columns of region B (other rows x dense columns)
+  int32_t tiles;         // all tiles
+  int32_t tiled;         // entries inside tiles
+  int32_t rest;          // remainder entries
+  int32_t nb;            // remainder column buckets after the merge decision
+  uint32_t rest_count;   // classifier's running count of remainder entries
+  int32_t pad[6];
+};
+
 struct SddmmPlanDev {
   int64_t m = 0, n = 0, nnz = 0;
   double tau = 0;
-  int64_t n_rows_hot = 0, n_cols_hot = 0;   // dense rows, dense columns
-  int64_t tiled_nnz = 0, rest_nnz = 0, tiles = 0;
-  int64_t tiles_a = 0;        // tiles of region A (dense rows x all columns)
-  int64_t tiles_a_cols = 0;   // tile columns of region A
-  int64_t tiles_b_cols = 0;   // tile columns of region B (other rows x dense columns)
-  int64_t n_rows_cold = 0;    // rows of region B
-  int32_t* hot_rows = nullptr;   // [n_rows_hot]
-  int32_t* cold_rows = nullptr;  // [n_rows_cold]
-  int32_t* hot_cols = nullptr;   // [n_cols_hot]
-  int32_t* tile_start = nullptr; // [tiles+1] entry ranges per tile
-  int32_t* ent_pos = nullptr;    // [tiled_nnz] mask position
-  int32_t* ent_rc = nullptr;     // [tiled_nnz] (local row << 16) | local col
-  // remainder: entries sorted by (column bucket, row); bucket b holds
-  // columns [b*n/nb, (b+1)*n/nb) and runs on XCD b
-  int nb = 1;
-  int64_t bucket_start[kMaxBuckets + 1] = {};  // host copy, offsets into rest_*
-  int32_t* rest_pos = nullptr;   // [rest_nnz] mask position
-  int32_t* rest_row = nullptr;   // [rest_nnz] row
-  void* mem = nullptr;
+  int64_t tiles_a_cols = 0;  // tile columns of region A: cdiv(n, kSddmmTN)
+  int64_t max_tiles = 0;     // bound on the tile count (sizes the key space)
+  int64_t rest_key = 0;      // first remainder key (2 * max_tiles)
+  int nb_max = 1;            // remainder buckets planned before the merge decision
+  SddmmPlanScalars* sc = nullptr;  // device
+  int32_t* rows = nullptr;         // [m] dense rows, then the other rows
+  int32_t* hot_cols = nullptr;     // [n] dense columns
+  int32_t* key_start = nullptr;    // [rest_key + nb_max + 1] first sorted entry per key
+  int32_t* ent_pos = nullptr;      // [nnz] mask position of each sorted entry
+  int32_t* ent_rc = nullptr;       // [nnz] (tile row << 16) | tile column; remainder: row
+  // host copy of the counts (plans made by spops_sddmm_plan_create)
+  bool host_ok = false;
+  SddmmPlanScalars h{};
+  int64_t bucket_start[kMaxBuckets + 1] = {};  // absolute entry positions of the buckets
+  int64_t max_tile_nnz = 0;        // most entries in one tile (host counts)
+  int cus = 256;                   // compute units of the device
+  void* mem = nullptr;             // owning allocation (null when carved from a workspace)
   // identity of the mask it was built for
   const void* mask_ro = nullptr;
   const void* mask_col = nullptr;
 };
-hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
-                            const void* col, int col_i32, double tau, SddmmPlanDev* out,
-                            hipStream_t s);
-void free_sddmm_plan(SddmmPlanDev* p);
+// Device memory of a plan (kept) and of its build (temporary).
+size_t sddmm_plan_bytes(int64_t m, int64_t n, int64_t nnz);
+size_t sddmm_plan_scratch_bytes(int64_t m, int64_t n, int64_t nnz);
+// Enqueues the plan's kernels on s (no allocation, no synchronization): the
+// plan's arrays are carved from `mem` (sddmm_plan_bytes), temporaries from
+// `scratch` (sddmm_plan_scratch_bytes).  Fills *out (counts stay on the
+// device; out->host_ok false).
+hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
+                              const void* col, int col_i32, double tau, void* mem,
+                              void* scratch, SddmmPlanDev* out, hipStream_t s);
+// Copies the counts to the host (synchronizes s).
+hipError_t fetch_sddmm_plan_counts(SddmmPlanDev* p, hipStream_t s);
+// Work schedule of the dense tiles for a plan and K, and the fp32 partial
+// sums it needs (bytes).
+struct SddmmTileSched {
+  int splits;     // K splits per tile (1: a tile is one item)
+};
+SddmmTileSched sddmm_tile_schedule(const SddmmPlanDev& p, int64_t K);
+size_t sddmm_split_bytes(const SddmmPlanDev& p, const SddmmTileSched& sched);
+// Dense tiles (with several splits: partial sums into part, then their
+// fixed-order sum into out).
 hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, int64_t lda,
                               const void* BT, int64_t ldbt, int dtype, void* out, int out_dtype,
-                              hipStream_t s);
+                              const SddmmTileSched& sched, float* part, hipStream_t s);
 
-// General SDDMM over an explicit entry list (the plan's remainder): entry j
-// is mask position pos[j] in row rows[j]; entries of bucket b are
-// [bstart[b], bstart[b+1]) and run on the blocks b, b+nb, ...
+// General SDDMM over an entry list: entry j is mask position pos[j] in row
+// rows[j]; entries of bucket b are [bstart[b], bstart[b+1]) and run on the
+// blocks b, b+nb, ... (which share XCD b when nb is 8).
 struct SddmmListArgs {
   int64_t m, n, K, lda, ldbt;
   // CSR order when ro is set: entry j is mask position j, its row is found in
@@ -180,8 +215,24 @@ struct SddmmListArgs {
   int dtype, out_dtype;
   int nb;
   int64_t bstart[kMaxBuckets + 1];
+  // bucket bounds in device memory instead of bstart (nullable); max_bucket
+  // bounds the entries of one bucket
+  const int32_t* bstart_dev;
+  int64_t max_bucket;
 };
 hipError_t launch_sddmm_list(const SddmmListArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- options --
+// Process-wide switches (spops_set_option), read on every call.
+enum Option : int {
+  kOptSpmmPointerLoads = 0,
+  kOptTransposeForceScan = 1,
+  kOptTransposeWideRecords = 2,
+  kOptSddmmBuckets = 3,
+  kOptSddmmSplits = 4,
+  kOptCount = 5
+};
+int64_t option(int o);
 
 // --------------------------------------------------------------- csr_add --
 hipError_t launch_csr_add(int64_t m, int64_t n, int64_t nnz, const int32_t* ro, const void* col,

@@ -1015,6 +1015,17 @@ hipError_t radix_sort_u32_iota(const uint32_t* keys, int64_t n, int bits, uint32
   return hipMemcpyAsync(sorted_vals, R.vals[res], (size_t)n * 4, hipMemcpyDeviceToDevice, s);
 }
 
+hipError_t radix_sort_u32_iota_ptrs(const uint32_t* keys, int64_t n, int bits, void* ws,
+                                    const uint32_t** sorted_keys, const uint32_t** sorted_vals,
+                                    hipStream_t s) {
+  RadixWs R = carve_radix_ws(ws, n);
+  int res = 0;
+  hipError_t e = n > 0 ? radix_sort_iota(KeyFromU32{keys}, n, bits, R, &res, s) : hipSuccess;
+  *sorted_keys = R.keys[res < 0 ? 0 : res];
+  *sorted_vals = R.vals[res < 0 ? 0 : res];
+  return e;
+}
+
 // Stable two-level sort of n entries by key (< nkeys <= 2^17): one radix
 // pass on the top 8 key bits, then one workgroup per coarse bucket orders it
 // by the remaining <= 9 bits (transpose_bucket_kernel), which writes the
@@ -1043,17 +1054,16 @@ hipError_t two_level_sort(KS ks, int64_t n, int64_t nkeys, const int32_t* ro, in
   const int64_t cgrid =
       ntiles > cdiv(erows, kExpandRows) ? ntiles : cdiv(erows, kExpandRows);
   const int64_t rpb = cdiv(erows, cgrid);
-  // (SPOPS_TRANSPOSE_SCAN=1, read per call, forces the scan path for its test)
-  const char* fs = getenv("SPOPS_TRANSPOSE_SCAN");
-  const bool self = ntiles <= kSelfMaxTiles && !(fs && fs[0] == '1');
+  // (the kOptTransposeForceScan switch forces the scan path, for its test)
+  const bool self = ntiles <= kSelfMaxTiles && option(kOptTransposeForceScan) == 0;
   // first pass: keys with their payloads and value bits, one record per
   // entry over the key and payload buffers of the workspace (which lie back
   // to back and hold at least 16 bytes per entry): 8 bytes while the
   // payloads fit above the fine digit, else 16
   uint32_t* rec = R.keys[0];
-  // (SPOPS_TRANSPOSE_REC16=1, read per call, selects 16 for its test)
-  const char* r16 = getenv("SPOPS_TRANSPOSE_REC16");
-  const bool rec8 = pay_max <= ((int64_t)1 << (32 - sh)) && !(r16 && r16[0] == '1');
+  // (the kOptTransposeWideRecords switch selects 16, for its test)
+  const bool rec8 =
+      pay_max <= ((int64_t)1 << (32 - sh)) && option(kOptTransposeWideRecords) == 0;
   auto scatter = [&](auto vs, auto rb, auto sf) -> hipError_t {
     using VS = decltype(vs);
     constexpr int RB = decltype(rb)::value;

@@ -2,22 +2,31 @@
 // "Sampled Dense-Dense Matrix Multiplication (SDDMM)", the kernel for masks
 // whose entries cluster in a small subset of rows and columns).
 //
-// Plan (integer work, once per mask, on the device):
+// Plan (integer work, once per mask, entirely on the device: no host
+// round trip, so it can also be built inside an execute call from the
+// caller's workspace):
 //   * a row is dense when it holds at least tau*n entries;
 //   * over the remaining rows, a column is dense when it holds at least
 //     tau*(remaining rows) entries;
 //   * region A = dense rows x all columns, region B = remaining rows x dense
 //     columns; both are cut into TM x TN tiles of gathered rows / columns;
-//   * every entry gets a tile key (or a sentinel for "neither"), and a stable
-//     radix sort groups the entries tile by tile, keeping the remainder in
-//     CSR order; the remainder becomes a sub-CSR for the general kernel.
+//   * every entry gets a key: 2*tile + (row in the tile's lower half) for a
+//     tile entry, rest_key + (column bucket) for the remainder; a stable
+//     radix sort groups the entries by key (the remainder of each bucket
+//     stays in CSR order), and key_start[k] is the first sorted entry with
+//     key >= k.  Counts (dense rows, tiles, ...) stay in device memory; the
+//     key space is sized by bounds the host knows from (m, n, nnz).
 //
-// Execute: one workgroup per non-empty tile computes the dense TM x TN block
-// A[rows] * BT[cols]^T with v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate),
-// staging 64-wide K slices of the gathered rows through two LDS stages, then
-// writes only the tile's mask positions from an LDS copy of the block.  Every mask entry
-// belongs to exactly one tile or to the remainder, so each output is written
-// once.
+// Execute: a workgroup takes one (tile, K split) item and computes the dense
+// TM x TN block A[rows] * BT[cols]^T over its share of K with
+// v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate), then writes the tile's
+// mask positions from an LDS copy of the block (half the rows at a time).
+// The (tile, K slice) units are spread evenly over the compute units; a
+// tile computed in one piece writes the output, a tile cut into several
+// pieces writes fp32 partial sums and a second kernel adds them in order
+// (deterministic).  Every mask entry belongs to exactly
+// one tile or to the remainder, so each output is written once.
+#include <math.h>
 #include <stdlib.h>
 
 #include "common.h"
@@ -26,17 +35,26 @@
 namespace spops {
 namespace {
 
-constexpr int TM = 128;       // tile rows
-constexpr int TN = 128;       // tile columns
-constexpr int TK = 64;        // K slice staged per step
-constexpr int LDK = TK + 8;   // padded LDS row (16-bit elements)
-constexpr int LDC = TN + 4;   // padded LDS row of the fp32 result block
-constexpr int kThreads = 256;
-constexpr int kStage = (TM + TN) * LDK;  // 16-bit elements per LDS stage (A, then BT)
-constexpr int kChunks = TM * TK / 8 / kThreads;  // 16-byte chunks per thread per operand
-static_assert(TM == TN, "A and BT tiles share the staging map");
-static_assert(TM * LDC * 4 <= 2 * kStage * 2, "the fp32 block reuses the LDS stages");
-
+constexpr int TM = kSddmmTM;           // tile rows
+constexpr int TN = kSddmmTN;           // tile columns
+constexpr int TK = 64;                 // K slice staged per step
+constexpr int LDK = TK + 8;            // padded LDS row (16-bit elements)
+constexpr int kThreads = 256;          // 4 waves, 2 x 2 over the tile
+constexpr int kTileWgPerCu = 2;        // workgroups resident per compute unit
+constexpr int WM = TM / 2, WN = TN / 2;  // wave tile
+constexpr int BM = WM / 32, BN = WN / 32;  // 32 x 32 MFMA blocks per wave
+constexpr int kStaged = TM + TN;       // rows staged per slice (A rows, then BT rows)
+constexpr int kChunks = kStaged * (TK / 8) / kThreads;  // 16-byte chunks per thread and slice
+constexpr int kChunksA = TM * (TK / 8) / kThreads;      // the first ones are A rows
+constexpr int kStage = kStaged * LDK;  // 16-bit elements per LDS stage
+constexpr int HALF = TM / 2;           // rows of the block written to LDS per pass
+constexpr int LDR = HALF + 4;          // padded fp32 column of that half block
+constexpr int kEpi = 8;                // entries per thread per epilogue round
+static_assert(kChunks * kThreads * 8 == kStaged * TK, "chunks cover the staged slice");
+static_assert(HALF == WM, "one wave row per half block");
+static_assert(TN * LDR * 4 <= 2 * kStage * 2, "a half block reuses the LDS stages");
+static_assert(LDR % 4 == 0, "16-byte column segments");
+static_assert(TM < 65536 && TN < 65536, "tile coordinates pack into 16 bits");
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168v __attribute__((ext_vector_type(8)));
@@ -46,14 +64,16 @@ struct TileArgs {
   int64_t K, lda, ldbt, n;
   const uint16_t* A;
   const uint16_t* BT;
-  const int32_t* hot_rows;
-  const int32_t* cold_rows;
+  uint32_t a_bytes, bt_bytes;  // extents of A and BT (each below 2 GiB)
+  const int32_t* rows;       // dense rows, then the other rows
   const int32_t* hot_cols;
-  int64_t n_rows_hot, n_rows_cold, n_cols_hot;
-  int64_t tiles_a, tiles_a_cols, tiles_b_cols;
-  const int32_t* tile_start;
+  const SddmmPlanScalars* sc;
+  int64_t tiles_a_cols;
+  const int32_t* key_start;
   const int32_t* ent_pos;
   const int32_t* ent_rc;
+  int splits;                // K splits per tile; item i = (tile i / splits, split i % splits)
+  float* part;               // [splits][tiled] partial sums when splits > 1
   void* out;
 };
 
@@ -68,176 +88,337 @@ __device__ __forceinline__ float16v mfma32(const uint4& a, const uint4& b, float
   }
 }
 
-// One workgroup (4 waves) per tile; wave (wr, wc) computes the 64 x 64
-// quarter (wr, wc) as 2 x 2 MFMA 32x32x16 blocks.  K runs in slices of TK = 64
-// through two LDS stages: while the waves multiply out of one stage, the next
-// slice's gathered rows are already in registers and are stored into the
-// other stage afterwards, so each slice costs one barrier.  After the K loop
-// the fp32 block goes to LDS and only the tile's mask positions are written.
+// A workgroup computes items: the K slices [s0, s0 + nst) of one tile (the
+// whole tile, or one of its `splits` fixed splits).
+// Wave (wr, wc) owns the WM x WN quarter (wr, wc) of the tile as BM x BN
+// MFMA 32x32x16 blocks (accumulators in the matrix-core registers), one wave
+// per SIMD.  K runs in slices of TK through two LDS stages; each thread
+// gathers its 16-byte chunks of the next slice into registers while the
+// current slice is multiplied, so a load has one slice of MFMA work to land,
+// and each slice costs one barrier.  A segment that covers its whole tile writes the output;
+// segment j of a tile split into several writes partial sums to part[j].
+// The epilogue's entry metadata (in-tile coordinates, positions) for the
+// first kEpi entries per thread of each half is requested before the K loop
+// so that its latency hides behind the MFMA work.
+//
+// MFMA 32x32x16 operand layout: lane l supplies row (l mod 32) of the A
+// block and column (l mod 32) of the B block, K elements 8*(l/32)..+8; it
+// receives column (l mod 32) of the result, value v at row
+// 8*(v/4) + 4*(l/32) + (v mod 4).
 template <bool BF16, typename OT>
-__global__ __launch_bounds__(kThreads, 2) void sddmm_tile_kernel(TileArgs t) {
-  const int64_t tile = blockIdx.x;
-  const int32_t e0 = t.tile_start[tile], e1 = t.tile_start[tile + 1];
-  if (e1 <= e0) return;  // no mask entry in this tile
-
-  // region and gathered row/column lists
-  const int32_t* rlist;
-  const int32_t* clist;
-  int64_t rcount, ccount, tr, tc;
-  if (tile < t.tiles_a) {
-    tr = tile / t.tiles_a_cols;
-    tc = tile % t.tiles_a_cols;
-    rlist = t.hot_rows;
-    rcount = t.n_rows_hot;
-    clist = nullptr;  // identity over all columns
-    ccount = t.n;
-  } else {
-    const int64_t b = tile - t.tiles_a;
-    tr = b / t.tiles_b_cols;
-    tc = b % t.tiles_b_cols;
-    rlist = t.cold_rows;
-    rcount = t.n_rows_cold;
-    clist = t.hot_cols;
-    ccount = t.n_cols_hot;
-  }
-
+__global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(TileArgs t) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
-  float* Cs = (float*)smem;  // [TM][LDC] after the K loop
-
   const int tid = threadIdx.x;
-  // chunk q = tid + 256*h: tile row q / 8, K offset (q % 8) * 8
-  const uint16_t* ap[kChunks];
-  const uint16_t* bp[kChunks];
-  const int skc = (tid & 7) * 8;
-#pragma unroll
-  for (int h = 0; h < kChunks; ++h) {
-    const int row = (tid >> 3) + h * (kThreads / 8);
-    const int64_t ri = tr * TM + row;
-    const int64_t ci = tc * TN + row;
-    ap[h] = ri < rcount ? t.A + (int64_t)rlist[ri] * t.lda : nullptr;
-    bp[h] = ci < ccount ? t.BT + (int64_t)(clist ? clist[ci] : ci) * t.ldbt : nullptr;
-  }
-  uint4 ra[kChunks], rb[kChunks];
-  auto fetch = [&](int64_t k0) {
-    const int64_t k = k0 + skc;
-    const bool ok = k < t.K;  // K is a multiple of 8: a chunk is all in or all out
-#pragma unroll
-    for (int h = 0; h < kChunks; ++h) {
-      ra[h] = (ap[h] && ok) ? *(const uint4*)(ap[h] + k) : make_uint4(0, 0, 0, 0);
-      rb[h] = (bp[h] && ok) ? *(const uint4*)(bp[h] + k) : make_uint4(0, 0, 0, 0);
+  const int w = tid / kWave, l = lane_id();
+  const int wr = w >> 1, wc = w & 1;
+  const int64_t H = t.sc->H, mc = t.sc->mc, Hc = t.sc->Hc;
+  const int64_t tiles_a = t.sc->tiles_a, tiles_b_cols = t.sc->tiles_b_cols;
+  const int64_t tiled = t.sc->tiled;
+  const int64_t tiles = t.sc->tiles;
+  const int64_t nsl = cdiv(t.K, TK);
+  const int64_t per = cdiv(nsl, t.splits);
+  const int kc = (tid & 7) * 8;  // K offset of this thread's chunks in a slice
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(t.A, t.a_bytes);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(t.BT, t.bt_bytes);
+  // XCD-aware order: workgroup b runs on XCD b mod 8, so with a grid that is
+  // a multiple of 8 the logical index (b mod 8) * (grid / 8) + b / 8 gives
+  // each XCD a run of consecutive items; items are ordered so that tiles
+  // sharing gathered rows are neighbours (region A column-major over its
+  // tile rows, which share BT's columns; region B row-major, whose tiles of
+  // one row share A's rows), so those rows are fetched once per L2.
+  const int64_t nb8 = gridDim.x / 8;
+  const int64_t lb = (gridDim.x % 8 == 0) ? (blockIdx.x % 8) * nb8 + blockIdx.x / 8 : blockIdx.x;
+  const int64_t ra = tiles_a > 0 ? tiles_a / t.tiles_a_cols : 0;  // tile rows of region A
+  for (int64_t item = lb; item < tiles * t.splits; item += gridDim.x) {
+    const int64_t ord = item / t.splits;
+    const int64_t tile = ord < tiles_a ? (ord % ra) * t.tiles_a_cols + ord / ra : ord;
+    const int seg = (int)(item % t.splits);
+    const int64_t s0 = (int64_t)seg * per;
+    const int64_t nst = s0 < nsl ? (s0 + per < nsl ? per : nsl - s0) : 0;
+    const bool direct = t.splits == 1;
+    // gathered rows (region A: dense rows x all columns; region B: other
+    // rows x dense columns), requested before the tile's entry range is
+    // known so that the two loads overlap
+    int64_t tr, tcol, rcount, ccount;
+    const int32_t* rlist;
+    const int32_t* clist;
+    if (tile < tiles_a) {
+      tr = tile / t.tiles_a_cols;
+      tcol = tile % t.tiles_a_cols;
+      rlist = t.rows;
+      rcount = H;
+      clist = nullptr;  // identity over all columns
+      ccount = t.n;
+    } else {
+      const int64_t b = tile - tiles_a;
+      tr = b / tiles_b_cols;
+      tcol = b % tiles_b_cols;
+      rlist = t.rows + H;
+      rcount = mc;
+      clist = t.hot_cols;
+      ccount = Hc;
     }
-  };
-  auto stash = [&](int stage) {
-    uint16_t* As = smem + stage * kStage;
-    uint16_t* Bs = As + TM * LDK;
+    // chunk h covers staged row (tid / 8) + (kThreads / 8) h: A rows first,
+    // then BT rows; roff = byte offset of its row, or kOob for padding rows
+    // (their buffer loads return zeros without a memory access)
+    uint32_t roff[kChunks];
 #pragma unroll
     for (int h = 0; h < kChunks; ++h) {
       const int row = (tid >> 3) + h * (kThreads / 8);
-      *(uint4*)(As + row * LDK + skc) = ra[h];
-      *(uint4*)(Bs + row * LDK + skc) = rb[h];
-    }
-  };
-
-  const int w = tid / kWave, l = lane_id();
-  const int wr = w >> 1, wc = w & 1;
-  float16v acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int64_t nst = cdiv(t.K, TK);
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int64_t st = 0; st < nst; ++st) {
-    const int stage = (int)(st & 1);
-    if (st + 1 < nst) fetch((st + 1) * TK);
-    const uint16_t* As = smem + stage * kStage;
-    const uint16_t* Bs = As + TM * LDK;
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      const int kk = ks * 16 + (l >> 5) * 8;
-      uint4 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *(const uint4*)(As + (wr * 64 + i * 32 + (l & 31)) * LDK + kk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *(const uint4*)(Bs + (wc * 64 + j * 32 + (l & 31)) * LDK + kk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<BF16>(fa[i], fb[j], acc[i][j]);
-    }
-    if (st + 1 < nst) stash(stage ^ 1);
-    __syncthreads();
-  }
-  // 32x32 fp32 result layout: lane l holds column l%32; value v sits at row
-  // (v/4)*8 + (l/32)*4 + v%4.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wr * 64 + i * 32 + (v >> 2) * 8 + (l >> 5) * 4 + (v & 3);
-        const int col = wc * 64 + j * 32 + (l & 31);
-        Cs[row * LDC + col] = acc[i][j][v];
+      if (h < kChunksA) {
+        const int64_t i = tr * TM + row;
+        roff[h] = i < rcount ? (uint32_t)rlist[i] * (uint32_t)(t.lda * 2) : kOob;
+      } else {
+        const int64_t j = tcol * TN + (row - TM);
+        roff[h] = j < ccount ? (uint32_t)(clist ? clist[j] : (int32_t)j) * (uint32_t)(t.ldbt * 2)
+                             : kOob;
       }
-  __syncthreads();
-  OT* out = (OT*)t.out;
-  for (int32_t e = e0 + tid; e < e1; e += kThreads) {
-    const int32_t rc = t.ent_rc[e];
-    out[t.ent_pos[e]] = from_f32<OT>(Cs[(rc >> 16) * LDC + (rc & 0xffff)]);
+    }
+    const int32_t e0 = t.key_start[2 * tile], e1 = t.key_start[2 * tile + 2];
+    if (e1 <= e0) continue;  // no mask entry in this tile
+
+    // in-tile coordinates of the first epilogue round of each half,
+    // requested now (positions, needed only by whole-tile segments, are
+    // loaded in the epilogue)
+    int32_t qh[3] = {e0, t.key_start[2 * tile + 1], e1};
+    int32_t pre_rc[2][kEpi];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < kEpi; ++u) {
+        const int32_t q = qh[h] + tid + u * kThreads;
+        pre_rc[h][u] = q < qh[h + 1] ? t.ent_rc[q] : 0;
+      }
+
+    // always issued (a slice past the segment loads from kOob: zeros, no
+    // memory access), so the compiler can count the loads in flight and wait
+    // only for the older buffer
+    auto fetch = [&](uint4 (&rb)[kChunks], int64_t slice, bool live) {
+      const int64_t k = slice * TK + kc;
+      const bool ok = live && k < t.K;  // K is a multiple of 8: a chunk is all in or out
+      const uint32_t kb = (uint32_t)k * 2;
+#pragma unroll
+      for (int h = 0; h < kChunks; ++h) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(h < kChunksA ? rsA : rsB,
+                                                             ok ? roff[h] + kb : kOob, 0, 0);
+        rb[h] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    };
+    auto stash = [&](int stage, const uint4 (&rb)[kChunks]) {
+      uint16_t* S = smem + stage * kStage;
+#pragma unroll
+      for (int h = 0; h < kChunks; ++h) {
+        const int row = (tid >> 3) + h * (kThreads / 8);
+        *(uint4*)(S + row * LDK + kc) = rb[h];
+      }
+    };
+
+    float16v acc[BM][BN];
+#pragma unroll
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+      for (int j = 0; j < BN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto compute = [&](int stage) {
+      const uint16_t* As = smem + stage * kStage;
+      const uint16_t* Bs = As + TM * LDK;
+#pragma unroll
+      for (int ks = 0; ks < TK / 16; ++ks) {
+        const int kk = ks * 16 + (l >> 5) * 8;
+        uint4 fa[BM], fb[BN];
+#pragma unroll
+        for (int i = 0; i < BM; ++i)
+          fa[i] = *(const uint4*)(As + (wr * WM + i * 32 + (l & 31)) * LDK + kk);
+#pragma unroll
+        for (int j = 0; j < BN; ++j)
+          fb[j] = *(const uint4*)(Bs + (wc * WN + j * 32 + (l & 31)) * LDK + kk);
+#pragma unroll
+        for (int i = 0; i < BM; ++i)
+#pragma unroll
+          for (int j = 0; j < BN; ++j) acc[i][j] = mfma32<BF16>(fa[i], fb[j], acc[i][j]);
+      }
+    };
+
+    // slices [s0, s0 + nst) of K: slice st is computed from LDS stage st & 1
+    // while slice st + 1 is in flight into the register buffer
+    uint4 rb[kChunks];
+    fetch(rb, s0, nst > 0);
+    stash(0, rb);
+    fetch(rb, s0 + 1, nst > 1);
+    __syncthreads();
+    for (int64_t st = 0; st < nst; ++st) {
+      compute((int)(st & 1));
+      if (st + 1 < nst) stash((int)((st + 1) & 1), rb);
+      __syncthreads();
+      fetch(rb, s0 + st + 2, st + 2 < nst);
+    }
+
+    // epilogue: rows [half*HALF, (half+1)*HALF) of the block (the waves with
+    // wr == half) go to LDS, then every thread writes entries of that half,
+    // kEpi per round with all their loads issued together
+    float* Cs = (float*)smem;
+    auto write_round = [&](const int32_t (&rc)[kEpi], const int32_t (&pos)[kEpi], int32_t e,
+                           int32_t q1, int half) {
+#pragma unroll
+      for (int u = 0; u < kEpi; ++u) {
+        const int32_t q = e + u * kThreads;
+        if (q < q1) {
+          const float v = Cs[(rc[u] & 0xffff) * LDR + ((rc[u] >> 16) - half * HALF)];
+          if (direct)
+            ((OT*)t.out)[pos[u]] = from_f32<OT>(v);
+          else
+            t.part[(int64_t)seg * tiled + q] = v;
+        }
+      }
+    };
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int32_t q0 = qh[half], q1 = qh[half + 1];
+      if (q1 > q0) {
+        if (wr == half) {
+          // column-major: a lane's values v = 4q..4q+3 are 4 consecutive
+          // rows of one column, one 16-byte store (every store of the lane
+          // is an immediate offset from one address)
+          float* cb = Cs + (wc * WN + (l & 31)) * LDR + (l >> 5) * 4;
+#pragma unroll
+          for (int i = 0; i < BM; ++i)
+#pragma unroll
+            for (int j = 0; j < BN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *(float4*)(cb + j * 32 * LDR + i * 32 + q * 8) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]);
+        }
+        __syncthreads();
+        {
+          int32_t pos[kEpi];
+#pragma unroll
+          for (int u = 0; u < kEpi; ++u) {
+            const int32_t q = q0 + tid + u * kThreads;
+            pos[u] = (q < q1 && direct) ? t.ent_pos[q] : 0;
+          }
+          write_round(pre_rc[half], pos, q0 + tid, q1, half);
+        }
+        for (int32_t e = q0 + tid + kEpi * kThreads; e < q1; e += kEpi * kThreads) {
+          int32_t rc[kEpi], pos[kEpi];
+#pragma unroll
+          for (int u = 0; u < kEpi; ++u) {
+            const int32_t q = e + u * kThreads;
+            rc[u] = q < q1 ? t.ent_rc[q] : 0;
+            pos[u] = (q < q1 && direct) ? t.ent_pos[q] : 0;
+          }
+          write_round(rc, pos, e, q1, half);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// Tiles computed in several splits: out[ent_pos[e]] = sum over the tile's
+// splits j (in order) of part[j][e].  Workgroup (x, y) takes tile
+// x's entries [y * kSumChunk, (y + 1) * kSumChunk), kEpi per thread with all
+// loads of a round issued together.
+constexpr int kSumChunk = kEpi * 256;
+template <typename OT>
+__global__ __launch_bounds__(256) void sddmm_split_sum_kernel(TileArgs t) {
+  const int64_t tile = blockIdx.x;
+  if (tile >= t.sc->tiles) return;
+  const int nseg = t.splits;
+  if (nseg <= 1) return;
+  const int64_t tiled = t.sc->tiled;
+  const int32_t e1 = t.key_start[2 * tile + 2];
+  for (int32_t e = t.key_start[2 * tile] + (int32_t)(blockIdx.y * kSumChunk + threadIdx.x);
+       e < e1; e += (int32_t)(gridDim.y * kSumChunk)) {
+    float v[kEpi];
+    int32_t pos[kEpi];
+#pragma unroll
+    for (int u = 0; u < kEpi; ++u) {
+      const int32_t q = e + u * 256;
+      v[u] = q < e1 ? t.part[q] : 0.f;
+      pos[u] = q < e1 ? t.ent_pos[q] : 0;
+    }
+    for (int j = 1; j < nseg; ++j) {
+#pragma unroll
+      for (int u = 0; u < kEpi; ++u) {
+        const int32_t q = e + u * 256;
+        if (q < e1) v[u] += t.part[(int64_t)j * tiled + q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kEpi; ++u)
+      if (e + u * 256 < e1) ((OT*)t.out)[pos[u]] = from_f32<OT>(v[u]);
   }
 }
 
 // ----------------------------------------------------------------- plan --
 
+__global__ void plan_init_kernel(SddmmPlanScalars* sc) {
+  if (threadIdx.x == 0) *sc = SddmmPlanScalars{};
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Row offsets clamped into [0, nnz] and nondecreasing within a row.
+__device__ __forceinline__ void clamped_row(const int32_t* ro, int64_t r, int64_t nnz,
+                                            int64_t& p0, int64_t& p1) {
+  p0 = ro[r];
+  p1 = ro[r + 1];
+  p0 = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
+  p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
+}
+
 __global__ void row_flags_kernel(const int32_t* ro, int64_t m, int64_t nnz, int64_t thr,
                                  uint32_t* hot) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= m) return;
-  int64_t p0 = ro[r], p1 = ro[r + 1];
-  p0 = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
-  p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
+  int64_t p0, p1;
+  clamped_row(ro, r, nnz, p0, p1);
   const int64_t len = p1 - p0;
   hot[r] = (len > 0 && len >= thr) ? 1u : 0u;
 }
 
-__global__ void compact_rows_kernel(const uint32_t* hot, const uint32_t* rank, int64_t m,
-                                    int32_t* hot_rows, int32_t* cold_rows) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= m) return;
-  if (hot[r])
-    hot_rows[rank[r]] = (int32_t)r;
-  else
-    cold_rows[r - rank[r]] = (int32_t)r;
-}
-
-// 16 lanes per row.
+// 16 lanes per row: column counts over the rows that are not dense.
 template <typename IT>
 __global__ void col_count_kernel(const int32_t* ro, const IT* col, int64_t m, int64_t n,
                                  int64_t nnz, const uint32_t* hot, uint32_t* cnt) {
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
   const int sub = threadIdx.x & 15;
   if (r >= m || hot[r]) return;
-  int64_t p0 = ro[r], p1 = ro[r + 1];
-  p0 = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
-  p1 = p1 < p0 ? p0 : (p1 > nnz ? nnz : p1);
+  int64_t p0, p1;
+  clamped_row(ro, r, nnz, p0, p1);
   for (int64_t p = p0 + sub; p < p1; p += 16) {
     const int c = (int)col[p];
     if ((unsigned)c < (unsigned)n) atomicAdd(&cnt[c], 1u);
   }
 }
 
-__global__ void col_flags_kernel(const uint32_t* cnt, int64_t n, int64_t thr, uint32_t* flag) {
+// A column is dense when, over the mc = m - H other rows, it holds at least
+// ceil(tau * mc) entries (and at least one).
+__global__ void col_flags_kernel(const uint32_t* cnt, int64_t n, int64_t m, double tau,
+                                 const SddmmPlanScalars* sc, uint32_t* flag) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= n) return;
-  flag[c] = (cnt[c] > 0 && (int64_t)cnt[c] >= thr) ? 1u : 0u;
+  const int64_t mc = m - sc->H;
+  const int64_t thr = (int64_t)ceil(tau * (double)mc);
+  flag[c] = (mc > 0 && cnt[c] > 0 && (int64_t)cnt[c] >= thr) ? 1u : 0u;
+}
+
+// rows[0, H) = dense rows ascending, rows[H, m) = the others ascending.
+__global__ void compact_rows_kernel(const uint32_t* hot, const uint32_t* rank, int64_t m,
+                                    const SddmmPlanScalars* sc, int32_t* rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= m) return;
+  if (hot[r])
+    rows[rank[r]] = (int32_t)r;
+  else
+    rows[sc->H + (r - rank[r])] = (int32_t)r;
 }
 
 __global__ void compact_cols_kernel(const uint32_t* flag, const uint32_t* rank, int64_t n,
@@ -252,6 +433,22 @@ __global__ void compact_cols_kernel(const uint32_t* flag, const uint32_t* rank, 
   }
 }
 
+// Tile counts from the dense row and column counts.
+__global__ void derive_tiles_kernel(int64_t m, int64_t tiles_a_cols, SddmmPlanScalars* sc) {
+  if (threadIdx.x != 0) return;
+  const int64_t H = sc->H;
+  const int64_t mc = m - H;
+  const int64_t Hc = mc > 0 ? sc->Hc : 0;
+  const int64_t tiles_a = H > 0 ? cdiv(H, TM) * tiles_a_cols : 0;
+  const int64_t tbc = Hc > 0 ? cdiv(Hc, TN) : 0;
+  sc->mc = (int32_t)mc;
+  sc->Hc = (int32_t)Hc;
+  sc->tiles_a = (int32_t)tiles_a;
+  sc->tiles_b_cols = (int32_t)tbc;
+  sc->tiles = (int32_t)(tiles_a + (tbc > 0 ? cdiv(mc, TM) * tbc : 0));
+  sc->rest_count = 0;
+}
+
 struct ClassifyArgs {
   const int32_t* ro;
   const void* col;
@@ -259,42 +456,45 @@ struct ClassifyArgs {
   const uint32_t* hot;       // row flags
   const uint32_t* row_rank;  // exclusive rank among dense rows
   const int32_t* col_map;    // dense-column index or -1
-  int64_t tiles_a, tiles_a_cols, tiles_b_cols, tiles;
+  SddmmPlanScalars* sc;
+  int64_t tiles_a_cols;
+  int64_t rest_key;
   int nb;                    // column buckets of the remainder
   uint32_t* key;             // [nnz]
   uint32_t* rc;              // [nnz] in-tile coordinates, or the row (remainder)
-  uint32_t* rest_total;      // number of remainder entries (accumulated)
 };
 
-// 16 lanes per row: tile key and in-tile coordinates of every entry; an
-// entry of neither region gets key tiles + (its column bucket) and keeps its
-// row in rc.
+// 16 lanes per row: the key and in-tile coordinates of every entry; an entry
+// of neither region gets rest_key + (its column bucket) and keeps its row in
+// rc.
 template <typename IT>
 __global__ void classify_kernel(ClassifyArgs a) {
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
   const int sub = threadIdx.x & 15;
   if (r >= a.m) return;
   const IT* col = (const IT*)a.col;
-  int64_t p0 = a.ro[r], p1 = a.ro[r + 1];
-  p0 = p0 < 0 ? 0 : (p0 > a.nnz ? a.nnz : p0);
-  p1 = p1 < p0 ? p0 : (p1 > a.nnz ? a.nnz : p1);
+  int64_t p0, p1;
+  clamped_row(a.ro, r, a.nnz, p0, p1);
   const bool hot = a.hot[r] != 0;
-  const int64_t hr = a.row_rank[r];        // rank among dense rows
-  const int64_t cr = r - hr;               // rank among the other rows
+  const int64_t hr = a.row_rank[r];  // rank among dense rows
+  const int64_t cr = r - hr;         // rank among the other rows
+  const int64_t tiles_a = a.sc->tiles_a, tbc = a.sc->tiles_b_cols;
   uint32_t rest = 0;
   for (int64_t p = p0 + sub; p < p1; p += 16) {
     int c = (int)col[p];
     c = (unsigned)c < (unsigned)a.n ? c : 0;
-    uint32_t key, rc = 0;
+    uint32_t key, rc;
     if (hot) {
-      key = (uint32_t)((hr / TM) * a.tiles_a_cols + c / TN);
+      const int64_t tile = (hr / TM) * a.tiles_a_cols + c / TN;
+      key = (uint32_t)(2 * tile + ((hr % TM) >= HALF ? 1 : 0));
       rc = ((uint32_t)(hr % TM) << 16) | (uint32_t)(c % TN);
     } else if (a.col_map[c] >= 0) {
       const int64_t hc = a.col_map[c];
-      key = (uint32_t)(a.tiles_a + (cr / TM) * a.tiles_b_cols + hc / TN);
+      const int64_t tile = tiles_a + (cr / TM) * tbc + hc / TN;
+      key = (uint32_t)(2 * tile + ((cr % TM) >= HALF ? 1 : 0));
       rc = ((uint32_t)(cr % TM) << 16) | (uint32_t)(hc % TN);
     } else {
-      key = (uint32_t)(a.tiles + ((int64_t)c * a.nb) / a.n);
+      key = (uint32_t)(a.rest_key + ((int64_t)c * a.nb) / a.n);
       rc = (uint32_t)r;
       ++rest;
     }
@@ -302,30 +502,44 @@ __global__ void classify_kernel(ClassifyArgs a) {
     a.rc[p] = rc;
   }
   for (int o = 8; o > 0; o >>= 1) rest += __shfl_xor(rest, o, 16);
-  if (sub == 0 && rest) atomicAdd(a.rest_total, rest);
+  if (sub == 0 && rest) atomicAdd(&a.sc->rest_count, rest);
 }
 
-// All remainder entries into one bucket (keys tiles+b -> tiles).
-__global__ void merge_buckets_kernel(uint32_t* key, int64_t nnz, uint32_t tiles) {
+// Buckets pay when each remaining row keeps several remainder entries per
+// bucket (a row's A slice is reloaded once per row and bucket): at least 32
+// remainder entries per remaining row on average, else every remainder entry
+// goes to bucket 0.  Thread 0 records the bucket count.
+__global__ void merge_buckets_kernel(uint32_t* key, int64_t nnz, uint32_t rest_key, int nb_max,
+                                     int forced, SddmmPlanScalars* sc) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (p < nnz && key[p] > tiles) key[p] = tiles;
+  const int64_t mc = sc->mc;
+  const bool merge = !forced && nb_max > 1 && (int64_t)sc->rest_count < 32 * (mc > 0 ? mc : 1);
+  if (p == 0) sc->nb = merge ? 1 : nb_max;
+  if (merge && p < nnz && key[p] > rest_key) key[p] = rest_key;
 }
 
-// Key boundaries (tile_start[t] = first sorted entry with key >= t, for
-// t in [0, nkeys]: tiles, then the remainder buckets) and the gathered
-// in-tile coordinates / remainder rows.
-__global__ void tile_bounds_kernel(const uint32_t* skey, const uint32_t* src, const uint32_t* rc,
-                                   int64_t nnz, int64_t nkeys, int32_t* tile_start,
-                                   int32_t* ent_pos, int32_t* ent_rc) {
+// key_start[k] = first sorted entry with key >= k for k in [0, nkeys], and
+// the gathered positions and in-tile coordinates / rows.
+__global__ void key_bounds_kernel(const uint32_t* skey, const uint32_t* src, const uint32_t* rc,
+                                  int64_t nnz, int64_t nkeys, int32_t* key_start,
+                                  int32_t* ent_pos, int32_t* ent_rc) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q > nnz) return;
   const int64_t kprev = q == 0 ? -1 : (int64_t)skey[q - 1];
   const int64_t kcur = q == nnz ? nkeys : (int64_t)skey[q];
-  for (int64_t k = kprev + 1; k <= kcur; ++k) tile_start[k] = (int32_t)q;
+  for (int64_t k = kprev + 1; k <= kcur; ++k) key_start[k] = (int32_t)q;
   if (q == nnz) return;
   const uint32_t p = src[q];
   ent_pos[q] = (int32_t)p;
   ent_rc[q] = (int32_t)rc[p];
+}
+
+__global__ void plan_finish_kernel(const int32_t* key_start, int64_t nnz,
+                                   SddmmPlanScalars* sc) {
+  if (threadIdx.x != 0) return;
+  const int32_t tiled = key_start[2 * (int64_t)sc->tiles];
+  sc->tiled = tiled;
+  sc->rest = (int32_t)(nnz - tiled);
 }
 
 int bit_length(uint64_t v) {
@@ -337,23 +551,101 @@ int bit_length(uint64_t v) {
   return b;
 }
 
+int64_t max_tiles_for(int64_t m, int64_t n) { return (cdiv(m, TM) + 1) * cdiv(n, TN); }
+
+int planned_buckets(int64_t n, int* forced) {
+  const int64_t opt = option(kOptSddmmBuckets);
+  *forced = opt > 0;
+  if (opt > 0) return (int)(opt > kMaxBuckets ? kMaxBuckets : opt);
+  return n >= 1024 ? kMaxBuckets : 1;
+}
+
+struct PlanLayout {
+  size_t sc, rows, hot_cols, key_start, ent_pos, ent_rc, total;
+};
+PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
+  PlanLayout L{};
+  const int64_t nkeys = 2 * max_tiles_for(m, n) + kMaxBuckets;
+  size_t o = 0;
+  L.sc = o;
+  o += align256(sizeof(SddmmPlanScalars));
+  L.rows = o;
+  o += align256((size_t)(m > 0 ? m : 1) * 4);
+  L.hot_cols = o;
+  o += align256((size_t)(n > 0 ? n : 1) * 4);
+  L.key_start = o;
+  o += align256((size_t)(nkeys + 1) * 4);
+  L.ent_pos = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.ent_rc = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.total = o;
+  return L;
+}
+
+struct ScratchLayout {
+  size_t hot, rrank, ccnt, cflag, crank, col_map, key, rc, scan, radix, total;
+};
+ScratchLayout scratch_layout(int64_t m, int64_t n, int64_t nnz) {
+  ScratchLayout L{};
+  const size_t mb = align256((size_t)(m > 0 ? m : 1) * 4);
+  const size_t nb = align256((size_t)(n > 0 ? n : 1) * 4);
+  const size_t zb = align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  size_t o = 0;
+  L.hot = o;
+  o += mb;
+  L.rrank = o;
+  o += mb;
+  L.ccnt = o;
+  o += nb;
+  L.cflag = o;
+  o += nb;
+  L.crank = o;
+  o += nb;
+  L.col_map = o;
+  o += nb;
+  L.key = o;
+  o += zb;
+  L.rc = o;
+  o += zb;
+  L.scan = o;
+  o += align256(scan_workspace_bytes(m > n ? m : n));
+  L.radix = o;
+  o += align256(radix_pairs_workspace_bytes(nnz > 0 ? nnz : 1));
+  L.total = o;
+  return L;
+}
+
 template <typename OT>
-hipError_t launch_tiles_typed(const SddmmPlanDev& p, const TileArgs& ta, int dtype,
-                              hipStream_t s) {
+hipError_t launch_tiles_typed(const TileArgs& ta, unsigned grid, int dtype, hipStream_t s) {
   if (dtype == kBF16)
-    hipLaunchKernelGGL((sddmm_tile_kernel<true, OT>), dim3((unsigned)p.tiles), dim3(kThreads), 0,
-                       s, ta);
+    hipLaunchKernelGGL((sddmm_tile_kernel<true, OT>), dim3(grid), dim3(kThreads), 0, s, ta);
   else
-    hipLaunchKernelGGL((sddmm_tile_kernel<false, OT>), dim3((unsigned)p.tiles), dim3(kThreads),
-                       0, s, ta);
+    hipLaunchKernelGGL((sddmm_tile_kernel<false, OT>), dim3(grid), dim3(kThreads), 0, s, ta);
+  return hipGetLastError();
+}
+
+template <typename OT>
+hipError_t launch_split_sum(const TileArgs& ta, int64_t tiles, int64_t most, hipStream_t s) {
+  const int64_t chunks = cdiv(most > 0 ? most : 1, kSumChunk);
+  hipLaunchKernelGGL(sddmm_split_sum_kernel<OT>, dim3((unsigned)tiles, (unsigned)chunks),
+                     dim3(256), 0, s, ta);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
-                            const void* col, int col_i32, double tau, SddmmPlanDev* out,
-                            hipStream_t s) {
+size_t sddmm_plan_bytes(int64_t m, int64_t n, int64_t nnz) {
+  return plan_layout(m, n, nnz).total;
+}
+
+size_t sddmm_plan_scratch_bytes(int64_t m, int64_t n, int64_t nnz) {
+  return scratch_layout(m, n, nnz).total;
+}
+
+hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
+                              const void* col, int col_i32, double tau, void* mem,
+                              void* scratch, SddmmPlanDev* out, hipStream_t s) {
   *out = SddmmPlanDev{};
   out->m = m;
   out->n = n;
@@ -361,40 +653,51 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
   out->tau = tau;
   out->mask_ro = ro;
   out->mask_col = col;
-  const size_t mb = align256((size_t)(m + 1) * 4), nb = align256((size_t)(n + 1) * 4);
-  const size_t zb = align256((size_t)(nnz > 0 ? nnz : 1) * 4);
-  const size_t sws = scan_workspace_bytes(m > n ? m + 1 : n + 1);
-  const size_t rws = radix_pairs_workspace_bytes(nnz);
-  char* tmp = nullptr;
-  hipError_t e = hipMalloc(&tmp, 3 * mb + 3 * nb + 4 * zb + sws + rws + 256);
-  if (e != hipSuccess) return e;
-  uint32_t* hot = (uint32_t*)tmp;
-  uint32_t* rrank = (uint32_t*)(tmp + mb);
-  uint32_t* ccnt = (uint32_t*)(tmp + 3 * mb);
-  uint32_t* cflag = (uint32_t*)(tmp + 3 * mb + nb);
-  uint32_t* crank = (uint32_t*)(tmp + 3 * mb + 2 * nb);
-  uint32_t* key = (uint32_t*)(tmp + 3 * mb + 3 * nb);
-  uint32_t* rc = (uint32_t*)(tmp + 3 * mb + 3 * nb + zb);
-  uint32_t* skey = (uint32_t*)(tmp + 3 * mb + 3 * nb + 2 * zb);
-  uint32_t* src = (uint32_t*)(tmp + 3 * mb + 3 * nb + 3 * zb);
-  uint32_t* dtot = (uint32_t*)(tmp + 3 * mb + 3 * nb + 4 * zb);  // 4 counters
-  void* scan_ws = tmp + 3 * mb + 3 * nb + 4 * zb + 256;
-  void* radix_ws = (char*)scan_ws + sws;
-  uint32_t htot[4] = {0, 0, 0, 0};
+  out->tiles_a_cols = cdiv(n, TN);
+  out->max_tiles = max_tiles_for(m, n);
+  out->rest_key = 2 * out->max_tiles;
+  int forced = 0;
+  out->nb_max = planned_buckets(n, &forced);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0)
+    out->cus = cus;
+  const PlanLayout P = plan_layout(m, n, nnz);
+  const ScratchLayout W = scratch_layout(m, n, nnz);
+  char* pm = (char*)mem;
+  char* ws = (char*)scratch;
+  SddmmPlanScalars* sc = (SddmmPlanScalars*)(pm + P.sc);
+  out->sc = sc;
+  out->rows = (int32_t*)(pm + P.rows);
+  out->hot_cols = (int32_t*)(pm + P.hot_cols);
+  out->key_start = (int32_t*)(pm + P.key_start);
+  out->ent_pos = (int32_t*)(pm + P.ent_pos);
+  out->ent_rc = (int32_t*)(pm + P.ent_rc);
+  uint32_t* hot = (uint32_t*)(ws + W.hot);
+  uint32_t* rrank = (uint32_t*)(ws + W.rrank);
+  uint32_t* ccnt = (uint32_t*)(ws + W.ccnt);
+  uint32_t* cflag = (uint32_t*)(ws + W.cflag);
+  uint32_t* crank = (uint32_t*)(ws + W.crank);
+  int32_t* col_map = (int32_t*)(ws + W.col_map);
+  uint32_t* key = (uint32_t*)(ws + W.key);
+  uint32_t* rc = (uint32_t*)(ws + W.rc);
+  void* scan_ws = ws + W.scan;
+  void* radix_ws = ws + W.radix;
+
   const unsigned gm = (unsigned)cdiv(m > 0 ? m : 1, 256), gn = (unsigned)cdiv(n > 0 ? n : 1, 256);
   const unsigned gm16 = (unsigned)cdiv((m > 0 ? m : 1) * 16, 256);
-  do {
+  const int64_t nkeys = out->rest_key + out->nb_max;
+  hipError_t e;
+  hipLaunchKernelGGL(plan_init_kernel, dim3(1), dim3(64), 0, s, sc);
+  if (m > 0) {
     const int64_t thr_r = (int64_t)ceil(tau * (double)n);
-    if (m > 0) {
-      hipLaunchKernelGGL(row_flags_kernel, dim3(gm), dim3(256), 0, s, ro, m, nnz, thr_r, hot);
-      if ((e = exclusive_scan_u32(hot, rrank, m, dtot, scan_ws, s)) != hipSuccess) break;
-    }
-    if ((e = hipMemcpyAsync(htot, dtot, 4, hipMemcpyDeviceToHost, s)) != hipSuccess) break;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
-    const int64_t H = m > 0 ? htot[0] : 0;
-    const int64_t mc = m - H;
-    // column counts over the remaining rows
-    if ((e = hipMemsetAsync(ccnt, 0, (size_t)(n + 1) * 4, s)) != hipSuccess) break;
+    hipLaunchKernelGGL(row_flags_kernel, dim3(gm), dim3(256), 0, s, ro, m, nnz, thr_r, hot);
+    if ((e = exclusive_scan_u32(hot, rrank, m, (uint32_t*)&sc->H, scan_ws, s)) != hipSuccess)
+      return e;
+  }
+  if (n > 0) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(gn), dim3(256), 0, s, ccnt, n, 0u);
     if (m > 0) {
       if (col_i32)
         hipLaunchKernelGGL(col_count_kernel<int32_t>, dim3(gm16), dim3(256), 0, s, ro,
@@ -403,126 +706,134 @@ hipError_t build_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
         hipLaunchKernelGGL(col_count_kernel<int16_t>, dim3(gm16), dim3(256), 0, s, ro,
                            (const int16_t*)col, m, n, nnz, hot, ccnt);
     }
-    const int64_t thr_c = (int64_t)ceil(tau * (double)mc);
-    int64_t Hc = 0;
-    if (n > 0) {
-      hipLaunchKernelGGL(col_flags_kernel, dim3(gn), dim3(256), 0, s, ccnt, n, thr_c, cflag);
-      if ((e = exclusive_scan_u32(cflag, crank, n, dtot + 1, scan_ws, s)) != hipSuccess) break;
-      if ((e = hipMemcpyAsync(htot + 1, dtot + 1, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
-        break;
-      if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
-      Hc = htot[1];
-    }
-    if (mc == 0) Hc = 0;
-    out->n_rows_hot = H;
-    out->n_rows_cold = mc;
-    out->n_cols_hot = Hc;
-    out->tiles_a_cols = cdiv(n, TN);
-    out->tiles_a = H > 0 ? cdiv(H, TM) * out->tiles_a_cols : 0;
-    out->tiles_b_cols = Hc > 0 ? cdiv(Hc, TN) : 0;
-    const int64_t tiles_b = (Hc > 0 && mc > 0) ? cdiv(mc, TM) * out->tiles_b_cols : 0;
-    out->tiles = out->tiles_a + tiles_b;
-    // remainder column buckets, one per XCD when there are enough columns
-    // (revisited below once the remainder is counted)
-    out->nb = n >= 1024 ? kMaxBuckets : 1;
-    int forced = 0;
-    if (const char* env = getenv("SPOPS_SDDMM_BUCKETS")) {
-      const int v = atoi(env);
-      out->nb = v < 1 ? 1 : (v > kMaxBuckets ? kMaxBuckets : v);
-      forced = 1;
-    }
-    // plan memory
-    const size_t b_hot = align256((size_t)(H + 1) * 4), b_cold = align256((size_t)(mc + 1) * 4);
-    const size_t b_hc = align256((size_t)(Hc + 1) * 4), b_cm = nb;
-    const size_t b_ts = align256((size_t)(out->tiles + kMaxBuckets + 1) * 4);
-    char* mem = nullptr;
-    if ((e = hipMalloc(&mem, b_hot + b_cold + b_hc + b_cm + b_ts + 2 * zb)) != hipSuccess)
-      break;
-    out->mem = mem;
-    out->hot_rows = (int32_t*)mem;
-    out->cold_rows = (int32_t*)(mem + b_hot);
-    out->hot_cols = (int32_t*)(mem + b_hot + b_cold);
-    int32_t* col_map = (int32_t*)(mem + b_hot + b_cold + b_hc);
-    out->tile_start = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm);
-    out->ent_pos = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm + b_ts);
-    out->ent_rc = (int32_t*)(mem + b_hot + b_cold + b_hc + b_cm + b_ts + zb);
-    if (m > 0)
-      hipLaunchKernelGGL(compact_rows_kernel, dim3(gm), dim3(256), 0, s, hot, rrank, m,
-                         out->hot_rows, out->cold_rows);
-    if (n > 0) {
-      if (mc > 0) {
-        hipLaunchKernelGGL(compact_cols_kernel, dim3(gn), dim3(256), 0, s, cflag, crank, n,
-                           out->hot_cols, col_map);
-      } else {
-        if ((e = hipMemsetAsync(col_map, 0xff, (size_t)n * 4, s)) != hipSuccess) break;
-      }
-    }
-    if ((e = hipGetLastError()) != hipSuccess) break;
-    if (m > 0) {
-      if ((e = hipMemsetAsync(dtot + 2, 0, 4, s)) != hipSuccess) break;
-      ClassifyArgs ca{ro,   col,       m,     n,    nnz,      hot, rrank, col_map,
-                      out->tiles_a, out->tiles_a_cols, out->tiles_b_cols, out->tiles,
-                      out->nb, key,  rc, dtot + 2};
-      if (col_i32)
-        hipLaunchKernelGGL(classify_kernel<int32_t>, dim3(gm16), dim3(256), 0, s, ca);
-      else
-        hipLaunchKernelGGL(classify_kernel<int16_t>, dim3(gm16), dim3(256), 0, s, ca);
-      if ((e = hipGetLastError()) != hipSuccess) break;
-      if ((e = hipMemcpyAsync(htot + 2, dtot + 2, 4, hipMemcpyDeviceToHost, s)) != hipSuccess)
-        break;
-      if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
-      // Buckets pay when each remaining row keeps several entries per bucket
-      // (A's row is reloaded once per row and bucket): at least 32 remainder
-      // entries per remaining row on average, else one bucket.
-      if (!forced && out->nb > 1 && (int64_t)htot[2] < 32 * (mc > 0 ? mc : 1)) {
-        out->nb = 1;
-        hipLaunchKernelGGL(merge_buckets_kernel, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s,
-                           key, nnz, (uint32_t)out->tiles);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-      }
-    }
-    const int64_t nkeys = out->tiles + out->nb;
-    if (nnz > 0) {
-      if ((e = radix_sort_u32_iota(key, nnz, bit_length((uint64_t)(nkeys - 1)), skey, src,
-                                   radix_ws, s)) != hipSuccess)
-        break;
-    }
-    hipLaunchKernelGGL(tile_bounds_kernel, dim3((unsigned)cdiv(nnz + 1, 256)), dim3(256), 0, s,
-                       skey, src, rc, nnz, nkeys, out->tile_start, out->ent_pos, out->ent_rc);
-    if ((e = hipGetLastError()) != hipSuccess) break;
-    int32_t bounds[kMaxBuckets + 1] = {};
-    if ((e = hipMemcpyAsync(bounds, out->tile_start + out->tiles, (size_t)(out->nb + 1) * 4,
-                            hipMemcpyDeviceToHost, s)) != hipSuccess)
-      break;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
-    const int32_t tiled = bounds[0];
-    out->tiled_nnz = tiled;
-    out->rest_nnz = nnz - tiled;
-    for (int b = 0; b <= out->nb; ++b) out->bucket_start[b] = bounds[b] - tiled;
-    out->rest_pos = out->ent_pos + tiled;
-    out->rest_row = out->ent_rc + tiled;
-  } while (0);
-  hipFree(tmp);
-  if (e != hipSuccess) free_sddmm_plan(out);
-  return e;
+    hipLaunchKernelGGL(col_flags_kernel, dim3(gn), dim3(256), 0, s, ccnt, n, m, tau, sc, cflag);
+    if ((e = exclusive_scan_u32(cflag, crank, n, (uint32_t*)&sc->Hc, scan_ws, s)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(compact_cols_kernel, dim3(gn), dim3(256), 0, s, cflag, crank, n,
+                       out->hot_cols, col_map);
+  }
+  if (m > 0)
+    hipLaunchKernelGGL(compact_rows_kernel, dim3(gm), dim3(256), 0, s, hot, rrank, m, sc,
+                       out->rows);
+  hipLaunchKernelGGL(derive_tiles_kernel, dim3(1), dim3(64), 0, s, m, out->tiles_a_cols, sc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (nnz > 0) {
+    ClassifyArgs ca{ro,  col,  m,       n,   nnz, hot, rrank, col_map, sc, out->tiles_a_cols,
+                    out->rest_key, out->nb_max, key, rc};
+    if (col_i32)
+      hipLaunchKernelGGL(classify_kernel<int32_t>, dim3(gm16), dim3(256), 0, s, ca);
+    else
+      hipLaunchKernelGGL(classify_kernel<int16_t>, dim3(gm16), dim3(256), 0, s, ca);
+  }
+  hipLaunchKernelGGL(merge_buckets_kernel, dim3((unsigned)cdiv(nnz > 0 ? nnz : 1, 256)),
+                     dim3(256), 0, s, key, nnz, (uint32_t)out->rest_key, out->nb_max, forced,
+                     sc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const uint32_t* skey = key;
+  const uint32_t* src = key;
+  if (nnz > 0) {
+    if ((e = radix_sort_u32_iota_ptrs(key, nnz, bit_length((uint64_t)(nkeys - 1)), radix_ws,
+                                      &skey, &src, s)) != hipSuccess)
+      return e;
+  }
+  hipLaunchKernelGGL(key_bounds_kernel, dim3((unsigned)cdiv(nnz + 1, 256)), dim3(256), 0, s,
+                     skey, src, rc, nnz, nkeys, out->key_start, out->ent_pos, out->ent_rc);
+  hipLaunchKernelGGL(plan_finish_kernel, dim3(1), dim3(64), 0, s, out->key_start, nnz, sc);
+  return hipGetLastError();
 }
 
-void free_sddmm_plan(SddmmPlanDev* p) {
-  if (p->mem) hipFree(p->mem);
-  *p = SddmmPlanDev{};
+hipError_t fetch_sddmm_plan_counts(SddmmPlanDev* p, hipStream_t s) {
+  int32_t ks[kMaxBuckets + 1] = {};
+  hipError_t e = hipMemcpyAsync(&p->h, p->sc, sizeof(SddmmPlanScalars), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ks, p->key_start + p->rest_key, (size_t)(p->nb_max + 1) * 4,
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  for (int b = 0; b <= kMaxBuckets; ++b) p->bucket_start[b] = ks[b <= p->h.nb ? b : p->h.nb];
+  // most entries in one tile (sizes the grid of the partial-sum kernel)
+  p->max_tile_nnz = 0;
+  if (p->h.tiles > 0) {
+    int32_t* kst = (int32_t*)malloc((size_t)(2 * p->h.tiles + 1) * 4);
+    if (!kst) return hipErrorOutOfMemory;
+    e = hipMemcpyAsync(kst, p->key_start, (size_t)(2 * p->h.tiles + 1) * 4,
+                       hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess)
+      for (int64_t t = 0; t < p->h.tiles; ++t) {
+        const int64_t c = kst[2 * t + 2] - kst[2 * t];
+        p->max_tile_nnz = c > p->max_tile_nnz ? c : p->max_tile_nnz;
+      }
+    free(kst);
+    if (e != hipSuccess) return e;
+  }
+  p->host_ok = true;
+  return hipSuccess;
+}
+
+// K splits of the dense tiles for this plan and K.  With the tile count on
+// the host (plans made by spops_sddmm_plan_create): kOptSddmmSplits when set,
+// else the count S (at most the number of K slices, and at most 16) that
+// minimizes rounds * (slices per item + 2), where a round is one item per
+// compute unit and 2 slices stand for an item's fixed cost (gathering its
+// rows, pipeline start, epilogue); ties go to fewer splits.  Without host
+// counts: 1.
+SddmmTileSched sddmm_tile_schedule(const SddmmPlanDev& p, int64_t K) {
+  SddmmTileSched sc{};
+  sc.splits = 1;
+  if (!p.host_ok || p.h.tiles <= 0 || K <= 0) return sc;
+  const int64_t nsl = cdiv(K, TK);
+  const int64_t smax = nsl < 16 ? nsl : 16;
+  const int64_t opt = option(kOptSddmmSplits);
+  if (opt > 0) {
+    sc.splits = (int)(opt < smax ? opt : smax);
+    return sc;
+  }
+  int64_t best_cost = INT64_MAX;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t cost = cdiv(p.h.tiles * S, (int64_t)p.cus * kTileWgPerCu) * (cdiv(nsl, S) + 2);
+    if (cost < best_cost) {
+      best_cost = cost;
+      sc.splits = (int)S;
+    }
+  }
+  return sc;
+}
+
+size_t sddmm_split_bytes(const SddmmPlanDev& p, const SddmmTileSched& sc) {
+  if (sc.splits <= 1 || !p.host_ok) return 0;
+  return align256((size_t)sc.splits * (size_t)(p.h.tiled > 0 ? p.h.tiled : 1) * 4);
 }
 
 hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, int64_t lda,
                               const void* BT, int64_t ldbt, int dtype, void* out, int out_dtype,
-                              hipStream_t s) {
-  if (p.tiles == 0 || p.tiled_nnz == 0) return hipSuccess;
-  TileArgs ta{K,          lda,          ldbt,          p.n,           (const uint16_t*)A,
-              (const uint16_t*)BT,      p.hot_rows,    p.cold_rows,   p.hot_cols,
-              p.n_rows_hot, p.n_rows_cold, p.n_cols_hot, p.tiles_a,    p.tiles_a_cols,
-              p.tiles_b_cols, p.tile_start, p.ent_pos,  p.ent_rc,      out};
-  if (out_dtype == kF32) return launch_tiles_typed<float>(p, ta, dtype, s);
-  if (dtype == kBF16) return launch_tiles_typed<bf16_t>(p, ta, dtype, s);
-  return launch_tiles_typed<_Float16>(p, ta, dtype, s);
+                              const SddmmTileSched& sched, float* part, hipStream_t s) {
+  if (p.host_ok && (p.h.tiles == 0 || p.h.tiled == 0)) return hipSuccess;
+  SddmmTileSched sc = sched;
+  if (!p.host_ok || (sc.splits > 1 && !part)) sc.splits = 1;
+  TileArgs ta{K,           lda,        ldbt,         p.n,          (const uint16_t*)A,
+              (const uint16_t*)BT,     (uint32_t)(p.m * lda * 2),  (uint32_t)(p.n * ldbt * 2),
+              p.rows,       p.hot_cols,   p.sc,
+              p.tiles_a_cols,          p.key_start,  p.ent_pos,    p.ent_rc,
+              sc.splits,   part,       out};
+  // one workgroup per item when the tile count is known on the host, else a
+  // grid of at most two rounds over the compute units looping over the
+  // items; a multiple of 8 (the kernel's XCD-aware order needs it)
+  int64_t grid = p.host_ok ? p.h.tiles * (int64_t)sc.splits : p.max_tiles;
+  if (!p.host_ok && grid > 2 * kTileWgPerCu * p.cus) grid = 2 * kTileWgPerCu * p.cus;
+  grid = (grid + 7) & ~(int64_t)7;
+  hipError_t e;
+  if (out_dtype == kF32)
+    e = launch_tiles_typed<float>(ta, (unsigned)grid, dtype, s);
+  else if (dtype == kBF16)
+    e = launch_tiles_typed<bf16_t>(ta, (unsigned)grid, dtype, s);
+  else
+    e = launch_tiles_typed<_Float16>(ta, (unsigned)grid, dtype, s);
+  if (e != hipSuccess || sc.splits <= 1) return e;
+  const int64_t most = p.max_tile_nnz;
+  if (out_dtype == kF32) return launch_split_sum<float>(ta, p.h.tiles, most, s);
+  if (dtype == kBF16) return launch_split_sum<bf16_t>(ta, p.h.tiles, most, s);
+  return launch_split_sum<_Float16>(ta, p.h.tiles, most, s);
 }
 
 }  // namespace spops

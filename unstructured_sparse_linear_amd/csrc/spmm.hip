@@ -809,199 +809,6 @@ __global__ __launch_bounds__(kBlock) void spmv_row_kernel(SpmmArgs a) {
   }
 }
 
-// --------------------------------------------------------- wide-N waves --
-
-// Eight consecutive entries starting at p (a multiple of 8): column words and
-// value words.  Wave-uniform addresses, so full groups become scalar loads;
-// the group that reaches past nnz is read entry by entry.
-template <typename VT, typename IT>
-__device__ __forceinline__ void load_entries(const IT* col, const VT* val, int64_t p, int64_t nnz,
-                                             int* c, uint32_t* vw) {
-  constexpr int VW = sizeof(VT) == 4 ? 8 : 4;  // value words per 8 entries
-  if (p + 8 <= nnz) {
-    if constexpr (sizeof(IT) == 2) {
-      const uint4 q = *(const uint4*)(col + p);
-      const uint32_t cw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = (int)(int16_t)(cw[u >> 1] >> ((u & 1) * 16));
-    } else {
-      const uint4 q0 = *(const uint4*)(col + p), q1 = *(const uint4*)(col + p + 4);
-      c[0] = (int)q0.x; c[1] = (int)q0.y; c[2] = (int)q0.z; c[3] = (int)q0.w;
-      c[4] = (int)q1.x; c[5] = (int)q1.y; c[6] = (int)q1.z; c[7] = (int)q1.w;
-    }
-    const uint4 v0 = *(const uint4*)(val + p);
-    vw[0] = v0.x; vw[1] = v0.y; vw[2] = v0.z; vw[3] = v0.w;
-    if constexpr (VW == 8) {
-      const uint4 v1 = *(const uint4*)(val + p + 4);
-      vw[4] = v1.x; vw[5] = v1.y; vw[6] = v1.z; vw[7] = v1.w;
-    }
-  } else {
-    const uint16_t* v16 = (const uint16_t*)val;
-    const uint32_t* v32 = (const uint32_t*)val;
-#pragma unroll
-    for (int u = 0; u < VW; ++u) vw[u] = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool in = p + u < nnz;
-      c[u] = in ? (int)col[p + u] : -1;
-      if constexpr (VW == 8) {
-        vw[u] = in ? v32[p + u] : 0u;
-      } else {
-        vw[u >> 1] |= (in ? (uint32_t)v16[p + u] : 0u) << ((u & 1) * 16);
-      }
-    }
-  }
-}
-
-// One batch of 8 consecutive entries: which are in range, their value words,
-// and the lane's B vectors for them (loads in flight until consumed).
-template <typename VT, int W>
-struct WaveBatch {
-  uint32_t b[8][W];
-  uint32_t vw[sizeof(VT) == 4 ? 8 : 4];
-  bool ok[8];
-};
-
-template <typename VT, typename IT, int VEC>
-__device__ __forceinline__ void fetch_batch(const SpmmArgs& a, __amdgpu_buffer_rsrc_t rs,
-                                            uint32_t bbytes, int64_t p, int64_t q0, int64_t q1,
-                                            uint32_t joff,
-                                            WaveBatch<VT, BufLoad<VEC * sizeof(VT)>::words>& bt) {
-  constexpr int BYTES = VEC * (int)sizeof(VT);
-  const uint32_t ldbb = (uint32_t)(a.ldb * (int64_t)sizeof(VT));
-  int c[8];
-  load_entries<VT, IT>((const IT*)a.col, (const VT*)a.val, p, a.nnz, c, bt.vw);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    bt.ok[u] = (p + u >= q0) && (p + u < q1);
-    const bool use = bt.ok[u] && (unsigned)c[u] < (unsigned)a.k;
-    BufLoad<BYTES>::load(rs, joff, use ? (uint32_t)c[u] * ldbb : bbytes, bt.b[u]);
-  }
-}
-
-template <typename VT, int VEC>
-__device__ __forceinline__ void consume_batch(
-    const WaveBatch<VT, BufLoad<VEC * sizeof(VT)>::words>& bt, float* acc) {
-  constexpr int W = BufLoad<VEC * sizeof(VT)>::words;
-  if constexpr (sizeof(VT) == 4) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float v = bt.ok[u] ? __uint_as_float(bt.vw[u]) : 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(v, __uint_as_float(bt.b[u][e]), acc[e]);
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t vp = bt.vw[t];
-      if (!bt.ok[2 * t]) vp &= 0xffff0000u;
-      if (!bt.ok[2 * t + 1]) vp &= 0x0000ffffu;
-#pragma unroll
-      for (int d = 0; d < W; ++d) {
-        const uint32_t lo = __builtin_amdgcn_perm(bt.b[2 * t + 1][d], bt.b[2 * t][d], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(bt.b[2 * t + 1][d], bt.b[2 * t][d], 0x07060302u);
-        acc[2 * d] = dot2(lo, vp, acc[2 * d], (VT*)nullptr);
-        acc[2 * d + 1] = dot2(hi, vp, acc[2 * d + 1], (VT*)nullptr);
-      }
-    }
-  }
-}
-
-// Entries [q0, q1) of one row, columns [j, j+VEC) of this lane (byte offset
-// joff inside a B row).  Entries outside the range or with a column outside
-// [0, k) load from past the end of B (zeros) and carry a zero value.  Two
-// batches are in flight: the next one is fetched before the current one is
-// consumed.
-template <typename VT, typename IT, int VEC>
-__device__ __forceinline__ void accumulate_wave(const SpmmArgs& a, __amdgpu_buffer_rsrc_t rs,
-                                                uint32_t bbytes, int64_t q0, int64_t q1,
-                                                uint32_t joff, float* acc) {
-  constexpr int W = BufLoad<VEC * sizeof(VT)>::words;
-  int64_t p = q0 & ~(int64_t)7;
-  if (p >= q1) return;
-  WaveBatch<VT, W> x, y;
-  fetch_batch<VT, IT, VEC>(a, rs, bbytes, p, q0, q1, joff, x);
-  while (true) {
-    const bool more = p + 8 < q1;
-    if (more) fetch_batch<VT, IT, VEC>(a, rs, bbytes, p + 8, q0, q1, joff, y);
-    consume_batch<VT, VEC>(x, acc);
-    if (!more) break;
-    p += 8;
-    const bool more2 = p + 8 < q1;
-    if (more2) fetch_batch<VT, IT, VEC>(a, rs, bbytes, p + 8, q0, q1, joff, x);
-    consume_batch<VT, VEC>(y, acc);
-    if (!more2) break;
-    p += 8;
-  }
-}
-
-// Blocks are (item, slice) with slice = blockIdx % ns.  Items [0, P): one
-// chunk of a long row, its 4 waves summed in LDS.  Items [P, ...): 4 whole
-// rows, one per wave.
-template <typename VT, typename OT, typename IT, int VEC>
-__global__ __launch_bounds__(kBlock) void spmm_wave_kernel(SpmmArgs a, int64_t ns,
-                                                           int64_t nbw_padded, uint32_t bbytes) {
-  constexpr int NW = kBlock / kWave;
-  const int64_t slice = (int64_t)blockIdx.x % ns;
-  const int64_t item = (int64_t)blockIdx.x / ns;
-  const int w = wave_uniform((int)(threadIdx.x / kWave));
-  const int lane = lane_id();
-  const int64_t j = slice * (kWave * VEC) + (int64_t)lane * VEC;
-  const uint32_t joff = (uint32_t)(j * (int64_t)sizeof(VT));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B, bbytes);
-  float acc[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-
-  if (item < a.P) {
-    __shared__ float red[NW - 1][kWave * VEC];
-    const int64_t g = item;
-    const int64_t i = a.item_pos[g];
-    const int64_t ch = a.item_chunk[g];
-    const int64_t r = load_row(a.row_idx, a.ri_i32, i);
-    int64_t rs0 = 0, re0 = 0;
-    if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, rs0, re0);
-    const int64_t c0 = rs0 + ch * kChunkLen;
-    const int64_t c1 = (c0 + kChunkLen < re0) ? c0 + kChunkLen : re0;
-    const int64_t len = c1 > c0 ? c1 - c0 : 0;
-    const int64_t sub = (cdiv(len, NW) + 7) & ~(int64_t)7;
-    int64_t q0 = c0 + w * sub;
-    int64_t q1 = q0 + sub;
-    q0 = q0 < c1 ? q0 : c1;
-    q1 = q1 < c1 ? q1 : c1;
-    accumulate_wave<VT, IT, VEC>(a, rs, bbytes, q0, q1, joff, acc);
-    if (w > 0) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) red[w - 1][lane * VEC + e] = acc[e];
-    }
-    __syncthreads();
-    if (w == 0 && j < a.N) {
-      for (int q = 0; q < NW - 1; ++q) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += red[q][lane * VEC + e];
-      }
-      const int64_t nch = cdiv(re0 - rs0, kChunkLen);
-      if (nch <= 1) {
-        if (r >= 0 && r < a.m) store_vec<OT, VEC>((OT*)a.C + r * a.ldc + j, acc);
-      } else {
-        store_vec<float, VEC>(a.partial + g * a.N + j, acc);
-      }
-    }
-    return;
-  }
-  const int64_t i = row_block(item - a.P, nbw_padded, a.natural) * NW + w;
-  if (i >= a.m) return;
-  const int64_t r = wave_uniform((int)(a.natural ? i : load_row(a.row_idx, a.ri_i32, i)));
-  if (r < 0 || r >= a.m) return;
-  int64_t p0, p1;
-  row_range(a.ro, r, a.nnz, p0, p1);
-  p0 = wave_uniform((int)p0);
-  p1 = wave_uniform((int)p1);
-  if (a.P > 0 && p1 - p0 > a.T) return;  // handled by the chunk blocks
-  accumulate_wave<VT, IT, VEC>(a, rs, bbytes, p0, p1, joff, acc);
-  if (j < a.N) store_vec<OT, VEC>((OT*)a.C + r * a.ldc + j, acc);
-}
-
 // Sum the partial rows of each multi-chunk row in chunk order.
 template <typename OT>
 __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(SpmmArgs a) {
@@ -1040,11 +847,11 @@ hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
     const int64_t nwin = cdiv(a.N, LPR * VEC);
     const int64_t blocks = (a.P + nbw) * nwin;
     if (blocks == 0) return hipSuccess;
-    // SPOPS_SPMM_NOBUF=1 selects the pointer-load path, which otherwise only
-    // runs for operands of 2 GiB and more (read per call, for tests)
-    const char* noBuf = getenv("SPOPS_SPMM_NOBUF");
+    // the pointer-load path runs for operands of 2 GiB and more, or when the
+    // kOptSpmmPointerLoads switch asks for it (for its test)
     const int64_t esz = sizeof(VT) > sizeof(IT) ? sizeof(VT) : sizeof(IT);
-    const bool buf = !(noBuf && noBuf[0] == '1') && a.k * a.ldb * (int64_t)sizeof(VT) < ((int64_t)1 << 31) &&
+    const bool buf = option(kOptSpmmPointerLoads) == 0 &&
+                     a.k * a.ldb * (int64_t)sizeof(VT) < ((int64_t)1 << 31) &&
                      (a.nnz + 64) * esz < ((int64_t)1 << 31);
     if (buf)
       hipLaunchKernelGGL((spmm_kernel<VT, OT, IT, LPR, VEC, true, true>), dim3((unsigned)blocks),
@@ -1063,34 +870,6 @@ hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
                        dim3(kBlock), 0, s, a, nwin);
   }
   return hipGetLastError();
-}
-
-template <typename VT, typename OT, typename IT, int VEC>
-hipError_t launch_waves(const SpmmArgs& a, uint32_t bbytes, hipStream_t s) {
-  const int64_t ns = cdiv(a.N, kWave * VEC);
-  const int64_t nbw = a.natural ? pad8(cdiv(a.m, kBlock / kWave)) : cdiv(a.m, kBlock / kWave);
-  const int64_t blocks = ns * (a.P + nbw);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((spmm_wave_kernel<VT, OT, IT, VEC>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                     s, a, ns, nbw, bbytes);
-  return hipGetLastError();
-}
-
-// Per-lane vector width for the wave kernel: the widest (up to 16 bytes) whose
-// 64*v-column slice of B (k rows) stays within ~2.5 MB, so one slice fits an
-// XCD's L2 with room for the rest; if none fits, the narrowest (most slices).
-// 0 when N is narrower than one wave of the narrowest width.
-template <typename VT>
-int wave_vec(int64_t k, int64_t N) {
-  const int64_t budget = 5 << 19;
-  const int lo = sizeof(VT) == 2 ? 2 : 1;
-  int best = 0;
-  for (int v = 16 / (int)sizeof(VT); v >= lo; v /= 2) {
-    if ((int64_t)kWave * v > N) continue;
-    if (k * kWave * v * (int64_t)sizeof(VT) <= budget) return v;
-    best = v;
-  }
-  return best;
 }
 
 template <typename VT, typename OT, typename IT>
@@ -1144,46 +923,22 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     }
     e = hipGetLastError();
   } else {
-    // The wave kernel is kept for shapes where it measures faster; by default
-    // (and with SPOPS_SPMM_KERNEL=group) the group kernel runs, which was
-    // faster on every workload measured so far.
-    static const char* choice = getenv("SPOPS_SPMM_KERNEL");  // "wave" | "group" | unset
-    const bool allow_wave = choice && choice[0] == 'w';
-    const int wv = allow_wave ? wave_vec<VT>(a.k, a.N) : 0;
-    const int64_t bbytes = a.k * a.ldb * (int64_t)sizeof(VT);
-    const bool wave_ok = wv > 0 && a.N % wv == 0 && a.ldb % wv == 0 &&
-                         a.ldc % wv == 0 && bbytes + 64 < ((int64_t)1 << 31) &&
+    const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
                          ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
-                         ((uintptr_t)a.partial % 16 == 0) && ((uintptr_t)a.col % 16 == 0) &&
-                         ((uintptr_t)a.val % 16 == 0);
-    if (wave_ok) {
-      if constexpr (sizeof(VT) == 2) {
-        if (wv == 8) e = launch_waves<VT, OT, IT, 8>(a, (uint32_t)bbytes, s);
-        else if (wv == 4) e = launch_waves<VT, OT, IT, 4>(a, (uint32_t)bbytes, s);
-        else e = launch_waves<VT, OT, IT, 2>(a, (uint32_t)bbytes, s);
-      } else {
-        if (wv == 4) e = launch_waves<VT, OT, IT, 4>(a, (uint32_t)bbytes, s);
-        else if (wv == 2) e = launch_waves<VT, OT, IT, 2>(a, (uint32_t)bbytes, s);
-        else e = launch_waves<VT, OT, IT, 1>(a, (uint32_t)bbytes, s);
-      }
-    } else {
-      const bool aligned = (a.N % VEC == 0) && (a.ldb % VEC == 0) && (a.ldc % VEC == 0) &&
-                           ((uintptr_t)a.B % 16 == 0) && ((uintptr_t)a.C % 16 == 0) &&
-                           ((uintptr_t)a.partial % 16 == 0);
-      // lanes per row: enough for N (at most a wave), then halved (not below
-      // 16) while the B columns one window reads exceed an XCD's 4 MB L2, so
-      // that the windows the dispatcher spreads over the XCDs stay cached
-      int64_t nv = cdiv(a.N, VEC);
-      int64_t lpr = 4;
-      while (lpr < 64 && lpr < nv) lpr *= 2;
-      while (lpr > 16 && a.k * lpr * 16 > ((int64_t)4 << 20)) lpr /= 2;
-      nv = lpr;
-      if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
-      else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
-      else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
-      else if (nv <= 32) e = launch_rows<VT, OT, IT, 32>(a, aligned, s);
-      else e = launch_rows<VT, OT, IT, 64>(a, aligned, s);
-    }
+                         ((uintptr_t)a.partial % 16 == 0);
+    // lanes per row: enough for N (at most a wave), then halved (not below
+    // 16) while the B columns one window reads exceed an XCD's 4 MB L2, so
+    // that the windows the dispatcher spreads over the XCDs stay cached
+    int64_t nv = cdiv(a.N, VEC);
+    int64_t lpr = 4;
+    while (lpr < 64 && lpr < nv) lpr *= 2;
+    while (lpr > 16 && a.k * lpr * 16 > ((int64_t)4 << 20)) lpr /= 2;
+    nv = lpr;
+    if (nv <= 4) e = launch_rows<VT, OT, IT, 4>(a, aligned, s);
+    else if (nv <= 8) e = launch_rows<VT, OT, IT, 8>(a, aligned, s);
+    else if (nv <= 16) e = launch_rows<VT, OT, IT, 16>(a, aligned, s);
+    else if (nv <= 32) e = launch_rows<VT, OT, IT, 32>(a, aligned, s);
+    else e = launch_rows<VT, OT, IT, 64>(a, aligned, s);
   }
   if (e != hipSuccess) return e;
   if (a.S > 0 && !whole_rows) {

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "spops_sddmm": ([cp, vp, i64, i64, vp, i64, i32, vp, i32, i32, vp, vp, sz, vp],
                             i32),
             "spops_sddmm_workspace_size": ([cp, i64, i32, i32, vp, P(sz)], i32),
+            "spops_set_option": ([i32, i64], i32),
+            "spops_get_option": ([i32, P(i64)], i32),
             "spops_sddmm_plan_create": ([cp, ctypes.c_double, vp, P(vp)], i32),
             "spops_sddmm_plan_destroy": ([vp], i32),
             "spops_sddmm_plan_info": ([vp, P(i64), P(i64), P(i64), P(i64), P(i64)], i32),
@@ -202,7 +204,7 @@ class SddmmPlan:
         d = csr_desc(None, row_offsets, None, col_idx, m, n)
         h = ctypes.c_void_p()
         if tau is None:
-            tau = float(os.environ.get("SPOPS_HOT_DENSITY", "0"))
+            tau = 0.0  # the library's default density threshold
         _check("spops_sddmm_plan_create", lib().spops_sddmm_plan_create(
             ctypes.byref(d), ctypes.c_double(tau), _stream(row_offsets), ctypes.byref(h)))
         self.handle = h
@@ -272,6 +274,37 @@ def clear_plan_caches():
     _ws_pool.clear()
 
 
+# --------------------------------------------------------------- options --
+
+OPTIONS = {"spmm_pointer_loads": 0, "transpose_force_scan": 1, "transpose_wide_records": 2,
+           "sddmm_buckets": 3, "sddmm_splits": 4}
+
+
+def set_option(name: str, value: int) -> int:
+    """Sets a process-wide switch of the library (include/spops.h,
+    spops_set_option) and returns its previous value."""
+    o = OPTIONS[name]
+    old = ctypes.c_int64()
+    _check("spops_get_option", lib().spops_get_option(o, ctypes.byref(old)))
+    _check("spops_set_option", lib().spops_set_option(o, int(value)))
+    return old.value
+
+
+class option:
+    """Context manager: `with option("sddmm_splits", 4): ...`."""
+
+    def __init__(self, name: str, value: int):
+        self.name, self.value = name, value
+
+    def __enter__(self):
+        self.old = set_option(self.name, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        set_option(self.name, self.old)
+        return False
+
+
 # ------------------------------------------------------------ operations --
 
 def spmm(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.Tensor,
@@ -309,8 +342,11 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
           backend: str = "structure_aware", out_dtype: torch.dtype = torch.float32,
           plan: Optional[SddmmPlan] = None, tau: Optional[float] = None,
           out: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """values[p] = A[r(p)] . BT[c(p)] at every position of the CSR mask."""
+          workspace: Optional[torch.Tensor] = None, use_plan: bool = True) -> torch.Tensor:
+    """values[p] = A[r(p)] . BT[c(p)] at every position of the CSR mask.
+    The structure-aware backend uses `plan`, else a cached plan for this
+    mask; with use_plan=False and no plan the library partitions the mask
+    inside the call (in the workspace, no allocation or synchronization)."""
     if backend not in _BACKENDS:
         raise ValueError(f"backend must be one of {sorted(_BACKENDS)}")
     _require(A, "A", tuple(_DT))
@@ -324,7 +360,7 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
     if out is None:
         out = torch.empty(nnz, dtype=out_dtype, device=A.device)
     b = _BACKENDS[backend]
-    if b == STRUCTURE_AWARE and plan is None and nnz > 0:
+    if b == STRUCTURE_AWARE and plan is None and use_plan and nnz > 0:
         plan = _sddmm_plans.get(("sddmm", _tkey(out_row_offsets), _tkey(out_col_indices), m, n,
                                  tau), lambda: SddmmPlan(out_row_offsets, out_col_indices, m, n,
                                                          tau),
