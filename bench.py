@@ -1,27 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the CSR sparse-dense hot path on one MI355X.
 
-A step is one pass of the whole path over one synthetic workload, every
+Headline: the structure-aware SDDMM on the cross-clustered 4096 x 11008 mask
+with f16 operands (K = 2048), the largest workload in the metric's units.
+`value` is that operation's algorithmic bytes over its cold-cache time (GB/s);
+`roofline` describes its kernels against the HBM peak.
+
+A step is one pass of the whole hot path over the headline workload, every
 operation on the GPU through libspops:
   1. SpMM          C = A @ B                     (row order from row_idx)
   2. SDDMM         A_d @ BT^T sampled at A's mask (structure-aware backend)
   3. csr_add       W += A in place
   4. csr_transpose A^T in CSR
   5. row order     row_idx of A^T (rows by entry count)
-Plans (SpMM row splitting, SDDMM dense-row/column partition) depend only on
-the sparsity pattern; they are built once before timing (plan once, execute
+captured once as a HIP graph and replayed K times (ms_per_step).  Plans
+(SpMM row splitting, SDDMM dense-row/column partition) depend only on the
+sparsity pattern; they are built once before timing (plan once, execute
 many) and their build time is reported separately.
 
+`per_config` times every gated case of the other workloads the same way
+(SpMM on the LLM-adapter mask, SDDMM f16 and bf16 on the cross mask, SpMV
+and 32-column SpMM on the banded SPD matrix, SpMM and SDDMM on the Zipf-row
+matrix): cold median / p10 / p90, algorithmic bytes, fraction of the HBM
+peak, counter traffic where committed, the on-chip gather rate against the
+measured ceiling, and the float64 oracle's time on the host for the same
+operation.
+
 Timing.  Every working set here fits in the 256 MB Infinity Cache, so each
-timed region starts after an untimed write of a 512 MiB scratch buffer that
-evicts L2 and the Infinity Cache (inputs resident in HBM, caches cold).  The
-step (all operations, in order) is captured once as a HIP graph and replayed,
-so host launch gaps do not count; each replay is bracketed by HIP events on
-its stream.  `value` = algorithmic bytes of the step / mean replay time.  The
-per-operation breakdown times each operation alone, eagerly, right after its
-own flush (the flush keeps the GPU busy while the host enqueues the
-operation, so the events bracket the kernels only).  The wall clock of the K
-graph steps (synchronize on both sides, flushes included) is reported too.
+timed call starts after an untimed write of a 512 MiB scratch buffer that
+evicts L2 and the Infinity Cache (inputs resident in HBM, caches cold), and
+is bracketed by HIP events on the stream the library launches on.
 
 Algorithmic bytes per operation (each input read once, each output written
 once; k' / n' = distinct columns touched, m' = rows with entries):
@@ -47,7 +55,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 512 << 20        # > 256 MB Infinity Cache + 8 x 4 MB L2
-DEFAULT_CONFIG = 2             # the configuration the metric is quoted on
+DEFAULT_CONFIG = 3             # headline: the largest workload in the metric's units
+DEFAULT_DTYPE = "f16"
+# the operations each workload names (the others are run as derived cases)
+NAMED_OPS = {1: ("spmm", "sddmm"), 2: ("spmm",), 3: ("sddmm",), 4: ("spmv", "spmm"),
+             5: ("spmm", "sddmm")}
+# gated cases of every workload: (config, value dtype, operation)
+GATED = [(2, "f16", "spmm"), (3, "f16", "sddmm"), (3, "bf16", "sddmm"), (4, "f32", "spmv"),
+         (4, "f32", "spmm"), (5, "bf16", "spmm"), (5, "bf16", "sddmm")]
 ESZ = {"f32": 4, "f16": 2, "bf16": 2}
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -58,8 +73,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=DEFAULT_CONFIG,
-                   help="workload 1-5 (2 is the headline configuration)")
-    p.add_argument("--dtype", default=None, help="value dtype override (config 3: f16|bf16)")
+                   help="workload 1-5 (3, the cross-clustered SDDMM, is the headline)")
+    p.add_argument("--dtype", default=None,
+                   help="value dtype of config 3 (f16, the default, or bf16)")
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the metric)")
     p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
     p.add_argument("--serial-step", action="store_true",
@@ -74,6 +90,8 @@ def parse():
                    help="also write one JSON record per operation to this file (JSONL)")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the copy and gather rate measurements")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip the per-workload table of the gated cases")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
@@ -180,15 +198,17 @@ def op_kernels(spmm_info, sddmm_info, m, n, nnz):
                                 "store_perm_kernel"])}
 
 
-def traffic_for(op, config):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def traffic_for(op, config, dt=None):
+    """HBM bytes per call (all the operation's kernels) from committed
+    rocprofv3 counter runs, if they were taken on the current kernel source;
+    else None.  Keyed by workload ("config3_f16") or config ("config3")."""
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(f"config{config}", {}).get(op)
+    ent = (rec.get(f"config{config}_{dt}", {}) if dt else {}).get(op) or \
+        rec.get(f"config{config}", {}).get(op)
     if not ent or ent.get("source_sha") != kernel_sources_sha(KERNEL_FILES[op]):
         return None
     return ent.get("hbm_bytes_per_launch")
@@ -479,6 +499,104 @@ def gathered_bytes(op, A, N, K, dt):
     return 0, 0
 
 
+def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None):
+    """One gated case alone: plan built untimed, then `reps` cold calls (each
+    after the cache flush) bracketed by HIP events on the current stream.
+    With `oracle`, the float64 oracle of the same operation on the host
+    (one warm-up, median of 3)."""
+    import torch
+    from unstructured_sparse_linear_amd import gen
+
+    w = gen.make_config(cfg, dt=dt if cfg == 3 else None)
+    A = w.get("A")
+    dt = w.dt
+
+    def to(x, d=None):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    ro, ci = to(A.row_offsets), to(A.col_idx)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    N, K = 1, w.K
+    t0 = time.perf_counter()
+    if op in ("spmm", "spmv"):
+        v = to(A.values, dt)
+        Bh = w.get("B1") if op == "spmv" else w.get("B")
+        B = to(Bh, dt)
+        N = B.shape[1]
+        plan = S.SpmmPlan(ro, ri, ci, A.n)
+        out = torch.empty((A.m, N), dtype=torch.float32, device=dev)
+        ws = plan.workspace(N, dev)
+        fn = lambda: S.spmm(v, ro, ri, ci, B, A.m, plan=plan, out=out)  # noqa: E731
+        info = plan.info()
+    else:
+        Ad, BT = to(w.get("Ad"), dt), to(w.get("BT"), dt)
+        plan = S.SddmmPlan(ro, ci, A.m, A.n)
+        out = torch.empty(A.nnz, dtype=torch.float32, device=dev)
+        fn = lambda: S.sddmm(ro, ri, ci, Ad, BT, plan=plan, out=out)  # noqa: E731
+        info = plan.info()
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = []
+    for _ in range(reps):
+        if not args.no_flush:
+            flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    t = float(np.median(ts))
+    ab = alg_bytes(A, N, K, dt)[op if op != "spmv" else "spmv"]
+    fl = flops(A, N, K)[op]
+    traffic = traffic_for(op, cfg, dt)
+    ent = {"workload": w.name if cfg == 3 else gen.CONFIG_NAMES[cfg], "op": op, "dtype": dt,
+           "m": A.m, "n": A.n, "nnz": A.nnz, "N_or_K": N if op in ("spmm", "spmv") else K,
+           "kernels": op_kernels(info if op != "sddmm" else {}, info if op == "sddmm" else {},
+                                 A.m, A.n, A.nnz)[op],
+           "plan": info, "plan_ms": round(plan_ms, 2),
+           "us_median": round(t * 1e3, 2), "us_p10": round(ts[len(ts) // 10] * 1e3, 2),
+           "us_p90": round(ts[(9 * len(ts)) // 10] * 1e3, 2),
+           "alg_bytes": int(ab), "gbps": round(ab / t / 1e6, 1),
+           "frac_hbm": round(ab / t / 1e6 / HBM_PEAK_GBS, 4),
+           "gflops": round(fl / t / 1e6, 1),
+           "hbm_bytes_counters": traffic,
+           "traffic_ratio": round(traffic / ab, 2) if traffic else None}
+    gb, seg = gathered_bytes(op, A, N, K, dt)
+    if ceil and gb:
+        key = ("gather_l2_4kib_gbps" if seg > 2048 else "gather_l2_1kib_gbps" if seg > 512
+               else "gather_l2_512b_gbps")
+        rate = gb / t / 1e6
+        ent["gather_rate_gbps"] = round(rate, 1)
+        ent["frac_of_gather_ceiling"] = round(rate / ceil[key], 4)
+        ent["gather_ceiling"] = key
+    if oracle is not None:
+        if op in ("spmm", "spmv"):
+            f = lambda: oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, Bh, dt)  # noqa
+        else:
+            Adh, BTh = w.get("Ad"), w.get("BT")
+            f = lambda: oracle.sddmm(A.row_offsets, A.col_idx, Adh, BTh, dt)  # noqa
+        f()
+        cts = []
+        for _ in range(3):
+            c0 = time.perf_counter()
+            f()
+            cts.append(time.perf_counter() - c0)
+        ct = float(np.median(cts))
+        ent["oracle_ms"] = round(ct * 1e3, 2)
+        ent["oracle_gbps"] = round(ab / ct / 1e9, 3)
+        ent["oracle_threads"] = oracle.num_threads()
+        ent["gpu_over_oracle"] = round(ct * 1e3 / t, 1)
+    return ent
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -555,7 +673,8 @@ def main():
     if args.config == 4 and "spmm" in ops and "spmv" not in ops:
         ops.insert(ops.index("spmm") + 1, "spmv")  # config 4 names both N = 1 and N = 32
 
-    w = gen.make_config(args.config, dt=args.dtype)
+    w = gen.make_config(args.config,
+                        dt=args.dtype or (DEFAULT_DTYPE if args.config == 3 else None))
     A = w.get("A")
     dt = w.dt
     N = w.N[-1]
@@ -730,7 +849,7 @@ def main():
     total_flops = sum(fl.get(o, 0) for o in ops)
     breakdown = {}
     for op in ops:
-        t = float(np.mean(per_op[op]))
+        t = float(np.median(per_op[op]))
         breakdown[op] = {"ms": round(t, 4), "ms_p10": round(float(np.percentile(per_op[op], 10)), 4),
                          "ms_p90": round(float(np.percentile(per_op[op], 90)), 4),
                          "alg_bytes": int(ab[op]), "gbps": round(ab[op] / t / 1e6, 1),
@@ -738,17 +857,17 @@ def main():
         if op in fl:
             breakdown[op]["gflops"] = round(fl[op] / t / 1e6, 1)
         breakdown[op]["ms_warm"] = round(warm[op], 4)
-    # the dominant kernel: the longer of SpMM and SDDMM (the operations the
-    # metric is about; each is one kernel unless long rows are split or the
-    # mask has dense tiles, and then its kernels are listed together)
+    # the headline operation: the longer of the operations the workload names
+    # (its kernels listed together: long rows split, dense tiles plus the
+    # remainder)
     kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.n, A.nnz)
-    gated = [o for o in ops if o in ("spmm", "spmv", "sddmm")]
+    gated = [o for o in ops if o in NAMED_OPS[args.config]]
     dom = max(gated or ops, key=lambda o: breakdown[o]["ms"])
     achieved = ab[dom] / breakdown[dom]["ms"] / 1e6
-    traffic = traffic_for(dom, args.config)
+    traffic = traffic_for(dom, args.config, dt)
     result = {
         "metric": "SpMM/SDDMM effective HBM GB/s and GFLOP/s (2*nnz*N), % of HBM roofline",
-        "value": round(total_bytes / mean_step / 1e6, 2),
+        "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -764,9 +883,13 @@ def main():
                    "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)",
                    "step": "eager" if args.no_graph else
                    "hip graph replay, streams: " + " | ".join("+".join(x) for x in lanes)},
+        "value_op": {"op": dom, "us": round(breakdown[dom]["ms"] * 1e3, 2),
+                     "alg_bytes": int(ab[dom]), "gflops": breakdown[dom].get("gflops"),
+                     "frac_hbm": round(achieved / HBM_PEAK_GBS, 4),
+                     "timing": "cold median over the steps, HIP events on the library's stream"},
         "eager_sum_of_ops_ms": round(sum(float(np.mean(v)) for v in per_op.values()), 4),
-        "gflops": round(total_flops / mean_step / 1e6, 1),
-        "frac_hbm": round(total_bytes / mean_step / 1e6 / HBM_PEAK_GBS, 4),
+        "step_gbps_all_ops": round(total_bytes / mean_step / 1e6, 2),
+        "step_gflops": round(total_flops / mean_step / 1e6, 1),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 4),
                                 round(float(np.percentile(step_ms, 90)), 4)],
@@ -794,13 +917,27 @@ def main():
             result["roofline"]["frac_of_gather_ceiling"] = round(rate / ceil[key], 4)
     if not args.no_adapter:
         result["next_adapter_step"] = adapter_step(S, w, A, dt, N, dev, flush, args)
-    if args.config == 4:
-        result["next_cg"] = cg_solve(S, w, A, dev, args)
-    if args.config == DEFAULT_CONFIG and not args.no_adapter:
-        result["next_delta_spmv"] = delta_spmv_bench(S, dev, flush, args)
+    oracle = None
     if not args.no_cpu_baseline:
         import oracle
-        result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, ops, oracle)
+        result["cpu_baseline"] = cpu_baseline(w, A, dt, N, K, [dom], oracle)
+        result["cpu_baseline"]["sample"] = (
+            f"the headline operation ({dom}) on the full workload, one warm-up then the "
+            "median of 3; the float64 oracle as it stands")
+    if not args.no_per_config:
+        ceil = result.get("ceilings")
+        per = {}
+        for cfg, cdt, op in GATED:
+            ent = measure_case(S, cfg, cdt, op, dev, flush, max(args.steps, 10), args, ceil,
+                               oracle)
+            per[f"{ent['workload']}:{op}"] = ent
+            torch.cuda.empty_cache()
+        result["per_config"] = per
+    if not args.no_adapter:
+        w4 = gen.make_config(4)
+        result["next_cg"] = cg_solve(S, w4, w4.get("A"), dev, args)
+        if args.config == DEFAULT_CONFIG:
+            result["next_delta_spmv"] = delta_spmv_bench(S, dev, flush, args)
     if args.records:
         write_records(args.records, result, args, A, dt, N, K, ab, fl)
     print(json.dumps(result))
