@@ -115,6 +115,9 @@ const char* spops_status_string(spops_status status);
  *       remainder in plans built afterwards (0: chosen per mask).
  *   SPOPS_OPT_SDDMM_SPLITS   1..16: K splits of the structure-aware dense
  *       tiles (0: chosen per plan and K); changes spops_sddmm_workspace_size.
+ *   SPOPS_OPT_SDDMM_REST_SPLIT  1..8 or 16: pieces of K for the structure-aware
+ *       remainder (1: no split; 0: chosen from the size of BT); changes
+ *       spops_sddmm_workspace_size.
  * spops_set_option returns SPOPS_ERR_UNSUPPORTED for an unknown option and
  * SPOPS_ERR_ARGUMENT for a negative value.  Calls running concurrently with
  * a change may see either value. */
@@ -123,7 +126,8 @@ typedef enum spops_option {
   SPOPS_OPT_TRANSPOSE_FORCE_SCAN = 1,
   SPOPS_OPT_TRANSPOSE_WIDE_RECORDS = 2,
   SPOPS_OPT_SDDMM_BUCKETS = 3,
-  SPOPS_OPT_SDDMM_SPLITS = 4
+  SPOPS_OPT_SDDMM_SPLITS = 4,
+  SPOPS_OPT_SDDMM_REST_SPLIT = 5
 } spops_option;
 spops_status spops_set_option(spops_option option, int64_t value);
 spops_status spops_get_option(spops_option option, int64_t* value);

@@ -136,12 +136,12 @@ def test_sddmm_workspace_size_contract(L):
 
 def test_options_round_trip(L):
     v = ctypes.c_int64()
-    for opt in range(5):
+    for opt in range(6):
         assert L.spops_get_option(opt, ctypes.byref(v)) == 0 and v.value == 0
         assert L.spops_set_option(opt, 3) == 0
         assert L.spops_get_option(opt, ctypes.byref(v)) == 0 and v.value == 3
         assert L.spops_set_option(opt, 0) == 0
-    assert L.spops_set_option(5, 1) == 6 and L.spops_set_option(-1, 1) == 6
+    assert L.spops_set_option(6, 1) == 6 and L.spops_set_option(-1, 1) == 6
     assert L.spops_set_option(0, -1) == 9
     assert L.spops_get_option(0, None) == 1
     assert S.set_option("sddmm_splits", 4) == 0

@@ -474,6 +474,31 @@ def test_sddmm_tiles_split_k(dt, m, n, K, hr, hc, splits):
     assert np.array_equal(host_f64(outi), refi)
 
 
+@pytest.mark.parametrize("dt,m,n,K,hr,hc", TILE_CASES)
+@pytest.mark.parametrize("pieces", [1, 2, 8, 16])
+def test_sddmm_remainder_k_pieces(dt, m, n, K, hr, hc, pieces):
+    # the plan's remainder with K cut into pieces (one per XCD, fp32 partial
+    # sums added in piece order) against the oracle; bit-exact on integers
+    M = cross_csr(13, m, n, hr, hc)
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, n)
+    plan = S.SddmmPlan(ro, ci, m, n)
+    assert plan.info()["rest_nnz"] > 0
+    Ad = gen.dense(13, 100, gen.S_A, (m, K), dt)
+    BT = gen.dense(13, 100, gen.S_BT, (n, K), dt)
+    Ai = gen.dense(14, 100, gen.S_A, (m, K), dt, integer_values=True)
+    Bi = gen.dense(14, 100, gen.S_BT, (n, K), dt, integer_values=True)
+    with S.option("sddmm_rest_split", pieces):
+        out = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan)
+        outi = S.sddmm(ro, ri, ci, dev(Ai, dt), dev(Bi, dt), plan=plan)
+        out16 = S.sddmm(ro, ri, ci, dev(Ad, dt), dev(BT, dt), plan=plan,
+                        out_dtype=TORCH_DT[dt])
+    ref = oracle.sddmm(M.row_offsets, M.col_idx, Ad, BT, dt)
+    assert_close(host_f64(out), ref, dt, f"sddmm remainder in {pieces} pieces")
+    assert rel_err(host_f64(out16), ref) <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -11) + 1e-5
+    assert np.array_equal(host_f64(outi), oracle.sddmm(M.row_offsets, M.col_idx, Ai, Bi, dt))
+
+
 @pytest.mark.parametrize("dt,m,n,K,hr,hc", TILE_CASES[:2])
 def test_sddmm_inline_plan_matches_plan(dt, m, n, K, hr, hc):
     # without a plan the partition is built in the call's workspace; on

@@ -302,6 +302,29 @@ static size_t sddmm_inline_plan_bytes(const spops_csr* mask) {
          sddmm_plan_scratch_bytes(mask->rows, mask->cols, mask->nnz);
 }
 
+// Pieces of K for the plan's remainder (1: none).  Splitting K over the
+// XCDs (piece b on XCD b) lets each L2 hold its slice of BT, so the
+// remainder's BT rows, each gathered by several entries, come from L2; it
+// pays when BT exceeds what the eight L2s hold together.  The option
+// kOptSddmmRestSplit sets the count (1 turns the split off).
+static int sddmm_rest_pieces(const SddmmPlanDev& P, int64_t K, spops_dtype in_type) {
+  if (!P.host_ok || P.h.rest <= 0 || in_type == SPOPS_F32) return 1;
+  const int64_t opt = option(kOptSddmmRestSplit);
+  int pieces = opt > 0 ? (int)(opt < 16 ? opt : 16)
+                       : (P.n * K * 2 > ((int64_t)32 << 20) ? 8 : 1);
+  if (pieces > 8) pieces = 16;
+  while (pieces > 1 && K % (8 * pieces) != 0) pieces /= 2;
+  return pieces;
+}
+
+static size_t sddmm_plan_ws_bytes(const SddmmPlanDev& P, int64_t K, spops_dtype in_type,
+                                  size_t* rest_off) {
+  const size_t tiles = align256(sddmm_split_bytes(P, sddmm_tile_schedule(P, K)));
+  const int pieces = sddmm_rest_pieces(P, K, in_type);
+  *rest_off = tiles;
+  return tiles + (pieces > 1 ? align256((size_t)pieces * (size_t)P.h.rest * 4) : 0);
+}
+
 spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_dtype in_type,
                                         spops_sddmm_backend backend,
                                         const spops_sddmm_plan* plan, size_t* bytes) {
@@ -316,8 +339,9 @@ spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_
   if (backend != SPOPS_SDDMM_STRUCTURE_AWARE || !sddmm_tiles_possible(in_type, K) ||
       mask->nnz == 0)
     return SPOPS_OK;
+  size_t rest_off = 0;
   if (plan)
-    *bytes = sddmm_split_bytes(plan->dev, sddmm_tile_schedule(plan->dev, K));
+    *bytes = sddmm_plan_ws_bytes(plan->dev, K, in_type, &rest_off);
   else
     *bytes = sddmm_inline_plan_bytes(mask);
   return SPOPS_OK;
@@ -386,12 +410,25 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     g.out_dtype = out_type;
     return from_hip(launch_sddmm_general(g, s));
   };
-  // the plan's remainder through the entry-list kernel, bucket by bucket
-  auto remainder = [&](const SddmmPlanDev& P) {
+  // the plan's remainder through the entry-list kernel, bucket by bucket,
+  // or with K cut into pieces (partial sums in `part`, then their sum)
+  auto remainder = [&](const SddmmPlanDev& P, int pieces, float* part) {
     r.pos = P.ent_pos;
     r.rows = P.ent_rc;
     if (P.host_ok) {
       if (P.h.rest == 0) return hipSuccess;
+      if (pieces > 1) {
+        r.nb = pieces;
+        r.ksplit = pieces;
+        r.kpiece = K / pieces;
+        r.part = part;
+        r.bstart[0] = P.bucket_start[0];
+        r.bstart[1] = P.bucket_start[P.h.nb];
+        hipError_t e = launch_sddmm_list(r, s);
+        if (e != hipSuccess) return e;
+        return launch_sddmm_piece_sum(part, pieces, P.h.rest, P.ent_pos, P.bucket_start[0],
+                                      out_values, out_type, s);
+      }
       r.nb = P.h.nb;
       for (int b = 0; b <= P.h.nb; ++b) r.bstart[b] = P.bucket_start[b];
     } else {
@@ -406,7 +443,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     // 32-bit or unaligned inputs: the plan's remainder still runs where the
     // plan found no tiles (its remainder is then the whole mask)
     if (plan && plan->dev.host_ok && plan->dev.h.tiles == 0 && list_ok)
-      return from_hip(remainder(plan->dev));
+      return from_hip(remainder(plan->dev, 1, nullptr));
     return general();
   }
   if (!plan) {
@@ -424,17 +461,19 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     if (e == hipSuccess)
       e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type,
                              sddmm_tile_schedule(P, K), nullptr, s);
-    if (e == hipSuccess) e = remainder(P);
+    if (e == hipSuccess) e = remainder(P, 1, nullptr);
     return from_hip(e);
   }
   const SddmmPlanDev& P = plan->dev;
   const SddmmTileSched sched = sddmm_tile_schedule(P, K);
-  const size_t need = sddmm_split_bytes(P, sched);
+  size_t rest_off = 0;
+  const size_t need = sddmm_plan_ws_bytes(P, K, in_type, &rest_off);
   if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0))
     return SPOPS_ERR_WORKSPACE;
   hipError_t e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type,
                                     sched, (float*)workspace, s);
-  if (e == hipSuccess) e = remainder(P);
+  if (e == hipSuccess)
+    e = remainder(P, sddmm_rest_pieces(P, K, in_type), (float*)((char*)workspace + rest_off));
   return from_hip(e);
 }
 

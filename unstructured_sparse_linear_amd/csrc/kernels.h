@@ -219,8 +219,19 @@ struct SddmmListArgs {
   // bounds the entries of one bucket
   const int32_t* bstart_dev;
   int64_t max_bucket;
+  // K split (ksplit > 1, nb == ksplit): bucket b is piece b of K (kpiece
+  // elements at offset b * kpiece) over all entries of bucket 0's range; the
+  // piece's fp32 dot products go to part[b * (range length) + entry - start]
+  int ksplit;
+  int64_t kpiece;
+  float* part;
 };
 hipError_t launch_sddmm_list(const SddmmListArgs& a, hipStream_t s);
+// out[pos[j]] = sum over pieces b (in order) of part[b * count + j - start]
+// for the entries j in [start, start + count) of a K-split list.
+hipError_t launch_sddmm_piece_sum(const float* part, int pieces, int64_t count,
+                                  const int32_t* pos, int64_t start, void* out, int out_dtype,
+                                  hipStream_t s);
 
 // ------------------------------------------------------------- options --
 // Process-wide switches (spops_set_option), read on every call.
@@ -230,7 +241,8 @@ enum Option : int {
   kOptTransposeWideRecords = 2,
   kOptSddmmBuckets = 3,
   kOptSddmmSplits = 4,
-  kOptCount = 5
+  kOptSddmmRestSplit = 5,
+  kOptCount = 6
 };
 int64_t option(int o);
 

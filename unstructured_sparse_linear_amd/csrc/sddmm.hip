@@ -211,11 +211,20 @@ __global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
   // One wave per workgroup: the wave index is blockIdx, a scalar, so the
   // loop bounds and the rows derived from it stay in scalar registers.
   // The grid is a multiple of nb; a wave takes chunks wave, wave + per, ...
-  const int b = (int)(blockIdx.x % (unsigned)a.nb);
+  const bool split = a.ksplit > 1;
+  // buckets: b = blockIdx mod nb (bucket b on XCD b mod 8); with more than
+  // 8 K pieces, the first 8 * per workgroups take pieces 0..7 (piece x on
+  // XCD x), the next 8 * per pieces 8..15, and so on, so each XCD works
+  // through its pieces one after the other
   const int64_t per = gridDim.x / (unsigned)a.nb;
-  const int64_t bs = a.bstart_dev ? (int64_t)a.bstart_dev[b] : a.bstart[b];
-  const int64_t be = a.bstart_dev ? (int64_t)a.bstart_dev[b + 1] : a.bstart[b + 1];
-  for (int64_t wave = blockIdx.x / (unsigned)a.nb; bs + wave * E < be; wave += per) {
+  const bool seq = split && a.nb > 8;
+  const int b = seq ? (int)(blockIdx.x % 8 + 8 * ((blockIdx.x / 8) / per))
+                    : (int)(blockIdx.x % (unsigned)a.nb);
+  const int64_t w0 = seq ? (int64_t)((blockIdx.x / 8) % per) : (int64_t)(blockIdx.x / a.nb);
+  const int bb = split ? 0 : b;  // K pieces share bucket 0's entry range
+  const int64_t bs = a.bstart_dev ? (int64_t)a.bstart_dev[bb] : a.bstart[bb];
+  const int64_t be = a.bstart_dev ? (int64_t)a.bstart_dev[bb + 1] : a.bstart[bb + 1];
+  for (int64_t wave = w0; bs + wave * E < be; wave += per) {
   const int64_t wb = bs + wave * E;
   const int nw = (int)((be - wb < E) ? be - wb : E);
   const int lane = lane_id();
@@ -241,14 +250,17 @@ __global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
   // raw column (validated where it is used, so the first A load below need
   // not wait for it)
   if (lane < nw) my_c = (int)col[my_p];
+  // from here on my_p is the output index: the mask position, or with a K
+  // split the entry's index in the range (into this piece's partial sums)
+  if (split) my_p = (int)(wb + lane - bs);
 
   const int g0 = g * EG;
   const int g1 = (g0 + EG < nw) ? g0 + EG : nw;  // may be <= g0
   const int64_t kvec = a.K / VEC;
   const int64_t npass = cdiv(kvec, (int64_t)LPN * KV);
-  const VT* A = (const VT*)a.A;
-  const VT* BT = (const VT*)a.BT;
-  OT* out = (OT*)a.out;
+  const VT* A = (const VT*)a.A + (split ? b * a.kpiece : 0);
+  const VT* BT = (const VT*)a.BT + (split ? b * a.kpiece : 0);
+  OT* out = split ? (OT*)(a.part + (int64_t)b * (be - bs)) : (OT*)a.out;
   const bool cache_a = FULL || npass == 1;
 
   // FULL: K is exactly one pass (kvec == LPN * KV), so no vector is out of
@@ -368,7 +380,9 @@ __global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
 template <typename VT, typename OT, typename IT, int LPN, int KV, int U, int E>
 hipError_t launch_list_ue(const SddmmListArgs& a, hipStream_t s) {
   int64_t most = 0;
-  if (a.bstart_dev) {
+  if (a.ksplit > 1) {
+    most = a.bstart_dev ? a.max_bucket : a.bstart[1] - a.bstart[0];
+  } else if (a.bstart_dev) {
     most = a.max_bucket;  // bucket bounds on the device: a host-side bound
   } else {
     for (int b = 0; b < a.nb; ++b) {
@@ -445,6 +459,38 @@ hipError_t launch_vt(const SddmmArgs& a, hipStream_t s) {
 
 // K, leading dimensions or pointers that do not allow 16-byte vectors along K
 // (the entry-list kernel needs them).
+namespace {
+template <typename OT>
+__global__ __launch_bounds__(256) void sddmm_piece_sum_kernel(const float* part, int pieces,
+                                                              int64_t count, const int32_t* pos,
+                                                              int64_t start, OT* out) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * 256) {
+    float v = part[j];
+    for (int b = 1; b < pieces; ++b) v += part[(int64_t)b * count + j];
+    out[pos[start + j]] = from_f32<OT>(v);
+  }
+}
+}  // namespace
+
+hipError_t launch_sddmm_piece_sum(const float* part, int pieces, int64_t count,
+                                  const int32_t* pos, int64_t start, void* out, int out_dtype,
+                                  hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int64_t g = cdiv(count, 256);
+  const dim3 grid((unsigned)(g < 2048 ? g : 2048));
+  if (out_dtype == kF32)
+    hipLaunchKernelGGL(sddmm_piece_sum_kernel<float>, grid, dim3(256), 0, s, part, pieces, count,
+                       pos, start, (float*)out);
+  else if (out_dtype == kF16)
+    hipLaunchKernelGGL(sddmm_piece_sum_kernel<_Float16>, grid, dim3(256), 0, s, part, pieces,
+                       count, pos, start, (_Float16*)out);
+  else
+    hipLaunchKernelGGL(sddmm_piece_sum_kernel<bf16_t>, grid, dim3(256), 0, s, part, pieces,
+                       count, pos, start, (bf16_t*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s) {
   switch (a.dtype) {
     case kF32: return launch_vt<float>(a, s);
@@ -456,8 +502,20 @@ hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s) {
 
 // The list kernel needs 16-byte vectors along K (K, lda, ldbt multiples of
 // the vector width, 16-byte aligned A and BT); the caller checks.
-hipError_t launch_sddmm_list(const SddmmListArgs& a, hipStream_t s) {
-  if (a.nb < 1 || a.nb > kMaxBuckets) return hipErrorInvalidValue;
+hipError_t launch_sddmm_list(const SddmmListArgs& a0, hipStream_t s) {
+  SddmmListArgs a = a0;
+  if (a.ksplit > 1) {
+    // pieces of K: the kernel takes K = kpiece (a multiple of the vector)
+    // and writes fp32 partial sums
+    if (!a.part || a.kpiece <= 0 || a.ksplit * a.kpiece != a.K || a.ksplit > 16 ||
+        (a.ksplit > 8 && a.ksplit % 8 != 0))
+      return hipErrorInvalidValue;
+    a.nb = a.ksplit;
+    a.K = a.kpiece;
+    a.out_dtype = kF32;
+  } else if (a.nb < 1 || a.nb > kMaxBuckets) {
+    return hipErrorInvalidValue;
+  }
   switch (a.dtype) {
     case kF32: return launch_list_vt<float>(a, s);
     case kF16: return launch_list_vt<_Float16>(a, s);

@@ -773,10 +773,11 @@ hipError_t fetch_sddmm_plan_counts(SddmmPlanDev* p, hipStream_t s) {
 
 // K splits of the dense tiles for this plan and K.  With the tile count on
 // the host (plans made by spops_sddmm_plan_create): kOptSddmmSplits when set,
-// else the count S (at most the number of K slices, and at most 16) that
-// minimizes rounds * (slices per item + 2), where a round is one item per
-// compute unit and 2 slices stand for an item's fixed cost (gathering its
-// rows, pipeline start, epilogue); ties go to fewer splits.  Without host
+// else, when there are fewer tiles than compute units, the count S (at most
+// the number of K slices, and at most 16) that minimizes rounds * (slices
+// per item + 2), where a round is one item per resident workgroup slot and
+// 2 slices stand for an item's fixed cost (gathering its rows, pipeline
+// start, epilogue); ties go to fewer splits.  Otherwise, and without host
 // counts: 1.
 SddmmTileSched sddmm_tile_schedule(const SddmmPlanDev& p, int64_t K) {
   SddmmTileSched sc{};
@@ -789,6 +790,9 @@ SddmmTileSched sddmm_tile_schedule(const SddmmPlanDev& p, int64_t K) {
     sc.splits = (int)(opt < smax ? opt : smax);
     return sc;
   }
+  // a full round of tiles already keeps every compute unit busy; splitting
+  // then only adds items and the partial-sum pass (measured slower)
+  if (p.h.tiles >= p.cus) return sc;
   int64_t best_cost = INT64_MAX;
   for (int64_t S = 1; S <= smax; ++S) {
     const int64_t cost = cdiv(p.h.tiles * S, (int64_t)p.cus * kTileWgPerCu) * (cdiv(nsl, S) + 2);

@@ -277,7 +277,7 @@ def clear_plan_caches():
 # --------------------------------------------------------------- options --
 
 OPTIONS = {"spmm_pointer_loads": 0, "transpose_force_scan": 1, "transpose_wide_records": 2,
-           "sddmm_buckets": 3, "sddmm_splits": 4}
+           "sddmm_buckets": 3, "sddmm_splits": 4, "sddmm_rest_split": 5}
 
 
 def set_option(name: str, value: int) -> int:
