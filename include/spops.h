@@ -248,6 +248,23 @@ spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* 
                                  void* out_col_idx, spops_itype out_col_type, void* workspace,
                                  size_t workspace_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * transpose with its scratch in a fixed array inside the library instead of
+ * a workspace argument.  Inputs and outputs as for spops_csr_transpose.
+ * Allocates nothing and calls no allocating routine; the array (32 MiB, its
+ * size from spops_csr_transpose_noalloc_limit) exists once per GPU and is
+ * held until the process ends.  Inputs whose transpose needs more scratch
+ * than that (spops_csr_transpose_workspace_size) are rejected with
+ * SPOPS_ERR_WORKSPACE before anything is launched.  Every call on one GPU
+ * uses that GPU's array: calls that overlap in time on the same GPU (other
+ * streams, other threads) race and give undefined results; calls in order
+ * on one stream are safe.  The array's contents on entry do not matter. */
+spops_status spops_csr_transpose_noalloc(const spops_csr* A, void* out_values,
+                                         int32_t* out_row_offsets, void* out_col_idx,
+                                         spops_itype out_col_type, void* hip_stream);
+spops_status spops_csr_transpose_noalloc_limit(size_t* bytes);
+
 /* ------------------------------------------------------------ row order --
  * The row_idx list of section "Usage": rows sorted by entry count, most
  * entries first, equal counts in ascending row order (the page leaves

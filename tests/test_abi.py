@@ -160,6 +160,24 @@ def test_csr_add_rejects_bad_arguments(L):
     assert f(ctypes.byref(desc(ri=None, nnz=0, col=None, values=None)), None, 0, 4, None) == 0
 
 
+def test_transpose_noalloc_limit(L):
+    b = ctypes.c_size_t()
+    assert L.spops_csr_transpose_noalloc_limit(ctypes.byref(b)) == 0
+    assert b.value == 32 << 20
+    assert L.spops_csr_transpose_noalloc_limit(None) == 1
+    need = ctypes.c_size_t()
+    f = L.spops_csr_transpose_noalloc
+    # an input whose transpose needs more scratch than the array holds is
+    # refused before anything is launched
+    big = desc(rows=123440, cols=123440, nnz=3085894, ri_type=1, col_type=1)
+    assert L.spops_csr_transpose_workspace_size(123440, 123440, 3085894,
+                                                ctypes.byref(need)) == 0
+    assert need.value > b.value
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 1, None) == 5
+    assert f(ctypes.byref(desc(rows=40000, ri_type=1)), FAKE, FAKE, FAKE, 0, None) == 4
+    assert f(ctypes.byref(desc()), FAKE, None, FAKE, 0, None) == 1
+
+
 def test_transpose_and_sort_reject_bad_arguments(L):
     b = ctypes.c_size_t()
     assert L.spops_csr_transpose_workspace_size(4, 4, 4, ctypes.byref(b)) == 0 and b.value > 0

@@ -305,13 +305,14 @@ static size_t sddmm_inline_plan_bytes(const spops_csr* mask) {
 // Pieces of K for the plan's remainder (1: none).  Splitting K over the
 // XCDs (piece b on XCD b) lets each L2 hold its slice of BT, so the
 // remainder's BT rows, each gathered by several entries, come from L2; it
-// pays when BT exceeds what the eight L2s hold together.  The option
+// pays when BT exceeds what the eight L2s hold together (16 pieces, two
+// per XCD, measured best on the 45 MB BT of the cross-clustered mask).  The option
 // kOptSddmmRestSplit sets the count (1 turns the split off).
 static int sddmm_rest_pieces(const SddmmPlanDev& P, int64_t K, spops_dtype in_type) {
   if (!P.host_ok || P.h.rest <= 0 || in_type == SPOPS_F32) return 1;
   const int64_t opt = option(kOptSddmmRestSplit);
   int pieces = opt > 0 ? (int)(opt < 16 ? opt : 16)
-                       : (P.n * K * 2 > ((int64_t)32 << 20) ? 8 : 1);
+                       : (P.n * K * 2 > ((int64_t)32 << 20) ? 16 : 1);
   if (pieces > 8) pieces = 16;
   while (pieces > 1 && K % (8 * pieces) != 0) pieces /= 2;
   return pieces;
@@ -518,6 +519,58 @@ spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* 
       A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx, A->col_type == SPOPS_I32,
       A->values, A->values ? elem_bytes(A->val_type) : 0, out_values, out_row_offsets,
       out_col_idx, out_col_type == SPOPS_I32, workspace, as_stream(hip_stream)));
+}
+
+// ------------------------------------------------- transpose, no allocation ---
+
+// The scratch of spops_csr_transpose_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only names a stand-in); the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (looked up on the first
+// call on that device); nullptr on failure.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+}  // namespace
+
+spops_status spops_csr_transpose_noalloc(const spops_csr* A, void* out_values,
+                                         int32_t* out_row_offsets, void* out_col_idx,
+                                         spops_itype out_col_type, void* hip_stream) {
+  spops_status st = check_csr(A, A && A->values != nullptr, false);
+  if (st != SPOPS_OK) return st;
+  if (!itype_ok(out_col_type)) return SPOPS_ERR_DTYPE;
+  if (out_col_type == SPOPS_I16 && A->rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  if (!out_row_offsets) return SPOPS_ERR_NULL;
+  if (A->nnz > 0 && (!out_col_idx || (A->values && !out_values))) return SPOPS_ERR_NULL;
+  if (transpose_workspace_bytes(A->rows, A->cols, A->nnz) > kNoAllocScratchBytes)
+    return SPOPS_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return SPOPS_ERR_HIP;
+  return from_hip(launch_csr_transpose(
+      A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx, A->col_type == SPOPS_I32,
+      A->values, A->values ? elem_bytes(A->val_type) : 0, out_values, out_row_offsets,
+      out_col_idx, out_col_type == SPOPS_I32, ws, as_stream(hip_stream)));
+}
+
+spops_status spops_csr_transpose_noalloc_limit(size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  *bytes = kNoAllocScratchBytes;
+  return SPOPS_OK;
 }
 
 // ------------------------------------------------------------ row order ---

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "spops_csr_add": ([cp, vp, i32, i64, vp], i32),
             "spops_csr_transpose_workspace_size": ([i64, i64, i64, P(sz)], i32),
             "spops_csr_transpose": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
+            "spops_csr_transpose_noalloc": ([cp, vp, vp, vp, i32, vp], i32),
+            "spops_csr_transpose_noalloc_limit": ([P(sz)], i32),
             "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
             "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
             "spops_cg_workspace_size": ([cp, vp, P(sz)], i32),
