@@ -68,7 +68,8 @@ typedef enum spops_status {
   SPOPS_ERR_PLAN = 7,          /* plan built for a different mask */
   SPOPS_ERR_HIP = 8,           /* a HIP runtime call or kernel launch failed */
   SPOPS_ERR_ARGUMENT = 9,      /* a scalar argument (tolerance, rate, ...) out of its range */
-  SPOPS_ERR_INDEX_ORDER = 10   /* columns not strictly ascending inside a row, or out of range */
+  SPOPS_ERR_INDEX_ORDER = 10,  /* columns not strictly ascending inside a row, or out of range */
+  SPOPS_ERR_INVALID_INDEX = 11 /* spops_validate_csr found invalid index data */
 } spops_status;
 
 typedef enum spops_dtype { SPOPS_F32 = 0, SPOPS_F16 = 1, SPOPS_BF16 = 2 } spops_dtype;
@@ -221,6 +222,34 @@ spops_status spops_sddmm_plan_destroy(spops_sddmm_plan* plan);
 spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_rows,
                                    int64_t* dense_cols, int64_t* tiled_nnz,
                                    int64_t* rest_nnz, int64_t* tiles);
+
+/* ------------------------------------------------------------ validation --
+ * Checks a CSR's device-resident index data against the layout of section
+ * "Usage" (the operations themselves do not: they only avoid out-of-bounds
+ * accesses, and the results for invalid data are unspecified):
+ *   SPOPS_INVALID_OFFSETS    row_offsets[0] != 0, row_offsets[rows] != nnz,
+ *                            or a decreasing pair;
+ *   SPOPS_INVALID_COLUMN     a column index outside [0, cols);
+ *   SPOPS_INVALID_ROW_IDX    row_idx (checked when A->row_idx is not NULL)
+ *                            is not a permutation of 0..rows-1;
+ *   SPOPS_INVALID_DUPLICATE  a (row, column) pair stored twice (checked when
+ *                            check_duplicates is nonzero and offsets and
+ *                            columns are valid).
+ * Values are not read.  Every device read stays inside the lengths the
+ * descriptor gives.  Returns SPOPS_OK for valid data, SPOPS_ERR_INVALID_INDEX
+ * when any check fails, with the failed checks OR-ed into *findings
+ * (nullable).  workspace: spops_validate_csr_workspace_size bytes, 256-byte
+ * aligned, contents on entry irrelevant.  Synchronizes hip_stream. */
+typedef enum spops_invalid_flags {
+  SPOPS_INVALID_OFFSETS = 1,
+  SPOPS_INVALID_COLUMN = 2,
+  SPOPS_INVALID_ROW_IDX = 4,
+  SPOPS_INVALID_DUPLICATE = 8
+} spops_invalid_flags;
+spops_status spops_validate_csr_workspace_size(int64_t rows, int64_t cols, int64_t nnz,
+                                               size_t* bytes);
+spops_status spops_validate_csr(const spops_csr* A, int check_duplicates, void* workspace,
+                                size_t workspace_bytes, uint32_t* findings, void* hip_stream);
 
 /* --------------------------------------------------------------- csr_add --
  * Section "Sparse Addition", in place on the dense operand:

@@ -50,8 +50,8 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert L.spops_abi_version() == 1
-    for code in range(9):
-        assert L.spops_status_string(code)
+    for code in range(12):
+        assert L.spops_status_string(code) != b"unknown status"
     assert L.spops_status_string(0) == b"ok"
 
 
@@ -158,6 +158,20 @@ def test_csr_add_rejects_bad_arguments(L):
     # row_idx is not used by csr_add: its absence is not an error
     assert f(ctypes.byref(desc(ri=None, ri_type=9)), None, 0, 4, None) == 1
     assert f(ctypes.byref(desc(ri=None, nnz=0, col=None, values=None)), None, 0, 4, None) == 0
+
+
+def test_validate_rejects_bad_arguments(L):
+    b = ctypes.c_size_t()
+    assert L.spops_validate_csr_workspace_size(100, 50, 400, ctypes.byref(b)) == 0
+    assert b.value > 0
+    assert L.spops_validate_csr_workspace_size(-1, 50, 400, ctypes.byref(b)) == 2
+    f = L.spops_validate_csr
+    fd = ctypes.c_uint32(7)
+    assert f(ctypes.byref(desc()), 1, None, 0, ctypes.byref(fd), None) == 5
+    assert fd.value == 0
+    assert f(ctypes.byref(desc()), 1, FAKE, 1, None, None) == 5
+    assert f(ctypes.byref(desc(cols=40000)), 1, FAKE, 1 << 30, None, None) == 4
+    assert f(ctypes.byref(desc(ro=None)), 1, FAKE, 1 << 30, None, None) == 1
 
 
 def test_transpose_noalloc_limit(L):

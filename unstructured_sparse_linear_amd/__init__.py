@@ -12,6 +12,7 @@ from .spops import (  # noqa: F401
     SddmmPlan,
     SpmmPlan,
     DeltaMatrix,
+    InvalidCSR,
     SpopsError,
     cg,
     delta_encode,
@@ -28,10 +29,11 @@ from .spops import (  # noqa: F401
     sort_rows_by_nnz,
     sort_rows_workspace,
     spmm,
+    validate_csr,
 )
 
 __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "SpmmPlan",
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
            "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg",
            "masked_adam", "MaskedAdam", "DeltaMatrix", "delta_encode", "delta_spmv",
-           "option", "set_option"]
+           "option", "set_option", "validate_csr", "InvalidCSR"]

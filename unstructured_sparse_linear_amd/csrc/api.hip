@@ -141,6 +141,7 @@ const char* spops_status_string(spops_status s) {
     case SPOPS_ERR_HIP: return "HIP runtime error";
     case SPOPS_ERR_ARGUMENT: return "scalar argument out of range";
     case SPOPS_ERR_INDEX_ORDER: return "columns not strictly ascending in a row, or out of range";
+    case SPOPS_ERR_INVALID_INDEX: return "the CSR index data is invalid (see the validator's findings)";
   }
   return "unknown status";
 }
@@ -519,6 +520,40 @@ spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* 
       A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx, A->col_type == SPOPS_I32,
       A->values, A->values ? elem_bytes(A->val_type) : 0, out_values, out_row_offsets,
       out_col_idx, out_col_type == SPOPS_I32, workspace, as_stream(hip_stream)));
+}
+
+// ------------------------------------------------------------ validation ---
+
+spops_status spops_validate_csr_workspace_size(int64_t rows, int64_t cols, int64_t nnz,
+                                               size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (rows < 0 || cols < 0 || nnz < 0 || rows > INT32_MAX - 1 || cols > INT32_MAX - 1 ||
+      nnz > INT32_MAX)
+    return SPOPS_ERR_SHAPE;
+  *bytes = validate_workspace_bytes(rows, cols, nnz);
+  return SPOPS_OK;
+}
+
+spops_status spops_validate_csr(const spops_csr* A, int check_duplicates, void* workspace,
+                                size_t workspace_bytes, uint32_t* findings, void* hip_stream) {
+  if (findings) *findings = 0;
+  spops_status st = check_csr(A, false, false);
+  if (st != SPOPS_OK) return st;
+  if (A->row_idx) {
+    if (!itype_ok(A->row_idx_type)) return SPOPS_ERR_DTYPE;
+    if (A->row_idx_type == SPOPS_I16 && A->rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  }
+  if (!workspace || workspace_bytes < validate_workspace_bytes(A->rows, A->cols, A->nnz) ||
+      (uintptr_t)workspace % 256 != 0)
+    return SPOPS_ERR_WORKSPACE;
+  uint32_t f = 0;
+  hipError_t e = launch_validate(A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx,
+                                 A->col_type == SPOPS_I32, A->row_idx,
+                                 A->row_idx_type == SPOPS_I32, check_duplicates, workspace, &f,
+                                 as_stream(hip_stream));
+  if (e != hipSuccess) return SPOPS_ERR_HIP;
+  if (findings) *findings = f;
+  return f ? SPOPS_ERR_INVALID_INDEX : SPOPS_OK;
 }
 
 // ------------------------------------------------- transpose, no allocation ---

@@ -233,6 +233,19 @@ hipError_t launch_sddmm_piece_sum(const float* part, int pieces, int64_t count,
                                   const int32_t* pos, int64_t start, void* out, int out_dtype,
                                   hipStream_t s);
 
+// ------------------------------------------------------------ validation --
+// Findings of the CSR validator (bits of a flag word).
+constexpr uint32_t kValidateBadOffsets = 1u;
+constexpr uint32_t kValidateBadColumn = 2u;
+constexpr uint32_t kValidateBadRowIdx = 4u;
+constexpr uint32_t kValidateDuplicate = 8u;
+size_t validate_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz);
+// Runs the checks and copies the flag word to *flags_host (synchronizes s).
+hipError_t launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
+                           const void* col, int col_i32, const void* row_idx, int ri_i32,
+                           int check_duplicates, void* ws, uint32_t* flags_host,
+                           hipStream_t s);
+
 // ------------------------------------------------------------- options --
 // Process-wide switches (spops_set_option), read on every call.
 enum Option : int {

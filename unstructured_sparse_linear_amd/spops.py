@@ -29,7 +29,13 @@ _BACKENDS = {"structure_aware": STRUCTURE_AWARE, "sputnik": GENERAL, "general": 
 
 STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "dtype", 4: "index width",
           5: "workspace", 6: "unsupported", 7: "plan mismatch", 8: "HIP error",
-          9: "argument out of range", 10: "column order"}
+          9: "argument out of range", 10: "column order", 11: "invalid index data"}
+INVALID_FLAGS = {1: "offsets", 2: "column", 4: "row_idx", 8: "duplicate"}
+# Set SPOPS_VALIDATE=1 in the environment (read once, when this module is
+# imported) to run validate_csr on the sparse operands of every spmm, sddmm,
+# csr_add and csr_transpose call of this binding before the operation
+# (slow: it synchronizes; for debugging).
+VALIDATE = os.environ.get("SPOPS_VALIDATE", "") == "1"
 
 
 class SpopsError(RuntimeError):
@@ -80,6 +86,8 @@ def lib() -> ctypes.CDLL:
             "spops_csr_transpose_workspace_size": ([i64, i64, i64, P(sz)], i32),
             "spops_csr_transpose": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
             "spops_csr_transpose_noalloc": ([cp, vp, vp, vp, i32, vp], i32),
+            "spops_validate_csr_workspace_size": ([i64, i64, i64, P(sz)], i32),
+            "spops_validate_csr": ([cp, i32, vp, sz, P(ctypes.c_uint32), vp], i32),
             "spops_csr_transpose_noalloc_limit": ([P(sz)], i32),
             "spops_sort_rows_by_nnz_workspace_size": ([i64, i64, P(sz)], i32),
             "spops_sort_rows_by_nnz": ([vp, i64, i64, vp, i32, vp, sz, vp], i32),
@@ -276,6 +284,40 @@ def clear_plan_caches():
     _ws_pool.clear()
 
 
+# ------------------------------------------------------------ validation --
+
+class InvalidCSR(ValueError):
+    def __init__(self, findings: int):
+        names = [v for k, v in INVALID_FLAGS.items() if findings & k]
+        super().__init__(f"invalid CSR index data: {', '.join(names)}")
+        self.findings = findings
+
+
+def validate_csr(row_offsets: torch.Tensor, col_indices: torch.Tensor, m: int, n: int,
+                 row_indices: Optional[torch.Tensor] = None,
+                 check_duplicates: bool = True) -> int:
+    """Checks the CSR's index data on the device (include/spops.h,
+    spops_validate_csr); returns 0 or raises InvalidCSR with the failed
+    checks.  Synchronizes."""
+    d = csr_desc(None, row_offsets, row_indices, col_indices, m, n)
+    wb = ctypes.c_size_t()
+    _check("spops_validate_csr_workspace_size", lib().spops_validate_csr_workspace_size(
+        m, n, d.nnz, ctypes.byref(wb)))
+    ws = torch.empty(wb.value, dtype=torch.uint8, device=row_offsets.device)
+    f = ctypes.c_uint32()
+    st = lib().spops_validate_csr(ctypes.byref(d), int(bool(check_duplicates)), ws.data_ptr(),
+                                  ws.numel(), ctypes.byref(f), _stream(row_offsets))
+    if st == 11:
+        raise InvalidCSR(int(f.value))
+    _check("spops_validate_csr", st)
+    return 0
+
+
+def _maybe_validate(row_offsets, col_indices, m, n, row_indices=None):
+    if VALIDATE:
+        validate_csr(row_offsets, col_indices, m, n, row_indices)
+
+
 # --------------------------------------------------------------- options --
 
 OPTIONS = {"spmm_pointer_loads": 0, "transpose_force_scan": 1, "transpose_wide_records": 2,
@@ -321,6 +363,7 @@ def spmm(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: torch.
     if A_val.dtype != B.dtype:
         raise ValueError("A_val and B must share a dtype")
     d = csr_desc(A_val, A_row_offsets, A_row_indices, A_col_indices, m, k)
+    _maybe_validate(A_row_offsets, A_col_indices, m, k, A_row_indices)
     if out is None:
         out = torch.empty((m, N), dtype=out_dtype, device=B.device)
     else:
@@ -358,6 +401,7 @@ def sddmm(out_row_offsets: torch.Tensor, out_row_indices: torch.Tensor,
     m, K = A.shape
     n = BT.shape[0]
     d = csr_desc(None, out_row_offsets, out_row_indices, out_col_indices, m, n)
+    _maybe_validate(out_row_offsets, out_col_indices, m, n, out_row_indices)
     nnz = d.nnz
     if out is None:
         out = torch.empty(nnz, dtype=out_dtype, device=A.device)
@@ -390,6 +434,7 @@ def csr_add(A_val: torch.Tensor, A_row_offsets: torch.Tensor, A_row_indices: tor
     if A_val.dtype != B.dtype:
         raise ValueError("A_val and B must share a dtype")
     d = csr_desc(A_val, A_row_offsets, A_row_indices, A_col_indices, m, n)
+    _maybe_validate(A_row_offsets, A_col_indices, m, n, A_row_indices)
     _check("spops_csr_add", lib().spops_csr_add(ctypes.byref(d), _ptr(B), _DT[B.dtype], n,
                                                 _stream(B)))
     return B
@@ -411,6 +456,7 @@ def csr_transpose(A_val: Optional[torch.Tensor], A_row_offsets: torch.Tensor,
     """A^T as (values_T, row_offsets_T [n+1] int32, col_idx_T [nnz]); `out`
     gives preallocated (values_T or None, row_offsets_T, col_idx_T)."""
     d = csr_desc(A_val, A_row_offsets, None, A_col_indices, m, n)
+    _maybe_validate(A_row_offsets, A_col_indices, m, n)
     dev = A_row_offsets.device
     nnz = d.nnz
     oit = torch.int16 if m <= 32767 else torch.int32
