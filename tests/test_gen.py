@@ -115,3 +115,20 @@ def test_random_csr_options():
 def test_permutations(kind):
     p = gen.permutation(0, 1000, kind)
     assert np.array_equal(np.sort(p), np.arange(1000)) and p.dtype == np.int16
+
+
+def test_generator_checksums():
+    # SHA-256 of every array of the five workloads at seed 0, recorded by
+    # tests/golden/make_gen_checksums.py
+    import json
+    import os
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, os.path.join(here, "golden"))
+    import make_gen_checksums as mk
+    want = json.load(open(os.path.join(here, "golden", "gen_checksums.json")))
+    got = mk.checksums()
+    assert sorted(got) == sorted(want)
+    for name, ent in want.items():
+        for k, h in ent.items():
+            assert got[name][k] == h, (name, k)

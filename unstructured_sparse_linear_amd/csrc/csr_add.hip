@@ -8,8 +8,8 @@
 // "When is double rounding innocuous?", 1995); for f32 it is the single
 // rounding itself.  Entries are spread evenly over lanes (one entry per lane
 // per round, consecutive entries on consecutive lanes), which keeps rows of
-// any length balanced; each lane finds its row by walking forward from the
-// row of the wave's first entry.  Entries are unique within a row, so no two
+// any length balanced; each lane finds its row by a binary search between the
+// rows of the wave's first and last entries.  Entries are unique within a row, so no two
 // lanes touch the same element.
 #include "common.h"
 #include "kernels.h"
@@ -26,7 +26,12 @@ __global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, i
   const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
   const int64_t wb = wave * (kWave * kRounds);
   if (wb >= nnz) return;
-  int64_t r = wave_upper_row(ro, m, wb);
+  const int64_t we = (wb + kWave * kRounds < nnz ? wb + kWave * kRounds : nnz) - 1;
+  // rows of the wave's first and last entries (64-way searches), then each
+  // lane's row by binary search between them: a bounded number of loads
+  // however many empty rows the wave's entries span
+  const int64_t rf = wave_upper_row(ro, m, wb);
+  const int64_t rl = wave_upper_row(ro, m, we);
   const int lane = lane_id();
   // all loads of W first (positions are distinct), then the stores
   int64_t off[kRounds];
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(kBlock) void csr_add_kernel(int64_t m, int64_t n, i
     off[q] = -1;
     add[q] = 0.f;
     if (p < nnz) {
-      while (r < m - 1 && (int64_t)ro[r + 1] <= p) ++r;
+      const int64_t r = upper_row(ro, rf, rl + 1, p);
       const int c = (int)col[p];
       if ((unsigned)c < (unsigned)n) {
         off[q] = r * ldw + c;

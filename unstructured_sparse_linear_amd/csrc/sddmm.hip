@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_scalar_kernel(SddmmArgs a) {
   const VT* BT = (const VT*)a.BT;
   const IT* col = (const IT*)a.col;
   for (int64_t e = wb; e < we; ++e) {
-    while (r < m - 1 && (int64_t)a.ro[r + 1] <= e) ++r;
+    r = upper_row(a.ro, r, m, e);  // a binary search past any empty rows
     const int c = (int)col[e];
     float s = 0.f;
     if ((unsigned)c < (unsigned)a.n) {
