@@ -101,3 +101,46 @@ def test_rejects_mismatched_inputs():
         S.sparse_linear(dev(A.values, "f16"), dev(xt, "f16").float(), pattern)
     with pytest.raises(ValueError):
         S.sparse_linear(dev(A.values, "f16"), dev(xt, "f16")[:5], pattern)
+
+
+@pytest.mark.parametrize("cfg,dt", [(3, "f16"), (2, "f16")])
+def test_full_size_layer_on_sampled_outputs(cfg, dt):
+    # the layer at the size the benchmark times it (the workload's mask as S,
+    # its dense B as X^T, its A operand as dY^T, 2048 tokens): forward and
+    # both gradients on the GPU, checked on sampled rows of Y^T, the stored
+    # entries of those rows (dvalues) and sampled rows of dX^T, each computed
+    # by the oracle on the matching slab of S (or of S^T)
+    w = gen.make_config(cfg, dt=dt)
+    A = w.get("A")
+    xt, g = w.get("B"), w.get("Ad")
+    m, n = A.m, A.n
+    _, ro, ci = csr_dev(A)
+    pattern = S.SparsePattern(ro, ci, m, n)
+    layer = S.SparseAdapter(pattern, dev(A.values, dt).clone())
+    X = dev(xt, dt).clone().requires_grad_(True)
+    Y = layer(X)
+    Y.backward(dev(g, dt))
+    torch.cuda.synchronize()
+    bound = BAR[dt] + ROUND[dt]
+    rng = np.random.default_rng(cfg)
+    rows = np.sort(rng.choice(m, 48, replace=False))
+    Yh, dvh = host_f64(Y.detach()), host_f64(layer.values.grad)
+    for r in rows:
+        slab = gen.csr_row_slab(A, int(r), int(r) + 1)
+        yt = oracle.sparse_linear_forward(1, slab.row_offsets, slab.col_idx, slab.values, dt,
+                                          xt, dt)
+        dv, _ = oracle.sparse_linear_backward(1, n, slab.row_offsets, slab.col_idx,
+                                              slab.values, dt, xt, g[r:r + 1], dt)
+        assert rel_err(Yh[r], yt[0]) <= bound, ("forward row", r)
+        p0, p1 = int(A.row_offsets[r]), int(A.row_offsets[r + 1])
+        if p1 > p0:
+            assert rel_err(dvh[p0:p1], dv) <= bound, ("dvalues row", r)
+    # dX^T = S^T dY^T: rows of S^T are columns of S
+    vT, roT, ciT = oracle.csr_transpose(m, n, A.row_offsets, A.col_idx, A.values)
+    AT = gen.CSR(n, m, roT, ciT, vT, dt)
+    dxh = host_f64(X.grad)
+    for c in np.sort(rng.choice(n, 48, replace=False)):
+        slab = gen.csr_row_slab(AT, int(c), int(c) + 1)
+        dx = oracle.sparse_linear_forward(1, slab.row_offsets, slab.col_idx, slab.values, dt,
+                                          g, dt)
+        assert rel_err(dxh[c], dx[0]) <= bound, ("dX^T row", c)
