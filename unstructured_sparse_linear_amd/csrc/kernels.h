@@ -126,9 +126,8 @@ struct SddmmArgs {
 hipError_t launch_sddmm_general(const SddmmArgs& a, hipStream_t s);
 
 // Structure-aware SDDMM plan.  Dense tiles are kSddmmTM x kSddmmTN blocks of
-// gathered rows x gathered columns; tile t's entries carry the keys 2t and
-// 2t + 1 (upper and lower half of its rows), the remainder the keys
-// rest_key + column bucket.
+// gathered rows x gathered columns; tile t's entries carry the key t, the
+// remainder the keys rest_key + column bucket.
 constexpr int kMaxBuckets = 8;
 constexpr int kSddmmTM = 128;
 constexpr int kSddmmTN = 128;
@@ -153,7 +152,7 @@ struct SddmmPlanDev {
   double tau = 0;
   int64_t tiles_a_cols = 0;  // tile columns of region A: cdiv(n, kSddmmTN)
   int64_t max_tiles = 0;     // bound on the tile count (sizes the key space)
-  int64_t rest_key = 0;      // first remainder key (2 * max_tiles)
+  int64_t rest_key = 0;      // first remainder key (max_tiles)
   int nb_max = 1;            // remainder buckets planned before the merge decision
   SddmmPlanScalars* sc = nullptr;  // device
   int32_t* rows = nullptr;         // [m] dense rows, then the other rows

@@ -10,8 +10,8 @@
 //     tau*(remaining rows) entries;
 //   * region A = dense rows x all columns, region B = remaining rows x dense
 //     columns; both are cut into TM x TN tiles of gathered rows / columns;
-//   * every entry gets a key: 2*tile + (row in the tile's lower half) for a
-//     tile entry, rest_key + (column bucket) for the remainder; a stable
+//   * every entry gets a key: its tile for a tile entry, rest_key +
+//     (column bucket) for the remainder; a stable
 //     radix sort groups the entries by key (the remainder of each bucket
 //     stays in CSR order), and key_start[k] is the first sorted entry with
 //     key >= k.  Counts (dense rows, tiles, ...) stay in device memory; the
@@ -20,7 +20,7 @@
 // Execute: a workgroup takes one (tile, K split) item and computes the dense
 // TM x TN block A[rows] * BT[cols]^T over its share of K with
 // v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate), then writes the tile's
-// mask positions from an LDS copy of the block (half the rows at a time).
+// mask positions from an LDS copy of the block.
 // The (tile, K slice) units are spread evenly over the compute units; a
 // tile computed in one piece writes the output, a tile cut into several
 // pieces writes fp32 partial sums and a second kernel adds them in order
@@ -47,12 +47,10 @@ constexpr int kStaged = TM + TN;       // rows staged per slice (A rows, then BT
 constexpr int kChunks = kStaged * (TK / 8) / kThreads;  // 16-byte chunks per thread and slice
 constexpr int kChunksA = TM * (TK / 8) / kThreads;      // the first ones are A rows
 constexpr int kStage = kStaged * LDK;  // 16-bit elements per LDS stage
-constexpr int HALF = TM / 2;           // rows of the block written to LDS per pass
-constexpr int LDR = HALF + 4;          // padded fp32 column of that half block
+constexpr int LDR = TM + 4;            // padded fp32 column of the block in LDS
 constexpr int kEpi = 8;                // entries per thread per epilogue round
 static_assert(kChunks * kThreads * 8 == kStaged * TK, "chunks cover the staged slice");
-static_assert(HALF == WM, "one wave row per half block");
-static_assert(TN * LDR * 4 <= 2 * kStage * 2, "a half block reuses the LDS stages");
+static_assert(TN * LDR * 4 <= 2 * kStage * 2, "the fp32 block reuses the LDS stages");
 static_assert(LDR % 4 == 0, "16-byte column segments");
 static_assert(TM < 65536 && TN < 65536, "tile coordinates pack into 16 bits");
 
@@ -98,8 +96,8 @@ __device__ __forceinline__ float16v mfma32(const uint4& a, const uint4& b, float
 // and each slice costs one barrier.  A segment that covers its whole tile writes the output;
 // segment j of a tile split into several writes partial sums to part[j].
 // The epilogue's entry metadata (in-tile coordinates, positions) for the
-// first kEpi entries per thread of each half is requested before the K loop
-// so that its latency hides behind the MFMA work.
+// first kEpi entries per thread is requested before the K loop so that its
+// latency hides behind the MFMA work.
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (l mod 32) of the A
 // block and column (l mod 32) of the B block, K elements 8*(l/32)..+8; it
@@ -174,21 +172,18 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
                              : kOob;
       }
     }
-    const int32_t e0 = t.key_start[2 * tile], e1 = t.key_start[2 * tile + 2];
+    const int32_t e0 = t.key_start[tile], e1 = t.key_start[tile + 1];
     if (e1 <= e0) continue;  // no mask entry in this tile
 
-    // in-tile coordinates of the first epilogue round of each half,
-    // requested now (positions, needed only by whole-tile segments, are
-    // loaded in the epilogue)
-    int32_t qh[3] = {e0, t.key_start[2 * tile + 1], e1};
-    int32_t pre_rc[2][kEpi];
+    // in-tile coordinates and output positions of the first epilogue round,
+    // requested now so that they arrive during the K loop
+    int32_t pre_rc[kEpi], pre_pos[kEpi];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int u = 0; u < kEpi; ++u) {
-        const int32_t q = qh[h] + tid + u * kThreads;
-        pre_rc[h][u] = q < qh[h + 1] ? t.ent_rc[q] : 0;
-      }
+    for (int u = 0; u < kEpi; ++u) {
+      const int32_t q = e0 + tid + u * kThreads;
+      pre_rc[u] = q < e1 ? t.ent_rc[q] : 0;
+      pre_pos[u] = (q < e1 && direct) ? t.ent_pos[q] : 0;
+    }
 
     // always issued (a slice past the segment loads from kOob: zeros, no
     // memory access), so the compiler can count the loads in flight and wait
@@ -255,17 +250,16 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
       fetch(rb, s0 + st + 2, st + 2 < nst);
     }
 
-    // epilogue: rows [half*HALF, (half+1)*HALF) of the block (the waves with
-    // wr == half) go to LDS, then every thread writes entries of that half,
-    // kEpi per round with all their loads issued together
+    // epilogue: the whole fp32 block goes to LDS (column-major, in the
+    // stages' space), then every thread writes entries of the tile, kEpi per
+    // round with all their loads issued together
     float* Cs = (float*)smem;
-    auto write_round = [&](const int32_t (&rc)[kEpi], const int32_t (&pos)[kEpi], int32_t e,
-                           int32_t q1, int half) {
+    auto write_round = [&](const int32_t (&rc)[kEpi], const int32_t (&pos)[kEpi], int32_t e) {
 #pragma unroll
       for (int u = 0; u < kEpi; ++u) {
         const int32_t q = e + u * kThreads;
-        if (q < q1) {
-          const float v = Cs[(rc[u] & 0xffff) * LDR + ((rc[u] >> 16) - half * HALF)];
+        if (q < e1) {
+          const float v = Cs[(rc[u] & 0xffff) * LDR + (rc[u] >> 16)];
           if (direct)
             ((OT*)t.out)[pos[u]] = from_f32<OT>(v);
           else
@@ -273,48 +267,33 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
         }
       }
     };
+    {
+      // a lane's values v = 4q..4q+3 are 4 consecutive rows of one column:
+      // one 16-byte store each, all at immediate offsets from one address
+      float* cb = Cs + (wc * WN + (l & 31)) * LDR + wr * WM + (l >> 5) * 4;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int32_t q0 = qh[half], q1 = qh[half + 1];
-      if (q1 > q0) {
-        if (wr == half) {
-          // column-major: a lane's values v = 4q..4q+3 are 4 consecutive
-          // rows of one column, one 16-byte store (every store of the lane
-          // is an immediate offset from one address)
-          float* cb = Cs + (wc * WN + (l & 31)) * LDR + (l >> 5) * 4;
+      for (int i = 0; i < BM; ++i)
 #pragma unroll
-          for (int i = 0; i < BM; ++i)
+        for (int j = 0; j < BN; ++j)
 #pragma unroll
-            for (int j = 0; j < BN; ++j)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                *(float4*)(cb + j * 32 * LDR + i * 32 + q * 8) =
-                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                acc[i][j][4 * q + 3]);
-        }
-        __syncthreads();
-        {
-          int32_t pos[kEpi];
-#pragma unroll
-          for (int u = 0; u < kEpi; ++u) {
-            const int32_t q = q0 + tid + u * kThreads;
-            pos[u] = (q < q1 && direct) ? t.ent_pos[q] : 0;
-          }
-          write_round(pre_rc[half], pos, q0 + tid, q1, half);
-        }
-        for (int32_t e = q0 + tid + kEpi * kThreads; e < q1; e += kEpi * kThreads) {
-          int32_t rc[kEpi], pos[kEpi];
-#pragma unroll
-          for (int u = 0; u < kEpi; ++u) {
-            const int32_t q = e + u * kThreads;
-            rc[u] = q < q1 ? t.ent_rc[q] : 0;
-            pos[u] = (q < q1 && direct) ? t.ent_pos[q] : 0;
-          }
-          write_round(rc, pos, e, q1, half);
-        }
-        __syncthreads();
-      }
+          for (int q = 0; q < 4; ++q)
+            *(float4*)(cb + j * 32 * LDR + i * 32 + q * 8) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
     }
+    __syncthreads();
+    write_round(pre_rc, pre_pos, e0 + tid);
+    for (int32_t e = e0 + tid + kEpi * kThreads; e < e1; e += kEpi * kThreads) {
+      int32_t rc[kEpi], pos[kEpi];
+#pragma unroll
+      for (int u = 0; u < kEpi; ++u) {
+        const int32_t q = e + u * kThreads;
+        rc[u] = q < e1 ? t.ent_rc[q] : 0;
+        pos[u] = (q < e1 && direct) ? t.ent_pos[q] : 0;
+      }
+      write_round(rc, pos, e);
+    }
+    __syncthreads();
   }
 }
 
@@ -330,8 +309,8 @@ __global__ __launch_bounds__(256) void sddmm_split_sum_kernel(TileArgs t) {
   const int nseg = t.splits;
   if (nseg <= 1) return;
   const int64_t tiled = t.sc->tiled;
-  const int32_t e1 = t.key_start[2 * tile + 2];
-  for (int32_t e = t.key_start[2 * tile] + (int32_t)(blockIdx.y * kSumChunk + threadIdx.x);
+  const int32_t e1 = t.key_start[tile + 1];
+  for (int32_t e = t.key_start[tile] + (int32_t)(blockIdx.y * kSumChunk + threadIdx.x);
        e < e1; e += (int32_t)(gridDim.y * kSumChunk)) {
     float v[kEpi];
     int32_t pos[kEpi];
@@ -486,12 +465,12 @@ __global__ void classify_kernel(ClassifyArgs a) {
     uint32_t key, rc;
     if (hot) {
       const int64_t tile = (hr / TM) * a.tiles_a_cols + c / TN;
-      key = (uint32_t)(2 * tile + ((hr % TM) >= HALF ? 1 : 0));
+      key = (uint32_t)tile;
       rc = ((uint32_t)(hr % TM) << 16) | (uint32_t)(c % TN);
     } else if (a.col_map[c] >= 0) {
       const int64_t hc = a.col_map[c];
       const int64_t tile = tiles_a + (cr / TM) * tbc + hc / TN;
-      key = (uint32_t)(2 * tile + ((cr % TM) >= HALF ? 1 : 0));
+      key = (uint32_t)tile;
       rc = ((uint32_t)(cr % TM) << 16) | (uint32_t)(hc % TN);
     } else {
       key = (uint32_t)(a.rest_key + ((int64_t)c * a.nb) / a.n);
@@ -537,7 +516,7 @@ __global__ void key_bounds_kernel(const uint32_t* skey, const uint32_t* src, con
 __global__ void plan_finish_kernel(const int32_t* key_start, int64_t nnz,
                                    SddmmPlanScalars* sc) {
   if (threadIdx.x != 0) return;
-  const int32_t tiled = key_start[2 * (int64_t)sc->tiles];
+  const int32_t tiled = key_start[sc->tiles];
   sc->tiled = tiled;
   sc->rest = (int32_t)(nnz - tiled);
 }
@@ -565,7 +544,7 @@ struct PlanLayout {
 };
 PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
   PlanLayout L{};
-  const int64_t nkeys = 2 * max_tiles_for(m, n) + kMaxBuckets;
+  const int64_t nkeys = max_tiles_for(m, n) + kMaxBuckets;
   size_t o = 0;
   L.sc = o;
   o += align256(sizeof(SddmmPlanScalars));
@@ -655,7 +634,7 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
   out->mask_col = col;
   out->tiles_a_cols = cdiv(n, TN);
   out->max_tiles = max_tiles_for(m, n);
-  out->rest_key = 2 * out->max_tiles;
+  out->rest_key = out->max_tiles;
   int forced = 0;
   out->nb_max = planned_buckets(n, &forced);
   int dev = 0, cus = 0;
@@ -754,14 +733,14 @@ hipError_t fetch_sddmm_plan_counts(SddmmPlanDev* p, hipStream_t s) {
   // most entries in one tile (sizes the grid of the partial-sum kernel)
   p->max_tile_nnz = 0;
   if (p->h.tiles > 0) {
-    int32_t* kst = (int32_t*)malloc((size_t)(2 * p->h.tiles + 1) * 4);
+    int32_t* kst = (int32_t*)malloc((size_t)(p->h.tiles + 1) * 4);
     if (!kst) return hipErrorOutOfMemory;
-    e = hipMemcpyAsync(kst, p->key_start, (size_t)(2 * p->h.tiles + 1) * 4,
+    e = hipMemcpyAsync(kst, p->key_start, (size_t)(p->h.tiles + 1) * 4,
                        hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e == hipSuccess)
       for (int64_t t = 0; t < p->h.tiles; ++t) {
-        const int64_t c = kst[2 * t + 2] - kst[2 * t];
+        const int64_t c = kst[t + 1] - kst[t];
         p->max_tile_nnz = c > p->max_tile_nnz ? c : p->max_tile_nnz;
       }
     free(kst);
