@@ -232,6 +232,61 @@ def test_spmm_long_rows(dt, N, use_plan):
         assert info["max_row_nnz"] == 4500 and info["split_rows"] == 6
 
 
+@pytest.mark.parametrize("dt,N,n,col32", [("bf16", 256, 3000, False), ("f16", 520, 2500, False),
+                                           ("f32", 96, 2000, False), ("bf16", 64, 40000, True)])
+@pytest.mark.parametrize("kind", ["sorted", "random"])
+def test_spmm_dense_rows(dt, N, n, col32, kind):
+    # 70 long rows holding from 1/16 of the columns to all of them (split into
+    # many chunks and summed by the fixup), long rows below that and short
+    # rows; several column windows of B for N = 520; int32 columns for
+    # n = 40000; integer-valued data gives bit-identical results to the oracle
+    rng = np.random.default_rng(n + N)
+    lengths = ([n] * 6 + [max(1024, -(-n // 16))] * 20
+               + list(rng.integers(max(1024, -(-n // 16)), n, 44)) + [1023, 700, 513, 200])
+    A = heavy_csr(n + N, 300, n, lengths, dt)
+    assert (A.col_idx.dtype == np.int32) == col32
+    B = gen.dense(n + N, 100, gen.S_B, (n, N), dt)
+    v, ro, ci = csr_dev(A)
+    ri = row_order(A, kind, 5)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    assert p.info()["split_rows"] == 73
+    C = S.spmm(v, ro, ri, ci, dev(B, dt), A.m, plan=p)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert_close(host_f64(C), ref, dt, "spmm dense rows")
+    Ai = A.with_values(gen.f32_to_storage(
+        rng.integers(-3, 4, A.nnz).astype(np.float32), dt), dt)
+    Bi = gen.dense(n + N, 100, gen.S_B, (n, N), dt, integer_values=True)
+    Ci = S.spmm(dev(Ai.values, dt), ro, ri, ci, dev(Bi, dt), A.m, plan=p)
+    assert np.array_equal(host_f64(Ci),
+                          oracle.spmm(A.m, A.row_offsets, A.col_idx, Ai.values, dt, Bi, dt))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_spmm_long_rows_nonfinite_b(dt):
+    # infinities and NaNs in a few rows of B meet only the stored entries:
+    # results are NaN / +-inf exactly where the oracle's are
+    n, N = 3000, 256
+    A = heavy_csr(77, 200, n, [n, n, 1500, 1200, 1100, 1024] * 6, dt)
+    B = gen.dense(77, 100, gen.S_B, (n, N), dt)
+    B32 = gen.storage_to_f64(B, dt).astype(np.float32)
+    for r, c, x in [(5, 3, np.inf), (700, 100, -np.inf), (701, 100, np.inf), (1500, 255, np.nan),
+                    (2999, 0, np.inf), (1234, 17, np.nan)]:
+        B32[r, c] = x
+    B = gen.f32_to_storage(B32, dt)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    assert p.info()["split_rows"] == 36
+    C = host_f64(S.spmm(v, ro, ri, ci, dev(B, dt), A.m, plan=p))
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
+    assert np.array_equal(np.isnan(C), np.isnan(ref))
+    assert np.array_equal(np.isposinf(C), np.isposinf(ref))
+    assert np.array_equal(np.isneginf(C), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert fin.sum() < fin.size  # some outputs are not finite
+    assert_close(np.where(fin, C, 0.0), np.where(fin, ref, 0.0), dt, "spmm long rows, finite part")
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_spmm_many_column_windows(dt):
     # k = 9000 rows of B with N = 2048: 16-lane groups, 16 windows of 128

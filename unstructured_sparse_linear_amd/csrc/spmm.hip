@@ -1,26 +1,15 @@
 // spmm.hip -- C = A * B for a CSR matrix A and a dense row-major B on gfx950
 // (spops README, section "Sparse Matrix Multiplication (SpMM)").
 //
-// Three kernels, chosen per call from N and the data layout:
-//
-// * spmm_wave_kernel (N >= 64*VEC, the LLM-adapter shapes).  One wavefront per
-//   row and column slice: the row's entries are wave-uniform, so they come in
-//   through 16-byte scalar loads and every lane reuses them; each lane owns
-//   VEC consecutive columns of C.  B rows are read with buffer loads whose row
-//   offset sits in an SGPR (no per-lane address arithmetic; out-of-range
-//   offsets read as zero, which also masks padding entries).  Columns are cut
-//   into slices of 64*VEC and slice s runs on the blocks s, s+ns, ... which the
-//   dispatcher places on the same XCD, so each XCD's 4 MB L2 holds the part of
-//   B it gathers from.  16-bit inputs use v_dot2_f32_{f16,bf16} on pairs of
-//   entries after a v_perm_b32 repack, one instruction per two products.
-// * spmm_kernel (the default for N > 1): a group of LPR lanes owns one row
-//   and a window of LPR*VEC columns; lanes load 16-byte vectors of B rows.
-//   The entries' columns and values are loaded once per group (a few lanes
-//   load a batch of 8, the rest fetch them with ds_swizzle) and B, col_idx
-//   and values are read through buffer resources, whose range check turns
-//   padding entries into loads of zero that touch no memory.  LPR is halved
-//   while one window's share of B would overflow an XCD's L2.
-// * spmv_kernel (N == 1): LPR lanes share a row, striding over its entries.
+// Kernels, chosen per call from N and the data layout:
+// * spmm_kernel (N > 1): a group of LPR lanes owns one row and a window of
+//   LPR*VEC columns; lanes load 16-byte vectors of B rows.  The entries'
+//   columns and values are loaded once per group (a few lanes load a batch
+//   of 8, the rest fetch them with ds_swizzle) and B, col_idx and values are
+//   read through buffer resources, whose range check turns padding entries
+//   into loads of zero that touch no memory.  LPR is halved while one
+//   window's share of B would overflow an XCD's L2.
+// * spmv_stream_kernel, spmv_row_kernel, spmv_kernel (N == 1).
 //
 // Row order.  Work visits rows in row_idx order (section "Usage": rows sorted
 // by entry count) so that neighbouring waves get rows of similar length and
