@@ -150,13 +150,13 @@ KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "spmv": ["spmm.hip", "common.h
 MFMA_COUNTERS = os.path.join(ROOT, "profiles", "mfma_busy.json")
 
 
-def mfma_busy_for(op, config):
+def mfma_busy_for(op, config, dt):
     """MFMA busy fraction of the structure-aware SDDMM's tile kernel from the
-    committed counter run (profiles/mfma_busy.json), while the kernel sources
-    still match the ones it was taken on; else None."""
+    committed counter run (profiles/mfma_busy.json, keyed "config3_f16"),
+    while the kernel sources still match the ones it was taken on; else None."""
     if op != "sddmm" or not os.path.exists(MFMA_COUNTERS):
         return None
-    ent = json.load(open(MFMA_COUNTERS)).get(f"config{config}")
+    ent = json.load(open(MFMA_COUNTERS)).get(f"config{config}_{dt}")
     if not ent or ent.get("source_sha") != kernel_sources_sha(KERNEL_FILES[op]):
         return None
     return ent.get("mfma_busy_frac")
@@ -175,8 +175,10 @@ def transpose_kernels(n, nnz):
     return ["transpose_count_kernel"] + scan + ["radix_scatter_kernel", "transpose_bucket_kernel"]
 
 
-def op_kernels(spmm_info, sddmm_info, m, n, nnz):
-    """Kernels one call of each operation launches (names as in rocprofv3)."""
+def op_kernels(spmm_info, sddmm_info, m, n, nnz, K=0, esz=2):
+    """Kernels one call of each operation launches (names as in rocprofv3).
+    The structure-aware SDDMM adds its remainder's K pieces with a third
+    kernel when BT (n x K, 16-bit) exceeds 32 MiB."""
     spmm = ["spmm_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else [])
     # N == 1: row blocks through LDS when the plan finds the rows balanced
     # (longest row <= 2 * mean + 32) and short (<= 128 entries), else a group
@@ -185,8 +187,11 @@ def op_kernels(spmm_info, sddmm_info, m, n, nnz):
     balanced = m > 0 and 0 < mr <= min(128, 2 * (nnz // m) + 32)
     spmv = (["spmv_stream_kernel"] if balanced and not spmm_info.get("chunks", 0)
             else ["spmv_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else []))
+    pieces = (sddmm_info.get("tiles", 0) and sddmm_info.get("rest_nnz", 0) and esz == 2
+              and n * K * 2 > (32 << 20))
     sddmm = ((["sddmm_tile_kernel"] if sddmm_info.get("tiles", 0) else [])
-             + (["sddmm_list_kernel"] if sddmm_info.get("rest_nnz", 0) else []))
+             + (["sddmm_list_kernel"] if sddmm_info.get("rest_nnz", 0) else [])
+             + (["sddmm_piece_sum_kernel"] if pieces else []))
     return {"spmm": spmm, "spmv": spmv, "sddmm": sddmm or ["sddmm_list_kernel"],
             "csr_add": ["csr_add_kernel"],
             "transpose": transpose_kernels(n, nnz),
@@ -560,7 +565,7 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
     ent = {"workload": w.name if cfg == 3 else gen.CONFIG_NAMES[cfg], "op": op, "dtype": dt,
            "m": A.m, "n": A.n, "nnz": A.nnz, "N_or_K": N if op in ("spmm", "spmv") else K,
            "kernels": op_kernels(info if op != "sddmm" else {}, info if op == "sddmm" else {},
-                                 A.m, A.n, A.nnz)[op],
+                                 A.m, A.n, A.nnz, K, ESZ[dt])[op],
            "plan": info, "plan_ms": round(plan_ms, 2),
            "us_median": round(t * 1e3, 2), "us_p10": round(ts[len(ts) // 10] * 1e3, 2),
            "us_p90": round(ts[(9 * len(ts)) // 10] * 1e3, 2),
@@ -568,7 +573,8 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
            "frac_hbm": round(ab / t / 1e6 / HBM_PEAK_GBS, 4),
            "gflops": round(fl / t / 1e6, 1),
            "hbm_bytes_counters": traffic,
-           "traffic_ratio": round(traffic / ab, 2) if traffic else None}
+           "traffic_ratio": round(traffic / ab, 2) if traffic else None,
+           "mfma_busy": mfma_busy_for(op, cfg, dt)}
     gb, seg = gathered_bytes(op, A, N, K, dt)
     if ceil and gb:
         key = ("gather_l2_4kib_gbps" if seg > 2048 else "gather_l2_1kib_gbps" if seg > 512
@@ -620,7 +626,7 @@ def write_records(path, result, args, A, dt, N, K, ab, fl):
     with open(path, "a") as f:
         for op, b in result["ops_breakdown"].items():
             t = b["ms"]
-            traffic = traffic_for(op, args.config) if op in KERNEL_FILES else None
+            traffic = traffic_for(op, args.config, dt) if op in KERNEL_FILES else None
             rec = {
                 "config": args.config, "workload": result["config"]["workload"], "op": op,
                 "dtype": dt, "out_dtype": "f32" if op in ("spmm", "spmv", "sddmm") else dt,
@@ -640,7 +646,7 @@ def write_records(path, result, args, A, dt, N, K, ab, fl):
                 "frac_hbm_copy": round(b["gbps"] / copy, 4) if copy else None,
                 "hbm_bytes_counters": traffic,
                 "refetch": round(traffic / b["alg_bytes"], 2) if traffic else None,
-                "mfma_busy": mfma_busy_for(op, args.config),
+                "mfma_busy": mfma_busy_for(op, args.config, dt),
                 "oracle_s": (cpu.get("ms_per_op", {}).get(op, 0) / 1e3) if cpu else None,
                 "oracle_threads": cpu.get("cores"), "cpu_model": cpu_model() if cpu else None,
                 "max_rel_err": None, "normwise_err": None, "bitexact_idx": None,
@@ -860,7 +866,7 @@ def main():
     # the headline operation: the longer of the operations the workload names
     # (its kernels listed together: long rows split, dense tiles plus the
     # remainder)
-    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.n, A.nnz)
+    kernels = op_kernels(spmm_plan.info(), sddmm_plan.info(), m, A.n, A.nnz, K, ESZ[dt])
     gated = [o for o in ops if o in NAMED_OPS[args.config]]
     dom = max(gated or ops, key=lambda o: breakdown[o]["ms"])
     achieved = ab[dom] / breakdown[dom]["ms"] / 1e6
@@ -901,7 +907,9 @@ def main():
                      "launch_us": round(breakdown[dom]["ms"] * 1e3, 2),
                      "alg_bytes_per_launch": int(ab[dom]),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_ratio": round(traffic / ab[dom], 2) if traffic else None,
+                     "mfma_busy": mfma_busy_for(dom, args.config, dt)},
     }
     if not args.no_ceilings:
         ceil = measure_ceilings(dev, flush)
