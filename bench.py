@@ -492,14 +492,16 @@ def measure_ceilings(dev, flush):
     return out
 
 
-def gathered_bytes(op, A, N, K, dt):
+def gathered_bytes(op, A, N, K, dt, tiles=0):
     """Bytes the operation gathers on chip (one operand row segment per
-    stored entry) and the size of one gathered segment."""
+    stored entry) and the size of one gathered segment.  A structure-aware
+    SDDMM with dense tiles does not gather per entry (its figure is the
+    tile kernel's MFMA busy): none."""
     s = ESZ[dt]
     if op in ("spmm", "spmv"):
         n_ = N if op == "spmm" else 1
         return A.nnz * n_ * s, min(n_ * s, 1024)
-    if op == "sddmm":
+    if op == "sddmm" and not tiles:
         return A.nnz * K * s, K * s
     return 0, 0
 
@@ -575,7 +577,7 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
            "hbm_bytes_counters": traffic,
            "traffic_ratio": round(traffic / ab, 2) if traffic else None,
            "mfma_busy": mfma_busy_for(op, cfg, dt)}
-    gb, seg = gathered_bytes(op, A, N, K, dt)
+    gb, seg = gathered_bytes(op, A, N, K, dt, info.get("tiles", 0) if op == "sddmm" else 0)
     if ceil and gb:
         key = ("gather_l2_4kib_gbps" if seg > 2048 else "gather_l2_1kib_gbps" if seg > 512
                else "gather_l2_512b_gbps")
@@ -914,7 +916,8 @@ def main():
     if not args.no_ceilings:
         ceil = measure_ceilings(dev, flush)
         result["ceilings"] = ceil
-        gb, seg = gathered_bytes(dom, A, N if dom != "spmv" else 1, K, dt)
+        gb, seg = gathered_bytes(dom, A, N if dom != "spmv" else 1, K, dt,
+                                 sddmm_plan.info().get("tiles", 0) if dom == "sddmm" else 0)
         if gb:
             key = ("gather_l2_4kib_gbps" if seg > 2048 else "gather_l2_1kib_gbps" if seg > 512
                    else "gather_l2_512b_gbps")
