@@ -27,9 +27,11 @@ measured ceiling, and the float64 oracle's time on the host for the same
 operation.
 
 Timing.  Every working set here fits in the 256 MB Infinity Cache, so each
-timed call starts after an untimed write of a 512 MiB scratch buffer that
-evicts L2 and the Infinity Cache (inputs resident in HBM, caches cold), and
-is bracketed by HIP events on the stream the library launches on.
+timed call starts after an untimed read of a 512 MiB scratch buffer that
+evicts L2 and the Infinity Cache (inputs resident in HBM, caches cold; a
+write of the buffer would leave dirty lines whose write-back then runs
+during the timed call: --flush write), and is bracketed by HIP events on the
+stream the library launches on.
 
 Algorithmic bytes per operation (each input read once, each output written
 once; k' / n' = distinct columns touched, m' = rows with entries):
@@ -77,6 +79,8 @@ def parse():
     p.add_argument("--dtype", default=None,
                    help="value dtype of config 3 (f16, the default, or bf16)")
     p.add_argument("--no-flush", action="store_true", help="warm caches (not the metric)")
+    p.add_argument("--flush", default="read", choices=("read", "write"),
+                   help="how the caches are emptied before each timed call")
     p.add_argument("--no-graph", action="store_true", help="time the step eagerly")
     p.add_argument("--serial-step", action="store_true",
                    help="capture the step on one stream (no overlap of independent operations)")
@@ -95,6 +99,27 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 256 MiB device copies (reference for HBM counters)")
     return p.parse_args()
+
+
+class Flush:
+    """Empties the L2s and the Infinity Cache before a timed call by reading a
+    512 MiB buffer (default) or by writing it (--flush write).  Either way the
+    timed call's inputs then come from HBM.  A write leaves the Infinity Cache
+    full of dirty lines, and their write-back to HBM then runs during the
+    timed call and takes part of its bandwidth (a 27 MB streaming read: 9.2 us
+    after a read, 13.9 us after a write); a read leaves clean lines."""
+
+    def __init__(self, dev, mode="read"):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        self.mode = mode
+        self.sink = None
+
+    def __call__(self):
+        if self.mode == "write":
+            self.buf.fill_(1)
+        else:
+            self.sink = self.buf.sum()
 
 
 def copy_calibration(steps):
@@ -306,7 +331,7 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
     ts = []
     for _ in range(max(args.steps, 5)):
         if not args.no_flush:
-            flush.fill_(1)
+            flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         graph.replay()
@@ -412,7 +437,7 @@ def delta_spmv_bench(S, dev, flush, args):
             ts = []
             for _ in range(max(args.steps, 5)):
                 if not args.no_flush:
-                    flush.fill_(1)
+                    flush()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 fn()
@@ -456,7 +481,7 @@ def measure_ceilings(dev, flush):
     b = torch.empty_like(a)
     ts = []
     for _ in range(5):
-        flush.fill_(1)
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         b.copy_(a)
@@ -552,7 +577,7 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
     evs = []
     for _ in range(reps):
         if not args.no_flush:
-            flush.fill_(1)
+            flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -728,7 +753,7 @@ def main():
     roT = torch.empty(n + 1, dtype=torch.int32, device=dev)
     ciT = torch.empty(A.nnz, dtype=torch.int16 if m <= 32767 else torch.int32, device=dev)
     riT = torch.empty(n, dtype=torch.int16 if n <= 32767 else torch.int32, device=dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = Flush(dev, args.flush)
     ws = spmm_plan.workspace(N, dev)
     from unstructured_sparse_linear_amd import spops as SP
 
@@ -755,7 +780,7 @@ def main():
 
     def cold():
         if not args.no_flush:
-            flush.fill_(1)
+            flush()
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -888,7 +913,8 @@ def main():
         "data": "synthetic (seeded generators, seed 0)",
         "config": {"workload": w.name, "config_id": args.config, "m": m, "n": n, "nnz": A.nnz,
                    "N": N, "K": K, "value_dtype": dt, "ops": ops,
-                   "caches": "warm" if args.no_flush else "cold (512 MiB flush per step)",
+                   "caches": "warm" if args.no_flush else
+                   f"cold (512 MiB {args.flush} before each timed call)",
                    "step": "eager" if args.no_graph else
                    "hip graph replay, streams: " + " | ".join("+".join(x) for x in lanes)},
         "value_op": {"op": dom, "us": round(breakdown[dom]["ms"] * 1e3, 2),
