@@ -601,6 +601,7 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
            "gflops": round(fl / t / 1e6, 1),
            "hbm_bytes_counters": traffic,
            "traffic_ratio": round(traffic / ab, 2) if traffic else None,
+           "hbm_gbps_counters": round(traffic / t / 1e6, 1) if traffic else None,
            "mfma_busy": mfma_busy_for(op, cfg, dt)}
     gb, seg = gathered_bytes(op, A, N, K, dt, info.get("tiles", 0) if op == "sddmm" else 0)
     if ceil and gb:
@@ -937,6 +938,12 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_ratio": round(traffic / ab[dom], 2) if traffic else None,
+                     # the bandwidth the HBM byte counters imply (traffic over the
+                     # same cold time) and its fraction of the peak
+                     "traffic_gbps": (round(traffic / breakdown[dom]["ms"] / 1e6, 1)
+                                      if traffic else None),
+                     "traffic_frac": (round(traffic / breakdown[dom]["ms"] / 1e6 / HBM_PEAK_GBS,
+                                            4) if traffic else None),
                      "mfma_busy": mfma_busy_for(dom, args.config, dt)},
     }
     if not args.no_ceilings:
