@@ -17,8 +17,8 @@
 //     key >= k.  Counts (dense rows, tiles, ...) stay in device memory; the
 //     key space is sized by bounds the host knows from (m, n, nnz).
 //
-// Execute: a workgroup takes one (tile, K split) item and computes the dense
-// TM x TN block A[rows] * BT[cols]^T over its share of K with
+// Execute: a workgroup (8 waves) takes one (tile, K split) item and computes
+// the dense TM x TN block A[rows] * BT[cols]^T over its share of K with
 // v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate), then writes the tile's
 // mask positions from an LDS copy of the block.
 // The (tile, K slice) units are spread evenly over the compute units; a
@@ -39,16 +39,18 @@ constexpr int TM = kSddmmTM;           // tile rows
 constexpr int TN = kSddmmTN;           // tile columns
 constexpr int TK = 64;                 // K slice staged per step
 constexpr int LDK = TK + 8;            // padded LDS row (16-bit elements)
-constexpr int kThreads = 256;          // 4 waves, 2 x 2 over the tile
+constexpr int kThreads = 512;          // 8 waves, 2 x 4 over the tile
 constexpr int kTileWgPerCu = 2;        // workgroups resident per compute unit
-constexpr int WM = TM / 2, WN = TN / 2;  // wave tile
+constexpr int kTileWavesPerSimd = kTileWgPerCu * kThreads / kWave / 4;  // launch bound
+constexpr int WM = TM / 2, WN = TN / 4;  // wave tile
 constexpr int BM = WM / 32, BN = WN / 32;  // 32 x 32 MFMA blocks per wave
 constexpr int kStaged = TM + TN;       // rows staged per slice (A rows, then BT rows)
 constexpr int kChunks = kStaged * (TK / 8) / kThreads;  // 16-byte chunks per thread and slice
 constexpr int kChunksA = TM * (TK / 8) / kThreads;      // the first ones are A rows
 constexpr int kStage = kStaged * LDK;  // 16-bit elements per LDS stage
 constexpr int LDR = TM + 4;            // padded fp32 column of the block in LDS
-constexpr int kEpi = 8;                // entries per thread per epilogue round
+constexpr int kEpi = 8;                // entries per thread per round of the split sum
+constexpr int kTileEpi = 2;            // entries per thread per epilogue round
 static_assert(kChunks * kThreads * 8 == kStaged * TK, "chunks cover the staged slice");
 static_assert(TN * LDR * 4 <= 2 * kStage * 2, "the fp32 block reuses the LDS stages");
 static_assert(LDR % 4 == 0, "16-byte column segments");
@@ -88,27 +90,28 @@ __device__ __forceinline__ float16v mfma32(const uint4& a, const uint4& b, float
 
 // A workgroup computes items: the K slices [s0, s0 + nst) of one tile (the
 // whole tile, or one of its `splits` fixed splits).
-// Wave (wr, wc) owns the WM x WN quarter (wr, wc) of the tile as BM x BN
-// MFMA 32x32x16 blocks (accumulators in the matrix-core registers), one wave
-// per SIMD.  K runs in slices of TK through two LDS stages; each thread
-// gathers its 16-byte chunks of the next slice into registers while the
-// current slice is multiplied, so a load has one slice of MFMA work to land,
-// and each slice costs one barrier.  A segment that covers its whole tile writes the output;
-// segment j of a tile split into several writes partial sums to part[j].
-// The epilogue's entry metadata (in-tile coordinates, positions) for the
-// first kEpi entries per thread is requested before the K loop so that its
-// latency hides behind the MFMA work.
+// Eight waves in a 2 x 4 grid: wave (wr, wc) owns the WM x WN block (wr, wc)
+// of the tile as BM x BN MFMA 32x32x16 blocks (fp32 accumulators), two
+// waves per SIMD per workgroup and two workgroups per compute unit.  K runs
+// in slices of TK through two LDS stages; each thread gathers its 16-byte
+// chunks of the next slice into registers while the current slice is
+// multiplied, so a load has one slice of MFMA work to land, and each slice
+// costs one barrier.  A segment that covers its whole tile writes the
+// output; segment j of a tile split into several writes partial sums to
+// part[j].  The epilogue's entry metadata (in-tile coordinates, positions)
+// for the first kTileEpi entries per thread is requested before the K loop
+// so that its latency hides behind the MFMA work.
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (l mod 32) of the A
 // block and column (l mod 32) of the B block, K elements 8*(l/32)..+8; it
 // receives column (l mod 32) of the result, value v at row
 // 8*(v/4) + 4*(l/32) + (v mod 4).
 template <bool BF16, typename OT>
-__global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(TileArgs t) {
+__global__ __launch_bounds__(kThreads, kTileWavesPerSimd) void sddmm_tile_kernel(TileArgs t) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
   const int tid = threadIdx.x;
   const int w = tid / kWave, l = lane_id();
-  const int wr = w >> 1, wc = w & 1;
+  const int wr = w >> 2, wc = w & 3;
   const int64_t H = t.sc->H, mc = t.sc->mc, Hc = t.sc->Hc;
   const int64_t tiles_a = t.sc->tiles_a, tiles_b_cols = t.sc->tiles_b_cols;
   const int64_t tiled = t.sc->tiled;
@@ -177,9 +180,9 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
 
     // in-tile coordinates and output positions of the first epilogue round,
     // requested now so that they arrive during the K loop
-    int32_t pre_rc[kEpi], pre_pos[kEpi];
+    int32_t pre_rc[kTileEpi], pre_pos[kTileEpi];
 #pragma unroll
-    for (int u = 0; u < kEpi; ++u) {
+    for (int u = 0; u < kTileEpi; ++u) {
       const int32_t q = e0 + tid + u * kThreads;
       pre_rc[u] = q < e1 ? t.ent_rc[q] : 0;
       pre_pos[u] = (q < e1 && direct) ? t.ent_pos[q] : 0;
@@ -251,12 +254,12 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
     }
 
     // epilogue: the whole fp32 block goes to LDS (column-major, in the
-    // stages' space), then every thread writes entries of the tile, kEpi per
+    // stages' space), then every thread writes entries of the tile, kTileEpi per
     // round with all their loads issued together
     float* Cs = (float*)smem;
-    auto write_round = [&](const int32_t (&rc)[kEpi], const int32_t (&pos)[kEpi], int32_t e) {
+    auto write_round = [&](const int32_t (&rc)[kTileEpi], const int32_t (&pos)[kTileEpi], int32_t e) {
 #pragma unroll
-      for (int u = 0; u < kEpi; ++u) {
+      for (int u = 0; u < kTileEpi; ++u) {
         const int32_t q = e + u * kThreads;
         if (q < e1) {
           const float v = Cs[(rc[u] & 0xffff) * LDR + (rc[u] >> 16)];
@@ -283,10 +286,10 @@ __global__ __launch_bounds__(kThreads, kTileWgPerCu) void sddmm_tile_kernel(Tile
     }
     __syncthreads();
     write_round(pre_rc, pre_pos, e0 + tid);
-    for (int32_t e = e0 + tid + kEpi * kThreads; e < e1; e += kEpi * kThreads) {
-      int32_t rc[kEpi], pos[kEpi];
+    for (int32_t e = e0 + tid + kTileEpi * kThreads; e < e1; e += kTileEpi * kThreads) {
+      int32_t rc[kTileEpi], pos[kTileEpi];
 #pragma unroll
-      for (int u = 0; u < kEpi; ++u) {
+      for (int u = 0; u < kTileEpi; ++u) {
         const int32_t q = e + u * kThreads;
         rc[u] = q < e1 ? t.ent_rc[q] : 0;
         pos[u] = (q < e1 && direct) ? t.ent_pos[q] : 0;
