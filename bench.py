@@ -462,7 +462,11 @@ def measure_ceilings(dev, flush):
     half a wave per 512-byte row, 8 rows in flight per lane) of 512 B, 1 KiB
     and 4 KiB rows at random indices, from
     a 2 MiB slice per XCD (L2-resident) and from one 16 MiB source shared by
-    all XCDs (Infinity Cache), warm, 5 back-to-back launches."""
+    all XCDs (Infinity Cache), warm, 5 back-to-back launches; and the on-chip
+    rates of the kernels' inner loops, from the same library: 16-byte LDS
+    reads without bank conflicts, v_fma_f32 and v_dot2_f32_f16 (eight
+    independent chains per lane; 2 and 4 flops per instruction), 2048
+    workgroups of 256 threads, 5 back-to-back launches after one."""
     import ctypes
 
     import torch
@@ -514,6 +518,31 @@ def measure_ceilings(dev, flush):
             t = e0.elapsed_time(e1) / 5
             name = f"{rb // 1024}kib" if rb >= 1024 else f"{rb}b"
             out[f"gather_{label}_{name}_gbps"] = round(waves * per_wave * rb / t / 1e6, 1)
+
+    def rate(launch, work):
+        assert launch() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            assert launch() == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return work * 5 / (e0.elapsed_time(e1) * 1e-3)
+
+    st = ctypes.c_void_p(stream.cuda_stream)
+    L.spops_ceil_lds.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.spops_ceil_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    threads, iters = blocks * 256, 400
+    out["lds_read_gbps"] = round(rate(lambda: L.spops_ceil_lds(blocks, iters, sink.data_ptr(), st),
+                                      threads * iters * 128) / 1e9, 1)
+    out["valu_fma_f32_tflops"] = round(rate(
+        lambda: L.spops_ceil_valu(0, blocks, iters, sink.data_ptr(), st),
+        threads * iters * 32 * 2) / 1e12, 1)
+    out["valu_dot2_f16_tflops"] = round(rate(
+        lambda: L.spops_ceil_valu(1, blocks, iters, sink.data_ptr(), st),
+        threads * iters * 32 * 4) / 1e12, 1)
     return out
 
 
@@ -586,18 +615,31 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     t = float(np.median(ts))
+    wevs = []
+    for _ in range(5):  # back to back, no flush
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        wevs.append((e0, e1))
+    torch.cuda.synchronize()
+    warm = [a.elapsed_time(b) for a, b in wevs]
     ab = alg_bytes(A, N, K, dt)[op if op != "spmv" else "spmv"]
     fl = flops(A, N, K)[op]
     traffic = traffic_for(op, cfg, dt)
     ent = {"workload": w.name if cfg == 3 else gen.CONFIG_NAMES[cfg], "op": op, "dtype": dt,
+           "out_dtype": "f32", "backend": "structure_aware" if op == "sddmm" else None,
            "m": A.m, "n": A.n, "nnz": A.nnz, "N_or_K": N if op in ("spmm", "spmv") else K,
            "kernels": op_kernels(info if op != "sddmm" else {}, info if op == "sddmm" else {},
                                  A.m, A.n, A.nnz, K, ESZ[dt])[op],
            "plan": info, "plan_ms": round(plan_ms, 2),
            "us_median": round(t * 1e3, 2), "us_p10": round(ts[len(ts) // 10] * 1e3, 2),
            "us_p90": round(ts[(9 * len(ts)) // 10] * 1e3, 2),
-           "alg_bytes": int(ab), "gbps": round(ab / t / 1e6, 1),
+           "us_warm_median": round(float(np.median(warm)) * 1e3, 2),
+           "alg_bytes": int(ab), "flops": int(fl), "gbps": round(ab / t / 1e6, 1),
            "frac_hbm": round(ab / t / 1e6 / HBM_PEAK_GBS, 4),
+           "frac_hbm_copy": (round(ab / t / 1e6 / ceil["copy_gbps"], 4)
+                             if ceil and ceil.get("copy_gbps") else None),
            "gflops": round(fl / t / 1e6, 1),
            "hbm_bytes_counters": traffic,
            "traffic_ratio": round(traffic / ab, 2) if traffic else None,

@@ -12,6 +12,12 @@
 //     b mod 8), so the slice can stay in that XCD's L2; without it all
 //     workgroups share the whole source.  Lanes fold what they load into one
 //     word each, stored once, so the loads cannot be dropped.
+// and the on-chip rates the kernels' inner loops run against:
+//   * lds_kernel: 16-byte LDS reads, consecutive lanes at consecutive
+//     16-byte words (no bank conflicts), eight per lane per step;
+//   * fma_kernel: v_fma_f32, eight independent chains per lane;
+//   * dot2_kernel: v_dot2_f32_f16 (two products and their sum into an fp32
+//     accumulator), eight independent chains per lane.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,7 +59,93 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const uint4* src, int64_
   sink[(int64_t)blockIdx.x * kBlock + threadIdx.x] = acc;
 }
 
+constexpr int kLdsVecs = 1024;  // 16 KiB of LDS per workgroup
+
+__global__ __launch_bounds__(kBlock) void lds_kernel(int64_t iters, uint32_t* sink) {
+  __shared__ uint4 buf[kLdsVecs];
+  const int t = threadIdx.x;
+  for (int i = t; i < kLdsVecs; i += kBlock) buf[i] = make_uint4(i, 3 * i, 5 * i, 7 * i);
+  __syncthreads();
+  uint32_t acc = 0;
+  for (int64_t i = 0; i < iters; ++i) {
+    const int base = t + (int)(i & 3) * 32;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint4 v = buf[(base + u * 128) & (kLdsVecs - 1)];
+      acc += v.x + v.y + v.z + v.w;
+    }
+  }
+  sink[(int64_t)blockIdx.x * kBlock + t] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void fma_kernel(int64_t iters, float x, float y,
+                                                     float* sink) {
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (float)threadIdx.x * 1e-3f + (float)j;
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = __builtin_fmaf(a[j], x, y);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += a[j];
+  sink[(int64_t)blockIdx.x * kBlock + threadIdx.x] = s;
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(kBlock) void dot2_kernel(int64_t iters, uint32_t xbits,
+                                                      float* sink) {
+  const half2v x = __builtin_bit_cast(half2v, xbits);
+  half2v b[8];
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    b[j] = half2v{(_Float16)(threadIdx.x & 15), (_Float16)j};
+    a[j] = (float)j;
+  }
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = __builtin_amdgcn_fdot2(b[j], x, a[j], false);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += a[j];
+  sink[(int64_t)blockIdx.x * kBlock + threadIdx.x] = s;
+}
+
 }  // namespace
+
+// LDS reads: blocks x 256 threads, each iters x 8 reads of 16 bytes (iters x
+// 128 bytes per thread).  sink: blocks * 256 words.
+extern "C" int spops_ceil_lds(int blocks, int64_t iters, void* sink, void* stream) {
+  if (blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(lds_kernel, dim3(blocks), dim3(kBlock), 0, (hipStream_t)stream, iters,
+                     (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// VALU rates: blocks x 256 threads, each iters x 32 instructions; kind 0:
+// v_fma_f32 (2 flops each), kind 1: v_dot2_f32_f16 (4 flops each).  sink:
+// blocks * 256 floats.
+extern "C" int spops_ceil_valu(int kind, int blocks, int64_t iters, void* sink, void* stream) {
+  if (blocks <= 0 || iters <= 0) return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0)
+    hipLaunchKernelGGL(fma_kernel, dim3(blocks), dim3(kBlock), 0, s, iters, 0.999f, 1e-3f,
+                       (float*)sink);
+  else if (kind == 1)
+    hipLaunchKernelGGL(dot2_kernel, dim3(blocks), dim3(kBlock), 0, s, iters, 0x3bff3bffu,
+                       (float*)sink);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 // Gathers: blocks x 256 threads, each wave `per_wave` rows (a multiple of 16)
 // of row_bytes (512, 1024 or 4096) from src at idx[wave * per_wave + i] (row
