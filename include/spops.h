@@ -182,8 +182,9 @@ spops_status spops_spmm_plan_info(const spops_spmm_plan* plan, int64_t* split_ro
  *   on the stream, in the caller's workspace, with the default density
  *   threshold (slower than reusing a plan, but it neither allocates nor
  *   synchronizes, so it can be captured in a HIP graph).  The dense tiles
- *   need 16-bit inputs, K a multiple of 8, lda and ldbt multiples of 8 and
- *   16-byte aligned A and BT; other calls run the general kernel (with a
+ *   need 16-bit inputs, K a multiple of 8, lda and ldbt multiples of 8,
+ *   16-byte aligned A and BT, and rows x leading dimension x 2 bytes under
+ *   2 GiB for each of A and BT; other calls run the general kernel (with a
  *   plan that found no tiles, over the plan's column buckets).
  *   workspace: spops_sddmm_workspace_size bytes (NULL when that is 0),
  *   256-byte aligned; its contents on entry do not matter.  Too small:

@@ -529,6 +529,41 @@ def test_sddmm_tiles_split_k(dt, m, n, K, hr, hc, splits):
     assert np.array_equal(host_f64(outi), refi)
 
 
+def test_sddmm_operand_extent_over_4gib():
+    # A with a leading dimension that takes rows x lda x 2 bytes past 4 GiB
+    # (only the first K elements of each row hold data), beyond what 32-bit
+    # buffer offsets reach: the structure-aware call leaves the dense tiles
+    # to the entry-list kernel and still matches the oracle; bit-exact on
+    # integer data
+    import ctypes
+    m, n, K = 256, 300, 64
+    lda = (1 << 23) + 64
+    assert m * lda * 2 >= 1 << 32
+    M = cross_csr(21, m, n, 200, 250)
+    _, ro, ci = csr_dev(M)
+    ri = S.sort_rows_by_nnz(ro, n)
+    plan = S.SddmmPlan(ro, ci, m, n)
+    assert plan.info()["tiles"] >= 2
+    Ai = gen.dense(22, 100, gen.S_A, (m, K), "f16", integer_values=True)
+    Bi = gen.dense(22, 100, gen.S_BT, (n, K), "f16", integer_values=True)
+    big = torch.empty((m, lda), dtype=torch.float16, device="cuda")
+    big[:, :K] = dev(Ai, "f16")
+    BT = dev(Bi, "f16")
+    out = torch.full((M.nnz,), float("nan"), dtype=torch.float32, device="cuda")
+    L = S.spops.lib()
+    d = S.spops.csr_desc(None, ro, ri, ci, m, n)
+    wb = ctypes.c_size_t()
+    assert L.spops_sddmm_workspace_size(ctypes.byref(d), K, S.spops.F16, S.spops.STRUCTURE_AWARE,
+                                        plan.handle, ctypes.byref(wb)) == 0
+    ws = torch.empty(max(wb.value, 1), dtype=torch.uint8, device="cuda")
+    assert L.spops_sddmm(ctypes.byref(d), big.data_ptr(), K, lda, BT.data_ptr(), K,
+                         S.spops.F16, out.data_ptr(), S.spops.F32, S.spops.STRUCTURE_AWARE,
+                         plan.handle, ws.data_ptr(), ws.numel(), None) == 0
+    torch.cuda.synchronize()
+    del big
+    assert np.array_equal(host_f64(out), oracle.sddmm(M.row_offsets, M.col_idx, Ai, Bi, "f16"))
+
+
 @pytest.mark.parametrize("dt,m,n,K,hr,hc", TILE_CASES)
 @pytest.mark.parametrize("pieces", [1, 2, 8, 16])
 def test_sddmm_remainder_k_pieces(dt, m, n, K, hr, hc, pieces):

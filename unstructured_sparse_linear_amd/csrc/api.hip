@@ -282,10 +282,14 @@ spops_status spops_sddmm_plan_info(const spops_sddmm_plan* plan, int64_t* dense_
 static bool sddmm_tiles_possible(spops_dtype in_type, int64_t K) {
   return in_type != SPOPS_F32 && K > 0 && K % 8 == 0;
 }
-static bool sddmm_tiles_ok(spops_dtype in_type, int64_t K, int64_t lda, int64_t ldbt,
-                           const void* A, const void* BT) {
+// The tile kernel reads A and BT through buffer resources with 32-bit
+// offsets: each operand's extent (rows x leading dimension) must stay under
+// 2 GiB; larger operands take the entry-list path.
+static bool sddmm_tiles_ok(spops_dtype in_type, int64_t m, int64_t n, int64_t K, int64_t lda,
+                           int64_t ldbt, const void* A, const void* BT) {
   return sddmm_tiles_possible(in_type, K) && lda % 8 == 0 && ldbt % 8 == 0 &&
-         ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0);
+         ((uintptr_t)A % 16 == 0) && ((uintptr_t)BT % 16 == 0) &&
+         m * lda * 2 < ((int64_t)1 << 31) && n * ldbt * 2 < ((int64_t)1 << 31);
 }
 
 // The entry-list kernel reads 16-byte vectors along K.
@@ -370,7 +374,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     return SPOPS_ERR_PLAN;
   hipStream_t s = as_stream(hip_stream);
 
-  const bool tiles_ok = sddmm_tiles_ok(in_type, K, lda, ldbt, A, BT);
+  const bool tiles_ok = sddmm_tiles_ok(in_type, mask->rows, mask->cols, K, lda, ldbt, A, BT);
   const bool list_ok = sddmm_list_ok(in_type, K, lda, ldbt, A, BT);
   SddmmListArgs r{};
   r.m = mask->rows;

@@ -795,6 +795,9 @@ hipError_t launch_sddmm_tiles(const SddmmPlanDev& p, int64_t K, const void* A, i
                               const void* BT, int64_t ldbt, int dtype, void* out, int out_dtype,
                               const SddmmTileSched& sched, float* part, hipStream_t s) {
   if (p.host_ok && (p.h.tiles == 0 || p.h.tiled == 0)) return hipSuccess;
+  // buffer offsets are 32-bit: each operand under 2 GiB
+  if (p.m * lda * 2 >= ((int64_t)1 << 31) || p.n * ldbt * 2 >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
   SddmmTileSched sc = sched;
   if (!p.host_ok || (sc.splits > 1 && !part)) sc.splits = 1;
   TileArgs ta{K,           lda,        ldbt,         p.n,          (const uint16_t*)A,
