@@ -282,7 +282,8 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
     """One training step of the sparse layer Y^T = S . X^T with S = A (values
     A.values, pattern A) and X^T = the workload's dense B (k x N): forward,
     the gradients of the stored values (SDDMM of dY^T and X^T) and of X^T
-    (S^T . dY^T), a masked Adam step on the values, and the merge W += S;
+    (S^T's values by the pattern's transpose permutation, then S^T . dY^T),
+    a masked Adam step on the values, and the merge W += S;
     outputs in the input dtype, as the autograd layer produces them.
     Captured as a HIP graph, cold caches."""
     import torch
@@ -348,7 +349,9 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
         "forward_spmm": nnz * (s_v + s_ci) + 4 * (m + 1) + m * s_ri + kp * N * s_v + m * N * s_v,
         "grad_values_sddmm": nnz * s_ci + 4 * (m + 1) + m * s_ri + mp * N * s_v + kp * N * s_v
         + nnz * s_v,
-        "transpose": nnz * (s_v + s_ci) + 4 * (m + 1) + nnz * (s_v + s_riT) + 4 * (n + 1),
+        # S^T's values: S's values through the transpose's permutation (found
+        # once with the pattern): read the permutation and the values, write
+        "transposed_values": nnz * (4 + 2 * s_v),
         "grad_input_spmm": nnz * (s_v + s_riT) + 4 * (n + 1) + n * s_riT + mp * N * s_v
         + n * N * s_v,
     }

@@ -6,7 +6,9 @@
  *   spops_spmm            section "Sparse Matrix Multiplication (SpMM)"
  *   spops_sddmm           section "Sampled Dense-Dense Matrix Multiplication (SDDMM)"
  *   spops_csr_add         section "Sparse Addition"
- *   spops_csr_transpose   section "CSR Transpose"
+ *   spops_csr_transpose   section "CSR Transpose" (also as a permutation of
+ *                         the values: spops_csr_transpose_permutation and
+ *                         spops_permute_values)
  *   spops_sort_rows_by_nnz  the row_idx list of section "Usage"
  * and, built on spops_spmm, a conjugate-gradient solver (spops_cg; the
  * torchsparsegradutils README, section "Built-in Iterative Solvers"), and a
@@ -277,6 +279,28 @@ spops_status spops_csr_transpose_workspace_size(int64_t rows, int64_t cols, int6
 spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* out_row_offsets,
                                  void* out_col_idx, spops_itype out_col_type, void* workspace,
                                  size_t workspace_bytes, void* hip_stream);
+
+/* The permutation spops_csr_transpose applies to the values (section "CSR
+ * Transpose"), for a pattern whose values change while its positions do not
+ * (the transposed product in a sparse layer's backward pass):
+ *   out_src[j] = index among A's stored entries of A^T's stored entry j;
+ * out_row_offsets and out_col_idx are written as by spops_csr_transpose.
+ * A->values is not used.  Then A^T's values for any values of A are one
+ * spops_permute_values call.  workspace:
+ * spops_csr_transpose_permutation_workspace_size bytes, 256-byte aligned. */
+spops_status spops_csr_transpose_permutation_workspace_size(int64_t rows, int64_t cols,
+                                                            int64_t nnz, size_t* bytes);
+spops_status spops_csr_transpose_permutation(const spops_csr* A, int32_t* out_src,
+                                             int32_t* out_row_offsets, void* out_col_idx,
+                                             spops_itype out_col_type, void* workspace,
+                                             size_t workspace_bytes, void* hip_stream);
+
+/* out[j] = in[src[j]] for 0 <= j < n, elements of `type` moved bit for bit
+ * (with src from spops_csr_transpose_permutation: A^T's values from A's).
+ * in has n_in elements; an src[j] outside [0, n_in) writes zero bits.
+ * in and out must not overlap. */
+spops_status spops_permute_values(const void* in, int64_t n_in, spops_dtype type,
+                                  const int32_t* src, int64_t n, void* out, void* hip_stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

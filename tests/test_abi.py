@@ -209,6 +209,33 @@ def test_transpose_and_sort_reject_bad_arguments(L):
     assert g(FAKE, 0, 50, None, 0, None, 0, None) == 0
 
 
+def test_transpose_permutation_and_permute_reject_bad_arguments(L):
+    b = ctypes.c_size_t()
+    assert L.spops_csr_transpose_permutation_workspace_size(4, 4, 4, ctypes.byref(b)) == 0
+    t = ctypes.c_size_t()
+    assert L.spops_csr_transpose_workspace_size(4, 4, 4, ctypes.byref(t)) == 0
+    assert b.value >= t.value + 4 * 4                      # the transpose's, plus the indices
+    assert L.spops_csr_transpose_permutation_workspace_size(4, 4, -1, ctypes.byref(b)) == 2
+    assert L.spops_csr_transpose_permutation_workspace_size(4, 4, 4, None) == 1
+    assert L.spops_csr_transpose_permutation_workspace_size(4, 4, 4, ctypes.byref(b)) == 0
+    f = L.spops_csr_transpose_permutation
+    big = 1 << 20
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE, 0, FAKE, b.value - 1, None) == 5
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE, 0, FAKE + 16, big, None) == 5  # alignment
+    assert f(ctypes.byref(desc()), None, FAKE, FAKE, 0, FAKE, big, None) == 1
+    assert f(ctypes.byref(desc()), FAKE, None, FAKE, 0, FAKE, big, None) == 1
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE, 7, FAKE, big, None) == 3
+    assert f(ctypes.byref(desc(rows=40000, ri_type=1)), FAKE, FAKE, FAKE, 0, FAKE, 1 << 30,
+             None) == 4                                       # transposed indices need int32
+    g = L.spops_permute_values
+    assert g(FAKE, 10, 7, FAKE, 10, FAKE, None) == 3          # unknown dtype
+    assert g(FAKE, 10, 1, FAKE, -1, FAKE, None) == 2
+    assert g(FAKE, -1, 1, FAKE, 10, FAKE, None) == 2
+    assert g(FAKE, 10, 1, None, 10, FAKE, None) == 1
+    assert g(FAKE, 10, 1, FAKE, 10, None, None) == 1
+    assert g(None, 0, 1, None, 0, None, None) == 0            # nothing to do
+
+
 def test_python_binding_validates_before_the_library():
     import torch
     cpu = torch.zeros(4, dtype=torch.int32)

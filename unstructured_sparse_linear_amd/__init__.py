@@ -20,10 +20,12 @@ from .spops import (  # noqa: F401
     clear_plan_caches,
     csr_add,
     csr_transpose,
+    csr_transpose_permutation,
     csr_transpose_workspace,
     lib,
     masked_adam,
     option,
+    permute_values,
     sddmm,
     set_option,
     sort_rows_by_nnz,
@@ -36,4 +38,5 @@ __all__ = ["spmm", "sddmm", "csr_add", "csr_transpose", "sort_rows_by_nnz", "Spm
            "SddmmPlan", "SpopsError", "lib", "clear_plan_caches", "csr_transpose_workspace",
            "sort_rows_workspace", "SparsePattern", "SparseAdapter", "sparse_linear", "cg",
            "masked_adam", "MaskedAdam", "DeltaMatrix", "delta_encode", "delta_spmv",
-           "option", "set_option", "validate_csr", "InvalidCSR"]
+           "option", "set_option", "validate_csr", "InvalidCSR", "csr_transpose_permutation",
+           "permute_values"]

@@ -9,7 +9,9 @@ every step one call into libspops and needs no dense transpose:
 
     forward    Y^T  = S · X^T                         spmm
     backward   dS   = dY^T · (X^T)^T sampled at S     sddmm (A = dY^T, BT = X^T)
-               dX^T = S^T · dY^T                      csr_transpose + spmm
+               dX^T = S^T · dY^T                      values of S^T (the
+                                                      transpose's permutation,
+                                                      found once) + spmm
     merge      W   += S                               csr_add
     optimizer  values -= Adam step (masked)           masked_adam (MaskedAdam)
 
@@ -22,38 +24,34 @@ from typing import Optional
 
 import torch
 
-from .spops import (SddmmPlan, SpmmPlan, csr_add, csr_transpose, csr_transpose_workspace,
-                    masked_adam, sddmm, sort_rows_by_nnz, spmm)
+from .spops import (SddmmPlan, SpmmPlan, csr_add, csr_transpose_permutation, masked_adam,
+                    permute_values, sddmm, sort_rows_by_nnz, spmm)
 
 
 class SparsePattern:
     """A CSR sparsity pattern of S (out_features x in_features) and what is
-    derived from it once: the row order, the SpMM / SDDMM plans, and the
-    pattern of S^T with its own row order and plan."""
+    derived from it once: the row order, the SpMM / SDDMM plans, the pattern
+    of S^T with its own row order and plan, and the permutation that takes
+    S's values to S^T's."""
 
     def __init__(self, row_offsets: torch.Tensor, col_idx: torch.Tensor,
                  out_features: int, in_features: int):
         self.ro, self.ci = row_offsets, col_idx
         self.m, self.n = out_features, in_features
         self.nnz = col_idx.numel()
-        dev = row_offsets.device
         self.ri = sort_rows_by_nnz(row_offsets, in_features)
         self.spmm_plan = SpmmPlan(row_offsets, self.ri, col_idx, in_features)
         self.sddmm_plan = SddmmPlan(row_offsets, col_idx, out_features, in_features)
-        self.tws = csr_transpose_workspace(out_features, in_features, self.nnz, dev)
-        _, self.roT, self.ciT = csr_transpose(None, row_offsets, col_idx, out_features,
-                                              in_features, workspace=self.tws)
+        self.srcT, self.roT, self.ciT = csr_transpose_permutation(row_offsets, col_idx,
+                                                                  out_features, in_features)
         self.riT = sort_rows_by_nnz(self.roT, out_features)
         self.spmmT_plan = SpmmPlan(self.roT, self.riT, self.ciT, out_features)
 
     def transposed_values(self, values: torch.Tensor,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Values of S^T in the order of the transposed pattern."""
-        if out is None:
-            out = torch.empty_like(values)
-        csr_transpose(values, self.ro, self.ci, self.m, self.n, workspace=self.tws,
-                      out=(out, self.roT, self.ciT))
-        return out
+        """Values of S^T in the order of the transposed pattern (what
+        csr_transpose gives, bit for bit)."""
+        return permute_values(values, self.srcT, out=out)
 
 
 class _SparseLinearFn(torch.autograd.Function):

@@ -526,6 +526,50 @@ spops_status spops_csr_transpose(const spops_csr* A, void* out_values, int32_t* 
       out_col_idx, out_col_type == SPOPS_I32, workspace, as_stream(hip_stream)));
 }
 
+// ------------------------------------------------ transpose permutation ---
+
+static size_t transpose_perm_workspace_bytes(int64_t rows, int64_t cols, int64_t nnz) {
+  return align256(transpose_workspace_bytes(rows, cols, nnz)) + align256((size_t)nnz * 4);
+}
+
+spops_status spops_csr_transpose_permutation_workspace_size(int64_t rows, int64_t cols,
+                                                            int64_t nnz, size_t* bytes) {
+  if (!bytes) return SPOPS_ERR_NULL;
+  if (rows < 0 || cols < 0 || nnz < 0 || nnz > INT32_MAX) return SPOPS_ERR_SHAPE;
+  *bytes = transpose_perm_workspace_bytes(rows, cols, nnz);
+  return SPOPS_OK;
+}
+
+spops_status spops_csr_transpose_permutation(const spops_csr* A, int32_t* out_src,
+                                             int32_t* out_row_offsets, void* out_col_idx,
+                                             spops_itype out_col_type, void* workspace,
+                                             size_t workspace_bytes, void* hip_stream) {
+  spops_status st = check_csr(A, false, false);
+  if (st != SPOPS_OK) return st;
+  if (!itype_ok(out_col_type)) return SPOPS_ERR_DTYPE;
+  if (out_col_type == SPOPS_I16 && A->rows > 32767) return SPOPS_ERR_INDEX_WIDTH;
+  if (!out_row_offsets) return SPOPS_ERR_NULL;
+  if (A->nnz > 0 && (!out_col_idx || !out_src)) return SPOPS_ERR_NULL;
+  const size_t tws = align256(transpose_workspace_bytes(A->rows, A->cols, A->nnz));
+  const size_t need = transpose_perm_workspace_bytes(A->rows, A->cols, A->nnz);
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0))
+    return SPOPS_ERR_WORKSPACE;
+  return from_hip(launch_csr_transpose_perm(
+      A->rows, A->cols, A->nnz, A->row_offsets, A->col_idx, A->col_type == SPOPS_I32, out_src,
+      out_row_offsets, out_col_idx, out_col_type == SPOPS_I32, workspace,
+      (int32_t*)((char*)workspace + tws), as_stream(hip_stream)));
+}
+
+spops_status spops_permute_values(const void* in, int64_t n_in, spops_dtype type,
+                                  const int32_t* src, int64_t n, void* out, void* hip_stream) {
+  if (!dtype_ok(type)) return SPOPS_ERR_DTYPE;
+  if (n < 0 || n_in < 0 || n > INT32_MAX || n_in > INT32_MAX) return SPOPS_ERR_SHAPE;
+  if (n == 0) return SPOPS_OK;
+  if (!src || !out || (n_in > 0 && !in)) return SPOPS_ERR_NULL;
+  return from_hip(launch_permute_values(in, n_in, elem_bytes(type), src, n, out,
+                                        as_stream(hip_stream)));
+}
+
 // ------------------------------------------------------------ validation ---
 
 spops_status spops_validate_csr_workspace_size(int64_t rows, int64_t cols, int64_t nnz,

@@ -25,6 +25,16 @@ hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const i
                                 const void* col, int col_i32, const void* val, int val_bytes,
                                 void* out_val, int32_t* out_ro, void* out_col, int out_col_i32,
                                 void* ws, hipStream_t s);
+// The transpose's permutation: out_src[j] = source entry of A^T's entry j
+// (out_ro / out_col as launch_csr_transpose); iota: nnz int32 of scratch
+// beside the transpose workspace ws.
+hipError_t launch_csr_transpose_perm(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
+                                     const void* col, int col_i32, int32_t* out_src,
+                                     int32_t* out_ro, void* out_col, int out_col_i32, void* ws,
+                                     int32_t* iota, hipStream_t s);
+// out[j] = in[src[j]] for j < n (elem_bytes 2 or 4; src outside [0, n_in): 0).
+hipError_t launch_permute_values(const void* in, int64_t n_in, int elem_bytes,
+                                 const int32_t* src, int64_t n, void* out, hipStream_t s);
 
 // --------------------------------------------------------- row ordering --
 size_t sort_rows_workspace_bytes(int64_t rows, int64_t cols);

@@ -4,7 +4,10 @@
 //     the stored entries by column; the output row offsets are the column
 //     boundaries of the sorted keys;
 //   * the row_idx order (section "Usage"): rows sorted by entry count, most
-//     first, ties by ascending row -- a stable sort on (cols - count).
+//     first, ties by ascending row -- a stable sort on (cols - count);
+// and, for a pattern transposed once and its values many times, the
+// transpose's permutation (the transpose of the entry indices, moved as
+// 4-byte values) and a kernel that applies a permutation to values.
 //
 // Sorting is least-significant-digit radix with 8-bit digits, in three
 // kernels per pass: per-tile digit counts, one exclusive scan over the
@@ -705,6 +708,37 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, in
   if (i < n) p[i] = v;
 }
 
+__global__ __launch_bounds__(256) void iota_i32_kernel(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = (int32_t)i;
+}
+
+// out[j] = in[src[j]], T a 2- or 4-byte word moved as is; src[j] outside
+// [0, n_in) gives zero.  Four outputs per thread and round, their loads
+// issued together.
+template <typename T>
+__global__ __launch_bounds__(256) void permute_values_kernel(const T* in, int64_t n_in,
+                                                             const int32_t* src, int64_t n,
+                                                             T* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t j0 = (int64_t)blockIdx.x * 256 + threadIdx.x; j0 < n; j0 += 4 * stride) {
+    int32_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + u * stride;
+      q[u] = j < n ? src[j] : -1;
+    }
+    T v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (q[u] >= 0 && q[u] < n_in) ? in[q[u]] : T(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + u * stride;
+      if (j < n) out[j] = v[u];
+    }
+  }
+}
+
 template <typename OI, int RB>
 hipError_t launch_bucket_finish(const void* rec, const uint32_t* bstart, int64_t bstride,
                                 int64_t nnz, int64_t n, int sh, int vb, void* out_val,
@@ -1170,6 +1204,37 @@ hipError_t launch_csr_transpose(int64_t rows, int64_t cols, int64_t nnz, const i
                                      out_col, s);
   return finish_transpose<int16_t>(skeys, svals, rows_of, nnz, cols, val, vb, out_val, out_ro,
                                    out_col, s);
+}
+
+hipError_t launch_csr_transpose_perm(int64_t rows, int64_t cols, int64_t nnz, const int32_t* ro,
+                                     const void* col, int col_i32, int32_t* out_src,
+                                     int32_t* out_ro, void* out_col, int out_col_i32, void* ws,
+                                     int32_t* iota, hipStream_t s) {
+  if (nnz > 0) {
+    hipLaunchKernelGGL(iota_i32_kernel, dim3((unsigned)cdiv(nnz, 256)), dim3(256), 0, s, iota,
+                       nnz);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // the entry indices are 4-byte words that the transpose moves bit for bit
+  return launch_csr_transpose(rows, cols, nnz, ro, col, col_i32, iota, 4, out_src, out_ro,
+                              out_col, out_col_i32, ws, s);
+}
+
+hipError_t launch_permute_values(const void* in, int64_t n_in, int elem_bytes,
+                                 const int32_t* src, int64_t n, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = cdiv(n, 4 * 256);
+  const dim3 grid((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20)));
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(permute_values_kernel<uint32_t>, grid, dim3(256), 0, s,
+                       (const uint32_t*)in, n_in, src, n, (uint32_t*)out);
+  else if (elem_bytes == 2)
+    hipLaunchKernelGGL(permute_values_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       (const uint16_t*)in, n_in, src, n, (uint16_t*)out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 size_t sort_rows_workspace_bytes(int64_t rows, int64_t cols) {

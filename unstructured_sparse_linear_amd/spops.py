@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
             "spops_csr_transpose_workspace_size": ([i64, i64, i64, P(sz)], i32),
             "spops_csr_transpose": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
             "spops_csr_transpose_noalloc": ([cp, vp, vp, vp, i32, vp], i32),
+            "spops_csr_transpose_permutation_workspace_size": ([i64, i64, i64, P(sz)], i32),
+            "spops_csr_transpose_permutation": ([cp, vp, vp, vp, i32, vp, sz, vp], i32),
+            "spops_permute_values": ([vp, i64, i32, vp, i64, vp, vp], i32),
             "spops_validate_csr_workspace_size": ([i64, i64, i64, P(sz)], i32),
             "spops_validate_csr": ([cp, i32, vp, sz, P(ctypes.c_uint32), vp], i32),
             "spops_csr_transpose_noalloc_limit": ([P(sz)], i32),
@@ -482,6 +485,47 @@ def csr_transpose(A_val: Optional[torch.Tensor], A_row_offsets: torch.Tensor,
         ctypes.byref(d), _ptr(out_v), out_ro.data_ptr(), _ptr(out_ci), _IT[oit],
         workspace.data_ptr(), workspace.numel(), _stream(A_row_offsets)))
     return out_v, out_ro, out_ci
+
+
+def csr_transpose_permutation(A_row_offsets: torch.Tensor, A_col_indices: torch.Tensor,
+                              m: int, n: int) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The permutation csr_transpose applies to the values of this pattern:
+    (src [nnz] int32, row_offsets_T [n+1] int32, col_idx_T [nnz]), with
+    values_T = permute_values(values, src)."""
+    d = csr_desc(None, A_row_offsets, None, A_col_indices, m, n)
+    _maybe_validate(A_row_offsets, A_col_indices, m, n)
+    dev = A_row_offsets.device
+    nnz = d.nnz
+    oit = torch.int16 if m <= 32767 else torch.int32
+    src = torch.empty(nnz, dtype=torch.int32, device=dev)
+    out_ro = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    out_ci = torch.empty(nnz, dtype=oit, device=dev)
+    b = ctypes.c_size_t()
+    _check("spops_csr_transpose_permutation_workspace_size",
+           lib().spops_csr_transpose_permutation_workspace_size(m, n, nnz, ctypes.byref(b)))
+    ws = _workspace(b.value, dev)
+    _check("spops_csr_transpose_permutation", lib().spops_csr_transpose_permutation(
+        ctypes.byref(d), _ptr(src), out_ro.data_ptr(), _ptr(out_ci), _IT[oit], _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(A_row_offsets)))
+    return src, out_ro, out_ci
+
+
+def permute_values(values: torch.Tensor, src: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[j] = values[src[j]] (bit for bit); e.g. A^T's values from A's with
+    src from csr_transpose_permutation."""
+    _require(values, "values", (torch.float32, torch.float16, torch.bfloat16))
+    _require(src, "src", (torch.int32,))
+    if out is None:
+        out = torch.empty(src.numel(), dtype=values.dtype, device=values.device)
+    else:
+        _require(out, "out", (values.dtype,))
+        if out.numel() != src.numel():
+            raise ValueError("out has the wrong size")
+    _check("spops_permute_values", lib().spops_permute_values(
+        _ptr(values), values.numel(), _DT[values.dtype], _ptr(src), src.numel(), _ptr(out),
+        _stream(values)))
+    return out
 
 
 def sort_rows_workspace(m: int, n: int, device) -> torch.Tensor:
