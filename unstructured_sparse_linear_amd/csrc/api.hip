@@ -222,7 +222,7 @@ spops_status spops_spmm(const spops_csr* A, const void* B, spops_dtype b_type, i
 // --------------------------------------------------------------- SDDMM ---
 
 static void free_sddmm_plan_mem(SddmmPlanDev* p) {
-  if (p->mem) hipFree(p->mem);
+  if (p->mem) (void)hipFree(p->mem);  // teardown: nothing to report
   *p = SddmmPlanDev{};
 }
 
@@ -245,8 +245,8 @@ spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hi
     e = enqueue_sddmm_plan(m, n, nnz, mask->row_offsets, mask->col_idx,
                            mask->col_type == SPOPS_I32, tau, mem, scratch, &p->dev, s);
   if (e == hipSuccess) e = fetch_sddmm_plan_counts(&p->dev, s);  // synchronizes s
-  else if (scratch) hipStreamSynchronize(s);
-  if (scratch) hipFree(scratch);
+  else if (scratch) (void)hipStreamSynchronize(s);  // e already holds the failure
+  if (scratch) (void)hipFree(scratch);
   p->dev.mem = mem;
   if (e != hipSuccess) {
     free_sddmm_plan_mem(&p->dev);

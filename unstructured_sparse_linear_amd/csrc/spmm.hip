@@ -236,7 +236,6 @@ template <int BYTES>
 struct BufLoad;
 template <>
 struct BufLoad<4> {
-  static constexpr int words = 1;
   __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
                               uint32_t* w) {
     w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
@@ -244,7 +243,6 @@ struct BufLoad<4> {
 };
 template <>
 struct BufLoad<8> {
-  static constexpr int words = 2;
   __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
                               uint32_t* w) {
     auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
@@ -254,7 +252,6 @@ struct BufLoad<8> {
 };
 template <>
 struct BufLoad<16> {
-  static constexpr int words = 4;
   __device__ static void load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
                               uint32_t* w) {
     auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
@@ -1080,13 +1077,13 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
     }
     e = hipStreamSynchronize(s);
   } while (0);
-  hipFree(tmp);
+  (void)hipFree(tmp);  // e already reports the schedule's outcome
   if (e != hipSuccess) free_spmm_schedule(out);
   return e;
 }
 
 void free_spmm_schedule(SpmmSchedule* sch) {
-  if (sch->mem) hipFree(sch->mem);
+  if (sch->mem) (void)hipFree(sch->mem);  // teardown: nothing to report
   *sch = SpmmSchedule{};
 }
 
