@@ -262,6 +262,42 @@ def test_spmm_long_rows(dt, N, use_plan):
         assert info["max_row_nnz"] == 4500 and info["split_rows"] == 6
 
 
+@pytest.mark.parametrize("dt,N", [("f32", 8), ("f32", 64), ("bf16", 256), ("f16", 520),
+                                  ("f16", 30), ("f32", 1), ("bf16", 1)])
+@pytest.mark.parametrize("mid", [100, 600])
+def test_spmm_split_length_of_skewed_rows(dt, N, mid):
+    # skewed lengths with few (100 of 4000) rows of 56..139 entries: the plan
+    # gives a workgroup to every row of more than 64 entries; launches with
+    # narrow row groups (4 or 16 lanes) use them, wide ones (32 or 64 lanes,
+    # the scalar path, N = 1) take rows up to 128 whole and their chunk
+    # workgroups for rows of 65..128 entries must write nothing.  With many
+    # such rows (600) the plan splits from 129 entries on only.
+    rng = np.random.default_rng(N + mid)
+    lengths = [3000, 1500] + list(rng.integers(56, 140, mid))
+    A = heavy_csr(N + 1, 4000, 4000, lengths, dt)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, A.n)
+    rl = np.diff(A.row_offsets)
+    n_mid = int(np.sum((rl > 64) & (rl <= 128)))
+    split = 64 if n_mid * 32 <= A.m else 128
+    assert split == (64 if mid == 100 else 128)
+    info = p.info()
+    assert info["split_rows"] == 2
+    assert info["chunks"] == int(np.sum(rl > split)) + 5 + 2
+    Ai = A.with_values(gen.f32_to_storage(
+        rng.integers(-3, 4, A.nnz).astype(np.float32), dt), dt)
+    Bi = gen.dense(N, 100, gen.S_B, (A.n, N), dt, integer_values=True)
+    ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, Ai.values, dt, Bi, dt)
+    for out_dtype in (torch.float32, TORCH_DT[dt]):
+        C = torch.full((A.m, N), float("nan"), dtype=out_dtype, device="cuda")
+        S.spmm(dev(Ai.values, dt), ro, ri, ci, dev(Bi, dt), A.m, out_dtype=out_dtype, plan=p,
+               out=C)
+        # integer sums are exact in fp32; a 16-bit output is that sum rounded once
+        want = torch.from_numpy(ref).to(out_dtype).double().numpy()
+        assert np.array_equal(host_f64(C), want)
+
+
 @pytest.mark.parametrize("dt,N,n,col32", [("bf16", 256, 3000, False), ("f16", 520, 2500, False),
                                            ("f32", 96, 2000, False), ("bf16", 64, 40000, True)])
 @pytest.mark.parametrize("kind", ["sorted", "random"])

@@ -54,9 +54,14 @@ hipError_t radix_sort_u32_iota_ptrs(const uint32_t* keys, int64_t n, int bits, v
                                     hipStream_t s);
 
 // ------------------------------------------------------------------ SpMM --
-// Rows with more entries than kSpmmSplitLen are cut by the plan into chunks of
-// kSpmmChunkLen entries, one workgroup per chunk.
+// Rows with more entries than the plan's split length are cut into chunks of
+// kSpmmChunkLen entries, one workgroup per chunk: kSpmmSplitLenSkewed when the
+// row lengths are skewed and at most 1/32 of the rows have more entries than
+// that and at most kSpmmSplitLen, else kSpmmSplitLen.  A call whose row
+// groups span 32 or more lanes takes rows up to kSpmmSplitLen whole anyway
+// (their chunk workgroups return at once).
 constexpr int32_t kSpmmSplitLen = 128;
+constexpr int32_t kSpmmSplitLenSkewed = 64;
 constexpr int32_t kSpmmChunkLen = 512;
 
 struct SpmmArgs {
@@ -76,7 +81,7 @@ struct SpmmArgs {
   // row-splitting schedule (P == 0: none)
   int64_t P;            // number of chunk items of split rows
   int64_t S;            // number of split rows
-  int32_t T;            // chunk length; rows longer than T are split
+  int32_t T;            // split length: rows longer than T go to the chunk workgroups
   const int32_t* item_pos;    // [P] position in row_idx of the chunk's row
   const int32_t* item_chunk;  // [P] chunk number within its row
   const int32_t* split_pos;   // [S] position in row_idx of each multi-chunk row

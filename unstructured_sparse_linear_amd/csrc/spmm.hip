@@ -18,10 +18,14 @@
 // instead, each XCD taking one contiguous range of rows, which keeps the B
 // rows of banded matrices in L2; results are identical either way.
 //
-// Long rows.  The plan (build_spmm_schedule) lists the rows longer than
-// kSpmmSplitLen in row_idx order and cuts each into chunks of kSpmmChunkLen
+// Long rows.  The plan (build_spmm_schedule) lists the rows longer than its
+// split length (kSpmmSplitLen, or kSpmmSplitLenSkewed when the lengths are
+// not balanced and at most 1/32 of the rows fall between the two) in row_idx
+// order and cuts each into chunks of kSpmmChunkLen
 // entries; each chunk is one workgroup whose waves take contiguous slices and
-// are summed through LDS in wave order.  A row with several chunks writes fp32
+// are summed through LDS in wave order.  A launch with wide row groups raises
+// the split length back to kSpmmSplitLen: its chunk workgroups for shorter
+// rows return at once and the row path takes those rows.  A row with several chunks writes fp32
 // partial rows that spmm_fixup_kernel adds in chunk order.  Every sum has a
 // fixed order, so results are bitwise reproducible.
 #include <stdlib.h>
@@ -474,6 +478,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
     const int64_t r = load_row(a.row_idx, a.ri_i32, i);
     int64_t rs = 0, re = 0;
     if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, rs, re);
+    // a row within this launch's split length is the row path's (uniform
+    // over the workgroup: one item per workgroup)
+    if (re - rs <= a.T) return;
     const int64_t c0 = rs + ch * kChunkLen;
     const int64_t c1 = (c0 + kChunkLen < re) ? c0 + kChunkLen : re;
     const int64_t len = c1 > c0 ? c1 - c0 : 0;
@@ -542,6 +549,7 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
     const int64_t r = load_row(a.row_idx, a.ri_i32, i);
     int64_t rs = 0, re = 0;
     if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, rs, re);
+    if (re - rs <= a.T) return;  // the row path's (uniform over the workgroup)
     const int64_t c0 = rs + ch * kChunkLen;
     const int64_t c1 = (c0 + kChunkLen < re) ? c0 + kChunkLen : re;
     float s = 0.f;
@@ -824,9 +832,19 @@ __global__ __launch_bounds__(kBlock) void spmm_fixup_kernel(SpmmArgs a) {
 
 int64_t pad8(int64_t x) { return (x + 7) & ~(int64_t)7; }
 
+// Row groups of 32 or more lanes take rows up to kSpmmSplitLen whole (a
+// wide group gains little from splitting shorter rows); narrower groups use
+// the plan's split length.
+inline SpmmArgs with_split_len(const SpmmArgs& a, bool wide) {
+  SpmmArgs b = a;
+  if (wide && b.T < kSpmmSplitLen) b.T = kSpmmSplitLen;
+  return b;
+}
+
 template <typename VT, typename OT, typename IT, int LPR>
-hipError_t launch_rows(const SpmmArgs& a, bool aligned, hipStream_t s) {
+hipError_t launch_rows(const SpmmArgs& a0, bool aligned, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
+  const SpmmArgs a = with_split_len(a0, LPR >= 32 || !aligned);
   if (aligned) {
     constexpr int GPB = kBlock / LPR;
     const int64_t nbw = a.natural ? pad8(cdiv(a.m, GPB)) : cdiv(a.m, GPB);
@@ -899,13 +917,14 @@ hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
     const int64_t nbw = a.natural ? pad8(cdiv(a.m, gpb)) : cdiv(a.m, gpb);
     const dim3 grid((unsigned)(a.P + nbw));
     if (grid.x == 0) return hipSuccess;
+    const SpmmArgs b = with_split_len(a, true);
     switch (lpr) {
-      case 2: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 2>), grid, dim3(kBlock), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 4>), grid, dim3(kBlock), 0, s, a); break;
-      case 8: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 8>), grid, dim3(kBlock), 0, s, a); break;
-      case 16: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 16>), grid, dim3(kBlock), 0, s, a); break;
-      case 32: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 32>), grid, dim3(kBlock), 0, s, a); break;
-      default: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 64>), grid, dim3(kBlock), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 2>), grid, dim3(kBlock), 0, s, b); break;
+      case 4: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 4>), grid, dim3(kBlock), 0, s, b); break;
+      case 8: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 8>), grid, dim3(kBlock), 0, s, b); break;
+      case 16: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 16>), grid, dim3(kBlock), 0, s, b); break;
+      case 32: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 32>), grid, dim3(kBlock), 0, s, b); break;
+      default: hipLaunchKernelGGL((spmv_kernel<VT, OT, IT, 64>), grid, dim3(kBlock), 0, s, b); break;
     }
     e = hipGetLastError();
   } else {
@@ -1041,21 +1060,41 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
   void* sws = tmp + 4 * nb + 256;
   int32_t host_misc[3] = {0, 0, 0};
   const unsigned g = (unsigned)cdiv(m, 256);
-  do {
-    if ((e = hipMemcpyAsync(dev_misc, host_misc, 12, hipMemcpyHostToDevice, s)) != hipSuccess) break;
+  // chunk counts, their offsets and the split rows' ranks for split length t
+  auto count = [&](int32_t t) -> hipError_t {
+    host_misc[0] = host_misc[1] = host_misc[2] = 0;
+    hipError_t r = hipMemcpyAsync(dev_misc, host_misc, 12, hipMemcpyHostToDevice, s);
+    if (r != hipSuccess) return r;
     hipLaunchKernelGGL(sched_count_kernel, dim3(g), dim3(256), 0, s, ro, row_idx, ri_i32, m, nnz,
-                       T, nch, multi, dev_misc);
-    if ((e = hipGetLastError()) != hipSuccess) break;
-    if ((e = exclusive_scan_u32(nch, off, m, (uint32_t*)dev_misc + 1, sws, s)) != hipSuccess) break;
-    if ((e = exclusive_scan_u32(multi, mrank, m, (uint32_t*)dev_misc + 2, sws, s)) != hipSuccess)
-      break;
-    if ((e = hipMemcpyAsync(host_misc, dev_misc, 12, hipMemcpyDeviceToHost, s)) != hipSuccess) break;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
+                       t, nch, multi, dev_misc);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    if ((r = exclusive_scan_u32(nch, off, m, (uint32_t*)dev_misc + 1, sws, s)) != hipSuccess)
+      return r;
+    if ((r = exclusive_scan_u32(multi, mrank, m, (uint32_t*)dev_misc + 2, sws, s)) != hipSuccess)
+      return r;
+    if ((r = hipMemcpyAsync(host_misc, dev_misc, 12, hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return r;
+    return hipStreamSynchronize(s);
+  };
+  do {
+    if ((e = count(T)) != hipSuccess) break;
     out->max_row = host_misc[0];
-    out->P = host_misc[1];
-    out->S = host_misc[2];
     // balanced lengths: keep index order for locality
     out->natural = (out->max_row <= 2 * (nnz / m) + 32) ? 1 : 0;
+    // skewed lengths: rows from the shorter split length on get their own
+    // workgroups too, for the narrow row groups that can use them, when the
+    // rows this adds (one chunk each) are rare stragglers among short rows;
+    // where they are common, a workgroup each costs more than it saves
+    if (!out->natural && T > kSpmmSplitLenSkewed) {
+      const int64_t p_long = host_misc[1];
+      if ((e = count(kSpmmSplitLenSkewed)) != hipSuccess) break;
+      if ((host_misc[1] - p_long) * 32 <= m)
+        out->T = T = kSpmmSplitLenSkewed;
+      else if ((e = count(T)) != hipSuccess)
+        break;
+    }
+    out->P = host_misc[1];
+    out->S = host_misc[2];
     if (out->P > 0) {
       const size_t pb = align256((size_t)out->P * 4), sb = align256((size_t)(out->S + 1) * 4);
       char* mem = nullptr;
