@@ -421,6 +421,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
   auto remainder = [&](const SddmmPlanDev& P, int pieces, float* part) {
     r.pos = P.ent_pos;
     r.rows = P.ent_rc;
+    r.cols = P.ent_col;
     if (P.host_ok) {
       if (P.h.rest == 0) return hipSuccess;
       if (pieces > 1) {

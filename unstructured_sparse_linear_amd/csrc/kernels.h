@@ -175,6 +175,7 @@ struct SddmmPlanDev {
   int32_t* key_start = nullptr;    // [rest_key + nb_max + 1] first sorted entry per key
   int32_t* ent_pos = nullptr;      // [nnz] mask position of each sorted entry
   int32_t* ent_rc = nullptr;       // [nnz] (tile row << 16) | tile column; remainder: row
+  int32_t* ent_col = nullptr;      // [nnz] mask column of each sorted entry (as stored)
   // host copy of the counts (plans made by spops_sddmm_plan_create)
   bool host_ok = false;
   SddmmPlanScalars h{};
@@ -221,6 +222,9 @@ struct SddmmListArgs {
   const int32_t* ro;
   const int32_t* pos;
   const int32_t* rows;
+  // column of each list entry as stored in the mask (nullable: col[pos] is
+  // loaded instead, one load later)
+  const int32_t* cols;
   const void* col;
   int col_i32;
   const void* A;

@@ -248,8 +248,8 @@ __global__ __launch_bounds__(kWave) void sddmm_list_kernel(SddmmListArgs a) {
     my_p = a.pos[wb + lane];
   }
   // raw column (validated where it is used, so the first A load below need
-  // not wait for it)
-  if (lane < nw) my_c = (int)col[my_p];
+  // not wait for it); a list with its own columns saves the dependent load
+  if (lane < nw) my_c = (!a.ro && a.cols) ? a.cols[wb + lane] : (int)col[my_p];
   // from here on my_p is the output index: the mask position, or with a K
   // split the entry's index in the range (into this piece's partial sums)
   if (split) my_p = (int)(wb + lane - bs);

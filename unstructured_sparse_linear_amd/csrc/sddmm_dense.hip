@@ -500,20 +500,30 @@ __global__ void merge_buckets_kernel(uint32_t* key, int64_t nnz, uint32_t rest_k
   if (merge && p < nnz && key[p] > rest_key) key[p] = rest_key;
 }
 
-// key_start[k] = first sorted entry with key >= k for k in [0, nkeys], and
-// the gathered positions and in-tile coordinates / rows.
+// Thread t < nkeys + 1: key_start[t] = first sorted entry with key >= t (a
+// binary search over the sorted keys).  Thread t < nnz: the gathered
+// position, in-tile coordinates / row and column of sorted entry t.
+template <typename IT>
 __global__ void key_bounds_kernel(const uint32_t* skey, const uint32_t* src, const uint32_t* rc,
-                                  int64_t nnz, int64_t nkeys, int32_t* key_start,
-                                  int32_t* ent_pos, int32_t* ent_rc) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q > nnz) return;
-  const int64_t kprev = q == 0 ? -1 : (int64_t)skey[q - 1];
-  const int64_t kcur = q == nnz ? nkeys : (int64_t)skey[q];
-  for (int64_t k = kprev + 1; k <= kcur; ++k) key_start[k] = (int32_t)q;
-  if (q == nnz) return;
-  const uint32_t p = src[q];
-  ent_pos[q] = (int32_t)p;
-  ent_rc[q] = (int32_t)rc[p];
+                                  const IT* col, int64_t nnz, int64_t nkeys,
+                                  int32_t* key_start, int32_t* ent_pos, int32_t* ent_rc,
+                                  int32_t* ent_col) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t <= nkeys) {
+    int64_t lo = 0, hi = nnz;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if ((int64_t)skey[mid] < t) lo = mid + 1;
+      else hi = mid;
+    }
+    key_start[t] = (int32_t)lo;
+  }
+  if (t < nnz) {
+    const uint32_t p = src[t];
+    ent_pos[t] = (int32_t)p;
+    ent_rc[t] = (int32_t)rc[p];
+    ent_col[t] = (int32_t)col[p];
+  }
 }
 
 __global__ void plan_finish_kernel(const int32_t* key_start, int64_t nnz,
@@ -543,7 +553,7 @@ int planned_buckets(int64_t n, int* forced) {
 }
 
 struct PlanLayout {
-  size_t sc, rows, hot_cols, key_start, ent_pos, ent_rc, total;
+  size_t sc, rows, hot_cols, key_start, ent_pos, ent_rc, ent_col, total;
 };
 PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
   PlanLayout L{};
@@ -560,6 +570,8 @@ PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
   L.ent_pos = o;
   o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
   L.ent_rc = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.ent_col = o;
   o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
   L.total = o;
   return L;
@@ -656,6 +668,7 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
   out->key_start = (int32_t*)(pm + P.key_start);
   out->ent_pos = (int32_t*)(pm + P.ent_pos);
   out->ent_rc = (int32_t*)(pm + P.ent_rc);
+  out->ent_col = (int32_t*)(pm + P.ent_col);
   uint32_t* hot = (uint32_t*)(ws + W.hot);
   uint32_t* rrank = (uint32_t*)(ws + W.rrank);
   uint32_t* ccnt = (uint32_t*)(ws + W.ccnt);
@@ -718,8 +731,15 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
                                       &skey, &src, s)) != hipSuccess)
       return e;
   }
-  hipLaunchKernelGGL(key_bounds_kernel, dim3((unsigned)cdiv(nnz + 1, 256)), dim3(256), 0, s,
-                     skey, src, rc, nnz, nkeys, out->key_start, out->ent_pos, out->ent_rc);
+  const unsigned gkb = (unsigned)cdiv((nnz > nkeys ? nnz : nkeys) + 1, 256);
+  if (col_i32)
+    hipLaunchKernelGGL(key_bounds_kernel<int32_t>, dim3(gkb), dim3(256), 0, s, skey, src, rc,
+                       (const int32_t*)col, nnz, nkeys, out->key_start, out->ent_pos,
+                       out->ent_rc, out->ent_col);
+  else
+    hipLaunchKernelGGL(key_bounds_kernel<int16_t>, dim3(gkb), dim3(256), 0, s, skey, src, rc,
+                       (const int16_t*)col, nnz, nkeys, out->key_start, out->ent_pos,
+                       out->ent_rc, out->ent_col);
   hipLaunchKernelGGL(plan_finish_kernel, dim3(1), dim3(64), 0, s, out->key_start, nnz, sc);
   return hipGetLastError();
 }
