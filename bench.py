@@ -205,12 +205,12 @@ def op_kernels(spmm_info, sddmm_info, m, n, nnz, K=0, esz=2):
     The structure-aware SDDMM adds its remainder's K pieces with a third
     kernel when BT (n x K, 16-bit) exceeds 32 MiB."""
     spmm = ["spmm_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else [])
-    # N == 1: row blocks through LDS when the plan finds the rows balanced
-    # (longest row <= 2 * mean + 32) and short (<= 128 entries), else a group
-    # of lanes per row
+    # N == 1: entry-range blocks through LDS when the plan finds the rows
+    # balanced (longest row <= 2 * mean + 32) and short (<= 128 entries),
+    # else a group of lanes per row
     mr = spmm_info.get("max_row_nnz", 0)
     balanced = m > 0 and 0 < mr <= min(128, 2 * (nnz // m) + 32)
-    spmv = (["spmv_stream_kernel"] if balanced and not spmm_info.get("chunks", 0)
+    spmv = (["spmv_flat_kernel"] if balanced and not spmm_info.get("chunks", 0)
             else ["spmv_kernel"] + (["spmm_fixup_kernel"] if spmm_info.get("chunks", 0) else []))
     pieces = (sddmm_info.get("tiles", 0) and sddmm_info.get("rest_nnz", 0) and esz == 2
               and n * K * 2 > (32 << 20))

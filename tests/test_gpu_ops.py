@@ -416,13 +416,17 @@ def test_spmm_deterministic_and_stream_ordered():
 @pytest.mark.parametrize("dt,m,n,density,kw", [
     ("f32", 5000, 6000, 0.004, {"col_index_dtype": np.int32}),
     ("f16", 3001, 2000, 0.01, {"empty_row_frac": 0.2}),
-    ("bf16", 700, 900, 0.1, {}),             # ~90 per row: 71 rows per block
+    ("bf16", 700, 900, 0.1, {}),             # ~90 per row
     ("f32", 257, 300, 0.05, {"shuffle_within_rows": True}),
+    ("f32", 60000, 400, 0.0005, {}),         # ~5000 mostly empty rows per block
+    ("f16", 3, 4, 0.2, {}),                  # two entries: no whole group of four
+    ("bf16", 5, 8, 0.1, {}),                 # eight entries, empty rows inside
 ])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_spmv_row_blocks(dt, m, n, density, kw, offset):
-    # balanced rows with N == 1 run as row blocks streamed through LDS; an
-    # offset of one element makes col/val unaligned for the 4-entry loads
+    # balanced rows with N == 1 run as entry-range blocks staged through LDS,
+    # each writing the rows that start in its range; an offset of one element
+    # makes col/val unaligned for the 4-entry loads
     A = gen.random_csr(20 + m, m, n, density, dt, **kw)
     x = gen.dense(20 + m, 100, gen.S_B, (n, 1), dt)
     v, ro, ci = csr_dev(A)
@@ -435,6 +439,36 @@ def test_spmv_row_blocks(dt, m, n, density, kw, offset):
     y = S.spmm(v, ro, ri, ci, dev(x, dt), m, plan=p)
     ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt)
     assert_close(host_f64(y), ref, dt, "spmv row blocks")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_spmv_strided_x_and_y_through_the_abi(dt):
+    # N == 1 with leading dimensions above one (x in column 1 of a k x 3
+    # array, y in column 0 of an m x 2 array): the entry-range blocks read x
+    # with its stride and leave the other columns alone
+    import ctypes
+    m, n = 3001, 2000
+    A = gen.random_csr(41, m, n, 0.01, dt)
+    x = gen.dense(41, 100, gen.S_B, (n, 1), dt)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    assert 0 < p.info()["max_row_nnz"] <= 128 and p.info()["split_rows"] == 0
+    X = torch.zeros((n, 3), dtype=TORCH_DT[dt], device="cuda")
+    X[:, 1] = dev(x, dt)[:, 0]
+    Y = torch.full((m, 2), 7.0, dtype=torch.float32, device="cuda")
+    d = S.spops.csr_desc(v, ro, ri, ci, m, n)
+    ws = p.workspace(1, torch.device("cuda"))
+    rc = S.lib().spops_spmm(ctypes.byref(d), ctypes.c_void_p(X.data_ptr() + X.element_size()),
+                            S.spops._DT[X.dtype], 1, 3, ctypes.c_void_p(Y.data_ptr()),
+                            S.spops._DT[torch.float32], 2, p.handle, S.spops._ptr(ws),
+                            ws.numel() if ws is not None else 0,
+                            torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt)
+    assert_close(host_f64(Y[:, :1]), ref, dt, "spmv strided")
+    assert torch.all(Y[:, 1] == 7.0)
 
 
 @pytest.mark.parametrize("dt,m,n,density", [("f32", 300, 5000, 0.1), ("f16", 129, 8192, 0.5),
@@ -466,8 +500,8 @@ def test_spmv_balanced_long_rows(dt, m, n, density, offset):
 
 def test_spmv_row_blocks_offsets_changed_after_planning():
     # a plan made for short rows, then one row rewritten to hold every entry:
-    # the blocks find their range too large for LDS and fall back to a wave
-    # per row, still inside the buffers and still the product
+    # the blocks find their rows ending past the entries they loaded and fall
+    # back to a wave per row, still inside the buffers and still the product
     m, n = 2000, 3000
     A = gen.random_csr(31, m, n, 0.005, "f32")
     x = gen.dense(31, 100, gen.S_B, (n, 1), "f32")

@@ -94,6 +94,12 @@ SpmmArgs spmm_args(const spops_csr* A, const void* B, spops_dtype b_type, int64_
     a.natural = plan->sch.natural;
     a.max_row = plan->sch.max_row;
   }
+  if (plan && plan->sch.flat.U > 0 && plan->sch.blk_row) {
+    a.blk_row = plan->sch.blk_row;
+    a.flat_E = plan->sch.flat.E;
+    a.flat_T = plan->sch.flat.T;
+    a.flat_U = plan->sch.flat.U;
+  }
   if (plan && plan->sch.P > 0) {
     a.P = plan->sch.P;
     a.S = plan->sch.S;
@@ -693,10 +699,11 @@ static spops_status check_cg(const spops_csr* A, const spops_spmm_plan* plan) {
   return SPOPS_OK;
 }
 
-// Row-block plan of the fused iteration (ok == false: the library's SpMV).
-static SpmvBlocks cg_blocks(const spops_csr* A, const spops_spmm_plan* plan) {
-  if (!plan) return SpmvBlocks{};
-  return spmv_row_blocks(A->rows, A->nnz, plan->sch.max_row, plan->sch.natural, plan->sch.P);
+// Entry-range blocks of the fused iteration (0 workgroups: the library's
+// SpMV between the direction and update kernels).
+static int64_t cg_fused_blocks(const spops_csr* A, const spops_spmm_plan* plan) {
+  if (!plan || plan->sch.flat.U <= 0 || !plan->sch.blk_row) return 0;
+  return cg_fused_grid(A->nnz, plan->sch.flat.E);
 }
 
 spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* plan,
@@ -706,8 +713,7 @@ spops_status spops_cg_workspace_size(const spops_csr* A, const spops_spmm_plan* 
   if (st != SPOPS_OK) return st;
   size_t sp = 0;
   spops_spmm_workspace_size(plan, 1, &sp);
-  const SpmvBlocks sb = cg_blocks(A, plan);
-  *bytes = cg_workspace_bytes(A->rows, sb.ok ? sb.grid : 0, sp);
+  *bytes = cg_workspace_bytes(A->rows, cg_fused_blocks(A, plan), sp);
   return SPOPS_OK;
 }
 
@@ -728,8 +734,8 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
   spops_cg_workspace_size(A, plan, &need);
   if (!workspace || workspace_bytes < need) return SPOPS_ERR_WORKSPACE;
   hipStream_t s = as_stream(hip_stream);
-  const SpmvBlocks sb = cg_blocks(A, plan);
-  const CgBuffers w = carve_cg_workspace(workspace, m, sb.ok ? sb.grid : 0);
+  const int64_t fused = cg_fused_blocks(A, plan);
+  const CgBuffers w = carve_cg_workspace(workspace, m, fused);
   // q = A x0, then r = b - q
   const SpmmArgs ax = spmm_args(A, x, SPOPS_F32, 1, 1, w.q, SPOPS_F32, 1, plan, w.spmm_ws);
   hipError_t e = launch_spmm(ax, s);
@@ -742,6 +748,12 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
   fa.col = A->col_idx;
   fa.col_i32 = A->col_type == SPOPS_I32;
   fa.val = (const float*)A->values;
+  if (fused > 0) {
+    fa.blk_row = plan->sch.blk_row;
+    fa.E = plan->sch.flat.E;
+    fa.T = plan->sch.flat.T;
+    fa.U = plan->sch.flat.U;
+  }
   CgState h{};
   int64_t k = 0;
   for (;;) {
@@ -756,9 +768,9 @@ spops_status spops_cg(const spops_csr* A, const void* b, void* x, double rtol, i
     }
     const int64_t n = std::min<int64_t>(check_every, max_iter - k);
     for (int64_t j = 0; j < n; ++j, ++k) {
-      if (sb.ok) {
+      if (fused > 0) {
         fa.k = k;
-        e = launch_cg_fused(fa, sb, (float*)x, w, s);
+        e = launch_cg_fused(fa, (float*)x, w, s);
       } else {
         // p sits in the x slots of the (p, r) pairs: leading dimension 2
         const SpmmArgs ap = spmm_args(A, w.pr[(k + 1) & 1], SPOPS_F32, 1, 2, w.q, SPOPS_F32, 1,

@@ -14,8 +14,8 @@
 //            (0 for k = 0)
 //   product: p = r + beta p_prev and q = A p, with the partials of p.q
 //   update:  alpha = r.r / p.q, x += alpha p, r -= alpha q, partials of r.r
-// so that the whole iteration is two launches when the SpMV can run as row
-// blocks (balanced rows, see spmv_row_blocks): the direction is formed on the
+// so that the whole iteration is two launches when the SpMV can run as
+// entry-range blocks (balanced rows with a plan): the direction is formed on the
 // fly where the SpMV gathers it (every workgroup computes beta itself from
 // the same partials) and each workgroup writes p and q for its own rows and
 // the p.q partial of its rows.  p and r are stored interleaved, (p, r) pairs
@@ -234,41 +234,39 @@ __global__ __launch_bounds__(kBlock) void cg_update_kernel(
   if (threadIdx.x == 0) part_rr[blockIdx.x] = s;
 }
 
-// Begin + product of iteration k in one launch, as row blocks (the scheme of
-// the row-block SpMV: coalesced 4-entry loads of col/val, products in LDS,
-// one thread per row adds its products in stored order).  The gathered
-// operand is the new direction, formed from a (p_prev, r) pair where it is
-// read.  The first round of col/val loads is issued before the r.r sum, so
-// that its latency overlaps the sum.
-template <typename IT, bool QUAD>
-__global__ __launch_bounds__(kBlock) void cg_spmv_kernel(CgSpmvArgs a, int32_t R, int32_t cap) {
-  extern __shared__ __align__(16) float prod[];  // cap + 4 floats
+// Begin + product of iteration k in one launch, as the entry-range blocks of
+// the SpMV (spmv_flat_kernel): workgroup b loads the entries [b*E, (b+1)*E)
+// and the T after them in 4-entry groups, puts their products in LDS and
+// writes q, p and the p.q partial of the rows that start in its range
+// (blk_row), one thread per row adding its products in stored order.  The
+// gathered operand is the new direction, formed from a (p_prev, r) pair
+// where it is read.  The col/val loads are issued before the r.r sum, so
+// that their latency overlaps it.  Offsets that do not match the plan send
+// the block's rows to a wave per row.
+template <typename IT, int U, bool QUAD>
+__global__ __launch_bounds__(kBlock) void cg_spmv_kernel(CgSpmvArgs a) {
+  extern __shared__ __align__(16) float prod[];  // E + T + 8 floats
   __shared__ double lds[kWaves + 1];
   __shared__ int flag;
   if (stopped(a.st, &flag)) return;
   const IT* col = (const IT*)a.col;
   const float* val = a.val;
   const float2* pr = a.pr;
+  // entry positions fit in 32 bits with room for E + T past the last one
   const int m = (int)a.m, nnz = (int)a.nnz;
-  const int64_t r0 = row_block(blockIdx.x, gridDim.x, 1) * R;  // 0 for workgroup 0
+  const int E = a.E, T = a.T;
+  const int nblk = (nnz + E - 1) / E;
+  const int b = (int)row_block(blockIdx.x, gridDim.x, 1);  // 0 for workgroup 0
   const int t = threadIdx.x;
-  const bool live = r0 < m;
-  const int64_t r1 = !live ? r0 : (r0 + R < m ? r0 + R : m);
-  int base = 0, end = 0;
-  if (live) {
-    base = a.ro[r0];
-    end = a.ro[r1];
-    base = base < 0 ? 0 : (base > nnz ? nnz : base);
-    end = end < base ? base : (end > nnz ? nnz : end);
-  }
-  const int base4 = base & ~3;
-  const bool fits = end - base4 <= cap;
-  constexpr int U = kStreamQuads;
-  const int gend = QUAD ? min(nnz >> 2, (end + 3) >> 2) : 0;
-  const int gbeg = base >> 2;
+  const bool live = b < nblk;
+  const int e0 = live ? b * E : 0;
+  const int e1 = live ? min(e0 + E, nnz) : 0;
+  const int eL = live ? min(e1 + T, nnz) : 0;
+  const int gbeg = e0 >> 2;
+  const int gend = QUAD && live ? min(nnz >> 2, (eL + 3) >> 2) : gbeg;
   IT c[U][4];
   float v[U][4];
-  if (QUAD && fits && gend > gbeg) {
+  if (gend > gbeg) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gq = min(gbeg + t + u * kBlock, gend - 1);
@@ -282,18 +280,68 @@ __global__ __launch_bounds__(kBlock) void cg_spmv_kernel(CgSpmvArgs a, int32_t R
     if (t == 0) a.part_pq[blockIdx.x] = 0.0;
     return;
   }
-  float* p_next = (float*)a.pr_next;  // p of row i at p_next[2 i]
-  const int64_t r = r0 + t;
-  const int64_t rl = r < r1 ? r : r1 - 1;
+  const int rb = min(max(a.blk_row[b], 0), m);
+  const int re = min(max(a.blk_row[b + 1], rb), m);
+  const int lo = a.ro[rb], hi = a.ro[re];
+  const int r = rb + t;
+  const int rl = min(r < re ? r : rb, m - 1);
   const int o0 = a.ro[rl], o1 = a.ro[rl + 1];
+  float* p_next = (float*)a.pr_next;  // p of row i at p_next[2 i]
   double s = 0.0;
-  if (!fits) {
-    // wave per row (not reached with offsets that match the plan)
+  int p_done = e0;
+  if (gend > gbeg) {
+    p_done = max(e0, 4 * gend);
+    float xv[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ci = (int)c[u][q];
+        const bool ok = (unsigned)ci < (unsigned)m;
+        const float pv = direction(beta, pr[ok ? ci : 0]);
+        xv[u][q] = ok ? pv : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gu = gbeg + t + u * kBlock;
+      if (gu < gend) {
+        float4 pq4;
+        pq4.x = v[u][0] * xv[u][0];
+        pq4.y = v[u][1] * xv[u][1];
+        pq4.z = v[u][2] * xv[u][2];
+        pq4.w = v[u][3] * xv[u][3];
+        *reinterpret_cast<float4*>(prod + (4 * gu - e0)) = pq4;
+      }
+    }
+  }
+  for (int e = p_done + t; e < eL; e += kBlock) {
+    const int ci = (int)col[e];
+    const bool ok = (unsigned)ci < (unsigned)m;
+    const float pv = direction(beta, pr[ok ? ci : 0]);
+    prod[e - e0] = ok ? val[e] * pv : 0.f;
+  }
+  __syncthreads();
+  if (lo >= e0 && hi <= eL) {
+    for (int rr = r; rr < re; rr += kBlock) {
+      const int a0 = rr == r ? o0 : a.ro[rr];
+      const int a1 = rr == r ? o1 : a.ro[rr + 1];
+      const int q0 = a0 < e0 ? e0 : (a0 > eL ? eL : a0);
+      const int q1 = a1 < q0 ? q0 : (a1 > eL ? eL : a1);
+      float y = 0.f;
+#pragma unroll 4
+      for (int i = q0; i < q1; ++i) y += prod[i - e0];
+      const float pn = direction(beta, pr[rr]);
+      a.q[rr] = y;
+      p_next[2 * (int64_t)rr] = pn;
+      s += (double)pn * (double)y;
+    }
+  } else {
+    // offsets that do not match the plan: a wave per owned row
     const int w = t / kWave, l = lane_id();
-    for (int64_t rr = r0 + w; rr < r1; rr += kWaves) {
-      const int64_t lo = a.ro[rr], hi = a.ro[rr + 1];
-      const int64_t p0 = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
-      const int64_t p1 = hi < p0 ? p0 : (hi > nnz ? nnz : hi);
+    for (int rr = rb + w; rr < re; rr += kWaves) {
+      const int64_t lo2 = a.ro[rr], hi2 = a.ro[rr + 1];
+      const int64_t p0 = lo2 < 0 ? 0 : (lo2 > nnz ? nnz : lo2);
+      const int64_t p1 = hi2 < p0 ? p0 : (hi2 > nnz ? nnz : hi2);
       float y = 0.f;
       for (int64_t p = p0 + l; p < p1; p += kWave) {
         const int ci = (int)col[p];
@@ -303,66 +351,9 @@ __global__ __launch_bounds__(kBlock) void cg_spmv_kernel(CgSpmvArgs a, int32_t R
       if (l == 0) {
         const float pn = direction(beta, pr[rr]);
         a.q[rr] = y;
-        p_next[2 * rr] = pn;
+        p_next[2 * (int64_t)rr] = pn;
         s += (double)pn * (double)y;
       }
-    }
-  } else {
-    int p_done = base;
-    if constexpr (QUAD) {
-      if (gend > gbeg) {
-        p_done = max(base, 4 * gend);
-        for (int g = gbeg + t, round = 0; g < gend; g += kBlock * U, ++round) {
-          if (round > 0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-              const int gq = min(g + u * kBlock, gend - 1);
-              load_quad(col + 4 * gq, c[u]);
-              load_quad(val + 4 * gq, v[u]);
-            }
-          }
-          float xv[U][4];
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int ci = (int)c[u][q];
-              const bool ok = (unsigned)ci < (unsigned)m;
-              const float pv = direction(beta, pr[ok ? ci : 0]);
-              xv[u][q] = ok ? pv : 0.f;
-            }
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int gu = g + u * kBlock;
-            if (gu < gend) {
-              float4 pq4;
-              pq4.x = v[u][0] * xv[u][0];
-              pq4.y = v[u][1] * xv[u][1];
-              pq4.z = v[u][2] * xv[u][2];
-              pq4.w = v[u][3] * xv[u][3];
-              *reinterpret_cast<float4*>(prod + (4 * gu - base4)) = pq4;
-            }
-          }
-        }
-      }
-    }
-    for (int e = p_done + t; e < end; e += kBlock) {
-      const int ci = (int)col[e];
-      const bool ok = (unsigned)ci < (unsigned)m;
-      const float pv = direction(beta, pr[ok ? ci : 0]);
-      prod[e - base4] = ok ? val[e] * pv : 0.f;
-    }
-    __syncthreads();
-    if (r < r1) {
-      const int q0 = o0 < base ? base : (o0 > end ? end : o0);
-      const int q1 = o1 < q0 ? q0 : (o1 > end ? end : o1);
-      float y = 0.f;
-#pragma unroll 4
-      for (int i = q0; i < q1; ++i) y += prod[i - base4];
-      const float pn = direction(beta, pr[r]);
-      a.q[r] = y;
-      p_next[2 * r] = pn;
-      s = (double)pn * (double)y;
     }
   }
   s = block_sum(s, lds);
@@ -438,10 +429,11 @@ hipError_t launch_cg_dot_update(int64_t m, int64_t k, float* x, const CgBuffers&
   return hipGetLastError();
 }
 
-hipError_t launch_cg_fused(const CgSpmvArgs& a0, const SpmvBlocks& sb, float* x,
-                           const CgBuffers& w, hipStream_t s) {
+hipError_t launch_cg_fused(const CgSpmvArgs& a0, float* x, const CgBuffers& w, hipStream_t s) {
   CgSpmvArgs a = a0;
   const int64_t m = a.m, k = a.k;
+  if (a.U <= 0 || a.E <= 0 || a.E + a.T > a.U * 4 * kBlock || a.nnz + a.E + a.T >= INT32_MAX)
+    return hipErrorInvalidValue;
   a.pr = w.pr[k & 1];
   a.pr_next = w.pr[(k + 1) & 1];
   a.q = w.q;
@@ -451,26 +443,32 @@ hipError_t launch_cg_fused(const CgSpmvArgs& a0, const SpmvBlocks& sb, float* x,
   a.st = w.st;
   const bool quad = ((uintptr_t)a.col % (4 * (a.col_i32 ? 4 : 2)) == 0) &&
                     ((uintptr_t)a.val % 16 == 0);
-  const dim3 grid((unsigned)sb.grid);
-  if (a.col_i32) {
-    if (quad)
-      hipLaunchKernelGGL((cg_spmv_kernel<int32_t, true>), grid, dim3(kBlock), sb.lds_bytes, s, a,
-                         sb.R, sb.cap);
-    else
-      hipLaunchKernelGGL((cg_spmv_kernel<int32_t, false>), grid, dim3(kBlock), sb.lds_bytes, s,
-                         a, sb.R, sb.cap);
-  } else {
-    if (quad)
-      hipLaunchKernelGGL((cg_spmv_kernel<int16_t, true>), grid, dim3(kBlock), sb.lds_bytes, s, a,
-                         sb.R, sb.cap);
-    else
-      hipLaunchKernelGGL((cg_spmv_kernel<int16_t, false>), grid, dim3(kBlock), sb.lds_bytes, s,
-                         a, sb.R, sb.cap);
+  const int64_t grid = cg_fused_grid(a.nnz, a.E);
+  const size_t lds = (size_t)(a.E + a.T + 8) * sizeof(float);
+#define CGK(IT, U, Q) \
+  hipLaunchKernelGGL((cg_spmv_kernel<IT, U, Q>), dim3((unsigned)grid), dim3(kBlock), lds, s, a)
+#define CGU(IT, U)     \
+  if (quad)            \
+    CGK(IT, U, true);  \
+  else                 \
+    CGK(IT, U, false)
+  switch (a.U) {
+    case 1: if (a.col_i32) { CGU(int32_t, 1); } else { CGU(int16_t, 1); } break;
+    case 2: if (a.col_i32) { CGU(int32_t, 2); } else { CGU(int16_t, 2); } break;
+    case 4: if (a.col_i32) { CGU(int32_t, 4); } else { CGU(int16_t, 4); } break;
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(cg_update_kernel, dim3(cg_parts(m)), dim3(kBlock), 0, s, m, k,
-                     (int)sb.grid, (const double*)w.part_pq, x, (const float2*)a.pr, a.pr_next,
+#undef CGU
+#undef CGK
+  hipLaunchKernelGGL(cg_update_kernel, dim3(cg_parts(m)), dim3(kBlock), 0, s, m, k, (int)grid,
+                     (const double*)w.part_pq, x, (const float2*)a.pr, a.pr_next,
                      (const float*)w.q, w.part_rr, w.st);
   return hipGetLastError();
+}
+
+int64_t cg_fused_grid(int64_t nnz, int32_t E) {
+  if (E <= 0 || nnz <= 0) return 0;
+  return (cdiv(nnz, (int64_t)E) + 7) & ~(int64_t)7;
 }
 
 }  // namespace spops

@@ -88,25 +88,29 @@ struct SpmmArgs {
   const int32_t* split_start; // [S] first item of each multi-chunk row
   const int32_t* split_end;   // [S] one past its last item
   float* partial;             // [P][N]
+  // N == 1 entry-range blocks (blk_row null: none; see SpmvFlat)
+  const int32_t* blk_row;     // [nblk + 1] first row each block owns, then m
+  int32_t flat_E, flat_T, flat_U;
 };
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
 
-// N == 1 on balanced rows (the plan found the lengths balanced, no row is
-// split and the longest has at most kStreamCap / kStreamMinRows entries):
-// workgroups of kStreamBlock threads each own R consecutive rows and stream
-// their entries through `cap` floats of LDS (lds_bytes with slack); the grid
-// is padded to a multiple of 8.  ok == false: the other SpMV kernel runs.
-constexpr int kStreamBlock = 256;
-constexpr int kStreamCap = 8192;     // most products per workgroup held in LDS
-constexpr int kStreamQuads = 2;      // groups of four entries per lane per round
-constexpr int kStreamMinRows = 64;
-struct SpmvBlocks {
-  bool ok = false;
-  int32_t R = 0, cap = 0;
-  int64_t grid = 0;
-  size_t lds_bytes = 0;
+// N == 1 on balanced rows with a plan: workgroup b loads the entries
+// [b*E, (b+1)*E + T) (U groups of four per lane, E + T <= U * 1024) and
+// writes the rows that start in [b*E, (b+1)*E); blk_row[b] is the first of
+// them (the last workgroup also owns the empty rows at the end).  T is the
+// longest row rounded up to four, so those rows end inside the loaded range.
+constexpr int kFlatMaxRow = 128;     // longest row the entry-range blocks take
+constexpr int kFlatMinBlocks = 512;  // U is the largest of 4, 2, 1 giving this many blocks
+struct SpmvFlat {
+  int32_t E = 0, T = 0, U = 0;
+  int64_t blocks = 0;
 };
-SpmvBlocks spmv_row_blocks(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P);
+SpmvFlat spmv_flat_shape(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P);
+
+// Vector kernels' workgroup size, and groups of four entries per lane per
+// round of the SpMV on balanced long rows (spmv_row_kernel).
+constexpr int kStreamBlock = 256;
+constexpr int kStreamQuads = 2;
 
 // Row-splitting schedule for SpMM, built on the device.  chunk = T.
 struct SpmmSchedule {
@@ -119,6 +123,8 @@ struct SpmmSchedule {
   int32_t* split_start = nullptr;
   int32_t* split_end = nullptr;
   void* mem = nullptr;  // owning allocation
+  SpmvFlat flat;                 // entry-range SpMV blocks (flat.U == 0: none)
+  int32_t* blk_row = nullptr;    // [flat.blocks + 1], own allocation
 };
 hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i32, int64_t m,
                                int64_t nnz, int32_t T, SpmmSchedule* out, hipStream_t s);
@@ -334,9 +340,13 @@ struct CgSpmvArgs {
   const double* part_rr;
   int nparts_rr;
   CgState* st;
+  // entry-range blocks of the plan (SpmvFlat)
+  const int32_t* blk_row;
+  int32_t E, T, U;
 };
-hipError_t launch_cg_fused(const CgSpmvArgs& a, const SpmvBlocks& sb, float* x,
-                           const CgBuffers& w, hipStream_t s);
+// p.q partials of the fused iteration: one per workgroup of the grid.
+int64_t cg_fused_grid(int64_t nnz, int32_t E);
+hipError_t launch_cg_fused(const CgSpmvArgs& a, float* x, const CgBuffers& w, hipStream_t s);
 
 // ------------------------------------------------------------ masked Adam --
 struct AdamArgs {

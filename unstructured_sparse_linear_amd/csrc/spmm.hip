@@ -9,7 +9,7 @@
 //   read through buffer resources, whose range check turns padding entries
 //   into loads of zero that touch no memory.  LPR is halved while one
 //   window's share of B would overflow an XCD's L2.
-// * spmv_stream_kernel, spmv_row_kernel, spmv_kernel (N == 1).
+// * spmv_flat_kernel, spmv_row_kernel, spmv_kernel (N == 1).
 //
 // Row order.  Work visits rows in row_idx order (section "Usage": rows sorted
 // by entry count) so that neighbouring waves get rows of similar length and
@@ -610,125 +610,125 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
   if (gl == 0 && r >= 0) ((OT*)a.C)[r * a.ldc] = from_f32<OT>(s);
 }
 
-// N == 1 on balanced rows: a workgroup owns R consecutive rows and streams
-// their entries (one contiguous range of col/val) with coalesced loads, four
-// consecutive entries per lane, into LDS as products val * x[col]; then
-// thread t adds row t's products in stored order.  This is the row-block
-// streaming scheme of Greathouse and Daga ("Efficient Sparse Matrix-Vector
-// Multiplication on GPUs using the CSR Storage Format", SC 2014): every lane
-// is busy whatever the row lengths, and the only dependent load is the x
-// gather.  The host sizes R so that a block's entries take about one round of
-// loads per lane (the kernel is bound by the latency of that round, so many
-// small blocks beat few large ones) and R * (longest row) products fit in the
-// block's LDS (`cap` floats, dynamic); a block whose range is larger anyway
-// (row offsets that do not match the plan) takes a slower wave-per-row path,
-// so no input reaches past the buffers.
-
-template <typename VT, typename OT, typename IT, bool QUAD>
-__global__ __launch_bounds__(kBlock) void spmv_stream_kernel(SpmmArgs a, int32_t R,
-                                                             int32_t cap) {
-  extern __shared__ __align__(16) float prod[];  // cap + 4 floats
+// N == 1 on balanced rows: entry-range blocks.  Workgroup b takes the
+// entries [b*E, (b+1)*E) and writes the rows that start there (rows are
+// owned by their first entry; the plan lists each block's first row in
+// blk_row).  Its loads need no row offsets: it requests its entries, plus the
+// T that follow so that its last rows end inside what it loaded, as U groups
+// of four consecutive entries per lane (16-byte loads) right away, and looks
+// up its rows' offsets while they are in flight.  Products val * x[col] go to
+// LDS as 16-byte groups; then thread t adds row t's products in stored
+// order.  This is the LDS staging of Greathouse and Daga's CSR-Stream (SC
+// 2014) over an entry-balanced split of the kind Merrill and Garland use
+// (merge-based SpMV, SC 2016), with each row left whole to one block instead
+// of carried between blocks.  Row offsets that do not match the plan (a row
+// ending past the loaded range) send the block's rows to a wave-per-row path
+// that reads them from memory, so results stay the product and no access
+// leaves the buffers.
+// UNIT: x has a leading dimension of 1.
+template <typename VT, typename OT, typename IT, int U, bool QUAD, bool UNIT>
+__global__ __launch_bounds__(kBlock) void spmv_flat_kernel(SpmmArgs a) {
+  extern __shared__ __align__(16) float prod[];  // E + T + 8 floats
   const IT* col = (const IT*)a.col;
   const VT* val = (const VT*)a.val;
   const VT* x = (const VT*)a.B;
-  // entry positions fit in 32 bits (row offsets are int32)
-  const int k = (int)a.k, nnz = (int)a.nnz;
-  const int64_t ldx = a.ldb;
-  const int64_t r0 = row_block(blockIdx.x, gridDim.x, 1) * R;
-  if (r0 >= a.m) return;
-  const int64_t r1 = r0 + R < a.m ? r0 + R : a.m;
+  // entry positions and rows fit in 32 bits, with room for E + T past the
+  // last entry (the plan takes this path only when nnz + 8192 < 2^31)
+  const int k = (int)a.k, nnz = (int)a.nnz, m = (int)a.m;
+  const int64_t ldx = UNIT ? 1 : a.ldb;
+  const int E = a.flat_E, T = a.flat_T;
+  const int nblk = (nnz + E - 1) / E;
+  const int b = (int)row_block(blockIdx.x, gridDim.x, 1);
+  if (b >= nblk) return;
   const int t = threadIdx.x;
-  int base = a.ro[r0], end = a.ro[r1];
-  base = base < 0 ? 0 : (base > nnz ? nnz : base);
-  end = end < base ? base : (end > nnz ? nnz : end);
-  // this thread's row (a clamped row for the idle threads, so the loads need
-  // no branch); the offsets are used only after the products are in LDS
-  const int64_t r = r0 + t;
-  const int64_t rl = r < r1 ? r : r1 - 1;
-  const int o0 = a.ro[rl], o1 = a.ro[rl + 1];
-  // products sit at prod[p - base4]; base4 = base rounded down to a multiple
-  // of four, so each group of four lands on one 16-byte LDS slot
-  const int base4 = base & ~3;
-  if (end - base4 > cap) {
-    // wave per row (not reached with offsets that match the plan)
-    const int w = t / kWave, l = lane_id();
-    for (int64_t rr = r0 + w; rr < r1; rr += kBlock / kWave) {
-      int64_t p0, p1;
-      row_range(a.ro, rr, nnz, p0, p1);
-      float s = 0.f;
-      for (int64_t p = p0 + l; p < p1; p += kWave) {
-        const int c = (int)col[p];
-        if ((unsigned)c < (unsigned)k) s = __builtin_fmaf(to_f32(val[p]), to_f32(x[c * ldx]), s);
-      }
-      s = group_sum<kWave>(s);
-      if (l == 0) ((OT*)a.C)[rr * a.ldc] = from_f32<OT>(s);
+  const int e0 = b * E;  // a multiple of four
+  const int e1 = min(e0 + E, nnz);
+  const int eL = min(e1 + T, nnz);
+  // the entries first: groups of four [4g, 4g+4) inside the arrays, clamped
+  // (the last group may stick out of [e0, eL); the slots past eL are
+  // written but never read)
+  const int gbeg = e0 >> 2;
+  const int gend = QUAD ? min(nnz >> 2, (eL + 3) >> 2) : gbeg;
+  IT c[U][4];
+  VT v[U][4];
+  if (gend > gbeg) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gq = min(gbeg + t + u * kBlock, gend - 1);
+      load_quad(col + 4 * gq, c[u]);
+      load_quad(val + 4 * gq, v[u]);
     }
-    return;
   }
-  // Loads are unconditional at clamped, in-bounds addresses and masked
-  // afterwards, so that all of a lane's loads are in flight together.  x[0]
-  // stands in for an invalid column when x has a row at all.
-  const bool has_x = k > 0;
-  int p_done = base;  // entries below this one are handled by the main loop
-  if constexpr (QUAD) {
-    // groups of four entries [4g, 4g+4) that lie inside the arrays; the first
-    // and last groups may stick out of [base, end)
-    constexpr int U = kStreamQuads;
-    const int gend = min(nnz >> 2, (end + 3) >> 2);
-    const int gbeg = base >> 2;
-    if (gend > gbeg) {
-      p_done = max(base, 4 * gend);
-      for (int g = gbeg + t; g < gend; g += kBlock * U) {
-        IT c[U][4];
-        VT v[U][4];
+  // the owned rows [rb, re) and their offsets, while the entries arrive
+  const int rb = min(max(a.blk_row[b], 0), m);
+  const int re = min(max(a.blk_row[b + 1], rb), m);
+  const int lo = a.ro[rb], hi = a.ro[re];
+  const int r = rb + t;
+  const int rl = min(r < re ? r : rb, m - 1);
+  const int o0 = a.ro[rl], o1 = a.ro[rl + 1];
+  const bool has_x = k > 0;  // x[0] stands in for an invalid column
+  int p_done = e0;
+  if (gend > gbeg) {
+    p_done = max(e0, 4 * gend);
+    float xv[U][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int gq = min(g + u * kBlock, gend - 1);
-          load_quad(col + 4 * gq, c[u]);
-          load_quad(val + 4 * gq, v[u]);
-        }
-        float xv[U][4];
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+      for (int q = 0; q < 4; ++q) {
+        const int ci = (int)c[u][q];
+        const bool ok = (unsigned)ci < (unsigned)k;
+        const int xi = ok ? ci : 0;
+        const float xl = has_x ? to_f32(UNIT ? x[xi] : x[(int64_t)xi * ldx]) : 0.f;
+        xv[u][q] = ok ? xl : 0.f;
+      }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ci = (int)c[u][q];
-            const bool ok = (unsigned)ci < (unsigned)k;
-            const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
-            xv[u][q] = ok ? xl : 0.f;
-          }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          // slots before base or from end on are written but never read
-          const int gu = g + u * kBlock;
-          if (gu < gend) {
-            float4 pr;
-            pr.x = to_f32(v[u][0]) * xv[u][0];
-            pr.y = to_f32(v[u][1]) * xv[u][1];
-            pr.z = to_f32(v[u][2]) * xv[u][2];
-            pr.w = to_f32(v[u][3]) * xv[u][3];
-            *reinterpret_cast<float4*>(prod + (4 * gu - base4)) = pr;
-          }
-        }
+    for (int u = 0; u < U; ++u) {
+      const int gu = gbeg + t + u * kBlock;
+      if (gu < gend) {
+        float4 pr;
+        pr.x = to_f32(v[u][0]) * xv[u][0];
+        pr.y = to_f32(v[u][1]) * xv[u][1];
+        pr.z = to_f32(v[u][2]) * xv[u][2];
+        pr.w = to_f32(v[u][3]) * xv[u][3];
+        *reinterpret_cast<float4*>(prod + (4 * gu - e0)) = pr;
       }
     }
   }
   // entries one at a time: everything without the 4-entry loads, else the
   // at most three past the arrays' last whole group
-  for (int pp = p_done + t; pp < end; pp += kBlock) {
+  for (int pp = p_done + t; pp < eL; pp += kBlock) {
     const int ci = (int)col[pp];
     const bool ok = (unsigned)ci < (unsigned)k;
-    const float xl = has_x ? to_f32(x[(int64_t)(ok ? ci : 0) * ldx]) : 0.f;
-    prod[pp - base4] = ok ? to_f32(val[pp]) * xl : 0.f;
+    const int xi = ok ? ci : 0;
+    const float xl = has_x ? to_f32(UNIT ? x[xi] : x[(int64_t)xi * ldx]) : 0.f;
+    prod[pp - e0] = ok ? to_f32(val[pp]) * xl : 0.f;
   }
   __syncthreads();
-  if (r < r1) {
-    const int q0 = o0 < base ? base : (o0 > end ? end : o0);
-    const int q1 = o1 < q0 ? q0 : (o1 > end ? end : o1);
-    float s = 0.f;
+  if (lo >= e0 && hi <= eL) {
+    for (int rr = r; rr < re; rr += kBlock) {
+      const int a0 = rr == r ? o0 : a.ro[rr];
+      const int a1 = rr == r ? o1 : a.ro[rr + 1];
+      const int q0 = a0 < e0 ? e0 : (a0 > eL ? eL : a0);
+      const int q1 = a1 < q0 ? q0 : (a1 > eL ? eL : a1);
+      float s = 0.f;
 #pragma unroll 4
-    for (int pp = q0; pp < q1; ++pp) s += prod[pp - base4];
-    ((OT*)a.C)[r * a.ldc] = from_f32<OT>(s);
+      for (int pp = q0; pp < q1; ++pp) s += prod[pp - e0];
+      ((OT*)a.C)[(int64_t)rr * a.ldc] = from_f32<OT>(s);
+    }
+  } else {
+    // offsets that do not match the plan: a wave per owned row
+    const int w = t / kWave, l = lane_id();
+    for (int rr = rb + w; rr < re; rr += kBlock / kWave) {
+      int64_t p0, p1;
+      row_range(a.ro, rr, nnz, p0, p1);
+      float s = 0.f;
+      for (int64_t p = p0 + l; p < p1; p += kWave) {
+        const int ci = (int)col[p];
+        if ((unsigned)ci < (unsigned)k) s = __builtin_fmaf(to_f32(val[p]), to_f32(x[ci * ldx]), s);
+      }
+      s = group_sum<kWave>(s);
+      if (l == 0) ((OT*)a.C)[(int64_t)rr * a.ldc] = from_f32<OT>(s);
+    }
   }
 }
 
@@ -880,23 +880,35 @@ template <typename VT, typename OT, typename IT>
 hipError_t launch_typed(const SpmmArgs& a, hipStream_t s) {
   constexpr int VEC = Vec16<VT>::n;
   hipError_t e;
-  const SpmvBlocks sb = spmv_row_blocks(a.m, a.nnz, a.max_row, a.natural, a.P);
   bool whole_rows = false;  // every row written by one workgroup (no fixup)
-  if (a.N == 1 && sb.ok) {
-    // balanced rows: stream row blocks through LDS
-    const int32_t R = sb.R, cap = sb.cap;
-    const dim3 grid((unsigned)sb.grid);
-    const size_t lds = sb.lds_bytes;
+  if (a.N == 1 && a.blk_row && a.flat_U > 0 && a.flat_E > 0 && a.nnz > 0) {
+    // balanced rows with a plan: entry-range blocks
+    const int64_t nblk = cdiv(a.nnz, (int64_t)a.flat_E);
+    const dim3 grid((unsigned)pad8(nblk));
+    const size_t lds = (size_t)(a.flat_E + a.flat_T + 8) * sizeof(float);
     const bool quad = ((uintptr_t)a.col % (4 * sizeof(IT)) == 0) &&
                       ((uintptr_t)a.val % (4 * sizeof(VT)) == 0);
-    if (quad)
-      hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, true>), grid, dim3(kBlock), lds, s, a,
-                         R, cap);
-    else
-      hipLaunchKernelGGL((spmv_stream_kernel<VT, OT, IT, false>), grid, dim3(kBlock), lds, s, a,
-                         R, cap);
+    if (a.flat_E + a.flat_T > a.flat_U * 4 * kBlock ||
+        a.nnz + a.flat_E + a.flat_T >= INT32_MAX)
+      return hipErrorInvalidValue;
+#define FLAT(U, Q)                                                                              \
+  do {                                                                                          \
+    if (a.ldb == 1)                                                                             \
+      hipLaunchKernelGGL((spmv_flat_kernel<VT, OT, IT, U, Q, true>), grid, dim3(kBlock), lds, s, \
+                         a);                                                                    \
+    else                                                                                        \
+      hipLaunchKernelGGL((spmv_flat_kernel<VT, OT, IT, U, Q, false>), grid, dim3(kBlock), lds,   \
+                         s, a);                                                                 \
+  } while (0)
+    switch (a.flat_U) {
+      case 1: if (quad) FLAT(1, true); else FLAT(1, false); break;
+      case 2: if (quad) FLAT(2, true); else FLAT(2, false); break;
+      case 4: if (quad) FLAT(4, true); else FLAT(4, false); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef FLAT
     e = hipGetLastError();
-  } else if (a.N == 1 && a.natural && a.max_row > kStreamCap / kStreamMinRows) {
+  } else if (a.N == 1 && a.natural && a.max_row > kFlatMaxRow) {
     // balanced long rows: a workgroup per row (the plan's row splits are not
     // used, so there is nothing to fix up)
     whole_rows = true;
@@ -1015,22 +1027,23 @@ __global__ __launch_bounds__(256) void sched_ends_kernel(const uint32_t* nch, co
 
 }  // namespace
 
-SpmvBlocks spmv_row_blocks(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P) {
-  SpmvBlocks b;
-  if (!(m > 0 && natural && P == 0 && max_row > 0 && max_row <= kStreamCap / kStreamMinRows))
-    return b;
-  // about one round of loads per lane per block, and R * max_row products
-  // must fit the block's LDS
-  const int64_t mean = std::max<int64_t>(1, nnz / m);
-  int64_t R = (int64_t)kStreamBlock * 4 * kStreamQuads / mean;
-  R = std::max<int64_t>(1, std::min<int64_t>({R, (int64_t)kStreamBlock, kStreamCap / max_row}));
-  b.ok = true;
-  b.R = (int32_t)R;
-  // + 8: the first and last groups of four may stick out of the range
-  b.cap = (int32_t)(R * max_row) + 8;
-  b.grid = (cdiv(m, R) + 7) & ~(int64_t)7;
-  b.lds_bytes = (size_t)(b.cap + 4) * sizeof(float);
-  return b;
+SpmvFlat spmv_flat_shape(int64_t m, int64_t nnz, int64_t max_row, int natural, int64_t P) {
+  SpmvFlat f;
+  if (!(m > 0 && nnz > 0 && natural && P == 0 && max_row > 0 && max_row <= kFlatMaxRow &&
+        nnz + 8192 < (int64_t)INT32_MAX))
+    return f;
+  // the largest blocks that still give every CU about two: fewer, larger
+  // blocks measured faster on the banded 123440-row matrix (U = 4: 13.3 us,
+  // 2: 14.3, 1: 14.5 cold), down to about 500 blocks
+  const int32_t T = (int32_t)((max_row + 3) & ~(int64_t)3);
+  for (int U = 4; U >= 1; U /= 2) {
+    f.U = U;
+    f.T = T;
+    f.E = U * 4 * kStreamBlock - T;
+    f.blocks = cdiv(nnz, (int64_t)f.E);
+    if (f.blocks >= kFlatMinBlocks) break;
+  }
+  return f;
 }
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
@@ -1041,6 +1054,28 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
   }
   return hipErrorInvalidValue;
 }
+
+namespace {
+// blk_row[b] = first row r in [0, m] with ro[r] >= b * E for b < blocks;
+// blk_row[blocks] = m.
+__global__ void flat_rows_kernel(const int32_t* ro, int64_t m, int64_t E, int64_t blocks,
+                                 int32_t* blk_row) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b > blocks) return;
+  if (b == blocks) {
+    blk_row[b] = (int32_t)m;
+    return;
+  }
+  const int64_t e = b * E;
+  int64_t lo = 0, hi = m;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if ((int64_t)ro[mid] < e) lo = mid + 1;
+    else hi = mid;
+  }
+  blk_row[b] = (int32_t)lo;
+}
+}  // namespace
 
 hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i32, int64_t m,
                                int64_t nnz, int32_t T, SpmmSchedule* out, hipStream_t s) {
@@ -1114,6 +1149,14 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
         if ((e = hipGetLastError()) != hipSuccess) break;
       }
     }
+    out->flat = spmv_flat_shape(m, nnz, out->max_row, out->natural, out->P);
+    if (out->flat.U > 0) {
+      const int64_t nb = out->flat.blocks;
+      if ((e = hipMalloc(&out->blk_row, (size_t)(nb + 1) * 4)) != hipSuccess) break;
+      hipLaunchKernelGGL(flat_rows_kernel, dim3((unsigned)cdiv(nb + 1, 256)), dim3(256), 0, s, ro,
+                         m, (int64_t)out->flat.E, nb, out->blk_row);
+      if ((e = hipGetLastError()) != hipSuccess) break;
+    }
     e = hipStreamSynchronize(s);
   } while (0);
   (void)hipFree(tmp);  // e already reports the schedule's outcome
@@ -1122,7 +1165,9 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
 }
 
 void free_spmm_schedule(SpmmSchedule* sch) {
-  if (sch->mem) (void)hipFree(sch->mem);  // teardown: nothing to report
+  // teardown: nothing to report
+  if (sch->mem) (void)hipFree(sch->mem);
+  if (sch->blk_row) (void)hipFree(sch->blk_row);
   *sch = SpmmSchedule{};
 }
 
