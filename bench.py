@@ -124,7 +124,15 @@ class Flush:
 
 def copy_calibration(steps):
     """Plain device-to-device copies of a known size: what the HBM byte
-    counters read for them calibrates the counters of the real kernels."""
+    counters read for them calibrates the counters of the real kernels.  A
+    second check with the access shape of the gathers: after a 512 MiB read
+    that evicts the caches, each XCD gathers 4 KiB rows at random from its
+    own 2 MiB slice of a 16 MiB source (the measurement library's sliced
+    gather, 16 row reads per wave, every row of every slice touched with
+    near certainty), so the memory reads are the source once plus the index
+    list."""
+    import ctypes
+
     import torch
     n = 256 << 20
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -132,7 +140,30 @@ def copy_calibration(steps):
     for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": steps}))
+    del a, b
+    path = os.path.join(ROOT, "unstructured_sparse_linear_amd", "libspops_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    f = L.spops_ceil_gather
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    src = torch.full((16 << 20,), 3, dtype=torch.uint8, device="cuda")
+    blocks, per_wave, rows = 2048, 16, (2 << 20) // 4096
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    idx_np = np.random.default_rng(0).integers(0, rows, blocks * 4 * per_wave).astype(np.int32)
+    idx = torch.from_numpy(idx_np).to("cuda")
+    flush_buf = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(steps):
+        flush_buf.sum()
+        assert f(src.data_ptr(), rows, 4096, 1, idx.data_ptr(), per_wave, blocks,
+                 sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": steps,
+                      "gather_source_bytes": 16 << 20, "gather_index_bytes": int(idx_np.nbytes),
+                      "gathers": steps}))
 
 
 def alg_bytes(A, N, K, dt):
