@@ -461,14 +461,23 @@ hipError_t launch_vt(const SddmmArgs& a, hipStream_t s) {
 // (the entry-list kernel needs them).
 namespace {
 template <typename OT>
+// All of an entry's pieces (at most 16) and its position are requested
+// together, then added in piece order.
 __global__ __launch_bounds__(256) void sddmm_piece_sum_kernel(const float* part, int pieces,
                                                               int64_t count, const int32_t* pos,
                                                               int64_t start, OT* out) {
+  constexpr int kMaxPieces = 16;
   for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < count;
        j += (int64_t)gridDim.x * 256) {
-    float v = part[j];
-    for (int b = 1; b < pieces; ++b) v += part[(int64_t)b * count + j];
-    out[pos[start + j]] = from_f32<OT>(v);
+    const int32_t q = pos[start + j];
+    float p[kMaxPieces];
+#pragma unroll
+    for (int b = 0; b < kMaxPieces; ++b) p[b] = b < pieces ? part[(int64_t)b * count + j] : 0.f;
+    float v = p[0];
+#pragma unroll
+    for (int b = 1; b < kMaxPieces; ++b)
+      if (b < pieces) v += p[b];
+    out[q] = from_f32<OT>(v);
   }
 }
 }  // namespace
@@ -477,6 +486,7 @@ hipError_t launch_sddmm_piece_sum(const float* part, int pieces, int64_t count,
                                   const int32_t* pos, int64_t start, void* out, int out_dtype,
                                   hipStream_t s) {
   if (count <= 0) return hipSuccess;
+  if (pieces < 1 || pieces > 16) return hipErrorInvalidValue;
   const int64_t g = cdiv(count, 256);
   const dim3 grid((unsigned)(g < 2048 ? g : 2048));
   if (out_dtype == kF32)
