@@ -72,7 +72,7 @@ def rhs(seed, n):
                                                  (3, 12345, 8, 8)])
 @pytest.mark.parametrize("use_plan", [True, False])
 def test_cg_first_iterations_match_oracle(seed, n, iters, check, use_plan):
-    # with the plan the iterations run as fused row blocks; without it the
+    # with the plan the iterations run as fused entry-range blocks; without it the
     # direction, SpMV and p.q are separate kernels
     A, b = spd(seed, n), rhs(seed + 10, n)
     x, k, rel = solve(A, b, rtol=0.0, max_iter=iters, check_every=check, use_plan=use_plan)
@@ -148,7 +148,7 @@ def test_cg_deterministic(use_plan):
 
 def test_cg_int16_columns_and_unaligned_arrays():
     # n <= 32767 gives int16 columns; an offset of one element takes the
-    # entry-at-a-time loads of the fused row blocks
+    # entry-at-a-time loads of the fused entry-range blocks
     n = 6000
     A, b = spd(20, n), rhs(21, n)
     assert A.col_idx.dtype == np.int16

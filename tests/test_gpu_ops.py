@@ -475,7 +475,7 @@ def test_spmv_strided_x_and_y_through_the_abi(dt):
                                              ("bf16", 64, 3000, 0.9)])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_spmv_balanced_long_rows(dt, m, n, density, offset):
-    # balanced rows longer than the row-block limit: a workgroup per row; the
+    # balanced rows longer than 128 entries: a workgroup per row; the
     # plan's split of long rows is not used and must not be fixed up
     A = gen.random_csr(40 + m, m, n, density, dt)
     x = gen.dense(40 + m, 100, gen.S_B, (n, 1), dt)
