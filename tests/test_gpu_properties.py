@@ -113,3 +113,30 @@ def test_transpose_permutation_and_row_order(data):
     ri = S.sort_rows_by_nnz(ro, A.n)
     assert np.array_equal(host(ri).astype(np.int64),
                           oracle.row_idx(A.row_offsets).astype(np.int64))
+
+
+@settings(max_examples=15, deadline=None,
+          suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(data=st.data())
+def test_spmv_entry_ranges(data):
+    # balanced rows of 0..L entries over thousands of rows: the planned SpMV
+    # cuts the entries into ranges whose boundaries fall inside rows at
+    # random; every row is written once, by the range it starts in
+    m = data.draw(st.integers(1, 6000))
+    n = data.draw(st.integers(1, 3000))
+    L = data.draw(st.integers(1, 40))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    lengths = rng.integers(0, min(L, n) + 1, m)
+    rows = [np.sort(rng.choice(n, int(c), replace=False)) for c in lengths]
+    A = gen.csr_from_row_lists(m, n, rows)
+    if A.nnz == 0:
+        return
+    dt = data.draw(st.sampled_from(DTYPES))
+    A = A.with_values(gen.f32_to_storage(rng.integers(-8, 9, A.nnz).astype(np.float32), dt), dt)
+    x = ints(data.draw, (n, 1), dt)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, n)
+    p = S.SpmmPlan(ro, ri, ci, n)
+    y = S.spmm(v, ro, ri, ci, dev(x, dt), m, plan=p)
+    assert np.array_equal(host_f64(y),
+                          oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt))
