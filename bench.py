@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--settle-ms", type=float, default=50.0,
+                   help="untimed flush + call traffic before each timed loop (0: none)")
     p.add_argument("--config", type=int, default=DEFAULT_CONFIG,
                    help="workload 1-5 (3, the cross-clustered SDDMM, is the headline)")
     p.add_argument("--dtype", default=None,
@@ -120,6 +122,24 @@ class Flush:
             self.buf.fill_(1)
         else:
             self.sink = self.buf.sum()
+
+
+def settle(fn, ms):
+    """Runs fn (an untimed cache flush + call) back to back for about `ms`
+    milliseconds of host time.  After an idle spell the GPU's memory-side
+    clocks need tens of milliseconds of traffic to reach their sustained
+    state: on the cross-clustered SDDMM the first ~100 cold calls after idle
+    measured 72 -> 66.5 us, and a GPU-side delay before each call kept them
+    at ~72 us.  Timing from the sustained state matches a continuously
+    loaded GPU and makes the figures independent of what ran before."""
+    import torch
+    if ms <= 0:
+        return
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def copy_calibration(steps):
@@ -359,6 +379,12 @@ def adapter_step(S, w, A, dt, N, dev, flush, args):
     with torch.cuda.graph(graph):
         run()
     torch.cuda.synchronize()
+
+    def untimed_step():
+        if not args.no_flush:
+            flush()
+        graph.replay()
+    settle(untimed_step, args.settle_ms)
     stream = torch.cuda.current_stream(dev)
     ts = []
     for _ in range(max(args.steps, 5)):
@@ -636,6 +662,12 @@ def measure_case(S, cfg, dt, op, dev, flush, reps, args, ceil=None, oracle=None)
     plan_ms = (time.perf_counter() - t0) * 1e3
     fn()
     torch.cuda.synchronize()
+
+    def flushed_call():
+        if not args.no_flush:
+            flush()
+        fn()
+    settle(flushed_call, args.settle_ms)
     stream = torch.cuda.current_stream(dev)
     evs = []
     for _ in range(reps):
@@ -868,6 +900,12 @@ def main():
             run_op(op)
     torch.cuda.synchronize()
 
+    def warm_step():
+        cold()
+        for op in ops:
+            run_op(op)
+    settle(warm_step, args.settle_ms)
+
     # per-operation cold timing (eager)
     per_op = {op: [] for op in ops}
     for _ in range(args.steps):
@@ -943,6 +981,15 @@ def main():
 
     step()
     torch.cuda.synchronize()
+
+    def untimed_step():
+        cold()
+        if graph is not None:
+            graph.replay()
+        else:
+            for op in ops:
+                run_op(op)
+    settle(untimed_step, args.settle_ms)
     events = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -992,6 +1039,7 @@ def main():
                    "N": N, "K": K, "value_dtype": dt, "ops": ops,
                    "caches": "warm" if args.no_flush else
                    f"cold (512 MiB {args.flush} before each timed call)",
+                   "settle_ms": args.settle_ms,
                    "step": "eager" if args.no_graph else
                    "hip graph replay, streams: " + " | ".join("+".join(x) for x in lanes)},
         "value_op": {"op": dom, "us": round(breakdown[dom]["ms"] * 1e3, 2),
