@@ -126,12 +126,13 @@ class Flush:
 
 def settle(fn, ms):
     """Runs fn (an untimed cache flush + call) back to back for about `ms`
-    milliseconds of host time.  After an idle spell the GPU's memory-side
-    clocks need tens of milliseconds of traffic to reach their sustained
-    state: on the cross-clustered SDDMM the first ~100 cold calls after idle
-    measured 72 -> 66.5 us, and a GPU-side delay before each call kept them
-    at ~72 us.  Timing from the sustained state matches a continuously
-    loaded GPU and makes the figures independent of what ran before."""
+    milliseconds of host time.  After an idle spell the first cold calls
+    run slower until the GPU has carried this traffic for some tens of
+    milliseconds: on the cross-clustered SDDMM the first ~100 cold calls
+    after idle measured 72 -> 66.5 us, and a GPU-side delay before each call
+    kept them at ~72 us.  Timing from the sustained state matches a
+    continuously loaded GPU and makes the figures independent of what ran
+    before."""
     import torch
     if ms <= 0:
         return
