@@ -63,10 +63,23 @@ __device__ double block_sum(double v, double* lds) {
   return lds[kWaves];
 }
 
-// Sum of the n per-workgroup partials, in a fixed order.
+// Sum of the n per-workgroup partials, in a fixed order: thread t adds
+// partials t, t + kBlock, ... (up to eight of them requested together),
+// then the workgroup sum.
 __device__ double sum_partials(const double* part, int n, double* lds) {
+  constexpr int kTogether = 8;
   double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += kBlock) s += part[i];
+  for (int i0 = threadIdx.x; i0 < n; i0 += kBlock * kTogether) {
+    double v[kTogether];
+#pragma unroll
+    for (int u = 0; u < kTogether; ++u) {
+      const int i = i0 + u * kBlock;
+      v[u] = i < n ? part[i] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < kTogether; ++u)
+      if (i0 + u * kBlock < n) s += v[u];
+  }
   return block_sum(s, lds);
 }
 
