@@ -218,8 +218,7 @@ def kernel_sources_sha(files):
 
 
 KERNEL_FILES = {"spmm": ["spmm.hip", "common.h"], "spmv": ["spmm.hip", "common.h"],
-                "sddmm": ["sddmm.hip", "sddmm_dense.hip",
-                                                          "common.h"],
+                "sddmm": ["sddmm.hip", "sddmm_dense.hip", "common.h"],
                 "csr_add": ["csr_add.hip", "common.h"], "transpose": ["radix.hip", "common.h"],
                 "row_order": ["radix.hip", "common.h"]}
 
