@@ -193,13 +193,18 @@ class SpmmPlan:
         return {"split_rows": s.value, "chunks": c.value, "max_row_nnz": mx.value}
 
     def workspace(self, N: int, device) -> Optional[torch.Tensor]:
-        if N not in self._ws:
-            b = ctypes.c_size_t()
-            _check("spops_spmm_workspace_size",
-                   lib().spops_spmm_workspace_size(self.handle, N, ctypes.byref(b)))
-            self._ws[N] = torch.empty(b.value, dtype=torch.uint8, device=device) \
-                if b.value else None
-        return self._ws[N]
+        # asked every call (cheap), the buffer kept per N and grown when a
+        # call needs more
+        b = ctypes.c_size_t()
+        _check("spops_spmm_workspace_size",
+               lib().spops_spmm_workspace_size(self.handle, N, ctypes.byref(b)))
+        if b.value == 0:
+            return None
+        ws = self._ws.get(N)
+        if ws is None or ws.numel() < b.value:
+            ws = torch.empty(b.value, dtype=torch.uint8, device=device)
+            self._ws[N] = ws
+        return ws
 
     def __del__(self):
         h = getattr(self, "handle", None)
