@@ -37,6 +37,28 @@ def row_order(A, kind, seed=0):
     return dev(gen.permutation(seed, A.m, kind))
 
 
+def planned_chunks(row_lengths):
+    """(split length, chunk length, chunk items, split rows) the SpMM plan
+    chooses for these row lengths: split at 64 entries when the lengths are
+    skewed and at most 1/32 of the rows hold 65..128, else at 128; chunks of
+    the longest row rounded up to a power of two (at most 4096) when that
+    leaves at least 128 chunks, else of 512."""
+    rl = np.asarray(row_lengths, np.int64)
+    m, nnz, mx = rl.size, int(rl.sum()), int(rl.max())
+    natural = mx <= 2 * (nnz // m) + 32
+    mid = int(np.sum((rl > 64) & (rl <= 128)))
+    T = 64 if (not natural and mid * 32 <= m) else 128
+    items = lambda cl: int(np.sum(-(-rl[rl > T] // cl)))  # noqa: E731
+    CL = 512
+    if mx > CL:
+        cl = CL
+        while cl < mx and cl < 4096:
+            cl *= 2
+        if items(cl) >= 128:
+            CL = cl
+    return T, CL, items(CL), int(np.sum((rl > T) & (rl > CL)))
+
+
 def heavy_csr(seed, m, n, lengths, dt):
     """CSR whose first rows (in a shuffled order) have the given lengths."""
     rng = np.random.default_rng(seed)
@@ -315,7 +337,9 @@ def test_spmm_dense_rows(dt, N, n, col32, kind):
     v, ro, ci = csr_dev(A)
     ri = row_order(A, kind, 5)
     p = S.SpmmPlan(ro, ri, ci, n)
-    assert p.info()["split_rows"] == 73
+    _, CL, items, split = planned_chunks(np.diff(A.row_offsets))
+    assert p.info()["split_rows"] == split and p.info()["chunks"] == items
+    assert split == (73 if CL == 512 else 48)
     C = S.spmm(v, ro, ri, ci, dev(B, dt), A.m, plan=p)
     ref = oracle.spmm(A.m, A.row_offsets, A.col_idx, A.values, dt, B, dt)
     assert_close(host_f64(C), ref, dt, "spmm dense rows")
@@ -324,6 +348,30 @@ def test_spmm_dense_rows(dt, N, n, col32, kind):
     Bi = gen.dense(n + N, 100, gen.S_B, (n, N), dt, integer_values=True)
     Ci = S.spmm(dev(Ai.values, dt), ro, ri, ci, dev(Bi, dt), A.m, plan=p)
     assert np.array_equal(host_f64(Ci),
+                          oracle.spmm(A.m, A.row_offsets, A.col_idx, Ai.values, dt, Bi, dt))
+
+
+@pytest.mark.parametrize("dt,N", [("bf16", 256), ("f16", 64), ("f32", 8), ("bf16", 1)])
+def test_spmm_whole_row_chunks(dt, N):
+    # 200 rows of 600..4096 entries: chunks of 4096 leave 200 chunk
+    # workgroups (at least 128), so each long row is one chunk and nothing
+    # is added up afterwards; a row of 5000 still takes two chunks and the
+    # fixup; exact on integer data
+    rng = np.random.default_rng(N)
+    lengths = list(rng.integers(600, 4097, 200)) + [4096, 5000]
+    A = heavy_csr(N + 5, 2000, 6000, lengths, dt)
+    v, ro, ci = csr_dev(A)
+    ri = S.sort_rows_by_nnz(ro, A.n)
+    p = S.SpmmPlan(ro, ri, ci, A.n)
+    rl = np.diff(A.row_offsets)
+    info = p.info()
+    assert info["max_row_nnz"] == 5000 and info["split_rows"] == 1
+    assert info["chunks"] == int(np.sum(rl > 64)) + 1
+    Ai = A.with_values(gen.f32_to_storage(rng.integers(-3, 4, A.nnz).astype(np.float32), dt),
+                       dt)
+    Bi = gen.dense(N, 100, gen.S_B, (A.n, N), dt, integer_values=True)
+    C = S.spmm(dev(Ai.values, dt), ro, ri, ci, dev(Bi, dt), A.m, plan=p)
+    assert np.array_equal(host_f64(C),
                           oracle.spmm(A.m, A.row_offsets, A.col_idx, Ai.values, dt, Bi, dt))
 
 
@@ -476,7 +524,8 @@ def test_spmv_strided_x_and_y_through_the_abi(dt):
 @pytest.mark.parametrize("offset", [0, 1])
 def test_spmv_balanced_long_rows(dt, m, n, density, offset):
     # balanced rows longer than 128 entries: a workgroup per row; the
-    # plan's split of long rows is not used and must not be fixed up
+    # plan's chunks of long rows are not used (and, where rows span several
+    # chunks, must not be fixed up)
     A = gen.random_csr(40 + m, m, n, density, dt)
     x = gen.dense(40 + m, 100, gen.S_B, (n, 1), dt)
     v, ro, ci = csr_dev(A)
@@ -486,7 +535,7 @@ def test_spmv_balanced_long_rows(dt, m, n, density, offset):
     ri = S.sort_rows_by_nnz(ro, A.n)
     p = S.SpmmPlan(ro, ri, ci, n)
     info = p.info()
-    assert info["max_row_nnz"] > 128 and info["split_rows"] > 0
+    assert info["max_row_nnz"] > 128 and info["chunks"] > 0
     y = S.spmm(v, ro, ri, ci, dev(x, dt), m, plan=p)
     ref = oracle.spmm(m, A.row_offsets, A.col_idx, A.values, dt, x, dt)
     assert_close(host_f64(y), ref, dt, "spmv long rows")

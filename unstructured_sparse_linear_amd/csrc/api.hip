@@ -104,6 +104,8 @@ SpmmArgs spmm_args(const spops_csr* A, const void* B, spops_dtype b_type, int64_
     a.P = plan->sch.P;
     a.S = plan->sch.S;
     a.T = plan->sch.T;
+    a.CLs = 0;
+    while ((1 << a.CLs) < plan->sch.CL) ++a.CLs;
     a.item_pos = plan->sch.item_pos;
     a.item_chunk = plan->sch.item_chunk;
     a.split_pos = plan->sch.split_pos;

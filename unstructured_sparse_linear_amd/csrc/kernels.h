@@ -55,14 +55,22 @@ hipError_t radix_sort_u32_iota_ptrs(const uint32_t* keys, int64_t n, int bits, v
 
 // ------------------------------------------------------------------ SpMM --
 // Rows with more entries than the plan's split length are cut into chunks of
-// kSpmmChunkLen entries, one workgroup per chunk: kSpmmSplitLenSkewed when the
-// row lengths are skewed and at most 1/32 of the rows have more entries than
-// that and at most kSpmmSplitLen, else kSpmmSplitLen.  A call whose row
-// groups span 32 or more lanes takes rows up to kSpmmSplitLen whole anyway
-// (their chunk workgroups return at once).
+// the plan's chunk length, one workgroup per chunk.  Split length:
+// kSpmmSplitLenSkewed when the row lengths are skewed and at most 1/32 of the
+// rows have more entries than that and at most kSpmmSplitLen, else
+// kSpmmSplitLen; a call whose row groups span 32 or more lanes takes rows up
+// to kSpmmSplitLen whole anyway (their chunk workgroups return at once).
+// Chunk length: the longest row rounded up to a power of two, at most
+// kSpmmChunkLenMax, when that leaves at least kSpmmMinChunkItems chunks;
+// else kSpmmChunkLen.
 constexpr int32_t kSpmmSplitLen = 128;
 constexpr int32_t kSpmmSplitLenSkewed = 64;
 constexpr int32_t kSpmmChunkLen = 512;
+constexpr int32_t kSpmmChunkLenMax = 4096;
+constexpr int32_t kSpmmMinChunkItems = 128;
+static_assert((kSpmmChunkLen & (kSpmmChunkLen - 1)) == 0 &&
+                  (kSpmmChunkLenMax & (kSpmmChunkLenMax - 1)) == 0,
+              "chunk lengths are powers of two");
 
 struct SpmmArgs {
   int64_t m, k, nnz, N, ldb, ldc;
@@ -82,6 +90,7 @@ struct SpmmArgs {
   int64_t P;            // number of chunk items of split rows
   int64_t S;            // number of split rows
   int32_t T;            // split length: rows longer than T go to the chunk workgroups
+  int32_t CLs;          // chunk length = 1 << CLs (a power of two)
   const int32_t* item_pos;    // [P] position in row_idx of the chunk's row
   const int32_t* item_chunk;  // [P] chunk number within its row
   const int32_t* split_pos;   // [S] position in row_idx of each multi-chunk row
@@ -117,6 +126,7 @@ struct SpmmSchedule {
   int64_t P = 0, S = 0, max_row = 0;
   int natural = 0;  // row lengths balanced enough to keep index order (locality)
   int32_t T = 0;
+  int32_t CL = kSpmmChunkLen;
   int32_t* item_pos = nullptr;
   int32_t* item_chunk = nullptr;
   int32_t* split_pos = nullptr;

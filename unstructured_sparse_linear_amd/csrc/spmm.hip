@@ -21,11 +21,13 @@
 // Long rows.  The plan (build_spmm_schedule) lists the rows longer than its
 // split length (kSpmmSplitLen, or kSpmmSplitLenSkewed when the lengths are
 // not balanced and at most 1/32 of the rows fall between the two) in row_idx
-// order and cuts each into chunks of kSpmmChunkLen
-// entries; each chunk is one workgroup whose waves take contiguous slices and
-// are summed through LDS in wave order.  A launch with wide row groups raises
-// the split length back to kSpmmSplitLen: its chunk workgroups for shorter
-// rows return at once and the row path takes those rows.  A row with several chunks writes fp32
+// order and cuts each into chunks of the plan's chunk length (the longest
+// row rounded up to a power of two, up to 4096 entries, when that leaves at
+// least 128 chunks, else 512 entries); each chunk is one workgroup whose
+// waves take contiguous slices and are summed through LDS in wave order.  A
+// launch with wide row groups raises the split length back to
+// kSpmmSplitLen: its chunk workgroups for shorter rows return at once and
+// the row path takes those rows.  A row with several chunks writes fp32
 // partial rows that spmm_fixup_kernel adds in chunk order.  Every sum has a
 // fixed order, so results are bitwise reproducible.
 #include <stdlib.h>
@@ -41,7 +43,6 @@ namespace spops {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int32_t kChunkLen = kSpmmChunkLen;
 // entries whose B vectors are loaded together (bytes in flight per lane:
 // kUnroll * 16); the gathers are latency-bound, so deeper is faster
 constexpr int kUnroll = 8;
@@ -481,8 +482,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
     // a row within this launch's split length is the row path's (uniform
     // over the workgroup: one item per workgroup)
     if (re - rs <= a.T) return;
-    const int64_t c0 = rs + ch * kChunkLen;
-    const int64_t c1 = (c0 + kChunkLen < re) ? c0 + kChunkLen : re;
+    // chunk lengths are powers of two: shifts, no division
+    const int64_t c0 = rs + (ch << a.CLs);
+    const int64_t c1 = (c0 + ((int64_t)1 << a.CLs) < re) ? c0 + ((int64_t)1 << a.CLs) : re;
     const int64_t len = c1 > c0 ? c1 - c0 : 0;
     const int64_t sub = cdiv(len, GPB);
     int64_t q0 = c0 + grp * sub;
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a, int64_t nwin) 
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] += red[q][gl * VEC + e];
       }
-      const int64_t nch = cdiv(re - rs, kChunkLen);
+      const int64_t nch = (re - rs + ((int64_t)1 << a.CLs) - 1) >> a.CLs;
       if (nch <= 1) {
         if (r >= 0 && r < a.m) write_out<OT, VEC, ALIGNED>((OT*)a.C + r * a.ldc, j, a.N, acc);
       } else {
@@ -550,8 +552,8 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
     int64_t rs = 0, re = 0;
     if (r >= 0 && r < a.m) row_range(a.ro, r, a.nnz, rs, re);
     if (re - rs <= a.T) return;  // the row path's (uniform over the workgroup)
-    const int64_t c0 = rs + ch * kChunkLen;
-    const int64_t c1 = (c0 + kChunkLen < re) ? c0 + kChunkLen : re;
+    const int64_t c0 = rs + (ch << a.CLs);
+    const int64_t c1 = (c0 + ((int64_t)1 << a.CLs) < re) ? c0 + ((int64_t)1 << a.CLs) : re;
     float s = 0.f;
     for (int64_t p = c0 + threadIdx.x; p < c1; p += kBlock) {
       int c = (int)col[p];
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(SpmmArgs a) {
     if (threadIdx.x == 0) {
       float t = red[0];
       for (int q = 1; q < kBlock / kWave; ++q) t += red[q];
-      const int64_t nch = cdiv(re - rs, kChunkLen);
+      const int64_t nch = (re - rs + ((int64_t)1 << a.CLs) - 1) >> a.CLs;
       if (nch <= 1) {
         if (r >= 0 && r < a.m) ((OT*)a.C)[r * a.ldc] = from_f32<OT>(t);
       } else {
@@ -982,7 +984,7 @@ hipError_t launch_vt(const SpmmArgs& a, hipStream_t s) {
 
 __global__ __launch_bounds__(256) void sched_count_kernel(const int32_t* ro, const void* ri,
                                                           int ri_i32, int64_t m, int64_t nnz,
-                                                          int32_t T, uint32_t* nch,
+                                                          int32_t T, int32_t CL, uint32_t* nch,
                                                           uint32_t* multi, int32_t* maxlen) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= m) return;
@@ -990,7 +992,7 @@ __global__ __launch_bounds__(256) void sched_count_kernel(const int32_t* ro, con
   int64_t p0 = 0, p1 = 0;
   if (r >= 0 && r < m) row_range(ro, r, nnz, p0, p1);
   const int64_t len = p1 - p0;
-  const uint32_t c = len > T ? (uint32_t)cdiv(len, kChunkLen) : 0u;
+  const uint32_t c = len > T ? (uint32_t)cdiv(len, (int64_t)CL) : 0u;
   nch[i] = c;
   multi[i] = c > 1 ? 1u : 0u;
   atomicMax(maxlen, (int32_t)len);
@@ -1096,12 +1098,13 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
   int32_t host_misc[3] = {0, 0, 0};
   const unsigned g = (unsigned)cdiv(m, 256);
   // chunk counts, their offsets and the split rows' ranks for split length t
-  auto count = [&](int32_t t) -> hipError_t {
+  // and chunk length cl
+  auto count = [&](int32_t t, int32_t cl) -> hipError_t {
     host_misc[0] = host_misc[1] = host_misc[2] = 0;
     hipError_t r = hipMemcpyAsync(dev_misc, host_misc, 12, hipMemcpyHostToDevice, s);
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(sched_count_kernel, dim3(g), dim3(256), 0, s, ro, row_idx, ri_i32, m, nnz,
-                       t, nch, multi, dev_misc);
+                       t, cl, nch, multi, dev_misc);
     if ((r = hipGetLastError()) != hipSuccess) return r;
     if ((r = exclusive_scan_u32(nch, off, m, (uint32_t*)dev_misc + 1, sws, s)) != hipSuccess)
       return r;
@@ -1111,8 +1114,10 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
       return r;
     return hipStreamSynchronize(s);
   };
+  int32_t CL = kSpmmChunkLen;
+  out->CL = CL;
   do {
-    if ((e = count(T)) != hipSuccess) break;
+    if ((e = count(T, CL)) != hipSuccess) break;
     out->max_row = host_misc[0];
     // balanced lengths: keep index order for locality
     out->natural = (out->max_row <= 2 * (nnz / m) + 32) ? 1 : 0;
@@ -1122,10 +1127,22 @@ hipError_t build_spmm_schedule(const int32_t* ro, const void* row_idx, int ri_i3
     // where they are common, a workgroup each costs more than it saves
     if (!out->natural && T > kSpmmSplitLenSkewed) {
       const int64_t p_long = host_misc[1];
-      if ((e = count(kSpmmSplitLenSkewed)) != hipSuccess) break;
+      if ((e = count(kSpmmSplitLenSkewed, CL)) != hipSuccess) break;
       if ((host_misc[1] - p_long) * 32 <= m)
         out->T = T = kSpmmSplitLenSkewed;
-      else if ((e = count(T)) != hipSuccess)
+      else if ((e = count(T, CL)) != hipSuccess)
+        break;
+    }
+    // rows up to kSpmmChunkLenMax entries whole in one workgroup each (no
+    // partial rows to add up afterwards) while that still leaves at least
+    // kSpmmMinChunkItems chunk workgroups; else kSpmmChunkLen
+    if (out->max_row > CL) {
+      int32_t cl = CL;
+      while (cl < out->max_row && cl < kSpmmChunkLenMax) cl *= 2;
+      if ((e = count(T, cl)) != hipSuccess) break;
+      if (host_misc[1] >= kSpmmMinChunkItems)
+        out->CL = CL = cl;
+      else if ((e = count(T, CL)) != hipSuccess)
         break;
     }
     out->P = host_misc[1];
