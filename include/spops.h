@@ -165,12 +165,14 @@ spops_status spops_spmm_plan_create(const spops_csr* A, void* hip_stream,
 spops_status spops_spmm_plan_destroy(spops_spmm_plan* plan);
 /* Bytes of workspace spops_spmm needs with this plan for N columns. */
 spops_status spops_spmm_workspace_size(const spops_spmm_plan* plan, int64_t N, size_t* bytes);
-/* Plan summary: split_rows = rows of more than 512 entries (cut into chunks
- * of 512 whose partial rows are added afterwards); chunks = workgroups the
- * plan gives to long rows (every row of more than 128 entries, or of more
- * than 64 when the row lengths are skewed -- longest row above twice the
- * mean plus 32 -- and at most 1/32 of the rows have 65 to 128 entries);
- * max_row_nnz = longest row. */
+/* Plan summary: chunks = workgroups the plan gives to long rows (every row
+ * of more than 128 entries, or of more than 64 when the row lengths are
+ * skewed -- longest row above twice the mean plus 32 -- and at most 1/32 of
+ * the rows have 65 to 128 entries), each covering up to a chunk length of
+ * entries: the longest row rounded up to a power of two, at most 4096, when
+ * that still gives at least 128 chunks, else 512; split_rows = long rows of
+ * more than one chunk (their partial rows are added afterwards in chunk
+ * order); max_row_nnz = longest row. */
 spops_status spops_spmm_plan_info(const spops_spmm_plan* plan, int64_t* split_rows,
                                   int64_t* chunks, int64_t* max_row_nnz);
 
