@@ -433,16 +433,21 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     if (P.host_ok) {
       if (P.h.rest == 0) return hipSuccess;
       if (pieces > 1) {
+        // every piece covers the whole remainder: in row order, so that a
+        // row's A slice is loaded once per piece
+        r.pos = P.row_pos;
+        r.rows = P.row_rc;
+        r.cols = P.row_col;
         r.nb = pieces;
         r.ksplit = pieces;
         r.kpiece = K / pieces;
         r.part = part;
-        r.bstart[0] = P.bucket_start[0];
-        r.bstart[1] = P.bucket_start[P.h.nb];
+        r.bstart[0] = 0;
+        r.bstart[1] = P.h.rest;
         hipError_t e = launch_sddmm_list(r, s);
         if (e != hipSuccess) return e;
-        return launch_sddmm_piece_sum(part, pieces, P.h.rest, P.ent_pos, P.bucket_start[0],
-                                      out_values, out_type, s);
+        return launch_sddmm_piece_sum(part, pieces, P.h.rest, P.row_pos, 0, out_values, out_type,
+                                      s);
       }
       r.nb = P.h.nb;
       for (int b = 0; b <= P.h.nb; ++b) r.bstart[b] = P.bucket_start[b];

@@ -192,6 +192,10 @@ struct SddmmPlanDev {
   int32_t* ent_pos = nullptr;      // [nnz] mask position of each sorted entry
   int32_t* ent_rc = nullptr;       // [nnz] (tile row << 16) | tile column; remainder: row
   int32_t* ent_col = nullptr;      // [nnz] mask column of each sorted entry (as stored)
+  // the remainder in row order (its first `rest` entries), for K in pieces
+  int32_t* row_pos = nullptr;      // [nnz] mask position
+  int32_t* row_rc = nullptr;       // [nnz] row
+  int32_t* row_col = nullptr;      // [nnz] mask column
   // host copy of the counts (plans made by spops_sddmm_plan_create)
   bool host_ok = false;
   SddmmPlanScalars h{};

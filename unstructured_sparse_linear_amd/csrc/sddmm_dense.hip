@@ -487,17 +487,43 @@ __global__ void classify_kernel(ClassifyArgs a) {
   if (sub == 0 && rest) atomicAdd(&a.sc->rest_count, rest);
 }
 
-// Buckets pay when each remaining row keeps several remainder entries per
-// bucket (a row's A slice is reloaded once per row and bucket): at least 32
-// remainder entries per remaining row on average, else every remainder entry
-// goes to bucket 0.  Thread 0 records the bucket count.
+// Buckets pay while each remaining row keeps several remainder entries per
+// bucket (a row's A slice is reloaded once per row and bucket): the most
+// buckets (a power of two up to nb_max) with at least 4 remainder entries
+// per remaining row and bucket on average; adjacent buckets are merged into
+// one (contiguous column ranges).  Thread 0 records the bucket count.
 __global__ void merge_buckets_kernel(uint32_t* key, int64_t nnz, uint32_t rest_key, int nb_max,
                                      int forced, SddmmPlanScalars* sc) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t mc = sc->mc;
-  const bool merge = !forced && nb_max > 1 && (int64_t)sc->rest_count < 32 * (mc > 0 ? mc : 1);
-  if (p == 0) sc->nb = merge ? 1 : nb_max;
-  if (merge && p < nnz && key[p] > rest_key) key[p] = rest_key;
+  const int64_t mc = sc->mc > 0 ? sc->mc : 1;
+  int nb = nb_max;
+  if (!forced)
+    while (nb > 1 && (int64_t)sc->rest_count < 4 * (int64_t)nb * mc) nb /= 2;
+  if (p == 0) sc->nb = nb;
+  if (nb < nb_max && p < nnz && key[p] >= rest_key)
+    key[p] = rest_key + (key[p] - rest_key) * (uint32_t)nb / (uint32_t)nb_max;
+}
+
+// Thread q < nnz: the sort key of sorted entry q for the remainder's row
+// order (its row; m for a tile entry, which sorts them behind).
+__global__ void rest_row_key_kernel(const int32_t* ent_rc, int64_t nnz, int64_t m,
+                                    const SddmmPlanScalars* sc, uint32_t* key) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nnz) return;
+  const int64_t r = ent_rc[q];
+  key[q] = (uint32_t)((q >= sc->tiled && r >= 0 && r < m) ? r : m);
+}
+
+// The remainder in row order: entry i is sorted entry src[i].
+__global__ void rest_gather_kernel(const uint32_t* src, int64_t nnz, const int32_t* ent_pos,
+                                   const int32_t* ent_rc, const int32_t* ent_col, int32_t* pos,
+                                   int32_t* rc, int32_t* col) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nnz) return;
+  const uint32_t q = src[i];
+  pos[i] = ent_pos[q];
+  rc[i] = ent_rc[q];
+  col[i] = ent_col[q];
 }
 
 // Thread t < nkeys + 1: key_start[t] = first sorted entry with key >= t (a
@@ -553,7 +579,8 @@ int planned_buckets(int64_t n, int* forced) {
 }
 
 struct PlanLayout {
-  size_t sc, rows, hot_cols, key_start, ent_pos, ent_rc, ent_col, total;
+  size_t sc, rows, hot_cols, key_start, ent_pos, ent_rc, ent_col, row_pos, row_rc, row_col,
+      total;
 };
 PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
   PlanLayout L{};
@@ -572,6 +599,12 @@ PlanLayout plan_layout(int64_t m, int64_t n, int64_t nnz) {
   L.ent_rc = o;
   o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
   L.ent_col = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.row_pos = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.row_rc = o;
+  o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
+  L.row_col = o;
   o += align256((size_t)(nnz > 0 ? nnz : 1) * 4);
   L.total = o;
   return L;
@@ -669,6 +702,9 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
   out->ent_pos = (int32_t*)(pm + P.ent_pos);
   out->ent_rc = (int32_t*)(pm + P.ent_rc);
   out->ent_col = (int32_t*)(pm + P.ent_col);
+  out->row_pos = (int32_t*)(pm + P.row_pos);
+  out->row_rc = (int32_t*)(pm + P.row_rc);
+  out->row_col = (int32_t*)(pm + P.row_col);
   uint32_t* hot = (uint32_t*)(ws + W.hot);
   uint32_t* rrank = (uint32_t*)(ws + W.rrank);
   uint32_t* ccnt = (uint32_t*)(ws + W.ccnt);
@@ -741,6 +777,21 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
                        (const int16_t*)col, nnz, nkeys, out->key_start, out->ent_pos,
                        out->ent_rc, out->ent_col);
   hipLaunchKernelGGL(plan_finish_kernel, dim3(1), dim3(64), 0, s, out->key_start, nnz, sc);
+  if (nnz > 0) {
+    // the remainder once more in row order (tile entries behind it), for
+    // calls that cut K into pieces: the key array and the sort's workspace
+    // are free again
+    const unsigned gz = (unsigned)cdiv(nnz, 256);
+    hipLaunchKernelGGL(rest_row_key_kernel, dim3(gz), dim3(256), 0, s, out->ent_rc, nnz, m, sc,
+                       key);
+    const uint32_t* skey2 = key;
+    const uint32_t* src2 = key;
+    if ((e = radix_sort_u32_iota_ptrs(key, nnz, bit_length((uint64_t)m), radix_ws, &skey2, &src2,
+                                      s)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(rest_gather_kernel, dim3(gz), dim3(256), 0, s, src2, nnz, out->ent_pos,
+                       out->ent_rc, out->ent_col, out->row_pos, out->row_rc, out->row_col);
+  }
   return hipGetLastError();
 }
 
