@@ -221,7 +221,9 @@ spops_status spops_sddmm_workspace_size(const spops_csr* mask, int64_t K, spops_
 /* Finds the clustered rows/columns of the mask and partitions its entries.
  * A row is dense when its entry count is at least tau * cols; a column is
  * dense when, over the remaining rows, its count is at least tau * rows.
- * tau <= 0 selects the default.  tau > 1 disables the dense tiles (all
+ * tau <= 0 selects the default: tau = 0.02, and a dense row or column also
+ * holds at least 128 entries (one tile's width), so that small or uniform
+ * masks stay on the general kernel.  tau > 1 disables the dense tiles (all
  * entries go to the general kernel).  Allocates, synchronizes.  Valid while
  * the mask's row_offsets / col_idx contents are unchanged. */
 spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hip_stream,

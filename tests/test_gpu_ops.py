@@ -659,7 +659,7 @@ def test_sddmm_tiles_split_k(dt, m, n, K, hr, hc, splits):
     M = cross_csr(9, m, n, hr, hc)
     _, ro, ci = csr_dev(M)
     ri = S.sort_rows_by_nnz(ro, n)
-    plan = S.SddmmPlan(ro, ci, m, n)
+    plan = S.SddmmPlan(ro, ci, m, n, tau=0.04)  # tiles on these small masks
     info = plan.info()
     assert info["tiles"] >= 4 and info["tiled_nnz"] + info["rest_nnz"] == M.nnz
     Ad = gen.dense(9, 100, gen.S_A, (m, K), dt)
@@ -691,7 +691,7 @@ def test_sddmm_operand_extent_over_4gib():
     M = cross_csr(21, m, n, 200, 250)
     _, ro, ci = csr_dev(M)
     ri = S.sort_rows_by_nnz(ro, n)
-    plan = S.SddmmPlan(ro, ci, m, n)
+    plan = S.SddmmPlan(ro, ci, m, n, tau=0.04)  # tiles on these small masks
     assert plan.info()["tiles"] >= 2
     Ai = gen.dense(22, 100, gen.S_A, (m, K), "f16", integer_values=True)
     Bi = gen.dense(22, 100, gen.S_BT, (n, K), "f16", integer_values=True)
@@ -721,7 +721,7 @@ def test_sddmm_remainder_k_pieces(dt, m, n, K, hr, hc, pieces):
     M = cross_csr(13, m, n, hr, hc)
     _, ro, ci = csr_dev(M)
     ri = S.sort_rows_by_nnz(ro, n)
-    plan = S.SddmmPlan(ro, ci, m, n)
+    plan = S.SddmmPlan(ro, ci, m, n, tau=0.04)  # tiles on these small masks
     assert plan.info()["rest_nnz"] > 0
     Ad = gen.dense(13, 100, gen.S_A, (m, K), dt)
     BT = gen.dense(13, 100, gen.S_BT, (n, K), dt)

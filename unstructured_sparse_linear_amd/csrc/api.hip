@@ -35,7 +35,12 @@ int64_t option(int o) {
 
 namespace {
 
-constexpr double kDefaultTau = 0.04;
+// Default density threshold.  A row (column) is dense at 2% of the
+// columns (remaining rows), but never below one tile's width of entries:
+// on small matrices 2% is close to the mean row length, and such rows would
+// fill the 128-wide tiles far less than the general kernel's gathers.
+constexpr double kDefaultTau = 0.02;
+constexpr int64_t kDefaultMinDense = spops::kSddmmTN;
 
 bool dtype_ok(int d) { return d == SPOPS_F32 || d == SPOPS_F16 || d == SPOPS_BF16; }
 bool itype_ok(int t) { return t == SPOPS_I16 || t == SPOPS_I32; }
@@ -240,7 +245,11 @@ spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hi
   *plan = nullptr;
   spops_status st = check_csr(mask, false, false);
   if (st != SPOPS_OK) return st;
-  if (!(tau > 0.0) || isnan(tau)) tau = kDefaultTau;
+  int64_t min_dense = 1;
+  if (!(tau > 0.0) || isnan(tau)) {
+    tau = kDefaultTau;
+    min_dense = kDefaultMinDense;
+  }
   spops_sddmm_plan* p = new (std::nothrow) spops_sddmm_plan();
   if (!p) return SPOPS_ERR_HIP;
   hipStream_t s = as_stream(hip_stream);
@@ -251,7 +260,8 @@ spops_status spops_sddmm_plan_create(const spops_csr* mask, double tau, void* hi
   if (e == hipSuccess) e = hipMalloc(&scratch, sddmm_plan_scratch_bytes(m, n, nnz));
   if (e == hipSuccess)
     e = enqueue_sddmm_plan(m, n, nnz, mask->row_offsets, mask->col_idx,
-                           mask->col_type == SPOPS_I32, tau, mem, scratch, &p->dev, s);
+                           mask->col_type == SPOPS_I32, tau, min_dense, mem, scratch, &p->dev,
+                           s);
   if (e == hipSuccess) e = fetch_sddmm_plan_counts(&p->dev, s);  // synchronizes s
   else if (scratch) (void)hipStreamSynchronize(s);  // e already holds the failure
   if (scratch) (void)hipFree(scratch);
@@ -476,7 +486,7 @@ spops_status spops_sddmm(const spops_csr* mask, const void* A, int64_t K, int64_
     char* ws = (char*)workspace;
     hipError_t e = enqueue_sddmm_plan(
         mask->rows, mask->cols, mask->nnz, mask->row_offsets, mask->col_idx,
-        mask->col_type == SPOPS_I32, kDefaultTau, ws,
+        mask->col_type == SPOPS_I32, kDefaultTau, kDefaultMinDense, ws,
         ws + align256(sddmm_plan_bytes(mask->rows, mask->cols, mask->nnz)), &P, s);
     if (e == hipSuccess)
       e = launch_sddmm_tiles(P, K, A, lda, BT, ldbt, in_type, out_values, out_type,

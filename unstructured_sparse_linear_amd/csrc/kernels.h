@@ -213,10 +213,11 @@ size_t sddmm_plan_scratch_bytes(int64_t m, int64_t n, int64_t nnz);
 // Enqueues the plan's kernels on s (no allocation, no synchronization): the
 // plan's arrays are carved from `mem` (sddmm_plan_bytes), temporaries from
 // `scratch` (sddmm_plan_scratch_bytes).  Fills *out (counts stay on the
-// device; out->host_ok false).
+// device; out->host_ok false).  A dense row or column also needs at least
+// min_count entries (1 = the tau rule alone).
 hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
-                              const void* col, int col_i32, double tau, void* mem,
-                              void* scratch, SddmmPlanDev* out, hipStream_t s);
+                              const void* col, int col_i32, double tau, int64_t min_count,
+                              void* mem, void* scratch, SddmmPlanDev* out, hipStream_t s);
 // Copies the counts to the host (synchronizes s).
 hipError_t fetch_sddmm_plan_counts(SddmmPlanDev* p, hipStream_t s);
 // Work schedule of the dense tiles for a plan and K, and the fp32 partial

@@ -382,13 +382,15 @@ __global__ void col_count_kernel(const int32_t* ro, const IT* col, int64_t m, in
 }
 
 // A column is dense when, over the mc = m - H other rows, it holds at least
-// ceil(tau * mc) entries (and at least one).
+// max(ceil(tau * mc), min_count) entries (and at least one).
 __global__ void col_flags_kernel(const uint32_t* cnt, int64_t n, int64_t m, double tau,
-                                 const SddmmPlanScalars* sc, uint32_t* flag) {
+                                 int64_t min_count, const SddmmPlanScalars* sc,
+                                 uint32_t* flag) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= n) return;
   const int64_t mc = m - sc->H;
-  const int64_t thr = (int64_t)ceil(tau * (double)mc);
+  int64_t thr = (int64_t)ceil(tau * (double)mc);
+  if (thr < min_count) thr = min_count;
   flag[c] = (mc > 0 && cnt[c] > 0 && (int64_t)cnt[c] >= thr) ? 1u : 0u;
 }
 
@@ -671,8 +673,8 @@ size_t sddmm_plan_scratch_bytes(int64_t m, int64_t n, int64_t nnz) {
 }
 
 hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* ro,
-                              const void* col, int col_i32, double tau, void* mem,
-                              void* scratch, SddmmPlanDev* out, hipStream_t s) {
+                              const void* col, int col_i32, double tau, int64_t min_count,
+                              void* mem, void* scratch, SddmmPlanDev* out, hipStream_t s) {
   *out = SddmmPlanDev{};
   out->m = m;
   out->n = n;
@@ -722,7 +724,8 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
   hipError_t e;
   hipLaunchKernelGGL(plan_init_kernel, dim3(1), dim3(64), 0, s, sc);
   if (m > 0) {
-    const int64_t thr_r = (int64_t)ceil(tau * (double)n);
+    int64_t thr_r = (int64_t)ceil(tau * (double)n);
+    if (thr_r < min_count) thr_r = min_count;
     hipLaunchKernelGGL(row_flags_kernel, dim3(gm), dim3(256), 0, s, ro, m, nnz, thr_r, hot);
     if ((e = exclusive_scan_u32(hot, rrank, m, (uint32_t*)&sc->H, scan_ws, s)) != hipSuccess)
       return e;
@@ -737,7 +740,8 @@ hipError_t enqueue_sddmm_plan(int64_t m, int64_t n, int64_t nnz, const int32_t* 
         hipLaunchKernelGGL(col_count_kernel<int16_t>, dim3(gm16), dim3(256), 0, s, ro,
                            (const int16_t*)col, m, n, nnz, hot, ccnt);
     }
-    hipLaunchKernelGGL(col_flags_kernel, dim3(gn), dim3(256), 0, s, ccnt, n, m, tau, sc, cflag);
+    hipLaunchKernelGGL(col_flags_kernel, dim3(gn), dim3(256), 0, s, ccnt, n, m, tau, min_count,
+                       sc, cflag);
     if ((e = exclusive_scan_u32(cflag, crank, n, (uint32_t*)&sc->Hc, scan_ws, s)) != hipSuccess)
       return e;
     hipLaunchKernelGGL(compact_cols_kernel, dim3(gn), dim3(256), 0, s, cflag, crank, n,
