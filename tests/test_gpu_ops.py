@@ -750,6 +750,36 @@ def test_sddmm_inline_plan_matches_plan(dt, m, n, K, hr, hc):
         assert np.array_equal(host_f64(run_sddmm(M, Ai, Bi, dt, backend)), refi), backend
 
 
+def _dense_counts(M, tau, floor):
+    # the partition rule counted on the host: dense rows first, then dense
+    # columns over the remaining rows
+    rl = np.diff(M.row_offsets.astype(np.int64))
+    hot = rl >= max(int(np.ceil(tau * M.n)), floor)
+    keep = np.repeat(~hot, rl)
+    cc = np.bincount(M.col_idx.astype(np.int64)[keep], minlength=M.n)
+    mc = M.m - int(hot.sum())
+    cthr = max(int(np.ceil(tau * mc)), floor, 1)
+    return int(hot.sum()), int((cc >= cthr).sum()) if mc > 0 else 0
+
+
+def test_sddmm_default_threshold_floor():
+    # default threshold: 2 % of the columns (remaining rows) and at least one
+    # tile's width (128) of entries; an explicit threshold has no floor
+    small = gen.random_csr(41, 512, 512, 0.03, None)     # rows of ~15 entries
+    big = cross_csr(9, 3000, 1300, 300, 300)             # 300 hot rows of ~200
+    for M in (small, big):
+        _, ro, ci = csr_dev(M)
+        d = S.SddmmPlan(ro, ci, M.m, M.n).info()
+        assert (d["dense_rows"], d["dense_cols"]) == _dense_counts(M, 0.02, 128)
+        e = S.SddmmPlan(ro, ci, M.m, M.n, tau=0.02).info()
+        assert (e["dense_rows"], e["dense_cols"]) == _dense_counts(M, 0.02, 1)
+    _, ro, ci = csr_dev(small)
+    assert S.SddmmPlan(ro, ci, 512, 512).info()["tiles"] == 0
+    assert S.SddmmPlan(ro, ci, 512, 512, tau=0.02).info()["dense_rows"] > 0
+    _, ro, ci = csr_dev(big)
+    assert S.SddmmPlan(ro, ci, big.m, big.n).info()["dense_rows"] == 300
+
+
 def test_sddmm_keeps_f16_subnormals():
     m, n, K = 20, 30, 64
     M = gen.random_csr(5, m, n, 0.5, None)
